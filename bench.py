@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the long-context causal attention hot path on one MI355X.
+
+One step is one pass over the whole hot path on one GPU's Ulysses share of a
+Llama-3-8B-shaped layer (32 query / 8 key-value heads, D = 128, N = 32768
+tokens split P = 8 ways), with inputs already resident in HBM:
+
+  1. seq_to_head_relayout of Q, K, V, dO (all P shards)   -- the all-to-all's data movement
+  2. attn_fwd on shard 0 (4 query heads, 1 KV head, causal GQA, N = 32768)
+  3. the ring form of the same forward: 4 partial attn_fwd calls over
+     8192-key blocks (fp32 partials) + attn_partial_merge
+  4. attn_bwd on shard 0 (from step 2's O and LSE)
+  5. head_to_seq_relayout of O, dQ, dK, dV
+
+``value`` is the attention work of the step (forward + ring forward +
+backward, algorithmic flops: masked pairs not counted) divided by the step
+time.  The per-kernel breakdown, the roofline of the dominant kernel and the
+oracle's CPU rate on a bounded sample of the same workload are printed in the
+same JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBPS = 8000.0
+
+
+def fwd_flops(B, Hq, N, D):
+    """Causal forward: 4*D flops per visible (query, key) pair, N(N+1)/2 pairs."""
+    return 2.0 * B * Hq * D * N * (N + 1)
+
+
+def pair_flops_block(Hq, D, N, a, b):
+    """Forward flops of queries 0..N-1 against keys [a, b) (causal, global
+    positions): key j is seen by the N - j queries at or after it."""
+    pairs = (b - a) * N - (b * (b - 1) // 2 - a * (a - 1) // 2)
+    return 4.0 * Hq * D * pairs
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    p.add_argument("--profile-steps", action="store_true", help="short run for rocprofv3 (no CPU leg)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share only: this build runs no collectives, so --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_attention_fwd_amd as lc
+    from long_context_attention_fwd_amd.inputs import WORKLOADS, make_workload_inputs, normal_bf16
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["ulysses_shard_32k"]
+    P, N, D, Hq, Hkv = w.P, w.N, w.D, w.Hq, w.Hkv
+    hq, hkv = Hq // P, Hkv // P  # one shard's heads: 4 and 1
+
+    # ---- inputs, resident in HBM before timing ------------------------------
+    d = make_workload_inputs(w)
+    rng = np.random.default_rng(w.seed + 17)
+    d["do"] = normal_bf16(rng, (P, N // P, Hq, D))
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xs = {k: dev_bf16(v) for k, v in d.items()}
+    del d
+    heads = {"q": torch.empty((P, hq, N, D), dtype=torch.bfloat16, device=dev),
+             "do": torch.empty((P, hq, N, D), dtype=torch.bfloat16, device=dev),
+             "k": torch.empty((P, hkv, N, D), dtype=torch.bfloat16, device=dev),
+             "v": torch.empty((P, hkv, N, D), dtype=torch.bfloat16, device=dev)}
+    # token-major outputs of the inverse relayout.  Shard 0's results are
+    # written straight into slot 0 of the head-major buffers; the inverse
+    # relayout moves all P shards' bytes, as the exchange would.
+    o_all = torch.zeros((P, hq, N, D), dtype=torch.bfloat16, device=dev)
+    dq_all = torch.zeros_like(o_all)
+    dk_all = torch.zeros((P, hkv, N, D), dtype=torch.bfloat16, device=dev)
+    dv_all = torch.zeros_like(dk_all)
+    o, dq, dk, dv = o_all[0:1], dq_all[0:1], dk_all[0:1], dv_all[0:1]
+    lse = torch.empty((1, hq, N), dtype=torch.float32, device=dev)
+    o_tok = torch.empty((P, N // P, Hq, D), dtype=torch.bfloat16, device=dev)
+    dq_tok = torch.empty_like(o_tok)
+    dk_tok = torch.empty((P, N // P, Hkv, D), dtype=torch.bfloat16, device=dev)
+    dv_tok = torch.empty_like(dk_tok)
+    n_blk = 4
+    blk = N // n_blk
+    o_parts = torch.empty((n_blk, 1, hq, N, D), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((n_blk, 1, hq, N), dtype=torch.float32, device=dev)
+    o_ring = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
+    lse_ring = torch.empty_like(lse)
+    ws = torch.empty(lc.attn_bwd_workspace_size(1, hq, hkv, N, D), dtype=torch.uint8, device=dev)
+    scale = w.scale
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["relayout_in", "fwd", "ring_partials", "merge", "bwd", "relayout_out"]
+    ev = {n: [] for n in names}
+
+    def step(record):
+        marks = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
+
+        mark()
+        for n in ("q", "k", "v", "do"):
+            lc.seq_to_head_relayout(xs[n], P, out=heads[n])
+        mark()
+        q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
+        lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
+        mark()
+        for i, a in enumerate(range(0, N, blk)):
+            # one ring step: the queries against KV block [a, a + blk)
+            lc.attn_fwd(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], causal=True, scale=scale, k_pos0=a,
+                        out_dtype=torch.float32, o=o_parts[i], lse=lse_parts[i])
+        mark()
+        lc.attn_partial_merge(o_parts, lse_parts, o=o_ring, lse=lse_ring)
+        mark()
+        lc.attn_bwd(q0, k0, v0, o, do0, lse, causal=True, scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        mark()
+        lc.head_to_seq_relayout(o_all, P, out=o_tok)
+        lc.head_to_seq_relayout(dq_all, P, out=dq_tok)
+        lc.head_to_seq_relayout(dk_all, P, out=dk_tok)
+        lc.head_to_seq_relayout(dv_all, P, out=dv_tok)
+        mark()
+        return marks
+
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    all_marks = []
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        all_marks.append(step(True))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    per = {n: 0.0 for n in names}
+    for marks in all_marks:
+        for i, n in enumerate(names):
+            per[n] += marks[i].elapsed_time(marks[i + 1])
+    per = {n: v / args.steps for n, v in per.items()}
+
+    B = 1
+    f_fwd = fwd_flops(B, hq, N, D)
+    f_ring = sum(pair_flops_block(hq, D, N, a, a + blk) for a in range(0, N, blk))
+    f_bwd = 2.5 * f_fwd
+    attn_flops = f_fwd + f_ring + f_bwd
+    relayout_in_bytes = 2 * 2 * (xs["q"].numel() + xs["k"].numel() + xs["v"].numel() + xs["do"].numel())
+    relayout_out_bytes = 2 * 2 * (o_all.numel() + dq_all.numel() + dk_all.numel() + dv_all.numel())
+    merge_bytes = o_parts.numel() * 4 + lse_parts.numel() * 4 + o_ring.numel() * 2 + lse_ring.numel() * 4
+
+    def tflops(f, ms):
+        return f / (ms * 1e-3) / 1e12
+
+    def gbps(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    kernels = {
+        "fwd": {"ms": per["fwd"], "TFLOP/s": tflops(f_fwd, per["fwd"]),
+                "frac_peak": tflops(f_fwd, per["fwd"]) / PEAK_BF16_TFLOPS},
+        "ring_partials_x4": {"ms": per["ring_partials"], "TFLOP/s": tflops(f_ring, per["ring_partials"]),
+                             "frac_peak": tflops(f_ring, per["ring_partials"]) / PEAK_BF16_TFLOPS},
+        "merge": {"ms": per["merge"], "GB/s": gbps(merge_bytes, per["merge"]),
+                  "frac_peak": gbps(merge_bytes, per["merge"]) / PEAK_HBM_GBPS},
+        "bwd": {"ms": per["bwd"], "TFLOP/s": tflops(f_bwd, per["bwd"]),
+                "frac_peak": tflops(f_bwd, per["bwd"]) / PEAK_BF16_TFLOPS},
+        "relayout_seq_to_head_qkvdo": {"ms": per["relayout_in"], "GB/s": gbps(relayout_in_bytes, per["relayout_in"]),
+                                       "frac_peak": gbps(relayout_in_bytes, per["relayout_in"]) / PEAK_HBM_GBPS},
+        "relayout_head_to_seq_o_grads": {"ms": per["relayout_out"],
+                                         "GB/s": gbps(relayout_out_bytes, per["relayout_out"]),
+                                         "frac_peak": gbps(relayout_out_bytes, per["relayout_out"]) / PEAK_HBM_GBPS},
+    }
+    # dominant kernel of the step: the largest share of its time
+    dom = max(("fwd", "bwd"), key=lambda n: per[n])
+    dom_flops = f_fwd if dom == "fwd" else f_bwd
+    achieved = tflops(dom_flops, per[dom])
+    roofline = {"bound": "mfma", "kernel": "attn_fwd" if dom == "fwd" else "attn_bwd",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": dom_flops}
+
+    out = {
+        "metric": "causal attention TFLOP/s fwd/bwd at 1 GPU + % bf16 MFMA peak; relayout GB/s",
+        "value": round(tflops(attn_flops, ms_step), 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 (numpy PCG64), no dataset or weights",
+        "config": {"workload": w.name, "P": P, "N": N, "Hq_total": Hq, "Hkv_total": Hkv, "D": D,
+                   "shard_heads_q": hq, "shard_heads_kv": hkv, "causal": True, "ring_blocks": n_blk,
+                   "step": "relayout q,k,v,dO -> fwd -> 4 partial fwd + merge -> bwd -> relayout o,dq,dk,dv"},
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "roofline": roofline,
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+    if not args.no_cpu_baseline and not args.profile_steps:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same shard:
+    forward attention of the last rows of shard 0 (4 query heads, 1 KV head),
+    in chunks of 256 rows until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    from long_context_attention_fwd_amd.inputs import make_workload_inputs
+
+    d = make_workload_inputs(w)
+    ref = {n: oracle.seq_to_head(d[n], w.P)[0:1] for n in "qkv"}
+    N, D, hq = w.N, w.D, w.Hq // w.P
+    done_rows, flops, t_used = 0, 0.0, 0.0
+    end = N
+    while t_used < budget_s and end > 0:
+        rows = np.arange(max(0, end - 256), end)
+        t0 = time.perf_counter()
+        oracle.attention_forward(ref["q"], ref["k"], ref["v"], w.scale, True, rows=rows)
+        t_used += time.perf_counter() - t0
+        flops += 4.0 * hq * D * float((rows + 1).sum())
+        done_rows += len(rows)
+        end -= 256
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 forward of the last {done_rows} query rows x {hq} heads of shard 0 "
+                      f"(N={N}, D={D}); {t_used:.1f} s of CPU work",
+            "seconds": round(t_used, 2)}
+
+
+if __name__ == "__main__":
+    main()

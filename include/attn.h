@@ -1,0 +1,149 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) long-context causal attention library.
+ *
+ * What it computes.  Exact scaled-dot-product attention with a causal mask,
+ * O = softmax(scale * Q K^T + mask) V, plus the per-row log-sum-exp (natural
+ * log) of the scaled, masked scores.  This is the call the example program on
+ * the "Context Parallelism" glossary page (Ultralytics, German edition,
+ * section "Praktische Anwendung und Kompromisse") makes on [batch, heads,
+ * sequence, head_dim] bf16 tensors with the causal flag set, followed by a
+ * backward pass of a loss of the output.  The ring form (partial attention
+ * against one KV block, then a combine that equals full attention) is from the
+ * same page, section "So funktioniert Kontextparallelität"; the sequence-to-
+ * head exchange is the Ulysses all-to-all of "Million-Token-Kontexte im
+ * Training ..." (section "Ulysses: Die Sequenz als Verteilungseinheit") and of
+ * "Ulysses Sequence Parallelism: как тренировать модели с контекстом в миллион
+ * токенов" (section "Как работает Ulysses: технические детали"), carried out on
+ * one GPU.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers are device pointers (hipMalloc / torch CUDA tensors), 16-byte
+ *    aligned, all tensors contiguous row-major in the layouts stated below.
+ *  - bf16 tensors hold raw bfloat16 words; LSE and fp32 tensors hold float.
+ *  - Ownership: the caller owns every buffer, including the backward
+ *    workspace.  The library allocates and frees no device memory and keeps no
+ *    global state apart from a thread-local error text.
+ *  - Asynchrony: each call validates its arguments on the host, then enqueues
+ *    its kernels on `hip_stream` (a hipStream_t; NULL = the default stream)
+ *    and returns.  A validation failure returns a nonzero status before
+ *    anything is launched and leaves the outputs untouched.  A launch failure
+ *    returns ATTN_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Every element of every output is written, including masked rows.
+ *  - Inputs and outputs must not overlap.
+ */
+#ifndef LCATTN_ATTN_H
+#define LCATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is <= 0 or sizes are inconsistent */
+  ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. D not 64/128) */
+  ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  ATTN_ERR_ALIAS = 5,       /* an output overlaps an input */
+  ATTN_ERR_WORKSPACE = 6,   /* backward workspace missing or too small */
+  ATTN_ERR_HIP = 7          /* the HIP runtime reported an error */
+};
+
+enum { ATTN_BF16 = 0, ATTN_FP32 = 1 };
+
+/*
+ * attn_fwd -- fused causal attention forward with per-row log-sum-exp.
+ *
+ * q    [B, Hq,  Nq, D] bf16       k, v [B, Hkv, Nk, D] bf16
+ * o    [B, Hq,  Nq, D] bf16 (o_dtype = ATTN_BF16) or float (ATTN_FP32)
+ * lse  [B, Hq,  Nq]    float, natural log of sum_j exp(S_ij)
+ *
+ * S_ij = scale * <q_i, k_j>.  With causal != 0, key j is visible to query i
+ * iff k_pos0 + j <= q_pos0 + i (global token positions), so a call with a KV
+ * sub-range and its offsets is one ring step's partial attention.  Query head
+ * h reads key/value head h / (Hq / Hkv) (grouped-query attention).  A row
+ * with no visible key gets o = 0 and lse = -inf.  fp32 o keeps partial results
+ * unrounded for attn_partial_merge.
+ *
+ * Requires B, Hq, Hkv, Nq, Nk >= 1; Hkv divides Hq; D in {64, 128};
+ * q_pos0, k_pos0 >= 0; scale finite.  Deterministic: repeated calls give
+ * bit-identical outputs.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+             int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal,
+             int64_t q_pos0, int64_t k_pos0, void* hip_stream);
+
+/*
+ * attn_partial_merge -- log-sum-exp merge of partial attention results.
+ *
+ * o_parts   [n_parts, B, H, N, D] bf16 or float (part_dtype)
+ * lse_parts [n_parts, B, H, N]    float
+ * o         [B, H, N, D] bf16,  lse [B, H, N] float
+ *
+ * Part b must be attention of the same queries over a block of keys, the
+ * blocks being disjoint.  Then LSE = M + ln sum_b exp(LSE_b - M) with
+ * M = max_b LSE_b, and O = sum_b exp(LSE_b - LSE) O_b, which is attention
+ * over the union of the blocks ("So funktioniert Kontextparallelität": the
+ * ring result equals full attention).  Parts with LSE_b = -inf weigh zero;
+ * a row empty in every part gives o = 0, lse = -inf.  Requires n_parts >= 1,
+ * D in {64, 128}.
+ */
+int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_parts, int n_parts,
+                       void* o, float* lse, int B, int H, int64_t N, int D, void* hip_stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs
+ * (per-row <dO, O> in fp32).  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
+
+/*
+ * attn_bwd -- gradients of sum(O * dO) with respect to q, k and v.
+ *
+ * q, o, d_o, dq [B, Hq, N, D] bf16;  k, v, dk, dv [B, Hkv, N, D] bf16;
+ * lse [B, Hq, N] float from attn_fwd on the same inputs (Nq = Nk = N, equal
+ * offsets).  P is recomputed from q, k and lse; with Dv_i = <dO_i, O_i>,
+ * dS = P * (dO V^T - Dv), dq = scale dS K, dk = scale dS^T Q, dv = P^T dO,
+ * accumulated in fp32 and rounded once to bf16.  For grouped-query attention
+ * dk, dv of a key/value head sum over the query heads that read it.  The
+ * workspace (caller-owned, >= attn_bwd_workspace_size bytes, 16-byte aligned)
+ * is scratch; its contents on return are unspecified.  The glossary example
+ * backpropagates the mean of O^2, i.e. d_o = 2 O / numel.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+             int B, int Hq, int Hkv, int64_t N, int D, float scale, int causal, void* hip_stream);
+
+/*
+ * seq_to_head_relayout -- the Ulysses all-to-all's data movement on one GPU.
+ *
+ * in  [P, N/P, H, D]: shard p holds tokens p*N/P .. (p+1)*N/P - 1, all heads.
+ * out [P, H/P, N, D]: rank r holds heads r*H/P .. (r+1)*H/P - 1, all tokens.
+ * out[r, h', n, :] = in[n / (N/P), n % (N/P), r*(H/P) + h', :] -- the
+ * transpose [N, H, D] -> [H, N, D].  A bit copy of elem_bytes-wide words
+ * (2 for bf16, 4 for float).  Requires P | N, P | H (H >= P), D*elem_bytes a
+ * multiple of 16; in and out must not overlap.  For key/value tensors pass
+ * H = Hkv.
+ */
+int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
+                         void* hip_stream);
+
+/* head_to_seq_relayout -- the inverse: in [P, H/P, N, D] -> out [P, N/P, H, D]. */
+int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
+                         void* hip_stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Detail of the calling thread's last failure ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCATTN_ATTN_H */

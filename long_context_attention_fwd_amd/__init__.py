@@ -1,0 +1,239 @@
+"""MI355X-native long-context causal attention: Python binding of ``libattn.so``.
+
+The binding only marshals arguments: it checks dtypes, shapes, contiguity and
+devices of torch tensors, allocates outputs with torch when the caller did not
+pass them, and calls the C ABI declared in ``include/attn.h`` on torch's
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path.  If the library is missing, every call
+raises.
+
+Layouts follow the PyTorch call on the "Context Parallelism" glossary page
+(Ultralytics, "Praktische Anwendung und Kompromisse"): ``[B, H, N, D]`` with
+the sequence on dimension 2.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = [
+    "attn_fwd",
+    "attn_partial_merge",
+    "attn_bwd",
+    "attn_bwd_workspace_size",
+    "seq_to_head_relayout",
+    "head_to_seq_relayout",
+    "AttnError",
+    "lib",
+    "LIB_PATH",
+    "ATTN_BF16",
+    "ATTN_FP32",
+    "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_BF16, ATTN_FP32 = 0, 1
+STATUS = {
+    0: "ATTN_OK",
+    1: "ATTN_ERR_NULL",
+    2: "ATTN_ERR_SHAPE",
+    3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_ALIGN",
+    5: "ATTN_ERR_ALIAS",
+    6: "ATTN_ERR_WORKSPACE",
+    7: "ATTN_ERR_HIP",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_F = ctypes.c_float
+_SIGS = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P]),
+    "attn_partial_merge": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _L, _I, _P]),
+    "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
+    "seq_to_head_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
+    "head_to_seq_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_last_error": (ctypes.c_char_p, []),
+}
+
+
+class AttnError(RuntimeError):
+    """A nonzero status returned by the library."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types set (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m long_context_attention_fwd_amd.build`")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, lib().attn_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name, dtype=None, dims=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
+
+
+def attn_fwd(q, k, v, *, causal: bool = True, scale: float | None = None, q_pos0: int = 0, k_pos0: int = 0,
+             out_dtype=None, o=None, lse=None):
+    """Causal attention forward: returns (o [B,Hq,Nq,D], lse [B,Hq,Nq] float32).
+
+    q [B, Hq, Nq, D] bf16; k, v [B, Hkv, Nk, D] bf16.  ``out_dtype`` is
+    bfloat16 (default) or float32 (unrounded partials for the merge).
+    """
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if o is None:
+        o = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q.device)
+    _need(o, "o", out_dtype, 4)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Hq, Nq, D) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("o / lse have the wrong shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          ATTN_FP32 if out_dtype == torch.float32 else ATTN_BF16, lse.data_ptr(),
+                          B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, q_pos0, k_pos0, _stream(q)))
+    return o, lse
+
+
+def attn_partial_merge(o_parts, lse_parts, *, o=None, lse=None):
+    """Merge partials over disjoint key blocks: o_parts [n,B,H,N,D] (bf16 or
+    float32), lse_parts [n,B,H,N] float32 -> (o [B,H,N,D] bf16, lse [B,H,N])."""
+    torch = _torch()
+    _need(o_parts, "o_parts", (torch.bfloat16, torch.float32), 5)
+    _need(lse_parts, "lse_parts", torch.float32, 4)
+    n, B, H, N, D = o_parts.shape
+    if tuple(lse_parts.shape) != (n, B, H, N):
+        raise ValueError("lse_parts must be [n, B, H, N] matching o_parts")
+    if o is None:
+        o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    _need(o, "o", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    pd = ATTN_FP32 if o_parts.dtype == torch.float32 else ATTN_BF16
+    _check(lib().attn_partial_merge(o_parts.data_ptr(), pd, lse_parts.data_ptr(), n, o.data_ptr(), lse.data_ptr(),
+                                    B, H, N, D, _stream(o_parts)))
+    return o, lse
+
+
+def attn_bwd_workspace_size(B: int, Hq: int, Hkv: int, N: int, D: int) -> int:
+    return int(lib().attn_bwd_workspace_size(B, Hq, Hkv, N, D))
+
+
+def attn_bwd(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = None, workspace=None,
+             dq=None, dk=None, dv=None):
+    """Gradients of sum(o * do): returns (dq, dk, dv) as bf16, shaped like q, k, v."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _need(t, name, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must be shaped like q")
+    if tuple(k.shape) != (B, Hkv, N, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, N, D]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_size(B, Hq, Hkv, N, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D, scale,
+                          1 if causal else 0, _stream(q)))
+    return dq, dk, dv
+
+
+def _relayout(fn_name, x, P, out, to_head):
+    torch = _torch()
+    _need(x, "x", None, 4)
+    if x.dtype not in (torch.bfloat16, torch.float16, torch.float32, torch.int16):
+        raise TypeError("relayout supports 2- and 4-byte elements")
+    eb = x.element_size()
+    if to_head:
+        Pp, T, H, D = x.shape
+        N = Pp * T
+        shape = (Pp, H // Pp if Pp else 0, N, D)
+    else:
+        Pp, Hp, N, D = x.shape
+        H = Pp * Hp
+        shape = (Pp, N // Pp if Pp else 0, H, D)
+    if Pp != P:
+        raise ValueError(f"leading dimension must be P={P}")
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, 4)
+    _check(getattr(lib(), fn_name)(x.data_ptr(), out.data_ptr(), P, N, H, D, eb, _stream(x)))
+    return out
+
+
+def seq_to_head_relayout(x, P: int, *, out=None):
+    """[P, N/P, H, D] -> [P, H/P, N, D] (bit copy)."""
+    return _relayout("seq_to_head_relayout", x, P, out, True)
+
+
+def head_to_seq_relayout(y, P: int, *, out=None):
+    """[P, H/P, N, D] -> [P, N/P, H, D] (bit copy)."""
+    return _relayout("head_to_seq_relayout", y, P, out, False)

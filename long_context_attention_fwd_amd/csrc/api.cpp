@@ -1,0 +1,254 @@
+// api.cpp -- the library's C ABI: argument validation, dispatch, status codes.
+//
+// Every entry point validates on the host first and returns a status without
+// touching the GPU when validation fails, so the error paths are testable on a
+// machine without a GPU.  Kernels are enqueued on the caller's stream; the
+// library allocates nothing and keeps no state except a thread-local error
+// text.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Checked product of non-negative sizes; false on overflow of int64.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool elems(int64_t* out, std::initializer_list<int64_t> dims) {
+  int64_t n = 1;
+  for (int64_t d : dims)
+    if (!mul_ok(n, d, &n)) return false;
+  *out = n;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "invalid shape";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ATTN_ERR_ALIAS: return "output overlaps input";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int Hq,
+             int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0, int64_t k_pos0,
+             void* hip_stream) {
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "attn_fwd: q, k, v, o and lse must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || D < 1)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%lld Nk=%lld D=%d)", B, Hq,
+                Hkv, (long long)Nq, (long long)Nk, D);
+  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "attn_fwd: Hkv=%d does not divide Hq=%d", Hkv, Hq);
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(ATTN_ERR_SHAPE, "attn_fwd: position offsets must be >= 0");
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: D=%d (supported: 64, 128)", D);
+  if (o_dtype != ATTN_BF16 && o_dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: o_dtype=%d (ATTN_BF16 or ATTN_FP32)", o_dtype);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: scale must be finite and > 0");
+  if (Hq / Hkv > 1 && Hq > 65535 * 4) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: too many heads");
+  int64_t nq_el, nk_el, nl;
+  if (!elems(&nq_el, {B, Hq, Nq, D}) || !elems(&nk_el, {B, Hkv, Nk, D}) || !elems(&nl, {B, Hq, Nq}) ||
+      nq_el > (INT64_MAX / 8))
+    return fail(ATTN_ERR_SHAPE, "attn_fwd: tensor sizes overflow");
+  if ((Nq + 31) / 32 > INT32_MAX || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(ATTN_ERR_ALIGN, "attn_fwd: pointers must be 16-byte aligned");
+  const size_t ob = (size_t)nq_el * (o_dtype == ATTN_FP32 ? 4 : 2);
+  const size_t lb = (size_t)nl * 4;
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2};
+  for (int i = 0; i < 3; ++i)
+    if (overlap(o, ob, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]))
+      return fail(ATTN_ERR_ALIAS, "attn_fwd: outputs overlap inputs");
+  if (overlap(o, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "attn_fwd: o overlaps lse");
+
+  lcattn::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.lse = lse;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal ? 1 : 0;
+  a.q_pos0 = q_pos0;
+  a.k_pos0 = k_pos0;
+  return hip_status(lcattn::launch_attn_fwd(a, B, D, o_dtype == ATTN_FP32, static_cast<hipStream_t>(hip_stream)),
+                    "attn_fwd launch");
+}
+
+int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_parts, int n_parts, void* o,
+                       float* lse, int B, int H, int64_t N, int D, void* hip_stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return fail(ATTN_ERR_NULL, "attn_partial_merge: null pointer");
+  if (n_parts < 1 || B < 1 || H < 1 || N < 1 || D < 1)
+    return fail(ATTN_ERR_SHAPE, "attn_partial_merge: sizes and n_parts must be >= 1");
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_partial_merge: D=%d (supported: 64, 128)", D);
+  if (part_dtype != ATTN_BF16 && part_dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_partial_merge: part_dtype=%d", part_dtype);
+  int64_t rows, parts_el, out_el;
+  if (!elems(&rows, {B, H, N}) || !elems(&parts_el, {n_parts, rows, D}) || !elems(&out_el, {rows, D}) ||
+      parts_el > INT64_MAX / 8 || (rows * (D / 8) + 255) / 256 > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "attn_partial_merge: tensor sizes overflow");
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
+    return fail(ATTN_ERR_ALIGN, "attn_partial_merge: pointers must be 16-byte aligned");
+  const size_t pb = (size_t)parts_el * (part_dtype == ATTN_FP32 ? 4 : 2);
+  const size_t plb = (size_t)n_parts * rows * 4, ob = (size_t)out_el * 2, lb = (size_t)rows * 4;
+  if (overlap(o, ob, o_parts, pb) || overlap(o, ob, lse_parts, plb) || overlap(lse, lb, o_parts, pb) ||
+      overlap(lse, lb, lse_parts, plb) || overlap(o, ob, lse, lb))
+    return fail(ATTN_ERR_ALIAS, "attn_partial_merge: outputs overlap inputs");
+  return hip_status(lcattn::launch_partial_merge(o_parts, part_dtype == ATTN_FP32, lse_parts, n_parts,
+                                                 static_cast<uint16_t*>(o), lse, rows, D,
+                                                 static_cast<hipStream_t>(hip_stream)),
+                    "attn_partial_merge launch");
+}
+
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv) return 0;
+  int64_t rows;
+  if (!elems(&rows, {B, Hq, N}) || rows > INT64_MAX / 8) return 0;
+  // per-row <dO, O> in fp32, rounded up to 256 bytes
+  return (size_t)((rows * 4 + 255) / 256 * 256);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+             int64_t N, int D, float scale, int causal, void* hip_stream) {
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv)
+    return fail(ATTN_ERR_NULL, "attn_bwd: tensor pointers must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "attn_bwd: sizes must be >= 1");
+  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "attn_bwd: Hkv=%d does not divide Hq=%d", Hkv, Hq);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: D=%d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: scale must be > 0");
+  int64_t nq_el, nk_el, nl;
+  if (!elems(&nq_el, {B, Hq, N, D}) || !elems(&nk_el, {B, Hkv, N, D}) || !elems(&nl, {B, Hq, N}) ||
+      nq_el > INT64_MAX / 8 || (N + 31) / 32 > INT32_MAX || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_SHAPE, "attn_bwd: tensor sizes overflow");
+  const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, N, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "attn_bwd: workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  const void* ptrs[11] = {q, k, v, o, d_o, lse, dq, dk, dv, workspace, nullptr};
+  for (int i = 0; i < 10; ++i)
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_ALIGN, "attn_bwd: pointers must be 16-byte aligned");
+  const size_t qb = (size_t)nq_el * 2, kb = (size_t)nk_el * 2, lb = (size_t)nl * 4;
+  const void* ins[6] = {q, k, v, o, d_o, lse};
+  const size_t inb[6] = {qb, kb, kb, qb, qb, lb};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t outb[4] = {qb, kb, kb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outb[i], ins[j], inb[j])) return fail(ATTN_ERR_ALIAS, "attn_bwd: outputs overlap inputs");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return fail(ATTN_ERR_ALIAS, "attn_bwd: outputs overlap");
+  }
+  lcattn::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(workspace);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.N = N;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd launch");
+}
+
+static int relayout(const char* name, bool to_head, const void* in, void* out, int P, int64_t N, int H, int D,
+                    int elem_bytes, void* hip_stream) {
+  if (!in || !out) return fail(ATTN_ERR_NULL, "%s: null pointer", name);
+  if (P < 1 || N < 1 || H < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
+  if (N % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide N=%lld", name, P, (long long)N);
+  if (H < P) return fail(ATTN_ERR_UNSUPPORTED, "%s: H=%d < P=%d needs head replication", name, H, P);
+  if (H % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide H=%d", name, P, H);
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(ATTN_ERR_UNSUPPORTED, "%s: elem_bytes must be 2 or 4", name);
+  const int64_t row_bytes = (int64_t)D * elem_bytes;
+  if (row_bytes % 16 || ((row_bytes / 16) & (row_bytes / 16 - 1)))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: D*elem_bytes=%lld must be 16 times a power of two", name,
+                (long long)row_bytes);
+  int64_t units;
+  if (!elems(&units, {N, H, row_bytes / 16}) || units >= (int64_t(1) << 32))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: tensor has 2^32 or more 16-byte units", name);
+  if (!aligned16(in) || !aligned16(out)) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
+  const size_t bytes = (size_t)units * 16;
+  if (overlap(in, bytes, out, bytes)) return fail(ATTN_ERR_ALIAS, "%s: in and out overlap", name);
+  // seq->head: out[h][n] = in[n][h] (A = H, Bn = N); head->seq: out[n][h] = in[h][n].
+  const unsigned A = to_head ? (unsigned)H : (unsigned)N;
+  const unsigned Bn = to_head ? (unsigned)N : (unsigned)H;
+  return hip_status(
+      lcattn::launch_transpose_rows(in, out, A, Bn, (unsigned)row_bytes, static_cast<hipStream_t>(hip_stream)),
+      name);
+}
+
+int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
+                         void* hip_stream) {
+  return relayout("seq_to_head_relayout", true, in, out, P, N, H, D, elem_bytes, hip_stream);
+}
+
+int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
+                         void* hip_stream) {
+  return relayout("head_to_seq_relayout", false, in, out, P, N, H, D, elem_bytes, hip_stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal to the library).
+//
+// Each launcher assumes its arguments were validated by api.cpp: pointers are
+// device pointers, aligned, sized and non-overlapping as the public header
+// states, and every size fits the index arithmetic of the kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcattn {
+
+// out[a, b, :] = in[b, a, :], rows of row_bytes (a power-of-two multiple of 16).
+hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned Bn, unsigned row_bytes,
+                                 hipStream_t stream);
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  int Hq, Hkv, G;
+  long long Nq, Nk;
+  float scale_log2;  // softmax scale times log2(e)
+  int causal;
+  long long q_pos0, k_pos0;
+};
+
+hipError_t launch_attn_fwd(const FwdArgs& a, int B, int D, bool out_f32, hipStream_t stream);
+
+hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
+                                uint16_t* o, float* lse, long long rows, int D, hipStream_t stream);
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* d_o;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;  // workspace: <dO_i, O_i> per query row
+  int Hq, Hkv, G;
+  long long N;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream);
+
+}  // namespace lcattn

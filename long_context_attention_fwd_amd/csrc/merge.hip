@@ -1,0 +1,92 @@
+// merge.hip -- log-sum-exp merge of partial attention results.
+//
+// "Context Parallelism" (Ultralytics glossary), section "So funktioniert
+// Kontextparallelität": in ring attention each device computes partial
+// attention of its queries against one KV block at a time, and the combined
+// result equals attention over the whole sequence.  For disjoint key blocks b
+// with partial output O_b and log-sum-exp LSE_b, the softmax over the union
+// renormalises by the summed exponentials:
+//   LSE = M + ln sum_b exp(LSE_b - M),  M = max_b LSE_b,
+//   O   = sum_b exp(LSE_b - LSE) O_b.
+// Parts with LSE_b = -inf weigh zero; rows empty in every part give O = 0,
+// LSE = -inf.
+//
+// Kernel: HBM bound.  One thread per (row, 8 consecutive head-dim elements);
+// the n_parts LSE values of a row are read by all of the row's threads (they
+// hit in cache), then n_parts 16- or 32-byte slices are streamed and one
+// 16-byte bf16 slice is written.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace lcattn {
+
+constexpr int kMergeThreads = 256;
+
+template <int D, bool PART_F32>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const void* __restrict__ o_parts,
+                                                              const float* __restrict__ lse_parts,
+                                                              int n_parts, long long rows,
+                                                              uint16_t* __restrict__ o,
+                                                              float* __restrict__ lse) {
+  constexpr int U = D / 8;  // 8-element slices per row
+  const long long idx = (long long)blockIdx.x * kMergeThreads + threadIdx.x;
+  const long long row = idx / U;
+  const int u = (int)(idx % U);
+  if (row >= rows) return;
+
+  float m = -INFINITY;
+  for (int b = 0; b < n_parts; ++b) m = fmaxf(m, lse_parts[(long long)b * rows + row]);
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float out_lse = -INFINITY;
+  if (m != -INFINITY) {
+    float tot = 0.f;
+    for (int b = 0; b < n_parts; ++b) tot += fast_exp2((lse_parts[(long long)b * rows + row] - m) * kLog2e);
+    const float inv = 1.0f / tot;
+    out_lse = m + fast_log2(tot) * kLn2;
+    for (int b = 0; b < n_parts; ++b) {
+      const float lb = lse_parts[(long long)b * rows + row];
+      const float w = fast_exp2((lb - m) * kLog2e) * inv;
+      if (w == 0.f) continue;  // empty part (LSE = -inf) or negligible weight
+      const long long off = ((long long)b * rows + row) * D + 8 * u;
+      if (PART_F32) {
+        const float* p = static_cast<const float*>(o_parts) + off;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += w * x0[e];
+          acc[4 + e] += w * x1[e];
+        }
+      } else {
+        const u32x4 x = ld_global16(static_cast<const uint16_t*>(o_parts) + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w * __uint_as_float(x[e] << 16);
+          acc[2 * e + 1] += w * __uint_as_float(x[e] & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+  const bf16x8 r = pack_bf16x8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7]);
+  st_global16(o + row * D + 8 * u, as_u32x4(r));
+  if (u == 0) lse[row] = out_lse;
+}
+
+hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
+                                uint16_t* o, float* lse, long long rows, int D, hipStream_t stream) {
+  const long long threads = rows * (D / 8);
+  const unsigned blocks = (unsigned)((threads + kMergeThreads - 1) / kMergeThreads);
+#define LCATTN_MERGE(DD, F32)                                                                      \
+  hipLaunchKernelGGL((merge_kernel<DD, F32>), dim3(blocks), dim3(kMergeThreads), 0, stream, o_parts, \
+                     lse_parts, n_parts, rows, o, lse)
+  if (D == 64) {
+    if (parts_f32) LCATTN_MERGE(64, true); else LCATTN_MERGE(64, false);
+  } else {
+    if (parts_f32) LCATTN_MERGE(128, true); else LCATTN_MERGE(128, false);
+  }
+#undef LCATTN_MERGE
+  return hipGetLastError();
+}
+
+}  // namespace lcattn

@@ -63,7 +63,8 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        return float(np.float32(1.0) / np.sqrt(np.float32(self.D)))
+        # SDPA's default 1/sqrt(D), as the fp32 value handed to the kernel
+        return float(np.float32(1.0 / np.sqrt(float(self.D))))
 
 
 WORKLOADS = {

@@ -19,6 +19,7 @@ from .attention import (  # noqa: F401
     lse_merge,
     attention_backward,
     attention_backward_sampled,
+    attention_backward_row_support,
     seq_to_head,
     head_to_seq,
 )

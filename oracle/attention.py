@@ -52,6 +52,7 @@ __all__ = [
     "lse_merge",
     "attention_backward",
     "attention_backward_sampled",
+    "attention_backward_row_support",
     "seq_to_head",
     "head_to_seq",
 ]
@@ -321,6 +322,47 @@ def attention_backward_sampled(q, k, v, do, scale, q_rows, kv_rows, causal=True,
                 dS = P * (do[b, h, rb] @ v[b, kh, kv_rows].T - dv[b, h, rb][:, None])
                 dK[b, kh] += s * (dS.T @ q[b, h, rb])
                 dV[b, kh] += P.T @ do[b, h, rb]
+    return dQ, dK, dV
+
+
+def attention_backward_row_support(q, k, v, do, scale, support, kv_rows=None, causal=True):
+    """Exact gradients when dO is zero outside the query rows ``support``.
+
+    Gradients are linear in dO, and a row i with dO_i = 0 has Dv_i = 0 and
+    dP_ij = 0, so it adds nothing to any of dQ, dK, dV.  Every sum then runs
+    over the support rows only, which need only their own LSE and Dv.
+    Returns (dQ [B,Hq,|support|,D], dK [B,Hkv,R,D], dV [B,Hkv,R,D]) with R the
+    key rows ``kv_rows`` (all keys by default).
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, Hq, Hkv, D = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    N = q.shape[2]
+    support = np.asarray(support, dtype=np.int64)
+    outside = np.ones(N, dtype=bool)
+    outside[support] = False
+    if np.any(do[:, :, outside] != 0):
+        raise ValueError("dO must be zero outside the support rows")
+    kv_rows = np.arange(N, dtype=np.int64) if kv_rows is None else np.asarray(kv_rows, dtype=np.int64)
+    s = np.float64(scale)
+    O, L = attention_forward(q, k, v, scale, causal, rows=support)
+    dQ = np.zeros((B, Hq, len(support), D))
+    dK = np.zeros((B, Hkv, len(kv_rows), D))
+    dV = np.zeros((B, Hkv, len(kv_rows), D))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // G
+            dor = do[b, h, support]
+            Dv = np.einsum("nd,nd->n", dor, O[b, h])
+            S = scores(q[b, h, support], k[b, kh], scale, causal, support, 0)
+            P = np.exp(S - L[b, h][:, None])
+            dS = P * (dor @ v[b, kh].T - Dv[:, None])
+            dQ[b, h] = s * (dS @ k[b, kh])
+            dK[b, kh] += s * (dS[:, kv_rows].T @ q[b, h, support])
+            dV[b, kh] += P[:, kv_rows].T @ dor
     return dQ, dK, dV
 
 

@@ -1,0 +1,131 @@
+"""The C ABI: the library loads, exports every function include/attn.h declares,
+and rejects bad arguments on the host before touching the GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_fwd_amd as lc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 0x100000  # 16-byte aligned fake device addresses: never dereferenced on error paths
+B_ = 0x10000000
+C_ = 0x20000000
+D_ = 0x30000000
+E_ = 0x40000000
+F_ = 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lc.LIB_PATH):
+        pytest.fail("libattn.so is not built (python -m long_context_attention_fwd_amd.build)")
+    return lc.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_partial_merge",
+              "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_status_strings(L):
+    assert L.attn_status_string(0) == b"ok"
+    for s in range(1, 8):
+        assert L.attn_status_string(s) and L.attn_status_string(s) != b"unknown status"
+    assert L.attn_status_string(99) == b"unknown status"
+
+
+def fwd(L, **kw):
+    args = dict(q=A, k=B_, v=C_, o=D_, o_dtype=0, lse=E_, B=1, Hq=4, Hkv=1, Nq=128, Nk=128, D=128,
+                scale=0.125, causal=1, q_pos0=0, k_pos0=0, stream=None)
+    args.update(kw)
+    return L.attn_fwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(Nq=0), 2), (dict(Nk=-1), 2), (dict(Hq=4, Hkv=3), 2), (dict(q_pos0=-1), 2),
+    (dict(D=96), 3), (dict(D=256), 3), (dict(o_dtype=7), 3), (dict(scale=0.0), 3), (dict(scale=float("nan")), 3),
+    (dict(q=A + 8), 4), (dict(lse=E_ + 4), 4),
+    (dict(o=A), 5), (dict(lse=B_ + 64), 5), (dict(o=E_ + 16), 5),
+])
+def test_fwd_rejects(L, kw, status):
+    assert fwd(L, **kw) == status
+    assert L.attn_last_error()
+
+
+def merge(L, **kw):
+    args = dict(o_parts=A, part_dtype=1, lse_parts=B_, n_parts=4, o=C_, lse=D_, B=1, H=8, N=1024, D=128, stream=None)
+    args.update(kw)
+    return L.attn_partial_merge(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o_parts=None), 1), (dict(n_parts=0), 2), (dict(N=0), 2), (dict(D=80), 3), (dict(part_dtype=5), 3),
+    (dict(o=C_ + 2), 4), (dict(o=A + 4096), 5), (dict(lse=B_), 5),
+])
+def test_merge_rejects(L, kw, status):
+    assert merge(L, **kw) == status
+
+
+def test_bwd_workspace_size(L):
+    assert L.attn_bwd_workspace_size(1, 8, 8, 65536, 128) >= 8 * 65536 * 4
+    assert L.attn_bwd_workspace_size(1, 8, 3, 1024, 128) == 0
+    assert L.attn_bwd_workspace_size(0, 8, 8, 1024, 128) == 0
+
+
+def bwd(L, **kw):
+    n = 1 << 22
+    args = dict(q=A, k=A + n, v=A + 2 * n, o=A + 3 * n, do=A + 4 * n, lse=A + 5 * n, dq=A + 6 * n, dk=A + 7 * n,
+                dv=A + 8 * n, ws=A + 9 * n, ws_bytes=1 << 20, B=1, Hq=8, Hkv=8, N=1024, D=128, scale=0.088,
+                causal=1, stream=None)
+    args.update(kw)
+    return L.attn_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), 1), (dict(N=0), 2), (dict(Hkv=3), 2), (dict(D=32), 3), (dict(scale=-1.0), 3),
+    (dict(ws=None), 6), (dict(ws_bytes=100), 6), (dict(dk=A + 8), 4), (dict(dq=A), 5),
+])
+def test_bwd_rejects(L, kw, status):
+    assert bwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["seq_to_head_relayout", "head_to_seq_relayout"])
+@pytest.mark.parametrize("args,status", [
+    ((None, B_, 8, 4096, 32, 128, 2), 1),
+    ((A, B_, 8, 4095, 32, 128, 2), 2),
+    ((A, B_, 8, 4096, 4, 128, 2), 3),      # H < P needs head replication
+    ((A, B_, 8, 4096, 12, 128, 2), 2),
+    ((A, B_, 8, 4096, 32, 128, 3), 3),
+    ((A, B_, 8, 4096, 32, 12, 2), 3),
+    ((A + 2, B_, 8, 4096, 32, 128, 2), 4),
+    ((A, A + 1024, 8, 4096, 32, 128, 2), 5),
+])
+def test_relayout_rejects(L, fn, args, status):
+    assert getattr(L, fn)(*args, None) == status
+
+
+def test_binding_raises_on_missing_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lc.attn_fwd(x, x, x)

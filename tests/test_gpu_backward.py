@@ -1,0 +1,128 @@
+"""GPU parity of attn_bwd against the fp64 oracle (through the C ABI).
+
+Gradient gate: per tensor, max |dX_gpu - dX_ref| / max |dX_ref| <= 2e-2 over
+the checked rows.  The forward's O and LSE that the GPU backward consumes come
+from the GPU forward, as in training; the oracle computes its own.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import long_context_attention_fwd_amd as lc
+from long_context_attention_fwd_amd.inputs import WORKLOADS, make_qkv, make_workload_inputs, sample_rows
+
+from gpu_util import GRAD_REL_TOL, check_forward, f64_of, grad_rel_err, poisoned, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def sdpa_scale(D):
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def gpu_fwd_bwd(q, k, v, do, scale, causal=True):
+    import torch
+    o, lse = lc.attn_fwd(q, k, v, causal=causal, scale=scale)
+    dq = poisoned(tuple(q.shape), torch.bfloat16)
+    dk = poisoned(tuple(k.shape), torch.bfloat16)
+    dv = poisoned(tuple(v.shape), torch.bfloat16)
+    lc.attn_bwd(q, k, v, o, do, lse, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def check_grads(got, ref, what):
+    errs = {n: grad_rel_err(f64_of(g), r) for n, g, r in zip(("dq", "dk", "dv"), got, ref)}
+    for n, e in errs.items():
+        assert np.isfinite(f64_of(got[("dq", "dk", "dv").index(n)])).all(), f"{what}: non-finite {n}"
+        assert e <= GRAD_REL_TOL, f"{what}: {n} relative error {e} ({errs})"
+    return errs
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 257, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,causal", [(1, True), (4, True), (2, False)])
+def test_bwd_small_sweep(gpu, N, D, G, causal):
+    Hkv = 2
+    d = make_qkv(1, Hkv * G, Hkv, N, D, seed=200 + N + D + G, with_do=True)
+    s = sdpa_scale(D)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s, causal)
+    O, L, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, causal)
+    check_forward(f64_of(o), f64_of(lse), O, L, f"fwd N={N}")
+    check_grads((dq, dk, dv), (dQ, dK, dV), f"N={N} D={D} G={G} causal={causal}")
+
+
+def test_bwd_full_1024(gpu):
+    """B=1, H=8, D=128, N=1024: every row of O, LSE, dQ, dK and dV."""
+    d = make_qkv(1, 8, 8, 1024, 128, seed=5, with_do=True)
+    s = sdpa_scale(128)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s)
+    O, L, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s)
+    check_forward(f64_of(o), f64_of(lse), O, L, "fwd N=1024")
+    check_grads((dq, dk, dv), (dQ, dK, dV), "N=1024")
+
+
+def test_bwd_listing_mean_square_loss(gpu):
+    """The glossary example's loss, mean(O^2), on its [1, 4, 4096, 64] shape:
+    dO = 2 O / numel, each side from its own forward."""
+    import torch
+    w = WORKLOADS["listing_4k"]
+    d = make_workload_inputs(w)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=w.scale)
+    do = (2.0 * o.float() / o.numel()).to(torch.bfloat16)
+    dq, dk, dv = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    O, _ = oracle.attention_forward(d["q"], d["k"], d["v"], w.scale)
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], 2.0 * O / O.size, w.scale)
+    check_grads((dq, dk, dv), (dQ, dK, dV), "mean(O^2)")
+
+
+def test_bwd_deterministic(gpu):
+    import torch
+    d = make_qkv(1, 4, 1, 700, 128, seed=36, with_do=True)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    r1 = gpu_fwd_bwd(q, k, v, do, sdpa_scale(128))
+    r2 = gpu_fwd_bwd(q, k, v, do, sdpa_scale(128))
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_bwd_train_64k_sampled(gpu):
+    """N = 65536, H = 8, D = 128.  (1) O and LSE at 128 sampled rows; (2) dQ at
+    those rows with the full dO; (3) with dO zeroed outside the sampled rows,
+    dK and dV at every key row (gradients are linear in dO, so the oracle's
+    sums run over the sampled rows only)."""
+    import torch
+    w = WORKLOADS["train_64k"]
+    d = make_workload_inputs(w)
+    s = w.scale
+    rows = sample_rows(w.N, w.seed, w.sampled_rows)
+    idx = torch.from_numpy(rows).cuda()
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s)
+    O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, True, rows=rows)
+    check_forward(f64_of(o[:, :, idx]), f64_of(lse[:, :, idx]), O, L, "train_64k fwd")
+    dq_s = f64_of(dq[:, :, idx])
+    del dq, dk, dv
+    # (3) dO restricted to the sampled rows
+    do_r = torch.zeros_like(do)
+    do_r[:, :, idx] = do[:, :, idx]
+    dq2, dk2, dv2 = lc.attn_bwd(q, k, v, o, do_r, lse, causal=True, scale=s)
+    torch.cuda.synchronize()
+    do_np = oracle.bf16_bits_to_f64(d["do"])
+    mask = np.zeros(w.N, dtype=bool)
+    mask[rows] = True
+    do_np[:, :, ~mask] = 0.0
+    rq, rk, rv = oracle.attention_backward_row_support(d["q"], d["k"], d["v"], do_np, s, rows)
+    e_dq = grad_rel_err(dq_s, rq)                      # (2): full dO, sampled rows
+    e_dq2 = grad_rel_err(f64_of(dq2[:, :, idx]), rq)   # same rows, restricted dO
+    e_dk = grad_rel_err(f64_of(dk2), rk)
+    e_dv = grad_rel_err(f64_of(dv2), rv)
+    assert max(e_dq, e_dq2, e_dk, e_dv) <= GRAD_REL_TOL, (e_dq, e_dq2, e_dk, e_dv)

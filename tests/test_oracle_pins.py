@@ -336,6 +336,22 @@ def test_backward_sampled_matches_full():
     assert np.abs(sv - dV[:, :, rows]).max() < 1e-12
 
 
+def test_backward_row_support_matches_full_with_masked_do():
+    d = make_qkv(1, 4, 2, 90, 8, seed=16, with_do=True)
+    support = np.array([0, 3, 40, 41, 89])
+    do = oracle.bf16_bits_to_f64(d["do"])
+    mask = np.zeros(90, dtype=bool)
+    mask[support] = True
+    do[:, :, ~mask] = 0.0
+    s = 1.0 / math.sqrt(8)
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], do, s)
+    rq, rk, rv = oracle.attention_backward_row_support(d["q"], d["k"], d["v"], do, s, support)
+    assert np.abs(rq - dQ[:, :, support]).max() < 1e-12
+    assert np.abs(rk - dK).max() < 1e-12 and np.abs(rv - dV).max() < 1e-12
+    with pytest.raises(ValueError):
+        oracle.attention_backward_row_support(d["q"], d["k"], d["v"], d["do"], s, support)
+
+
 # ---------------------------------------------------------------------------
 # relayout: a transpose of the flattened token and head indices
 # ---------------------------------------------------------------------------
