@@ -96,8 +96,10 @@ int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_par
                        void* o, float* lse, int B, int H, int64_t N, int D, void* hip_stream);
 
 /*
- * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs
- * (per-row <dO, O> in fp32).  Returns 0 for invalid sizes.
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs: the
+ * per-row <dO, O> in fp32 and, for grouped-query attention (Hq != Hkv),
+ * per-query-head fp32 partials of dK and dV (2 * B*Hq*N*D floats) that are
+ * summed over each group.  Returns 0 for invalid sizes.
  */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
 

@@ -100,8 +100,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, 
   if (!elems(&nq_el, {B, Hq, Nq, D}) || !elems(&nk_el, {B, Hkv, Nk, D}) || !elems(&nl, {B, Hq, Nq}) ||
       nq_el > (INT64_MAX / 8))
     return fail(ATTN_ERR_SHAPE, "attn_fwd: tensor sizes overflow");
-  if ((Nq + 31) / 32 > INT32_MAX || B > 65535 || Hq > 65535)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
+  if (Nq >= INT32_MAX || Nk >= INT32_MAX || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: sequence lengths must be < 2^31, B and Hq <= 65535");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(ATTN_ERR_ALIGN, "attn_fwd: pointers must be 16-byte aligned");
   const size_t ob = (size_t)nq_el * (o_dtype == ATTN_FP32 ? 4 : 2);
@@ -159,10 +159,9 @@ int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_par
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D) {
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv) return 0;
-  int64_t rows;
-  if (!elems(&rows, {B, Hq, N}) || rows > INT64_MAX / 8) return 0;
-  // per-row <dO, O> in fp32, rounded up to 256 bytes
-  return (size_t)((rows * 4 + 255) / 256 * 256);
+  int64_t el;
+  if (!elems(&el, {B, Hq, N, D}) || el > INT64_MAX / 16) return 0;
+  return (size_t)lcattn::bwd_workspace_bytes(B, Hq, Hkv, N, D);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -176,8 +175,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: scale must be > 0");
   int64_t nq_el, nk_el, nl;
   if (!elems(&nq_el, {B, Hq, N, D}) || !elems(&nk_el, {B, Hkv, N, D}) || !elems(&nl, {B, Hq, N}) ||
-      nq_el > INT64_MAX / 8 || (N + 31) / 32 > INT32_MAX || B > 65535 || Hq > 65535)
+      nq_el > INT64_MAX / 8)
     return fail(ATTN_ERR_SHAPE, "attn_bwd: tensor sizes overflow");
+  if (N >= INT32_MAX || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: N must be < 2^31, B and Hq <= 65535");
   const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, N, D);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "attn_bwd: workspace needs %zu bytes, got %zu", need, workspace_bytes);

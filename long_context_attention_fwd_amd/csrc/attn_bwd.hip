@@ -9,20 +9,26 @@
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j.
 // dK, dV of a key/value head sum over the query heads that read it.
 //
-// Three kernels, none of them with atomics (results are deterministic):
+// Kernels (no atomics anywhere: results are deterministic):
 //  * bwd_delta: Dv per query row, HBM bound.
-//  * bwd_dkdv: a workgroup owns 128 keys of one key/value head (4 waves x 32
-//    keys, K and V of its keys resident in registers as MFMA operands) and
-//    walks every query tile that can see them, for each query head of the
-//    group.  Per tile Q and dO are staged in LDS twice, row-major for the
-//    S = Q K^T and dP = dO V^T products and transposed for the
-//    dV^T += dO^T P and dK^T += Q^T dS products.  Query rows are fed to the
-//    MFMA in the pi order, so P and dS leave the accumulators already in the
-//    operand layout of the next product.
-//  * bwd_dq: like the forward, a workgroup owns query rows (the heads of a
-//    group packed together), walks the key tiles, recomputes S^T and
-//    dP^T = V dO^T, and accumulates dQ^T += K^T dS^T.  K is staged both
-//    row-major and transposed.
+//  * bwd_dkdv: a workgroup owns 128 keys (4 waves x 32 keys, K and V of those
+//    keys resident in registers as MFMA operands) and one query head, and
+//    walks every 64-row query tile that can see its keys.  Q and dO tiles
+//    arrive in LDS by direct loads (row-major, swizzled); S = Q K^T and
+//    dP = dO V^T read them by rows, dV^T += dO^T P and dK^T += Q^T dS through
+//    the transposing LDS read.  Query rows are fed to the MFMA in the pi
+//    order, so P and dS leave the accumulators already in the operand layout
+//    of the next product.  Iteration i does the dV/dK products of tile i-1,
+//    then issues tile i+1's loads, then the S/dP products and the elementwise
+//    step of tile i (three LDS buffers).
+//  * bwd_dkdv_reduce (grouped-query attention only): the per-query-head fp32
+//    partials of dK, dV are summed over the group and rounded to bf16.  One
+//    workgroup per (key tile, query head) gives G times more workgroups than
+//    one per key/value head, which a one-KV-head Ulysses share needs.
+//  * bwd_dq: like the forward, 8 waves own query rows (the heads of a group
+//    packed together) and walk the key tiles, recomputing S^T = K Q^T and
+//    dP^T = V dO^T and accumulating dQ^T += K^T dS^T (K through the
+//    transposing read), pipelined the same way.
 // dQ by a separate pass costs two recomputed products (7 contractions instead
 // of 5) but avoids fp32 atomic traffic proportional to N^2 / tile.
 #include "device_common.hpp"
@@ -31,9 +37,6 @@
 namespace lcattn {
 
 namespace {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------------------
 // Dv_i = <dO_i, O_i> (fp32), one thread per 8 elements
@@ -61,94 +64,69 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   if (row < rows && u == 0) delta[row] = s;
 }
 
-// Stage a 64-row x D tile (rows [r0, r0+64) of a [rows_total, D] bf16 matrix)
-// into LDS twice: row-major (rows read in pi order) and transposed (D rows of
-// 64 columns).  One 4-row x 8-column block per thread.  Rows past rows_total
-// are zero.
-template <int D>
-struct TileIO {
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int T_ROW_BYTES = 64 * 2;
-  static constexpr int BLOCKS = 16 * (D / 8);  // 4-row x 8-col blocks
-  static_assert(BLOCKS <= kThreads, "one block per thread at most");
-
-  __device__ static void load(const uint16_t* base, long long r0, long long rows_total, int tid, u32x4 reg[4]) {
-    if (tid < BLOCKS) {
-      const int dq = tid % (D / 8), kq = tid / (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const long long row = r0 + 4 * kq + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < rows_total) x = ld_global16(base + row * D + 8 * dq);
-        reg[r] = x;
-      }
-    }
-  }
-  __device__ static void store_rows(unsigned char* lds, int tid, const u32x4 reg[4]) {
-    if (tid < BLOCKS) {
-      const int dq = tid % (D / 8), kq = tid / (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * kq + r;
-        st_lds16(lds, row * ROW_BYTES + ((dq ^ swz_rows_pi(row)) << 4), reg[r]);
-      }
-    }
-  }
-  __device__ static void store_cols(unsigned char* lds, int tid, const u32x4 reg[4]) {
-    if (tid < BLOCKS) {
-      const int dq = tid % (D / 8), kq = tid / (D / 8);
-      u32x2 cols[8];
-      transpose4x8(reg, cols);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * dq + e;
-        st_lds8(lds, d * T_ROW_BYTES + (((kq >> 1) ^ swz_cols(d)) << 4) + ((kq & 1) << 3), cols[e]);
-      }
-    }
-  }
-  // A operand of a product reducing over D: row (block-local, already in pi
-  // order) and reduction step t.
-  __device__ static bf16x8 rows_frag(const unsigned char* lds, int row, int t, int grp) {
-    return as_bf16x8(ld_lds16(lds, row * ROW_BYTES + (((2 * t + grp) ^ swz_rows_pi(row)) << 4)));
-  }
-  // A operand of a product reducing over the 64 tile rows: row d of the
-  // transposed tile, 8 consecutive tile rows starting at 8 * unit.
-  __device__ static bf16x8 cols_frag(const unsigned char* lds, int d, int unit) {
-    return as_bf16x8(ld_lds16(lds, d * T_ROW_BYTES + ((unit ^ swz_cols(d)) << 4)));
-  }
-};
-
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 128 keys of one key/value head
+// dK, dV: workgroup = 128 keys of one key/value head x one query head
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+constexpr int kDkdvWaves = 4;
+constexpr int kBQ = 64;   // query rows per tile
+
+template <int D, bool PARTIAL>
+__global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a, float* __restrict__ dk_part,
+                                                                       float* __restrict__ dv_part) {
+  using T = LdsTile<D>;
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
-  constexpr int BQ = 64;     // queries per tile
-  constexpr int BK = 128;    // keys per workgroup
-  using IO = TileIO<D>;
-  constexpr int TILE = BQ * D * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TILE + 2 * BQ * 4];
-  unsigned char* q_rows = smem;
-  unsigned char* q_cols = smem + TILE;
-  unsigned char* o_rows = smem + 2 * TILE;   // dO
-  unsigned char* o_cols = smem + 3 * TILE;
-  float* lse_t = reinterpret_cast<float*>(smem + 4 * TILE);  // LSE * log2(e), +inf past N
-  float* dv_t = lse_t + BQ;
+  constexpr int NW = kDkdvWaves;
+  constexpr int BK = 32 * NW;  // keys per workgroup
+  // per buffer: Q tile, dO tile, LSE (64 floats), Dv (64 floats)
+  constexpr int BUF = 2 * T::BYTES + 2 * kBQ * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem2[BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
   const long long N = a.N;
   const long long bz = blockIdx.z;
-  const int kvh = blockIdx.y;
+  const int h = blockIdx.y;               // query head
+  const int kvh = h / a.G;
   const long long kt0 = (long long)blockIdx.x * BK;
-  const long long kw0 = kt0 + 32 * wave;       // this wave's first key
-  const long long key = kw0 + c;               // this lane's key
+  const long long kw0 = kt0 + 32 * wave;  // this wave's first key
+  const long long key = kw0 + c;          // this lane's key
   const float sl = a.scale * kLog2e;
 
   const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
   const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * N * D;
+  const long long hb = (bz * a.Hq + h) * N;
+  const uint16_t* qbase = a.q + hb * D;
+  const uint16_t* obase = a.d_o + hb * D;
+  const float* lbase = a.lse + hb;
+  const float* dbase = a.delta + hb;
+
+  const long long first_tile = a.causal ? kt0 / kBQ : 0;
+  const int n_tiles = (int)((N + kBQ - 1) / kBQ - first_tile);
+
+  auto issue = [&](int i, unsigned char* buf) __attribute__((always_inline)) {
+    const long long r0 = (first_tile + i) * kBQ;
+    T::template load_async<NW>(buf, qbase, r0, N, wave, lane);
+    T::template load_async<NW>(buf + T::BYTES, obase, r0, N, wave, lane);
+    // LSE and Dv of the tile's 64 rows, one dword per lane (rows past N
+    // repeat row N-1; they are masked)
+    if (wave == 0) {
+      long long row = r0 + lane;
+      row = row < N ? row : N - 1;
+      unsigned char* dst = buf + 2 * T::BYTES;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(lbase + row),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(dst)),
+                                       4, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dbase + row),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(dst) + kBQ * 4),
+                                       4, 0, 0);
+    }
+  };
+  if (n_tiles > 0) issue(0, smem0);
 
   // K and V rows of this lane's key as B operands (reduction over D)
   bf16x8 kf[KT], vf[KT];
@@ -171,48 +149,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dk_acc[db][v] = 0.f;
       dv_acc[db][v] = 0.f;
     }
+  // P and dS of the previous tile (2 query blocks x 2 halves), pending products
+  bf16x8 pb[2][2], sb[2][2];
+  bool live0 = false, live1 = false;  // query blocks of the previous tile with work
 
-  const long long first_tile = a.causal ? kt0 / BQ : 0;
-  const long long n_qt = (N + BQ - 1) / BQ;
-  const long long tiles_per_head = n_qt - first_tile;
-  const long long total = tiles_per_head * a.G;
-
-  u32x4 qreg[4], oreg[4];
-  float lse_reg = 0.f;
-  auto load = [&](long long it) {
-    const int hh = (int)(it / tiles_per_head);
-    const long long qt = first_tile + it % tiles_per_head;
-    const int h = kvh * a.G + hh;
-    const long long hb = (bz * a.Hq + h) * N;
-    IO::load(a.q + hb * D, qt * BQ, N, tid, qreg);
-    IO::load(a.d_o + hb * D, qt * BQ, N, tid, oreg);
-    if (tid < 2 * BQ) {
-      const long long row = qt * BQ + (tid & (BQ - 1));
-      if (tid < BQ) lse_reg = row < N ? a.lse[hb + row] * kLog2e : INFINITY;
-      else lse_reg = row < N ? a.delta[hb + row] : 0.f;
+  // products of one 32-row query block of the tile in buf
+  auto block_products = [&](const unsigned char* buf, int qb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dbk = 0; dbk < DB; ++dbk) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r0 = qb * 32 + 16 * u;
+        dv_acc[dbk] = mfma32x32x16(T::tr_frag(buf + T::BYTES, r0, dbk * 32, lane), pb[qb][u], dv_acc[dbk]);
+        dk_acc[dbk] = mfma32x32x16(T::tr_frag(buf, r0, dbk * 32, lane), sb[qb][u], dk_acc[dbk]);
+      }
     }
   };
-  auto store = [&]() {
-    IO::store_rows(q_rows, tid, qreg);
-    IO::store_cols(q_cols, tid, qreg);
-    IO::store_rows(o_rows, tid, oreg);
-    IO::store_cols(o_cols, tid, oreg);
-    if (tid < 2 * BQ) lse_t[tid] = lse_reg;  // lse_t and dv_t are adjacent
+  auto grad_products = [&](const unsigned char* buf) __attribute__((always_inline)) {
+    if (live0) block_products(buf, 0);
+    if (live1) block_products(buf, 1);
   };
 
-  if (total > 0) load(0);
-  for (long long it = 0; it < total; ++it) {
-    __syncthreads();  // previous tile's readers are done
-    store();
-    __syncthreads();
-    if (it + 1 < total) load(it + 1);
-    const long long qt0 = (first_tile + it % tiles_per_head) * BQ;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+  wait_vmem();
+  __syncthreads();
+
+  auto step = [&](int i, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt) __attribute__((always_inline)) {
+    grad_products(prev);
+    if (i + 1 < n_tiles) issue(i + 1, nxt);
+    const long long qt0 = (first_tile + i) * kBQ;
+    const float* lse_t = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
+    const float* dv_t = lse_t + kBQ;
+    // S, dP and the elementwise step of one 32-row query block
+    auto block_grads = [&](int qb) __attribute__((always_inline)) {
       const long long qb0 = qt0 + qb * 32;
-      // all 32 queries of the block precede every key of the wave: nothing visible
-      if (a.causal && qb0 + 31 < kw0) continue;
-      if (qb0 >= N || kw0 >= N) continue;
       f32x16 s, dp;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -222,11 +191,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int arow = qb * 32 + swap_bits23(c);
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        s = mfma32x32x16(IO::rows_frag(q_rows, arow, t, grp), kf[t], s);
-        dp = mfma32x32x16(IO::rows_frag(o_rows, arow, t, grp), vf[t], dp);
+        s = mfma32x32x16(T::row_frag(cur, arow, t, grp), kf[t], s);
+        dp = mfma32x32x16(T::row_frag(cur + T::BYTES, arow, t, grp), vf[t], dp);
       }
-      const bool need_mask = a.causal && (qb0 < kw0 + 31);
-      bf16x8 pb[2], db16[2];
+      const bool need_mask = (a.causal && qb0 < kw0 + 31) || qb0 + 32 > N;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r0 = qb * 32 + 16 * u + 8 * grp;  // tile rows of registers 8u..8u+7
@@ -239,59 +207,102 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float lv = e < 4 ? l0[e] : l1[e - 4];
           const float dvv = e < 4 ? d0[e] : d1[e - 4];
-          float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lv));
-          if (need_mask && qt0 + r0 + e < key) pe = 0.f;
+          float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lv * kLog2e));
+          if (need_mask) {
+            const int qrow = (int)qt0 + r0 + e;
+            if (qrow >= (int)N || (a.causal && qrow < (int)key)) pe = 0.f;
+          }
           p[e] = pe;
           ds[e] = pe * (dp[8 * u + e] - dvv);
         }
-        pb[u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        db16[u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        pb[qb][u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        sb[qb][u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       }
-#pragma unroll
-      for (int dbk = 0; dbk < DB; ++dbk) {
-        const int d = dbk * 32 + c;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int unit = 4 * qb + 2 * u + grp;
-          dv_acc[dbk] = mfma32x32x16(IO::cols_frag(o_cols, d, unit), pb[u], dv_acc[dbk]);
-          dk_acc[dbk] = mfma32x32x16(IO::cols_frag(q_cols, d, unit), db16[u], dk_acc[dbk]);
-        }
-      }
-    }
+    };
+    // a block has work unless all its queries precede every key of the wave
+    live0 = !(a.causal && qt0 + 31 < kw0) && qt0 < N && kw0 < N;
+    live1 = !(a.causal && qt0 + 63 < kw0) && qt0 + 32 < N && kw0 < N;
+    if (live0) block_grads(0);
+    if (live1) block_grads(1);
+    wait_vmem();
+    __syncthreads();
+  };
+  int i = 0;
+  for (; i + 3 <= n_tiles; i += 3) {
+    step(i, smem2, smem0, smem1);
+    step(i + 1, smem0, smem1, smem2);
+    step(i + 2, smem1, smem2, smem0);
+  }
+  if (i < n_tiles) step(i, smem2, smem0, smem1);
+  if (i + 1 < n_tiles) step(i + 1, smem0, smem1, smem2);
+  if (n_tiles > 0) {
+    const int r = (n_tiles - 1) % 3;
+    grad_products(r == 0 ? smem0 : (r == 1 ? smem1 : smem2));
   }
 
   if (key < N) {
-    const long long base = ((bz * a.Hkv + kvh) * N + key) * D;
 #pragma unroll
     for (int dbk = 0; dbk < DB; ++dbk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = dbk * 32 + 8 * j + 4 * grp;
-        *reinterpret_cast<u32x2*>(a.dk + base + d) =
-            pack_bf16x4_bits(dk_acc[dbk][4 * j] * a.scale, dk_acc[dbk][4 * j + 1] * a.scale,
-                             dk_acc[dbk][4 * j + 2] * a.scale, dk_acc[dbk][4 * j + 3] * a.scale);
-        *reinterpret_cast<u32x2*>(a.dv + base + d) =
-            pack_bf16x4_bits(dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2],
-                             dv_acc[dbk][4 * j + 3]);
+        const float k0 = dk_acc[dbk][4 * j] * a.scale, k1 = dk_acc[dbk][4 * j + 1] * a.scale;
+        const float k2 = dk_acc[dbk][4 * j + 2] * a.scale, k3 = dk_acc[dbk][4 * j + 3] * a.scale;
+        if (PARTIAL) {
+          const long long base = (hb + key) * D + d;
+          const f32x4 wk = {k0, k1, k2, k3};
+          const f32x4 wv = {dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2],
+                            dv_acc[dbk][4 * j + 3]};
+          *reinterpret_cast<f32x4*>(dk_part + base) = wk;
+          *reinterpret_cast<f32x4*>(dv_part + base) = wv;
+        } else {
+          const long long base = ((bz * a.Hkv + kvh) * N + key) * D + d;
+          *reinterpret_cast<u32x2*>(a.dk + base) = pack_bf16x4_bits(k0, k1, k2, k3);
+          *reinterpret_cast<u32x2*>(a.dv + base) = pack_bf16x4_bits(
+              dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2], dv_acc[dbk][4 * j + 3]);
+        }
       }
   }
+}
+
+// dK[b, kvh] = sum over the G query heads of the group of the fp32 partials.
+// One thread per 4 elements.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ dk_part,
+                                                              const float* __restrict__ dv_part,
+                                                              uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                                              int G, long long kv_heads_total, long long N) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // over kv_heads_total * N * D / 4
+  const long long per_head = N * D / 4;
+  if (idx >= kv_heads_total * per_head) return;
+  const long long hk = idx / per_head;        // flattened (b, kvh)
+  const long long rem = idx - hk * per_head;  // 4-element slot within the head
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < G; ++g) {
+    const long long src = ((hk * G + g) * per_head + rem) * 4;
+    sk += *reinterpret_cast<const f32x4*>(dk_part + src);
+    sv += *reinterpret_cast<const f32x4*>(dv_part + src);
+  }
+  *reinterpret_cast<u32x2*>(dk + idx * 4) = pack_bf16x4_bits(sk[0], sk[1], sk[2], sk[3]);
+  *reinterpret_cast<u32x2*>(dv + idx * 4) = pack_bf16x4_bits(sv[0], sv[1], sv[2], sv[3]);
 }
 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = query rows of HP heads sharing a key/value head
 // ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kBN = 64;
+
 template <int D, int HP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+__global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  using T = LdsTile<D>;
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
-  constexpr int BN = 64;
-  constexpr int SPAN = (kWaves / HP) * 32;
-  using IO = TileIO<D>;
-  constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * TILE];
-  unsigned char* k_rows = smem;
-  unsigned char* k_cols = smem + TILE;
-  unsigned char* v_rows = smem + 2 * TILE;
+  constexpr int NW = kDqWaves;
+  constexpr int SPAN = (NW / HP) * 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * T::BYTES];  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * T::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem2[2 * T::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
@@ -305,6 +316,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qt
   const long long qrow = wq0 + c;
   const float sl = a.scale * kLog2e;
   const long long hb = (bz * a.Hq + h) * N;
+  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
+  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * N * D;
+
+  long long kv_end = N;
+  if (a.causal) kv_end = min(N, q_start + SPAN);
+  const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
+  const long long wq_last = min(wq0 + 32, N) - 1;
+  const bool wave_live = wq0 < N;
+
+  auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
+    T::template load_async<NW>(buf, kbase, (long long)j * kBN, N, wave, lane);
+    T::template load_async<NW>(buf + T::BYTES, vbase, (long long)j * kBN, N, wave, lane);
+  };
+  if (n_tiles > 0) issue(0, smem0);
 
   bf16x8 qf[KT], of[KT];
 #pragma unroll
@@ -325,72 +350,73 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qt
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+  bf16x8 dsb[4];  // dS^T of the previous tile, pending its product
+  bool prev_active = false;
 
-  long long kv_end = N;
-  if (a.causal) kv_end = min(N, q_start + SPAN);
-  const int n_tiles = (int)((kv_end + BN - 1) / BN);
-  const long long wq_last = min(wq0 + 32, N) - 1;
-  const bool wave_live = wq0 < N;
-
-  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
-  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * N * D;
-  u32x4 kreg[4], vreg[4];
-  auto load = [&](int j) {
-    IO::load(kbase, (long long)j * BN, N, tid, kreg);
-    IO::load(vbase, (long long)j * BN, N, tid, vreg);
-  };
-  auto store = [&]() {
-    IO::store_rows(k_rows, tid, kreg);
-    IO::store_cols(k_cols, tid, kreg);
-    IO::store_rows(v_rows, tid, vreg);
-  };
-
-  if (n_tiles > 0) load(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (j + 1 < n_tiles) load(j + 1);
-    const long long kt = (long long)j * BN;
-    if (!wave_live || (a.causal && kt > wq_last)) continue;
-    const bool need_mask = (kt + BN > N) || (a.causal && kt + BN - 1 > wq0);
-    bf16x8 dsb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[v] = 0.f;
-        dp[v] = 0.f;
-      }
-      const int arow = kb * 32 + swap_bits23(c);
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        s = mfma32x32x16(IO::rows_frag(k_rows, arow, t, grp), qf[t], s);
-        dp = mfma32x32x16(IO::rows_frag(v_rows, arow, t, grp), of[t], dp);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = 8 * u + e;
-          float p = fast_exp2(__builtin_fmaf(s[v], sl, -lse2));
-          if (need_mask) {
-            const long long kk = kt + kb * 32 + acc_row_pi(v, grp);
-            if (kk >= N || (a.causal && kk > qrow)) p = 0.f;
-          }
-          ds[e] = p * (dp[v] - dvv);
-        }
-        dsb[2 * kb + u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-      }
-    }
+  auto dq_product = [&](const unsigned char* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + c;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[db] = mfma32x32x16(IO::cols_frag(k_cols, d, 2 * u + grp), dsb[u], acc[db]);
+      for (int u = 0; u < 4; ++u) acc[db] = mfma32x32x16(T::tr_frag(buf, 16 * u, db * 32, lane), dsb[u], acc[db]);
     }
+  };
+
+  wait_vmem();
+  __syncthreads();
+
+  auto step = [&](int j, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt) __attribute__((always_inline)) {
+    if (prev_active) dq_product(prev);
+    if (j + 1 < n_tiles) issue(j + 1, nxt);
+    const long long kt = (long long)j * kBN;
+    const bool active = wave_live && !(a.causal && kt > wq_last);
+    prev_active = active;
+    if (active) {
+      const bool need_mask = (kt + kBN > N) || (a.causal && kt + kBN - 1 > wq0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s[v] = 0.f;
+          dp[v] = 0.f;
+        }
+        const int arow = kb * 32 + swap_bits23(c);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          s = mfma32x32x16(T::row_frag(cur, arow, t, grp), qf[t], s);
+          dp = mfma32x32x16(T::row_frag(cur + T::BYTES, arow, t, grp), of[t], dp);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float ds[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int v = 8 * u + e;
+            float p = fast_exp2(__builtin_fmaf(s[v], sl, -lse2));
+            if (need_mask) {
+              const int kk = (int)kt + kb * 32 + acc_row_pi(v, grp);
+              if (kk >= (int)N || (a.causal && kk > (int)qrow)) p = 0.f;
+            }
+            ds[e] = p * (dp[v] - dvv);
+          }
+          dsb[2 * kb + u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 3 <= n_tiles; j += 3) {
+    step(j, smem2, smem0, smem1);
+    step(j + 1, smem0, smem1, smem2);
+    step(j + 2, smem1, smem2, smem0);
+  }
+  if (j < n_tiles) step(j, smem2, smem0, smem1);
+  if (j + 1 < n_tiles) step(j + 1, smem0, smem1, smem2);
+  if (prev_active) {
+    const int r = (n_tiles - 1) % 3;
+    dq_product(r == 0 ? smem0 : (r == 1 ? smem1 : smem2));
   }
 
   if (qrow < N) {
@@ -398,11 +424,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a, int n_qt
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * grp;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = db * 32 + 8 * jj + 4 * grp;
         *reinterpret_cast<u32x2*>(a.dq + base + d) =
-            pack_bf16x4_bits(acc[db][4 * j] * a.scale, acc[db][4 * j + 1] * a.scale, acc[db][4 * j + 2] * a.scale,
-                             acc[db][4 * j + 3] * a.scale);
+            pack_bf16x4_bits(acc[db][4 * jj] * a.scale, acc[db][4 * jj + 1] * a.scale,
+                             acc[db][4 * jj + 2] * a.scale, acc[db][4 * jj + 3] * a.scale);
       }
   }
 }
@@ -415,24 +441,46 @@ hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
                      a.d_o, a.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)((a.N + 127) / 128), (unsigned)a.Hkv, (unsigned)B),
-                     dim3(kThreads), 0, stream, a);
+  const dim3 kgrid((unsigned)((a.N + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
+  if (a.G == 1) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, nullptr, nullptr);
+  } else {
+    float* dk_part = a.delta + bwd_delta_floats(B, a.Hq, a.N);
+    float* dv_part = dk_part + (long long)B * a.Hq * a.N * D;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, dk_part, dv_part);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long slots = (long long)B * a.Hkv * a.N * D / 4;
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream,
+                       dk_part, dv_part, a.dk, a.dv, a.G, (long long)B * a.Hkv, a.N);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
-  const long long span = (kWaves / HP) * 32;
+  const long long span = (kDqWaves / HP) * 32;
   const int n_qt = (int)((a.N + span - 1) / span);
   dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
   if (HP == 4)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), grid, dim3(kThreads), 0, stream, a, n_qt);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
   else if (HP == 2)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a, n_qt);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), grid, dim3(kThreads), 0, stream, a, n_qt);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
   return hipGetLastError();
 }
 
 }  // namespace
+
+long long bwd_delta_floats(int B, int Hq, long long N) {
+  // Dv rows, padded to a multiple of 64 floats (256 bytes)
+  return ((long long)B * Hq * N + 63) / 64 * 64;
+}
+
+long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long N, int D) {
+  long long f = bwd_delta_floats(B, Hq, N);
+  if (Hq != Hkv) f += 2LL * B * Hq * N * D;  // per-query-head dK, dV partials
+  return f * 4;
+}
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream) {
   return D == 64 ? launch_d<64>(a, B, stream) : launch_d<128>(a, B, stream);

@@ -8,7 +8,9 @@
 // step's partial attention (same page, "So funktioniert Kontextparallelität").
 //
 // Design (CDNA4, wave64):
-//  * A workgroup is 4 waves.  Each wave owns 32*QB query rows of one query
+//  * A workgroup is 8 waves, two per SIMD, so the hardware overlaps one
+//    wave's softmax (VALU, exp) with the other's MFMAs.  Each wave owns
+//    32*QB query rows of one query
 //    head; the HP query heads that share a key/value head (grouped-query
 //    attention) are packed into one workgroup so each K/V tile staged in LDS
 //    serves all of them.
@@ -19,11 +21,13 @@
 //  * K rows are fed to the MFMA in the pi order (bits 2 and 3 of the row index
 //    swapped), which makes the fp32 S^T accumulator, packed to bf16, exactly
 //    the B operand of O^T += V^T P^T.  P never leaves registers.
-//  * V is staged transposed in LDS (V^T[d][key]) so that the A operand of the
-//    PV product is one 16-byte LDS read per lane.
-//  * K/V tiles of 64 keys are double buffered in LDS; the next tile's global
-//    loads are issued before the current tile's math, and one barrier per tile
-//    separates the buffers.
+//  * K and V tiles of 64 keys go global -> LDS with direct loads
+//    (global_load_lds_dwordx4: no registers, no VALU), row-major with a
+//    per-row XOR swizzle of 16-byte units.  K fragments are plain 16-byte
+//    reads; the V^T fragments of the PV product come from the row-major V tile
+//    through the transposing LDS read (ds_read_b64_tr_b16, two per fragment).
+//  * Tiles are double buffered: the next tile's direct loads are issued before
+//    the current tile's math, and one wait + barrier per tile hands over.
 //  * Online softmax in base 2 with the exact running maximum, so the largest
 //    weight of a row is exactly 1 and carries no bf16 rounding into P V (a
 //    stale maximum would let it pick up 2^-9 relative error, which shows on
@@ -41,25 +45,26 @@ namespace lcattn {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;      // two waves per SIMD: one's softmax overlaps the other's MFMAs
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;         // keys per tile
 
 template <int D, int QB, int HP, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
-  constexpr int NU = D / 8;        // 16-byte units per K row
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
+  using T = LdsTile<D>;
   constexpr int KT = D / 16;       // reduction steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
   constexpr int QW = 32 * QB;      // query rows per wave
   constexpr int SPAN = (kWaves / HP) * QW;  // query rows per workgroup (per head)
-  constexpr int K_TILE = kBN * D * 2;       // bytes of one K tile
-  constexpr int V_TILE = D * kBN * 2;       // bytes of one V^T tile
-  constexpr int K_CHUNKS = kBN * NU;        // 16-byte units of a K tile
-  constexpr int V_BLOCKS = (kBN / 4) * (D / 8);  // 4-key x 8-dim blocks of a V tile
-  static_assert(K_CHUNKS % kThreads == 0, "K tile staging must divide evenly");
-  static_assert(V_BLOCKS <= kThreads, "one V block per thread at most");
+  static_assert(kBN == 64, "LdsTile holds 64 rows");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (K_TILE + V_TILE)];
+  // Three buffers, each a K tile followed by a V tile (row-major, swizzled),
+  // as separate objects so the compiler can tell them apart.  Iteration j
+  // reads V of tile j-1 and K of tile j while the direct loads of tile j+1
+  // land in the third buffer.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * T::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * T::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem2[2 * T::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -88,6 +93,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a, int n_
   const bool wave_live = wq0 < a.Nq;
   const long long wpos_first = a.q_pos0 + wq0;
   const long long wpos_last = a.q_pos0 + wq_end - 1;
+  // q_pos0 - k_pos0, clamped to the int range (rows and keys are < 2^31)
+  const int dpos = (int)max(min(a.q_pos0 - a.k_pos0, (long long)INT32_MAX), (long long)INT32_MIN + 1);
+
+  auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
+    T::template load_async<kWaves>(buf, kh, (long long)j * kBN, a.Nk, wave, lane);
+    T::template load_async<kWaves>(buf + T::BYTES, vh, (long long)j * kBN, a.Nk, wave, lane);
+  };
+  if (n_tiles > 0) issue(0, smem0);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds its query row's dims
   // 16t + 8*grp .. +7 for every reduction step t.
@@ -105,6 +118,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a, int n_
 
   f32x16 acc[QB][DB];
   float m_run[QB], l_run[QB];
+  bf16x8 pf[QB][4];  // P of the previous tile, waiting for its PV product
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
@@ -114,63 +128,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a, int n_
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[qb][db][v] = 0.f;
   }
+  bool prev_active = false;
 
-  // ---- staging of one K/V tile: global -> registers -> LDS -------------------
-  u32x4 kreg[K_CHUNKS / kThreads];
-  u32x4 vreg[4];
-  const int v_dq = tid % (D / 8), v_kq = tid / (D / 8);
-  auto load_tile = [&](int j) {
-    const long long kt = (long long)j * kBN;
+  // O^T += V^T P^T for the tile whose V sits in buf
+  auto pv = [&](const unsigned char* buf) __attribute__((always_inline)) {
+    const unsigned char* vs = buf + T::BYTES;
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS / kThreads; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / NU, u = id % NU;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kt + row < a.Nk) x = ld_global16(kh + (kt + row) * D + 8 * u);
-      kreg[i] = x;
-    }
-    if (tid < V_BLOCKS) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const long long key = kt + 4 * v_kq + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < a.Nk) x = ld_global16(vh + key * D + 8 * v_dq);
-        vreg[r] = x;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* ks = smem + buf * (K_TILE + V_TILE);
-    unsigned char* vs = ks + K_TILE;
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 vf = T::tr_frag(vs, 16 * u, db * 32, lane);
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS / kThreads; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / NU, u = id % NU;
-      st_lds16(ks, row * (D * 2) + ((u ^ swz_rows_pi(row)) << 4), kreg[i]);
-    }
-    if (tid < V_BLOCKS) {
-      u32x2 cols[8];
-      transpose4x8(vreg, cols);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * v_dq + e;
-        st_lds8(vs, d * (kBN * 2) + ((((v_kq >> 1) ^ swz_cols(d))) << 4) + ((v_kq & 1) << 3), cols[e]);
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vf, pf[qb][u], acc[qb][db]);
       }
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j + 1 < n_tiles) load_tile(j + 1);
-    const unsigned char* ks = smem + (j & 1) * (K_TILE + V_TILE);
-    const unsigned char* vs = ks + K_TILE;
+  // one iteration: PV of tile j-1, prefetch of tile j+1, S and softmax of tile j
+  auto step = [&](int j, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt) __attribute__((always_inline)) {
+    if (prev_active) pv(prev);
+    if (j + 1 < n_tiles) issue(j + 1, nxt);
+    const unsigned char* ks = cur;
     const long long kt = (long long)j * kBN;
     const bool wave_active = wave_live && (!a.causal || a.k_pos0 + kt <= wpos_last);
+    prev_active = wave_active;
     if (wave_active) {
       const bool need_mask = (kt + kBN > a.Nk) || (a.causal && a.k_pos0 + kt + kBN - 1 > wpos_first);
       // S^T for the two 32-key halves of the tile
@@ -186,23 +170,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a, int n_
         const int row = kb * 32 + swap_bits23(c);
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          const bf16x8 kf = as_bf16x8(ld_lds16(ks, row * (D * 2) + (((2 * t + grp) ^ swz_rows_pi(row)) << 4)));
+          const bf16x8 kf = T::row_frag(ks, row, t, grp);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][t], s[qb][kb]);
         }
       }
-      // mask, online softmax, pack P
-      bf16x8 pf[QB][4];
+      // mask, online softmax, pack P (the PV product follows next iteration)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (need_mask) {
-          const long long qpos = a.q_pos0 + wq0 + qb * 32 + c;
+          // 32-bit index math: key k is visible to query row r iff
+          // k < Nk and (not causal or k - r <= q_pos0 - k_pos0)
+          const int qrow = (int)(wq0 + qb * 32 + c);
+          const int klim = (int)min(a.Nk, (long long)INT32_MAX);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const long long key = kt + kb * 32 + acc_row_pi(v, grp);
-              const bool vis = key < a.Nk && (!a.causal || a.k_pos0 + key <= qpos);
+              const int key = (int)kt + kb * 32 + acc_row_pi(v, grp);
+              const bool vis = key < klim && (!a.causal || key - qrow <= dpos);
               if (!vis) s[qb][kb][v] = -INFINITY;
             }
         }
@@ -243,20 +229,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a, int n_
             for (int v = 0; v < 16; ++v) acc[qb][db][v] *= alpha;
         }
       }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + c;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 vf = as_bf16x8(ld_lds16(vs, d * (kBN * 2) + (((2 * u + grp) ^ swz_cols(d)) << 4)));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vf, pf[qb][u], acc[qb][db]);
-        }
-      }
     }
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+    wait_vmem();  // this wave's part of tile j + 1 has landed in LDS
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 3 <= n_tiles; j += 3) {
+    step(j, smem2, smem0, smem1);
+    step(j + 1, smem0, smem1, smem2);
+    step(j + 2, smem1, smem2, smem0);
+  }
+  if (j < n_tiles) step(j, smem2, smem0, smem1);
+  if (j + 1 < n_tiles) step(j + 1, smem0, smem1, smem2);
+  // PV of the last tile
+  if (prev_active) {
+    const int r = (n_tiles - 1) % 3;
+    pv(r == 0 ? smem0 : (r == 1 ? smem1 : smem2));
   }
 
   // ---- epilogue: normalise, write O and LSE ---------------------------------

@@ -79,26 +79,83 @@ __device__ __forceinline__ int swap_bits23(int m) {
 // lane in group grp: 16*(v/8) + 8*grp + v%8.
 __device__ __forceinline__ int acc_row_pi(int v, int grp) { return 16 * (v >> 3) + 8 * grp + (v & 7); }
 
-// XOR swizzles of 16-byte LDS units, chosen so that the 8 lanes served in one
-// LDS cycle touch 8 distinct 16-byte bank groups.
-//  * row-major tiles read in pi row order (rows pi(0..7) = 0-3, 8-11):
-__device__ __forceinline__ int swz_rows_pi(int row) { return (row & 3) | ((row >> 1) & 4); }
-//  * transposed tiles [col][row] read by consecutive columns and written by
-//    columns 8 apart:
-__device__ __forceinline__ int swz_cols(int col) { return (col ^ (col >> 3)) & 7; }
+// ---------------------------------------------------------------------------
+// LDS tiles: 64 rows x D bf16, row-major, 16-byte units XOR-swizzled per row.
+//
+// Two read patterns touch every tile:
+//  (a) row fragments: lanes 0..31 read rows pi(0..31) (one 16-byte unit each),
+//      the A operand of a product that reduces over D;
+//  (b) transposed fragments via ds_read_b64_tr_b16: a 16-lane group reads
+//      8-byte chunks of 4 consecutive rows, the A operand of a product that
+//      reduces over the tile rows.
+// f(row) = ((row & 3) << 1) | ((row >> 3) & 1) gives the 8 lanes of one LDS
+// cycle in (a) 8 distinct units modulo 8, and the 4 rows x 2 units of one
+// 16-lane cycle in (b) 8 distinct units modulo 8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
 
-// Repack four 8-element bf16 rows x[r] (r = 0..3) into eight 4-element columns:
-// column e holds x[0][e], x[1][e], x[2][e], x[3][e].
-__device__ __forceinline__ void transpose4x8(const u32x4 x[4], u32x2 out[8]) {
+template <int D>
+struct LdsTile {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int UNITS = D / 8;          // 16-byte units per row
+  static constexpr int BYTES = 64 * ROW_BYTES;  // one 64-row tile
+  static constexpr int LOADS = BYTES / (64 * 16);  // wave-wide 1 KiB direct loads per tile
+
+  // Byte offset of 16-byte unit u of row r.
+  __device__ static int off(int r, int u) { return r * ROW_BYTES + ((u ^ tile_swz(r)) << 4); }
+
+  // Issue the direct global->LDS loads of rows [r0, r0 + 64) of a row-major
+  // [rows_total, D] bf16 matrix.  Wave w of NW waves issues loads w, w+NW, ...;
+  // load n fills LDS bytes [n KiB, n KiB + 1 KiB), lane i its 16 bytes at
+  // 16 i.  Rows past rows_total read row rows_total - 1 instead (finite data
+  // that the callers mask).
+  template <int NW>
+  __device__ static void load_async(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total,
+                                    int wave, int lane) {
+    static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const unsigned a = x[0][m], b = x[1][m], c = x[2][m], d = x[3][m];
-    // element 2m sits in the low half of word m, element 2m+1 in the high half
-    out[2 * m][0] = (a & 0xFFFFu) | (b << 16);
-    out[2 * m][1] = (c & 0xFFFFu) | (d << 16);
-    out[2 * m + 1][0] = (a >> 16) | (b & 0xFFFF0000u);
-    out[2 * m + 1][1] = (c >> 16) | (d & 0xFFFF0000u);
+    for (int i = 0; i < LOADS / NW; ++i) {
+      const int n = wave + i * NW;
+      const int slot = n * 64 + lane;
+      const int r = slot / UNITS, up = slot % UNITS;
+      const int u = up ^ tile_swz(r);
+      long long gr = r0 + r;
+      gr = gr < rows_total ? gr : rows_total - 1;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + gr * D + 8 * u),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(lds) + n * 1024),
+                                       16, 0, 0);
+    }
   }
-}
+
+  // (a) A operand reducing over D: row r (already in pi order), step t.
+  __device__ static bf16x8 row_frag(const unsigned char* lds, int r, int t, int grp) {
+    return as_bf16x8(ld_lds16(lds, off(r, 2 * t + grp)));
+  }
+
+  // (b) A operand reducing over tile rows: lane (c, grp) receives
+  // T[r0 + 8 grp + e][d0 + c] for e = 0..7 (r0 a multiple of 8, d0 of 32).
+  __device__ static bf16x8 tr_frag(const unsigned char* lds, int r0, int d0, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int gi = lane >> 4, s = lane & 15;
+    const int row = r0 + 8 * (gi >> 1) + (s >> 2);
+    const int col = d0 + 16 * (gi & 1) + 4 * (s & 3);
+    const int o = off(row, col >> 3) + ((col & 7) << 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o +
+                                                                   4 * ROW_BYTES));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// Wait until this wave's outstanding global loads (including direct-to-LDS
+// loads) have landed.
+// s_waitcnt simm16 on gfx9: vmcnt in bits [3:0] and [15:14], expcnt in
+// [6:4], lgkmcnt in [11:8]; 0x0F70 = vmcnt(0) with the other counters free.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace lcattn

@@ -42,12 +42,18 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;  // workspace: <dO_i, O_i> per query row
+  float* delta;  // workspace: <dO_i, O_i> per query row, then the dK/dV partials
   int Hq, Hkv, G;
   long long N;
   float scale;
   int causal;
 };
+
+// Backward workspace: Dv per query row (fp32, padded to 64 floats), then, for
+// grouped-query attention (Hq != Hkv), per-query-head fp32 partials of dK and
+// dV ([B, Hq, N, D] each).
+long long bwd_delta_floats(int B, int Hq, long long N);
+long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long N, int D);
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream);
 
