@@ -48,6 +48,44 @@ def pair_flops_block(Hq, D, N, a, b):
     return 4.0 * Hq * D * pairs
 
 
+def kernel_source_digest(name):
+    """sha256 of the sources a kernel is compiled from (to tell whether
+    committed counter figures still describe it)."""
+    csrc = os.path.join(ROOT, "long_context_attention_fwd_amd", "csrc")
+    files = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip", "attn_fwd_kernel": "attn_fwd.hip",
+             "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}.get(name)
+    if files is None:
+        return None
+    h = hashlib.sha256()
+    for f in (files, "device_common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_digest(name):
+        return None
+    try:
+        return {"read_bytes": float(fields["read_bytes_per_launch"]),
+                "write_bytes": float(fields["write_bytes_per_launch"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -162,11 +200,15 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     all_marks = []
     torch.cuda.synchronize()
+    lc.trace_collect()          # drop records of the warmup
+    lc.trace_enable(True)       # every library kernel bracketed by HIP events
     t_start.record(stream)
     for _ in range(args.steps):
         all_marks.append(step(True))
     t_end.record(stream)
     torch.cuda.synchronize()
+    lc.trace_enable(False)
+    traced = lc.trace_collect()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     per = {n: 0.0 for n in names}
@@ -205,14 +247,45 @@ def main():
                                          "GB/s": gbps(relayout_out_bytes, per["relayout_out"]),
                                          "frac_peak": gbps(relayout_out_bytes, per["relayout_out"]) / PEAK_HBM_GBPS},
     }
-    # dominant kernel of the step: the largest share of its time
-    dom = max(("fwd", "bwd"), key=lambda n: per[n])
-    dom_flops = f_fwd if dom == "fwd" else f_bwd
-    achieved = tflops(dom_flops, per[dom])
-    roofline = {"bound": "mfma", "kernel": "attn_fwd" if dom == "fwd" else "attn_bwd",
-                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "algorithmic_flops_per_launch": dom_flops}
+    # Per GPU kernel, from the library's HIP events over the timed region:
+    # algorithmic work of all its launches / its total time.  The backward's
+    # five counted contractions are S, dP, dV, dK (dK/dV kernel) and dQ (dQ
+    # kernel); the dQ kernel's recomputed S and dP are not counted.
+    alg = {
+        "attn_fwd_kernel": ("TFLOP/s", args.steps * (f_fwd + f_ring)),
+        "bwd_dkdv_kernel": ("TFLOP/s", args.steps * 0.8 * f_bwd),
+        "bwd_dq_kernel": ("TFLOP/s", args.steps * 0.2 * f_bwd),
+        "transpose_rows_kernel": ("GB/s", args.steps * (relayout_in_bytes + relayout_out_bytes)),
+        "merge_kernel": ("GB/s", args.steps * merge_bytes),
+        "bwd_delta_kernel": ("GB/s", args.steps * 2 * 2 * o_ring.numel() + args.steps * 4 * lse.numel()),
+        "bwd_dkdv_reduce_kernel": ("GB/s", args.steps * (2 * 4 * hq + 2 * 2 * hkv) * N * D),
+    }
+    gpu_kernels = {}
+    for name, (tot_ms, calls) in traced.items():
+        unit, work = alg.get(name, (None, None))
+        ent = {"calls_per_step": calls / args.steps, "avg_us": round(1e3 * tot_ms / calls, 2),
+               "share_of_step": round(tot_ms / total_ms, 4)}
+        if unit == "TFLOP/s":
+            ent["TFLOP/s"] = round(tflops(work, tot_ms), 2)
+            ent["frac_peak"] = round(tflops(work, tot_ms) / PEAK_BF16_TFLOPS, 4)
+        elif unit == "GB/s":
+            ent["GB/s"] = round(gbps(work, tot_ms), 1)
+            ent["frac_peak"] = round(gbps(work, tot_ms) / PEAK_HBM_GBPS, 4)
+        gpu_kernels[name] = ent
+    dom = max(traced, key=lambda n: traced[n][0])
+    tot_ms, calls = traced[dom]
+    unit, work = alg[dom]
+    mfma = unit == "TFLOP/s"
+    achieved = tflops(work, tot_ms) if mfma else gbps(work, tot_ms)
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBPS
+    roofline = {"bound": "mfma" if mfma else "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": None, "avg_launch_us": round(1e3 * tot_ms / calls, 2),
+                "algorithmic_per_launch": work / calls}
+    t = measured_traffic(dom)
+    if t is not None:
+        roofline["traffic"] = t["read_bytes"] + t["write_bytes"]
+        roofline["traffic_detail"] = t
 
     out = {
         "metric": "causal attention TFLOP/s fwd/bwd at 1 GPU + % bf16 MFMA peak; relayout GB/s",
@@ -230,8 +303,9 @@ def main():
         "config": {"workload": w.name, "P": P, "N": N, "Hq_total": Hq, "Hkv_total": Hkv, "D": D,
                    "shard_heads_q": hq, "shard_heads_kv": hkv, "causal": True, "ring_blocks": n_blk,
                    "step": "relayout q,k,v,dO -> fwd -> 4 partial fwd + merge -> bwd -> relayout o,dq,dk,dv"},
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kernels.items()},
+        "phases": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in kernels.items()},
+        "gpu_kernels": gpu_kernels,
         "roofline": roofline,
         "device": torch.cuda.get_device_name(dev),
     }

@@ -22,7 +22,8 @@
  *  - bf16 tensors hold raw bfloat16 words; LSE and fp32 tensors hold float.
  *  - Ownership: the caller owns every buffer, including the backward
  *    workspace.  The library allocates and frees no device memory and keeps no
- *    global state apart from a thread-local error text.
+ *    global state apart from a thread-local error text (and the records of
+ *    the optional measurement hook below).
  *  - Asynchrony: each call validates its arguments on the host, then enqueues
  *    its kernels on `hip_stream` (a hipStream_t; NULL = the default stream)
  *    and returns.  A validation failure returns a nonzero status before
@@ -137,6 +138,21 @@ int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int
 /* head_to_seq_relayout -- the inverse: in [P, H/P, N, D] -> out [P, N/P, H, D]. */
 int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
                          void* hip_stream);
+
+/*
+ * Measurement hook (not part of the computation).  While enabled, every
+ * kernel the library launches is bracketed by two HIP events recorded on its
+ * launch stream (at most 8192 launches are held).  attn_trace_collect waits
+ * for those events, writes per-kernel totals -- the kernel's name into
+ * names + i*name_len (NUL-terminated), the summed milliseconds into
+ * total_ms[i] and the launch count into calls[i] for i < max_kernels --
+ * releases the records and returns the number of distinct kernels, or
+ * -ATTN_ERR_HIP if an event could not be read.  The events are created once
+ * and reused; this is the library's only state besides the thread-local
+ * error text.  Thread-safe.
+ */
+int attn_trace_enable(int on);
+int attn_trace_collect(char* names, int name_len, double* total_ms, int* calls, int max_kernels);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

@@ -26,6 +26,8 @@ __all__ = [
     "attn_bwd_workspace_size",
     "seq_to_head_relayout",
     "head_to_seq_relayout",
+    "trace_enable",
+    "trace_collect",
     "AttnError",
     "lib",
     "LIB_PATH",
@@ -62,6 +64,8 @@ _SIGS = {
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
     "seq_to_head_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
     "head_to_seq_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
+    "attn_trace_enable": (_I, [_I]),
+    "attn_trace_collect": (_I, [ctypes.c_char_p, _I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I), _I]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -237,3 +241,25 @@ def seq_to_head_relayout(x, P: int, *, out=None):
 def head_to_seq_relayout(y, P: int, *, out=None):
     """[P, H/P, N, D] -> [P, N/P, H, D] (bit copy)."""
     return _relayout("head_to_seq_relayout", y, P, out, False)
+
+
+def trace_enable(on: bool = True) -> None:
+    """Bracket every kernel the library launches with HIP events (measurement only)."""
+    _check(lib().attn_trace_enable(1 if on else 0))
+
+
+def trace_collect(max_kernels: int = 64) -> dict:
+    """Per-kernel {name: (total_ms, calls)} of the launches recorded since the
+    last collect; waits for their events."""
+    name_len = 64
+    names = ctypes.create_string_buffer(name_len * max_kernels)
+    tot = (ctypes.c_double * max_kernels)()
+    calls = (ctypes.c_int * max_kernels)()
+    n = lib().attn_trace_collect(names, name_len, tot, calls, max_kernels)
+    if n < 0:
+        raise AttnError(-n, "trace events could not be read")
+    out = {}
+    for i in range(n):
+        nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (tot[i], calls[i])
+    return out

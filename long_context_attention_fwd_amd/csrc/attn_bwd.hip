@@ -33,6 +33,7 @@
 // of 5) but avoids fp32 atomic traffic proportional to N^2 / tile.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "trace.hpp"
 
 namespace lcattn {
 
@@ -437,21 +438,21 @@ template <int D>
 hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
   const long long rows = (long long)B * a.Hq * a.N;
   const long long threads = rows * (D / 8);
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.o,
+  LCATTN_LAUNCH("bwd_delta_kernel", (bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.o,
                      a.d_o, a.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 kgrid((unsigned)((a.N + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
   if (a.G == 1) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, nullptr, nullptr);
+    LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, nullptr, nullptr);
   } else {
     float* dk_part = a.delta + bwd_delta_floats(B, a.Hq, a.N);
     float* dv_part = dk_part + (long long)B * a.Hq * a.N * D;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, dk_part, dv_part);
+    LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, dk_part, dv_part);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long slots = (long long)B * a.Hkv * a.N * D / 4;
-    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream,
+    LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream,
                        dk_part, dv_part, a.dk, a.dv, a.G, (long long)B * a.Hkv, a.N);
   }
   e = hipGetLastError();
@@ -461,11 +462,11 @@ hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
   const int n_qt = (int)((a.N + span - 1) / span);
   dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
   if (HP == 4)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
   else if (HP == 2)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
   return hipGetLastError();
 }
 

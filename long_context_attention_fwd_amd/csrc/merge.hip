@@ -17,6 +17,7 @@
 // 16-byte bf16 slice is written.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "trace.hpp"
 
 namespace lcattn {
 
@@ -78,7 +79,7 @@ hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float
   const long long threads = rows * (D / 8);
   const unsigned blocks = (unsigned)((threads + kMergeThreads - 1) / kMergeThreads);
 #define LCATTN_MERGE(DD, F32)                                                                      \
-  hipLaunchKernelGGL((merge_kernel<DD, F32>), dim3(blocks), dim3(kMergeThreads), 0, stream, o_parts, \
+  LCATTN_LAUNCH("merge_kernel", (merge_kernel<DD, F32>), dim3(blocks), dim3(kMergeThreads), 0, stream, o_parts, \
                      lse_parts, n_parts, rows, o, lse)
   if (D == 64) {
     if (parts_f32) LCATTN_MERGE(64, true); else LCATTN_MERGE(64, false);

@@ -16,6 +16,7 @@
 // non-temporal because the output is not re-read by this kernel.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "trace.hpp"
 
 namespace lcattn {
 
@@ -60,7 +61,7 @@ hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned
   const unsigned total = A * Bn * units;
   const unsigned per_block = kRelayoutThreads * kRelayoutUnroll;
   const unsigned blocks = (total + per_block - 1) / per_block;
-  hipLaunchKernelGGL(transpose_rows_kernel, dim3(blocks), dim3(kRelayoutThreads), 0, stream,
+  LCATTN_LAUNCH("transpose_rows_kernel", transpose_rows_kernel, dim3(blocks), dim3(kRelayoutThreads), 0, stream,
                      static_cast<const u32x4*>(in), static_cast<u32x4*>(out), A, Bn, lg, total);
   return hipGetLastError();
 }

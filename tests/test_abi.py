@@ -129,3 +129,9 @@ def test_binding_raises_on_missing_gpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         lc.attn_fwd(x, x, x)
+
+
+def test_trace_hook_without_launches(L):
+    assert L.attn_trace_enable(1) == 0
+    assert lc.trace_collect() == {}
+    assert L.attn_trace_enable(0) == 0
