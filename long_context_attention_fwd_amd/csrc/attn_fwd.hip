@@ -26,8 +26,17 @@
 //    per-row XOR swizzle of 16-byte units.  K fragments are plain 16-byte
 //    reads; the V^T fragments of the PV product come from the row-major V tile
 //    through the transposing LDS read (ds_read_b64_tr_b16, two per fragment).
-//  * Tiles are double buffered: the next tile's direct loads are issued before
-//    the current tile's math, and one wait + barrier per tile hands over.
+//  * Pipeline over three LDS buffers: iteration j issues the direct loads of
+//    tile j+1, computes S(j) = K(j) Q^T, then the PV product of tile j-1 and
+//    the softmax of tile j (independent MFMA and VALU work), then one
+//    wait + barrier.  The transposing reads are issued through inline
+//    assembly with explicit lgkmcnt waits: the compiler cannot tell which
+//    LDS buffer such a read touches and would otherwise wait for the in-flight
+//    direct loads of tile j+1 before it.  The K reads are ordinary loads of
+//    distinct __shared__ objects, which it can tell apart.
+//  * Tiles that need no element mask for any wave run in a straight-line loop
+//    unrolled over the three buffers; the diagonal and tail tiles run a masked
+//    copy with buffers chosen at run time.
 //  * Online softmax in base 2 with the exact running maximum, so the largest
 //    weight of a row is exactly 1 and carries no bf16 rounding into P V (a
 //    stale maximum would let it pick up 2^-9 relative error, which shows on
@@ -41,6 +50,9 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "trace.hpp"
+
+#include <type_traits>
+
 
 namespace lcattn {
 
@@ -121,6 +133,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   float m_run[QB], l_run[QB];
   bf16x8 pf[QB][4];  // P of the previous tile, waiting for its PV product
 #pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pf[qb][u] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
@@ -130,17 +146,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
       for (int v = 0; v < 16; ++v) acc[qb][db][v] = 0.f;
   }
   bool prev_active = false;
+  const typename T::RowAddr ra = T::row_addr(swap_bits23(c), grp);
+  const typename T::TrAddr ta = T::tr_addr(lane);
 
   // O^T += V^T P^T for the tile whose V sits in buf
   auto pv = [&](const unsigned char* buf) __attribute__((always_inline)) {
-    const unsigned char* vs = buf + T::BYTES;
+    const unsigned vbase = (unsigned)reinterpret_cast<uintptr_t>(buf + T::BYTES);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      u32x4 f0 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 0, db));
+      u32x4 f1 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 16, db));
+      u32x4 f2 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 32, db));
+      u32x4 f3 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 48, db));
+      lds_wait_frags(f0, f1, f2, f3);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 vf = T::tr_frag(vs, 16 * u, db * 32, lane);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vf, pf[qb][u], acc[qb][db]);
+      for (int qb = 0; qb < QB; ++qb) {
+        acc[qb][db] = mfma32x32x16(as_bf16x8(f0), pf[qb][0], acc[qb][db]);
+        acc[qb][db] = mfma32x32x16(as_bf16x8(f1), pf[qb][1], acc[qb][db]);
+        acc[qb][db] = mfma32x32x16(as_bf16x8(f2), pf[qb][2], acc[qb][db]);
+        acc[qb][db] = mfma32x32x16(as_bf16x8(f3), pf[qb][3], acc[qb][db]);
       }
     }
   };
@@ -148,105 +172,125 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   wait_vmem();
   __syncthreads();
 
-  // one iteration: PV of tile j-1, prefetch of tile j+1, S and softmax of tile j
-  auto step = [&](int j, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt) __attribute__((always_inline)) {
-    if (prev_active) pv(prev);
-    if (j + 1 < n_tiles) issue(j + 1, nxt);
-    const unsigned char* ks = cur;
+  // one iteration: prefetch of tile j+1, S(j), then the PV product of tile
+  // j-1 (independent MFMAs) interleaved with the softmax of tile j (VALU).
+  // The body is straight-line code (one copy with the element mask, one
+  // without) so the scheduler can mix the two; a tile that is entirely past
+  // this wave's queries runs the masked copy and contributes nothing.
+  auto body = [&](auto masked_tag, int j, const unsigned char* prev, const unsigned char* cur, float* alpha_q)
+                  __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const long long kt = (long long)j * kBN;
-    const bool wave_active = wave_live && (!a.causal || a.k_pos0 + kt <= wpos_last);
-    prev_active = wave_active;
-    if (wave_active) {
-      const bool need_mask = (kt + kBN > a.Nk) || (a.causal && a.k_pos0 + kt + kBN - 1 > wpos_first);
-      // S^T for the two 32-key halves of the tile
-      f32x16 s[QB][2];
+    f32x16 s[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[qb][kb][v] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const bf16x8 kf = T::row_frag_at(cur, ra, t, kb * 32);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][t], s[qb][kb]);
+      }
+    }
+    pv(prev);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (MASKED) {
+        const int qrow = (int)(wq0 + qb * 32 + c);
+        const int klim = (int)min(a.Nk, (long long)INT32_MAX);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = (int)kt + kb * 32 + acc_row_pi(v, grp);
+            const bool vis = key < klim && (!a.causal || key - qrow <= dpos);
+            s[qb][kb][v] = vis ? s[qb][kb][v] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mx2 = mx * a.scale_log2;
+      const float m_old = m_run[qb];
+      const float m_new = fmaxf(m_old, mx2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha_q[qb] = (m_new == m_old) ? 1.f : fast_exp2(m_old - m_new);
+      m_run[qb] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(__builtin_fmaf(s[qb][kb][v], a.scale_log2, -m_use));
+          s[qb][kb][v] = p;
+          lsum += p;
+        }
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          const int o8 = 8 * uu;
+          pf[qb][2 * kb + uu] = pack_bf16x8(s[qb][kb][o8 + 0], s[qb][kb][o8 + 1], s[qb][kb][o8 + 2],
+                                            s[qb][kb][o8 + 3], s[qb][kb][o8 + 4], s[qb][kb][o8 + 5],
+                                            s[qb][kb][o8 + 6], s[qb][kb][o8 + 7]);
+        }
+      }
+      l_run[qb] = l_run[qb] * alpha_q[qb] + lsum;
+    }
+  };
+  auto finish = [&](const float* alpha_q) __attribute__((always_inline)) {
+    // rescale the accumulator (after the PV product of the previous tile)
+    bool any_rescale = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any_rescale |= alpha_q[qb] != 1.f;
+    if (__any(any_rescale)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[qb][kb][v] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + swap_bits23(c);
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          const bf16x8 kf = T::row_frag(ks, row, t, grp);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][t], s[qb][kb]);
-        }
-      }
-      // mask, online softmax, pack P (the PV product follows next iteration)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (need_mask) {
-          // 32-bit index math: key k is visible to query row r iff
-          // k < Nk and (not causal or k - r <= q_pos0 - k_pos0)
-          const int qrow = (int)(wq0 + qb * 32 + c);
-          const int klim = (int)min(a.Nk, (long long)INT32_MAX);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = (int)kt + kb * 32 + acc_row_pi(v, grp);
-              const bool vis = key < klim && (!a.causal || key - qrow <= dpos);
-              if (!vis) s[qb][kb][v] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mx2 = mx * a.scale_log2;
-        const float m_old = m_run[qb];
-        const float m_new = fmaxf(m_old, mx2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = (m_new == m_old) ? 1.f : fast_exp2(m_old - m_new);
-        m_run[qb] = m_new;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = fast_exp2(__builtin_fmaf(s[qb][kb][v], a.scale_log2, -m_use));
-            s[qb][kb][v] = p;
-            lsum += p;
-          }
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) {
-            const int o8 = 8 * uu;
-            pf[qb][2 * kb + uu] = pack_bf16x8(s[qb][kb][o8 + 0], s[qb][kb][o8 + 1], s[qb][kb][o8 + 2],
-                                              s[qb][kb][o8 + 3], s[qb][kb][o8 + 4], s[qb][kb][o8 + 5],
-                                              s[qb][kb][o8 + 6], s[qb][kb][o8 + 7]);
-          }
-        }
-        l_run[qb] = l_run[qb] * alpha + lsum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[qb][db][v] *= alpha;
-        }
-      }
+          for (int v = 0; v < 16; ++v) acc[qb][db][v] *= alpha_q[qb];
     }
-    wait_vmem();  // this wave's part of tile j + 1 has landed in LDS
+    wait_vmem();  // this wave's part of the next tile has landed in LDS
     __syncthreads();
   };
+  // Tiles [0, n_full) need no element mask for any wave of the workgroup:
+  // every key precedes the workgroup's first query and lies inside Nk.
+  long long full_keys = a.Nk;
+  if (a.causal) full_keys = min(full_keys, max(0LL, a.q_pos0 + q_start - a.k_pos0 + 1));
+  const int n_full = (int)min((long long)n_tiles, full_keys / kBN);
+  auto step_full = [&](int j, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt)
+                       __attribute__((always_inline)) {
+    issue(min(j + 1, n_tiles - 1), nxt);  // the last tile reloads itself into the free buffer
+    float alpha_q[QB];
+    body(std::false_type{}, j, prev, cur, alpha_q);
+    finish(alpha_q);
+  };
   int j = 0;
-  for (; j + 3 <= n_tiles; j += 3) {
-    step(j, smem2, smem0, smem1);
-    step(j + 1, smem0, smem1, smem2);
-    step(j + 2, smem1, smem2, smem0);
+  for (; j + 3 <= n_full; j += 3) {
+    step_full(j, smem2, smem0, smem1);
+    step_full(j + 1, smem0, smem1, smem2);
+    step_full(j + 2, smem1, smem2, smem0);
   }
-  if (j < n_tiles) step(j, smem2, smem0, smem1);
-  if (j + 1 < n_tiles) step(j + 1, smem0, smem1, smem2);
+  // the rest (the diagonal and tail tiles): buffers chosen at run time
+  auto buf = [&](int i) __attribute__((always_inline)) {
+    const int r = i % 3;
+    return r == 0 ? smem0 : (r == 1 ? smem1 : smem2);
+  };
+  for (; j < n_tiles; ++j) {
+    issue(min(j + 1, n_tiles - 1), buf(j + 1));
+    float alpha_q[QB];
+    body(std::true_type{}, j, buf(j + 2), buf(j), alpha_q);
+    finish(alpha_q);
+  }
   // PV of the last tile
-  if (prev_active) {
-    const int r = (n_tiles - 1) % 3;
-    pv(r == 0 ? smem0 : (r == 1 ? smem1 : smem2));
-  }
+  if (n_tiles > 0) pv(buf(n_tiles - 1));
 
   // ---- epilogue: normalise, write O and LSE ---------------------------------
 #pragma unroll

@@ -128,6 +128,44 @@ struct LdsTile {
     }
   }
 
+  // Per-lane base offsets for the row fragments of rows r + 32k (k any) and
+  // steps t: unit (2t + grp) ^ f(r) = 8 (t >> 2) + ((2 (t & 3)) ^ (grp ^ f(r)))
+  // because 2t and grp occupy different bits and f(r) < 8; so four bases and
+  // immediate offsets cover every t.
+  struct RowAddr {
+    int b[4];
+  };
+  __device__ static RowAddr row_addr(int r, int grp) {
+    RowAddr ra;
+    const int g = grp ^ tile_swz(r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra.b[i] = r * ROW_BYTES + (((2 * i) ^ g) << 4);
+    return ra;
+  }
+  __device__ static bf16x8 row_frag_at(const unsigned char* lds, const RowAddr& ra, int t, int row_off) {
+    return as_bf16x8(ld_lds16(lds, ra.b[t & 3] + (t >> 2) * 128 + row_off * ROW_BYTES));
+  }
+
+  // Per-lane base offsets of the transposed fragments T[r0 + 8 grp + e][d0 + c]
+  // for r0 a multiple of 16 and d0 = 32 db: the unit is (4 db + x) ^ f(row) with
+  // x < 4, which is a0's or a1's unit plus 8 (db >> 1); rows add 16-row steps.
+  struct TrAddr {
+    int a0, a1;
+  };
+  __device__ static TrAddr tr_addr(int lane) {
+    const int gi = lane >> 4, s = lane & 15;
+    const int row = 8 * (gi >> 1) + (s >> 2);
+    const int x = 2 * (gi & 1) + ((s & 3) >> 1);
+    const int y = x ^ tile_swz(row);
+    TrAddr ta;
+    ta.a0 = row * ROW_BYTES + (y << 4) + ((s & 1) << 3);
+    ta.a1 = row * ROW_BYTES + ((y ^ 4) << 4) + ((s & 1) << 3);
+    return ta;
+  }
+  __device__ static int tr_off(const TrAddr& ta, int r0, int db) {
+    return ((db & 1) ? ta.a1 : ta.a0) + (db >> 1) * 128 + r0 * ROW_BYTES;
+  }
+
   // (a) A operand reducing over D: row r (already in pi order), step t.
   __device__ static bf16x8 row_frag(const unsigned char* lds, int r, int t, int grp) {
     return as_bf16x8(ld_lds16(lds, off(r, 2 * t + grp)));
@@ -151,6 +189,27 @@ struct LdsTile {
     return __builtin_bit_cast(bf16x8, v);
   }
 };
+
+// Transposed fragment through inline assembly.  The compiler does not see
+// this as an LDS access, so it inserts neither the vmcnt wait it would place
+// before a transposing read while direct loads are in flight nor the lgkmcnt
+// wait before its result is used: callers must run lds_wait_frags on the
+// fragments before using them.
+template <int ROW_BYTES>
+__device__ __forceinline__ u32x4 tr_frag_asm_at(unsigned lds_base, int off) {
+  u32x2 lo, hi;
+  const unsigned addr = lds_base + off;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(4 * ROW_BYTES));
+  u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+  return r;
+}
+
+// Wait for all of this wave's LDS reads; the fragments pass through the
+// statement so that their uses are ordered after the wait.
+__device__ __forceinline__ void lds_wait_frags(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
 
 // Wait until this wave's outstanding global loads (including direct-to-LDS
 // loads) have landed.
