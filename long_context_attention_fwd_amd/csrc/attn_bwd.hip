@@ -13,14 +13,15 @@
 //  * bwd_delta: Dv per query row, HBM bound.
 //  * bwd_dkdv: a workgroup owns 128 keys (4 waves x 32 keys, K and V of those
 //    keys resident in registers as MFMA operands) and one query head, and
-//    walks every 64-row query tile that can see its keys.  Q and dO tiles
-//    arrive in LDS by direct loads (row-major, swizzled); S = Q K^T and
-//    dP = dO V^T read them by rows, dV^T += dO^T P and dK^T += Q^T dS through
-//    the transposing LDS read.  Query rows are fed to the MFMA in the pi
-//    order, so P and dS leave the accumulators already in the operand layout
-//    of the next product.  Iteration i does the dV/dK products of tile i-1,
-//    then issues tile i+1's loads, then the S/dP products and the elementwise
-//    step of tile i (three LDS buffers).
+//    walks every 64-row query tile that can see them.  Q and dO tiles travel
+//    global -> registers -> LDS (row-major, swizzled; three buffers): S = Q K^T
+//    and dP = dO V^T read them by rows, dV^T += dO^T P and dK^T += Q^T dS
+//    through the transposing LDS read.  Query rows are fed to the MFMA in the
+//    pi order, so P and dS leave the accumulators already in the operand
+//    layout of the next product.  Each 32-row query block is one straight-line
+//    block: its S/dP products, then the dV/dK products of the previous block
+//    interleaved with its own elementwise step (independent MFMA and VALU
+//    work).
 //  * bwd_dkdv_reduce (grouped-query attention only): the per-query-head fp32
 //    partials of dK, dV are summed over the group and rounded to bf16.  One
 //    workgroup per (key tile, query head) gives G times more workgroups than
@@ -34,6 +35,9 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "trace.hpp"
+
+#include <type_traits>
+
 
 namespace lcattn {
 
@@ -78,12 +82,12 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
   constexpr int NW = kDkdvWaves;
+  constexpr int NT = 64 * NW;
   constexpr int BK = 32 * NW;  // keys per workgroup
-  // per buffer: Q tile, dO tile, LSE (64 floats), Dv (64 floats)
+  // per buffer: Q tile, dO tile, LSE*log2(e) (64 floats), Dv (64 floats)
   constexpr int BUF = 2 * T::BYTES + 2 * kBQ * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem0[BUF];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem1[BUF];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem2[BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * BUF];
+  auto buf = [&](int i) __attribute__((always_inline)) { return smem + (i % 3) * BUF; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   const int kvh = h / a.G;
   const long long kt0 = (long long)blockIdx.x * BK;
   const long long kw0 = kt0 + 32 * wave;  // this wave's first key
-  const long long key = kw0 + c;          // this lane's key
+  const int key = (int)(kw0 + c);         // this lane's key
   const float sl = a.scale * kLog2e;
 
   const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
@@ -107,27 +111,26 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   const long long first_tile = a.causal ? kt0 / kBQ : 0;
   const int n_tiles = (int)((N + kBQ - 1) / kBQ - first_tile);
 
-  auto issue = [&](int i, unsigned char* buf) __attribute__((always_inline)) {
+  // global -> registers -> LDS staging of one query tile
+  typename T::template Stage<NT> qst, ost;
+  float lv = 0.f;
+  auto fetch = [&](int i) __attribute__((always_inline)) {
     const long long r0 = (first_tile + i) * kBQ;
-    T::template load_async<NW>(buf, qbase, r0, N, wave, lane);
-    T::template load_async<NW>(buf + T::BYTES, obase, r0, N, wave, lane);
-    // LSE and Dv of the tile's 64 rows, one dword per lane (rows past N
-    // repeat row N-1; they are masked)
-    if (wave == 0) {
-      long long row = r0 + lane;
+    qst.load(qbase, r0, N, tid);
+    ost.load(obase, r0, N, tid);
+    if (tid < 2 * kBQ) {
+      long long row = r0 + (tid & (kBQ - 1));
       row = row < N ? row : N - 1;
-      unsigned char* dst = buf + 2 * T::BYTES;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(lbase + row),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(dst)),
-                                       4, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dbase + row),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(dst) + kBQ * 4),
-                                       4, 0, 0);
+      lv = tid < kBQ ? lbase[row] * kLog2e : dbase[row];
     }
   };
-  if (n_tiles > 0) issue(0, smem0);
+  auto deposit = [&](int i) __attribute__((always_inline)) {
+    unsigned char* b = buf(i);
+    qst.store(b, tid);
+    ost.store(b + T::BYTES, tid);
+    if (tid < 2 * kBQ) reinterpret_cast<float*>(b + 2 * T::BYTES)[tid] = lv;
+  };
+  if (n_tiles > 0) fetch(0);
 
   // K and V rows of this lane's key as B operands (reduction over D)
   bf16x8 kf[KT], vf[KT];
@@ -135,8 +138,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   for (int t = 0; t < KT; ++t) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (key < N) {
-      x = ld_global16(kbase + key * D + 16 * t + 8 * grp);
-      y = ld_global16(vbase + key * D + 16 * t + 8 * grp);
+      x = ld_global16(kbase + (long long)key * D + 16 * t + 8 * grp);
+      y = ld_global16(vbase + (long long)key * D + 16 * t + 8 * grp);
     }
     kf[t] = as_bf16x8(x);
     vf[t] = as_bf16x8(y);
@@ -150,95 +153,131 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
       dk_acc[db][v] = 0.f;
       dv_acc[db][v] = 0.f;
     }
-  // P and dS of the previous tile (2 query blocks x 2 halves), pending products
-  bf16x8 pb[2][2], sb[2][2];
-  bool live0 = false, live1 = false;  // query blocks of the previous tile with work
-
-  // products of one 32-row query block of the tile in buf
-  auto block_products = [&](const unsigned char* buf, int qb) __attribute__((always_inline)) {
+  // P and dS of the previous 32-row query block (zero before the first)
+  bf16x8 pb[2], sb[2];
 #pragma unroll
-    for (int dbk = 0; dbk < DB; ++dbk) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r0 = qb * 32 + 16 * u;
-        dv_acc[dbk] = mfma32x32x16(T::tr_frag(buf + T::BYTES, r0, dbk * 32, lane), pb[qb][u], dv_acc[dbk]);
-        dk_acc[dbk] = mfma32x32x16(T::tr_frag(buf, r0, dbk * 32, lane), sb[qb][u], dk_acc[dbk]);
-      }
-    }
-  };
-  auto grad_products = [&](const unsigned char* buf) __attribute__((always_inline)) {
-    if (live0) block_products(buf, 0);
-    if (live1) block_products(buf, 1);
-  };
+  for (int u = 0; u < 2; ++u) {
+    pb[u] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    sb[u] = pb[u];
+  }
+  const typename T::RowAddr ra = T::row_addr(swap_bits23(c), grp);
+  const typename T::TrAddr ta = T::tr_addr(lane);
 
-  wait_vmem();
+  if (n_tiles > 0) deposit(0);
   __syncthreads();
 
-  auto step = [&](int i, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt) __attribute__((always_inline)) {
-    grad_products(prev);
-    if (i + 1 < n_tiles) issue(i + 1, nxt);
-    const long long qt0 = (first_tile + i) * kBQ;
-    const float* lse_t = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
-    const float* dv_t = lse_t + kBQ;
-    // S, dP and the elementwise step of one 32-row query block
-    auto block_grads = [&](int qb) __attribute__((always_inline)) {
-      const long long qb0 = qt0 + qb * 32;
-      f32x16 s, dp;
+  // One 32-row query block of the tile in cur (rows qb*32 ..): S, dP (MFMA),
+  // then the dV, dK products of the previous block (whose tile sits in pbuf at
+  // rows pqb*32 ..) next to this block's elementwise step (VALU).  Straight-
+  // line code; a block with nothing visible runs masked and adds zero.
+  auto block = [&](auto masked_tag, const unsigned char* cur, int qb, long long qt0, const unsigned char* pbuf,
+                   int pqb) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    bf16x8 qrf[KT], orf[KT];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[v] = 0.f;
-        dp[v] = 0.f;
-      }
-      const int arow = qb * 32 + swap_bits23(c);
+    for (int t = 0; t < KT; ++t) {
+      qrf[t] = T::row_frag_at(cur, ra, t, qb * 32);
+      orf[t] = T::row_frag_at(cur + T::BYTES, ra, t, qb * 32);
+    }
+    f32x16 s, dp;
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        s = mfma32x32x16(T::row_frag(cur, arow, t, grp), kf[t], s);
-        dp = mfma32x32x16(T::row_frag(cur + T::BYTES, arow, t, grp), vf[t], dp);
-      }
-      const bool need_mask = (a.causal && qb0 < kw0 + 31) || qb0 + 32 > N;
+    for (int v = 0; v < 16; ++v) {
+      s[v] = 0.f;
+      dp[v] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      s = mfma32x32x16(qrf[t], kf[t], s);
+      dp = mfma32x32x16(orf[t], vf[t], dp);
+    }
+    // previous block's products
+    bf16x8 tq[DB][2], to[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int r0 = qb * 32 + 16 * u + 8 * grp;  // tile rows of registers 8u..8u+7
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_t + r0);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_t + r0 + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dv_t + r0);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dv_t + r0 + 4);
-        float p[8], ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dvv = e < 4 ? d0[e] : d1[e - 4];
-          float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lv * kLog2e));
-          if (need_mask) {
-            const int qrow = (int)qt0 + r0 + e;
-            if (qrow >= (int)N || (a.causal && qrow < (int)key)) pe = 0.f;
-          }
-          p[e] = pe;
-          ds[e] = pe * (dp[8 * u + e] - dvv);
-        }
-        pb[qb][u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        sb[qb][u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        const int o = T::tr_off(ta, pqb * 32 + 16 * u, db);
+        tq[db][u] = T::tr_frag_at(pbuf, o);
+        to[db][u] = T::tr_frag_at(pbuf + T::BYTES, o);
       }
-    };
-    // a block has work unless all its queries precede every key of the wave
-    live0 = !(a.causal && qt0 + 31 < kw0) && qt0 < N && kw0 < N;
-    live1 = !(a.causal && qt0 + 63 < kw0) && qt0 + 32 < N && kw0 < N;
-    if (live0) block_grads(0);
-    if (live1) block_grads(1);
-    wait_vmem();
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        dv_acc[db] = mfma32x32x16(to[db][u], pb[u], dv_acc[db]);
+        dk_acc[db] = mfma32x32x16(tq[db][u], sb[u], dk_acc[db]);
+      }
+    // this block's elementwise step
+    const float* lse_t = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
+    const float* dv_t = lse_t + kBQ;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = qb * 32 + 16 * u + 8 * grp;  // tile rows of registers 8u..8u+7
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_t + r0);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_t + r0 + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dv_t + r0);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dv_t + r0 + 4);
+      float p[8], ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float lv2 = e < 4 ? l0[e] : l1[e - 4];
+        const float dvv = e < 4 ? d0[e] : d1[e - 4];
+        float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lv2));
+        if (MASKED) {
+          const int qrow = (int)qt0 + r0 + e;
+          pe = (qrow >= (int)N || (a.causal && qrow < key)) ? 0.f : pe;
+        }
+        p[e] = pe;
+        ds[e] = pe * (dp[8 * u + e] - dvv);
+      }
+      pb[u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      sb[u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    }
+    // Instruction order for the scheduler (groups: 0x100 LDS reads, 0x008
+    // MFMA, 0x002 VALU): the 16 row fragments, the 16 S/dP products, the
+    // transposed fragments and LSE/Dv reads, then each dV/dK product followed
+    // by a slice of the elementwise step, so the matrix cores and the vector
+    // ALU work side by side.
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 36, 0);
+#pragma unroll
+    for (int i_ = 0; i_ < 16; ++i_) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+  };
+  // one query tile: prefetch the next into registers, two blocks, deposit
+  auto step = [&](auto masked_tag, int i) __attribute__((always_inline)) {
+    const bool more = i + 1 < n_tiles;
+    if (more) fetch(i + 1);
+    const long long qt0 = (first_tile + i) * kBQ;
+    // before the first block the pending P, dS are zero; point the products at
+    // this tile (finite data) rather than an unwritten buffer
+    block(masked_tag, buf(i), 0, qt0, i == 0 ? buf(i) : buf(i + 2), 1);
+    block(masked_tag, buf(i), 1, qt0, buf(i), 0);
+    if (more) deposit(i + 1);
     __syncthreads();
   };
+  // masked tiles: those that hold the diagonal of some wave's keys, and the tail
+  const int head = a.causal ? (int)min((long long)n_tiles, (kt0 + BK - first_tile * kBQ + kBQ - 1) / kBQ) : 0;
+  const bool tail = (N % kBQ) != 0;
+  const int body_end = max(head, n_tiles - (tail ? 1 : 0));
   int i = 0;
-  for (; i + 3 <= n_tiles; i += 3) {
-    step(i, smem2, smem0, smem1);
-    step(i + 1, smem0, smem1, smem2);
-    step(i + 2, smem1, smem2, smem0);
-  }
-  if (i < n_tiles) step(i, smem2, smem0, smem1);
-  if (i + 1 < n_tiles) step(i + 1, smem0, smem1, smem2);
+  for (; i < head; ++i) step(std::true_type{}, i);
+  for (; i < body_end; ++i) step(std::false_type{}, i);
+  for (; i < n_tiles; ++i) step(std::true_type{}, i);
+  // products of the last block
   if (n_tiles > 0) {
-    const int r = (n_tiles - 1) % 3;
-    grad_products(r == 0 ? smem0 : (r == 1 ? smem1 : smem2));
+    const unsigned char* pbuf = buf(n_tiles - 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int o = T::tr_off(ta, 32 + 16 * u, db);
+        dv_acc[db] = mfma32x32x16(T::tr_frag_at(pbuf + T::BYTES, o), pb[u], dv_acc[db]);
+        dk_acc[db] = mfma32x32x16(T::tr_frag_at(pbuf, o), sb[u], dk_acc[db]);
+      }
   }
 
   if (key < N) {

@@ -166,6 +166,48 @@ struct LdsTile {
     return ((db & 1) ? ta.a1 : ta.a0) + (db >> 1) * 128 + r0 * ROW_BYTES;
   }
 
+  // Register-staged tile load: NT threads fetch rows [r0, r0 + 64) of a
+  // row-major [rows_total, D] matrix into CH 16-byte registers each, then store
+  // them into the swizzled LDS tile.  Rows past rows_total read row
+  // rows_total - 1 (finite data that the callers mask).
+  template <int NT>
+  struct Stage {
+    static constexpr int CH = 64 * UNITS / NT;
+    static_assert(CH >= 1 && 64 * UNITS % NT == 0, "threads must divide the tile");
+    u32x4 r[CH];
+    __device__ void load(const uint16_t* g, long long r0, long long rows_total, int tid) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int id = tid + i * NT;
+        const int row = id / UNITS, u = id % UNITS;
+        long long gr = r0 + row;
+        gr = gr < rows_total ? gr : rows_total - 1;
+        r[i] = ld_global16(g + gr * D + 8 * u);
+      }
+    }
+    __device__ void store(unsigned char* lds, int tid) const {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int id = tid + i * NT;
+        const int row = id / UNITS, u = id % UNITS;
+        st_lds16(lds, off(row, u), r[i]);
+      }
+    }
+  };
+
+  // Transposed fragment at a precomputed offset (see tr_addr / tr_off).
+  __device__ static bf16x8 tr_frag_at(const unsigned char* lds, int o) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o +
+                                                                   4 * ROW_BYTES));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+
   // (a) A operand reducing over D: row r (already in pi order), step t.
   __device__ static bf16x8 row_frag(const unsigned char* lds, int r, int t, int grp) {
     return as_bf16x8(ld_lds16(lds, off(r, 2 * t + grp)));
