@@ -8,7 +8,8 @@ tokens split P = 8 ways), with inputs already resident in HBM:
   1. seq_to_head_relayout of Q, K, V, dO (all P shards)   -- the all-to-all's data movement
   2. attn_fwd on shard 0 (4 query heads, 1 KV head, causal GQA, N = 32768)
   3. the ring form of the same forward: 4 partial attn_fwd calls over
-     8192-key blocks (fp32 partials) + attn_partial_merge
+     8192-key blocks (fp32 partials, run side by side on their own streams)
+     + attn_partial_merge
   4. attn_bwd on shard 0 (from step 2's O and LSE)
   5. head_to_seq_relayout of O, dQ, dK, dV
 
@@ -53,6 +54,7 @@ def kernel_source_digest(name):
     committed counter figures still describe it)."""
     csrc = os.path.join(ROOT, "long_context_attention_fwd_amd", "csrc")
     files = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip", "attn_fwd_kernel": "attn_fwd.hip",
+             "attn_fwd_kernel_fp32out": "attn_fwd.hip",
              "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}.get(name)
     if files is None:
         return None
@@ -154,6 +156,7 @@ def main():
     ws = torch.empty(lc.attn_bwd_workspace_size(1, hq, hkv, N, D), dtype=torch.uint8, device=dev)
     scale = w.scale
     stream = torch.cuda.current_stream(dev)
+    ring_streams = [torch.cuda.Stream(dev) for _ in range(n_blk)]  # default priority
 
     names = ["relayout_in", "fwd", "ring_partials", "merge", "bwd", "relayout_out"]
     ev = {n: [] for n in names}
@@ -174,10 +177,21 @@ def main():
         q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
         lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
         mark()
+        # The ring's partials, one per KV block [a, a + blk).  All blocks are
+        # resident on this GPU and independent, so they run side by side on
+        # their own streams (a late block has work only for the last queries
+        # and alone would leave most CUs idle); the merge waits for all.
+        fork = torch.cuda.Event()
+        fork.record(stream)
         for i, a in enumerate(range(0, N, blk)):
-            # one ring step: the queries against KV block [a, a + blk)
-            lc.attn_fwd(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], causal=True, scale=scale, k_pos0=a,
-                        out_dtype=torch.float32, o=o_parts[i], lse=lse_parts[i])
+            side = ring_streams[i]
+            side.wait_event(fork)
+            with torch.cuda.stream(side):
+                lc.attn_fwd(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], causal=True, scale=scale, k_pos0=a,
+                            out_dtype=torch.float32, o=o_parts[i], lse=lse_parts[i])
+            join = torch.cuda.Event()
+            join.record(side)
+            stream.wait_event(join)
         mark()
         lc.attn_partial_merge(o_parts, lse_parts, o=o_ring, lse=lse_ring)
         mark()
@@ -251,8 +265,12 @@ def main():
     # algorithmic work of all its launches / its total time.  The backward's
     # five counted contractions are S, dP, dV, dK (dK/dV kernel) and dQ (dQ
     # kernel); the dQ kernel's recomputed S and dP are not counted.
+    OVERLAPPED = {"attn_fwd_kernel_fp32out"}
     alg = {
-        "attn_fwd_kernel": ("TFLOP/s", args.steps * (f_fwd + f_ring)),
+        "attn_fwd_kernel": ("TFLOP/s", args.steps * f_fwd),
+        # the ring partials overlap one another, so their summed kernel time
+        # exceeds the wall time of that phase (see phases.ring_partials_x4)
+        "attn_fwd_kernel_fp32out": ("TFLOP/s", args.steps * f_ring),
         "bwd_dkdv_kernel": ("TFLOP/s", args.steps * 0.8 * f_bwd),
         "bwd_dq_kernel": ("TFLOP/s", args.steps * 0.2 * f_bwd),
         "transpose_rows_kernel": ("GB/s", args.steps * (relayout_in_bytes + relayout_out_bytes)),
@@ -271,8 +289,12 @@ def main():
         elif unit == "GB/s":
             ent["GB/s"] = round(gbps(work, tot_ms), 1)
             ent["frac_peak"] = round(gbps(work, tot_ms) / PEAK_HBM_GBPS, 4)
+        if name in OVERLAPPED:
+            ent["overlapped"] = True  # launches share the GPU: avg_us is not one launch's own time
         gpu_kernels[name] = ent
-    dom = max(traced, key=lambda n: traced[n][0])
+    # The dominant kernel is the one with the most time among kernels that run
+    # alone, so that its launch duration is its own.
+    dom = max((n for n in traced if n not in OVERLAPPED), key=lambda n: traced[n][0])
     tot_ms, calls = traced[dom]
     unit, work = alg[dom]
     mfma = unit == "TFLOP/s"

@@ -325,7 +325,8 @@ hipError_t launch_cfg(const FwdArgs& a, int B, hipStream_t stream) {
   constexpr int SPAN = (kWaves / HP) * 32 * QB;
   const long long n_qtiles = (a.Nq + SPAN - 1) / SPAN;
   dim3 grid((unsigned)n_qtiles, (unsigned)(a.Hq / HP), (unsigned)B);
-  LCATTN_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<D, QB, HP, F32>), grid, dim3(kThreads), 0, stream, a, (int)n_qtiles);
+  LCATTN_LAUNCH(F32 ? "attn_fwd_kernel_fp32out" : "attn_fwd_kernel", (attn_fwd_kernel<D, QB, HP, F32>), grid,
+                dim3(kThreads), 0, stream, a, (int)n_qtiles);
   return hipGetLastError();
 }
 
