@@ -64,17 +64,16 @@ constexpr int kBN = 64;         // keys per tile
 
 template <int D, int QB, int HP, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
-  using T = LdsTile<D>;
+  using T = OnePatternTile<D>;
   constexpr int KT = D / 16;       // reduction steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
   constexpr int QW = 32 * QB;      // query rows per wave
   constexpr int SPAN = (kWaves / HP) * QW;  // query rows per workgroup (per head)
+  static_assert(QB == 1, "one block of 32 query rows per wave");
   static_assert(kBN == 64, "LdsTile holds 64 rows");
 
   // Three buffers, each a K tile followed by a V tile (row-major, swizzled),
-  // as separate objects so the compiler can tell them apart.  Iteration j
-  // reads V of tile j-1 and K of tile j while the direct loads of tile j+1
-  // land in the third buffer.
+  // as separate objects so the compiler can tell them apart.
   __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * T::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * T::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char smem2[2 * T::BYTES];
@@ -100,205 +99,237 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     kv_end = max(0LL, min(a.Nk, a.q_pos0 + q_last - a.k_pos0 + 1));
   }
   const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
-
-  // this wave's query range (global positions) for tile skipping and masking
-  const long long wq_end = min(wq0 + QW, a.Nq);
-  const bool wave_live = wq0 < a.Nq;
-  const long long wpos_first = a.q_pos0 + wq0;
-  const long long wpos_last = a.q_pos0 + wq_end - 1;
+  const int n_sub = 2 * n_tiles;  // 32-key sub-tiles
   // q_pos0 - k_pos0, clamped to the int range (rows and keys are < 2^31)
   const int dpos = (int)max(min(a.q_pos0 - a.k_pos0, (long long)INT32_MAX), (long long)INT32_MIN + 1);
+  const int qrow = (int)(wq0 + c);
+  const int klim = (int)min(a.Nk, (long long)INT32_MAX);
 
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    T::template load_async<kWaves>(buf, kh, (long long)j * kBN, a.Nk, wave, lane);
-    T::template load_async<kWaves>(buf + T::BYTES, vh, (long long)j * kBN, a.Nk, wave, lane);
+    T::template load_async<kWaves, false>(buf, kh, (long long)j * kBN, a.Nk, wave, lane);
+    T::template load_async<kWaves, true>(buf + T::BYTES, vh, (long long)j * kBN, a.Nk, wave, lane);
   };
   if (n_tiles > 0) issue(0, smem0);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds its query row's dims
   // 16t + 8*grp .. +7 for every reduction step t.
-  bf16x8 qf[QB][KT];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const long long row = wq0 + qb * 32 + c;
+  bf16x8 qf[KT];
+  {
+    const long long row = wq0 + c;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row < a.Nq) x = ld_global16(qh + row * D + 16 * t + 8 * grp);
-      qf[qb][t] = as_bf16x8(x);
+      qf[t] = as_bf16x8(x);
     }
   }
 
-  f32x16 acc[QB][DB];
-  float m_run[QB], l_run[QB];
-  bf16x8 pf[QB][4];  // P of the previous tile, waiting for its PV product
+  f32x16 acc[DB];
+  float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pf[qb][u] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+  bf16x8 pf[2];  // P of the sub-tile waiting for its PV product (zero: no-op)
+  pf[0] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  pf[1] = pf[0];
+  // per-lane LDS offsets of the K row fragments and the V^T fragments
+  int koff[KT], voff[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+  for (int t = 0; t < KT; ++t) koff[t] = T::row_off(c, grp, t);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[qb][db][v] = 0.f;
-  }
-  bool prev_active = false;
-  const typename T::RowAddr ra = T::row_addr(swap_bits23(c), grp);
-  const typename T::TrAddr ta = T::tr_addr(lane);
+  for (int db = 0; db < DB; ++db) voff[db] = T::tr_off(lane, db);
 
-  // O^T += V^T P^T for the tile whose V sits in buf
-  auto pv = [&](const unsigned char* buf) __attribute__((always_inline)) {
-    const unsigned vbase = (unsigned)reinterpret_cast<uintptr_t>(buf + T::BYTES);
+  // S^T of the 32 keys in half kh of the K tile in buf (rows in pi order)
+  auto s_sub = [&](const unsigned char* buf, int khalf) __attribute__((always_inline)) {
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      s = mfma32x32x16(as_bf16x8(ld_lds16(buf, koff[t] + 32 * khalf * T::ROW_BYTES)), qf[t], s);
+    return s;
+  };
+
+  // Online softmax of one sub-tile: S^T (one query per lane, 16 of its 32
+  // keys; the other 16 sit in lane ^ 32) -> P packed as the B operand of the
+  // next PV product, the running max / sum, and the rescale factor alpha.
+  auto softmax = [&](auto masked_tag, f32x16 s, int t, float& alpha) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if (MASKED) {
+      const int kt = 32 * t;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kt + acc_row_pi(v, grp);
+        const bool vis = key < klim && (!a.causal || key - qrow <= dpos);
+        s[v] = vis ? s[v] : -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
+    mx = fmaxf(mx, s[15]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max with lane ^ 32
+    }
+    const float m_new = fmaxf(m_run, mx * a.scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, -m_use));
+      ls[v & 3] += s[v];
+    }
+    pf[0] = pack_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
+    pf[1] = pack_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+    l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+  };
+
+  // One step t of the pipeline over 32-key sub-tiles:
+  //   MFMA: S(t+1) from the K half in (kbuf, kh); O^T += V^T P(t-1)^T from the
+  //         V half in (vbuf, vh)
+  //   VALU: softmax of S(t) -> P(t)
+  // The MFMA and VALU work is independent, so it is interleaved one MFMA at
+  // a time.  Returns S(t+1).
+  auto step = [&](auto masked_tag, int t, f32x16 s_cur, const unsigned char* kbuf, int khalf,
+                  const unsigned char* vbuf, int vhalf) __attribute__((always_inline)) {
+    // V^T fragments of the previous sub-tile (transposing reads, waited below)
+    const unsigned vbase = (unsigned)reinterpret_cast<uintptr_t>(vbuf + T::BYTES);
+    u32x4 f[DB][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      u32x4 f0 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 0, db));
-      u32x4 f1 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 16, db));
-      u32x4 f2 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 32, db));
-      u32x4 f3 = tr_frag_asm_at<T::ROW_BYTES>(vbase, T::tr_off(ta, 48, db));
-      lds_wait_frags(f0, f1, f2, f3);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        acc[qb][db] = mfma32x32x16(as_bf16x8(f0), pf[qb][0], acc[qb][db]);
-        acc[qb][db] = mfma32x32x16(as_bf16x8(f1), pf[qb][1], acc[qb][db]);
-        acc[qb][db] = mfma32x32x16(as_bf16x8(f2), pf[qb][2], acc[qb][db]);
-        acc[qb][db] = mfma32x32x16(as_bf16x8(f3), pf[qb][3], acc[qb][db]);
-      }
+      f[db][0] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + 32 * vhalf * T::ROW_BYTES);
+      f[db][1] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + (32 * vhalf + 16) * T::ROW_BYTES);
     }
+    const f32x16 s_next = s_sub(kbuf, khalf);
+    if constexpr (DB == 4) {
+      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+      lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
+    } else {
+      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), pf[0], acc[db]);
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), pf[1], acc[db]);
+    }
+    float alpha;
+    softmax(masked_tag, s_cur, t, alpha);
+    constexpr int NM = KT + 2 * DB;
+    constexpr int VPM = (72 + NM - 1) / NM;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+    // keep P and the sum ahead of the rescale branch below (otherwise they
+    // are sunk past it, out of reach of the MFMAs they should overlap)
+    {
+      u32x4 p0 = as_u32x4(pf[0]), p1 = as_u32x4(pf[1]);
+      asm volatile("" : "+v"(p0), "+v"(p1), "+v"(l_run));
+      pf[0] = as_bf16x8(p0);
+      pf[1] = as_bf16x8(p1);
+    }
+    // the accumulator now holds PV up to t-1: bring it to the new maximum
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    }
+    return s_next;
   };
-
-  wait_vmem();
-  __syncthreads();
-
-  // one iteration: prefetch of tile j+1, S(j), then the PV product of tile
-  // j-1 (independent MFMAs) interleaved with the softmax of tile j (VALU).
-  // The body is straight-line code (one copy with the element mask, one
-  // without) so the scheduler can mix the two; a tile that is entirely past
-  // this wave's queries runs the masked copy and contributes nothing.
-  auto body = [&](auto masked_tag, int j, const unsigned char* prev, const unsigned char* cur, float* alpha_q)
-                  __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const long long kt = (long long)j * kBN;
-    f32x16 s[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[qb][kb][v] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const bf16x8 kf = T::row_frag_at(cur, ra, t, kb * 32);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][t], s[qb][kb]);
-      }
-    }
-    pv(prev);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (MASKED) {
-        const int qrow = (int)(wq0 + qb * 32 + c);
-        const int klim = (int)min(a.Nk, (long long)INT32_MAX);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = (int)kt + kb * 32 + acc_row_pi(v, grp);
-            const bool vis = key < klim && (!a.causal || key - qrow <= dpos);
-            s[qb][kb][v] = vis ? s[qb][kb][v] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mx2 = mx * a.scale_log2;
-      const float m_old = m_run[qb];
-      const float m_new = fmaxf(m_old, mx2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha_q[qb] = (m_new == m_old) ? 1.f : fast_exp2(m_old - m_new);
-      m_run[qb] = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(__builtin_fmaf(s[qb][kb][v], a.scale_log2, -m_use));
-          s[qb][kb][v] = p;
-          lsum += p;
-        }
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          const int o8 = 8 * uu;
-          pf[qb][2 * kb + uu] = pack_bf16x8(s[qb][kb][o8 + 0], s[qb][kb][o8 + 1], s[qb][kb][o8 + 2],
-                                            s[qb][kb][o8 + 3], s[qb][kb][o8 + 4], s[qb][kb][o8 + 5],
-                                            s[qb][kb][o8 + 6], s[qb][kb][o8 + 7]);
-        }
-      }
-      l_run[qb] = l_run[qb] * alpha_q[qb] + lsum;
-    }
-  };
-  auto finish = [&](const float* alpha_q) __attribute__((always_inline)) {
-    // rescale the accumulator (after the PV product of the previous tile)
-    bool any_rescale = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) any_rescale |= alpha_q[qb] != 1.f;
-    if (__any(any_rescale)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[qb][db][v] *= alpha_q[qb];
-    }
+  auto sync = [&]() __attribute__((always_inline)) {
     wait_vmem();  // this wave's part of the next tile has landed in LDS
     __syncthreads();
   };
+
   // Tiles [0, n_full) need no element mask for any wave of the workgroup:
   // every key precedes the workgroup's first query and lies inside Nk.
   long long full_keys = a.Nk;
   if (a.causal) full_keys = min(full_keys, max(0LL, a.q_pos0 + q_start - a.k_pos0 + 1));
   const int n_full = (int)min((long long)n_tiles, full_keys / kBN);
-  auto step_full = [&](int j, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt)
-                       __attribute__((always_inline)) {
-    issue(min(j + 1, n_tiles - 1), nxt);  // the last tile reloads itself into the free buffer
-    float alpha_q[QB];
-    body(std::false_type{}, j, prev, cur, alpha_q);
-    finish(alpha_q);
-  };
-  int j = 0;
-  for (; j + 3 <= n_full; j += 3) {
-    step_full(j, smem2, smem0, smem1);
-    step_full(j + 1, smem0, smem1, smem2);
-    step_full(j + 2, smem1, smem2, smem0);
-  }
-  // the rest (the diagonal and tail tiles): buffers chosen at run time
   auto buf = [&](int i) __attribute__((always_inline)) {
     const int r = i % 3;
     return r == 0 ? smem0 : (r == 1 ? smem1 : smem2);
   };
-  for (; j < n_tiles; ++j) {
-    issue(min(j + 1, n_tiles - 1), buf(j + 1));
-    float alpha_q[QB];
-    body(std::true_type{}, j, buf(j + 2), buf(j), alpha_q);
-    finish(alpha_q);
+
+  // Schedule: tile j lives in buffer j % 3.  Step t reads the K half of
+  // sub-tile t+1 and the V half of sub-tile t-1; odd steps t issue the direct
+  // loads of tile (t+3)/2 (its buffer was last read before the barrier that
+  // ended step t-1), even steps end with a barrier after which tile t/2+1 is
+  // resident.  Past the last tile the loads repeat it into the free buffer
+  // and S of the missing sub-tile is computed and dropped.
+  if (n_tiles > 0) {
+    wait_vmem();
+    __syncthreads();
+    issue(min(1, n_tiles - 1), smem1);
+    f32x16 s = s_sub(smem0, 0);
+    // step 0: nothing to multiply with V yet
+    {
+      float alpha;
+      const f32x16 s_next = s_sub(smem0, 1);
+      if (n_full > 0) softmax(std::false_type{}, s, 0, alpha);
+      else softmax(std::true_type{}, s, 0, alpha);
+      s = s_next;
+    }
+    sync();
+    int t = 1;
+    // unmasked steps, unrolled over the buffer pattern (period 6)
+    for (; t + 6 <= 2 * n_full; t += 6) {
+      const int j0 = (t - 1) / 2;  // multiple of 3
+      issue(min(j0 + 2, n_tiles - 1), smem2);
+      s = step(std::false_type{}, t, s, smem1, 0, smem0, 0);
+      s = step(std::false_type{}, t + 1, s, smem1, 1, smem0, 1);
+      sync();
+      issue(min(j0 + 3, n_tiles - 1), smem0);
+      s = step(std::false_type{}, t + 2, s, smem2, 0, smem1, 0);
+      s = step(std::false_type{}, t + 3, s, smem2, 1, smem1, 1);
+      sync();
+      issue(min(j0 + 4, n_tiles - 1), smem1);
+      s = step(std::false_type{}, t + 4, s, smem0, 0, smem2, 0);
+      s = step(std::false_type{}, t + 5, s, smem0, 1, smem2, 1);
+      sync();
+    }
+    // the rest (diagonal and tail tiles, and leftovers): buffers at run time
+    for (; t < n_sub; ++t) {
+      if (t & 1) issue(min((t + 3) / 2, n_tiles - 1), buf((t + 3) / 2));
+      s = step(std::true_type{}, t, s, buf((t + 1) / 2), (t + 1) & 1, buf((t - 1) / 2), (t - 1) & 1);
+      if (!(t & 1)) sync();
+    }
+    // PV of the last sub-tile
+    {
+      const unsigned vbase = (unsigned)reinterpret_cast<uintptr_t>(buf(n_tiles - 1) + T::BYTES);
+      u32x4 f[DB][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f[db][0] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + 32 * T::ROW_BYTES);
+        f[db][1] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + 48 * T::ROW_BYTES);
+      }
+      if constexpr (DB == 4) {
+        lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+        lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
+      } else {
+        lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), pf[0], acc[db]);
+        acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), pf[1], acc[db]);
+      }
+    }
+    wait_vmem();  // no direct load may still be in flight when the workgroup ends
   }
-  // PV of the last tile
-  if (n_tiles > 0) pv(buf(n_tiles - 1));
 
   // ---- epilogue: normalise, write O and LSE ---------------------------------
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const long long row = wq0 + qb * 32 + c;
-    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  {
+    const long long row = wq0 + c;
+    const float l = l_run + __shfl_xor(l_run, 32);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const float lse = l > 0.f ? (m_run[qb] + fast_log2(l)) * kLn2 : -INFINITY;
+    const float lse = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
     if (row < a.Nq) {
       const long long obase = ((bz * a.Hq + h) * a.Nq + row) * D;
 #pragma unroll
@@ -306,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d = db * 32 + 8 * jj + 4 * grp;
-          const float o0 = acc[qb][db][4 * jj + 0] * inv, o1 = acc[qb][db][4 * jj + 1] * inv;
-          const float o2 = acc[qb][db][4 * jj + 2] * inv, o3 = acc[qb][db][4 * jj + 3] * inv;
+          const float o0 = acc[db][4 * jj + 0] * inv, o1 = acc[db][4 * jj + 1] * inv;
+          const float o2 = acc[db][4 * jj + 2] * inv, o3 = acc[db][4 * jj + 3] * inv;
           if (OUT_F32) {
             f32x4 w = {o0, o1, o2, o3};
             *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + obase + d) = w;

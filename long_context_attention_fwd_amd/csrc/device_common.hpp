@@ -232,6 +232,66 @@ struct LdsTile {
   }
 };
 
+// Tiles that are read with one pattern only (the forward's K and V tiles) use
+// a swizzle chosen for that pattern.  Measured on gfx950 with 64-row x
+// 256-byte tiles and eight waves reading, the shared swizzle above reaches
+// about 115 B/clk/CU for either pattern; these reach about 170:
+//   row fragments (ds_read_b128):           s(r) = 4 (r & 3) + ((r >> 3) & 3)
+//   transposed fragments (ds_read_b64_tr):  s(r) = 4 (r & 3) + 2 ((r >> 3) & 1)
+// Neither depends on row bit 2, so the second half of a transposed fragment
+// (4 rows further) is an immediate offset; the row swizzle does not depend on
+// bits above 4 (row steps of 32 are immediates) and the transposed one not on
+// bits above 3 (row steps of 16 are immediates).  D = 64 (128-byte rows)
+// keeps tile_swz.
+template <int D>
+struct OnePatternTile {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int UNITS = D / 8;
+  static constexpr int BYTES = 64 * ROW_BYTES;
+  static constexpr int LOADS = BYTES / (64 * 16);
+
+  __device__ static int swz_rows(int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 3) & 3)) : tile_swz(r); }
+  __device__ static int swz_tr(int r) { return D == 128 ? (((r & 3) << 2) | (((r >> 3) & 1) << 1)) : tile_swz(r); }
+
+  // Direct global->LDS loads of rows [r0, r0 + 64) (see LdsTile::load_async),
+  // swizzled for row fragments (TR = false) or transposed fragments (TR = true).
+  template <int NW, bool TR>
+  __device__ static void load_async(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total,
+                                    int wave, int lane) {
+    static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
+#pragma unroll
+    for (int i = 0; i < LOADS / NW; ++i) {
+      const int n = wave + i * NW;
+      const int slot = n * 64 + lane;
+      const int r = slot / UNITS, up = slot % UNITS;
+      const int u = up ^ (TR ? swz_tr(r) : swz_rows(r));
+      long long gr = r0 + r;
+      gr = gr < rows_total ? gr : rows_total - 1;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + gr * D + 8 * u),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(lds) + n * 1024),
+                                       16, 0, 0);
+    }
+  }
+
+  // Byte offset of the row fragment of step t for lane (c, grp): row pi(c),
+  // dims 16 t + 8 grp .. +7.  Rows 32 k further are + 32 k ROW_BYTES.
+  __device__ static int row_off(int c, int grp, int t) {
+    const int r = swap_bits23(c);
+    return r * ROW_BYTES + (((2 * t + grp) ^ swz_rows(r)) << 4);
+  }
+
+  // Byte offset of the first transposing read of the fragment T[8 grp + e][32 db + c]
+  // (e = 0..7) for lane l; the second read is 4 rows further, and row
+  // blocks 16 k further are + 16 k ROW_BYTES.
+  __device__ static int tr_off(int lane, int db) {
+    const int gi = lane >> 4, s = lane & 15;
+    const int row = 8 * (gi >> 1) + (s >> 2);
+    const int x = 4 * db + 2 * (gi & 1) + ((s & 3) >> 1);
+    return row * ROW_BYTES + ((x ^ swz_tr(row)) << 4) + ((s & 1) << 3);
+  }
+};
+
 // Transposed fragment through inline assembly.  The compiler does not see
 // this as an LDS access, so it inserts neither the vmcnt wait it would place
 // before a transposing read while direct loads are in flight nor the lgkmcnt
