@@ -335,7 +335,8 @@ constexpr int kBN = 64;
 
 template <int D, int HP>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
-  using T = LdsTile<D>;
+  using T = SwzTile<D>;  // K tiles are read both ways, V tiles by rows: rows swizzle
+  using TR = LdsTile<D>;
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
   constexpr int NW = kDqWaves;
@@ -365,10 +366,19 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const long long wq_last = min(wq0 + 32, N) - 1;
   const bool wave_live = wq0 < N;
 
+  typename T::template AsyncLoader<NW> ld;
+  ld.init(wave, lane, false);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    T::template load_async<NW>(buf, kbase, (long long)j * kBN, N, wave, lane);
-    T::template load_async<NW>(buf + T::BYTES, vbase, (long long)j * kBN, N, wave, lane);
+    ld.load(buf, kbase, (long long)j * kBN, N, wave);
+    ld.load(buf + T::BYTES, vbase, (long long)j * kBN, N, wave);
   };
+  int roff[KT], toff[DB][2];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) roff[t] = T::row_off(c, grp, t);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) toff[db][u] = T::tr_off_rows(lane, db, u);
   if (n_tiles > 0) issue(0, smem0);
 
   bf16x8 qf[KT], of[KT];
@@ -397,7 +407,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[db] = mfma32x32x16(T::tr_frag(buf, 16 * u, db * 32, lane), dsb[u], acc[db]);
+      for (int u = 0; u < 4; ++u)
+        acc[db] = mfma32x32x16(TR::tr_frag_at(buf, toff[db][u & 1] + (u >> 1) * 32 * T::ROW_BYTES), dsb[u], acc[db]);
     }
   };
 
@@ -420,11 +431,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
           s[v] = 0.f;
           dp[v] = 0.f;
         }
-        const int arow = kb * 32 + swap_bits23(c);
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          s = mfma32x32x16(T::row_frag(cur, arow, t, grp), qf[t], s);
-          dp = mfma32x32x16(T::row_frag(cur + T::BYTES, arow, t, grp), of[t], dp);
+          const int o = roff[t] + kb * 32 * T::ROW_BYTES;
+          s = mfma32x32x16(as_bf16x8(ld_lds16(cur, o)), qf[t], s);
+          dp = mfma32x32x16(as_bf16x8(ld_lds16(cur + T::BYTES, o)), of[t], dp);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {

@@ -64,7 +64,7 @@ constexpr int kBN = 64;         // keys per tile
 
 template <int D, int QB, int HP, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
-  using T = OnePatternTile<D>;
+  using T = SwzTile<D>;
   constexpr int KT = D / 16;       // reduction steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
   constexpr int QW = 32 * QB;      // query rows per wave
@@ -105,9 +105,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   const int qrow = (int)(wq0 + c);
   const int klim = (int)min(a.Nk, (long long)INT32_MAX);
 
+  typename T::template AsyncLoader<kWaves> kload, vload;
+  kload.init(wave, lane, false);
+  vload.init(wave, lane, true);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    T::template load_async<kWaves, false>(buf, kh, (long long)j * kBN, a.Nk, wave, lane);
-    T::template load_async<kWaves, true>(buf + T::BYTES, vh, (long long)j * kBN, a.Nk, wave, lane);
+    kload.load(buf, kh, (long long)j * kBN, a.Nk, wave);
+    vload.load(buf + T::BYTES, vh, (long long)j * kBN, a.Nk, wave);
   };
   if (n_tiles > 0) issue(0, smem0);
 

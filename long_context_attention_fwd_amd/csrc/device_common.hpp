@@ -232,19 +232,19 @@ struct LdsTile {
   }
 };
 
-// Tiles that are read with one pattern only (the forward's K and V tiles) use
-// a swizzle chosen for that pattern.  Measured on gfx950 with 64-row x
-// 256-byte tiles and eight waves reading, the shared swizzle above reaches
-// about 115 B/clk/CU for either pattern; these reach about 170:
-//   row fragments (ds_read_b128):           s(r) = 4 (r & 3) + ((r >> 3) & 3)
-//   transposed fragments (ds_read_b64_tr):  s(r) = 4 (r & 3) + 2 ((r >> 3) & 1)
+// Swizzles measured for the two read patterns on gfx950 (64-row x 256-byte
+// tiles, eight waves reading).  tile_swz above reaches about 115 B/clk/CU for
+// either pattern; these reach about 170:
+//   rows: s(r) = 4 (r & 3) + ((r >> 3) & 3)      row fragments ~170, transposed ~180
+//   tr:   s(r) = 4 (r & 3) + 2 ((r >> 3) & 1)    transposed fragments ~173
 // Neither depends on row bit 2, so the second half of a transposed fragment
-// (4 rows further) is an immediate offset; the row swizzle does not depend on
-// bits above 4 (row steps of 32 are immediates) and the transposed one not on
-// bits above 3 (row steps of 16 are immediates).  D = 64 (128-byte rows)
-// keeps tile_swz.
+// (4 rows further) is an immediate offset.  The rows swizzle does not depend
+// on row bits above 4 (row steps of 32 are immediates) and serves tiles read
+// both ways; the tr swizzle does not depend on bits above 3 (row steps of 16
+// are immediates) and serves tiles read only through the transposing read.
+// D = 64 (128-byte rows) keeps tile_swz for both.
 template <int D>
-struct OnePatternTile {
+struct SwzTile {
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int UNITS = D / 8;
   static constexpr int BYTES = 64 * ROW_BYTES;
@@ -252,44 +252,106 @@ struct OnePatternTile {
 
   __device__ static int swz_rows(int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 3) & 3)) : tile_swz(r); }
   __device__ static int swz_tr(int r) { return D == 128 ? (((r & 3) << 2) | (((r >> 3) & 1) << 1)) : tile_swz(r); }
+  __device__ static int swz(bool tr, int r) { return tr ? swz_tr(r) : swz_rows(r); }
 
-  // Direct global->LDS loads of rows [r0, r0 + 64) (see LdsTile::load_async),
-  // swizzled for row fragments (TR = false) or transposed fragments (TR = true).
-  template <int NW, bool TR>
-  __device__ static void load_async(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total,
-                                    int wave, int lane) {
+  // Byte offset of logical unit u of row r in a rows-swizzled tile.
+  __device__ static int off_rows(int r, int u) { return r * ROW_BYTES + ((u ^ swz_rows(r)) << 4); }
+
+  // Direct global->LDS loads of rows [r0, r0 + 64) of a row-major
+  // [rows_total, D] bf16 matrix.  Wave w of NW waves issues loads w, w+NW, ...;
+  // load n fills LDS bytes [n KiB, n KiB + 1 KiB), lane i its 16 bytes at 16 i.
+  // The per-lane part (which unit of which row) is fixed for the kernel and
+  // kept in registers; the per-tile part is a base that is uniform over the
+  // wave.  Rows past rows_total read row rows_total - 1 (finite data that the
+  // callers mask).
+  template <int NW>
+  struct AsyncLoader {
+    static constexpr int N = LOADS / NW;
     static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
+    unsigned off[N];  // byte offset of this lane's unit within the tile (global side)
+    int row[N];       // tile row of that unit
+    __device__ void init(int wave, int lane, bool tr) {
 #pragma unroll
-    for (int i = 0; i < LOADS / NW; ++i) {
-      const int n = wave + i * NW;
-      const int slot = n * 64 + lane;
-      const int r = slot / UNITS, up = slot % UNITS;
-      const int u = up ^ (TR ? swz_tr(r) : swz_rows(r));
-      long long gr = r0 + r;
-      gr = gr < rows_total ? gr : rows_total - 1;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + gr * D + 8 * u),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(lds) + n * 1024),
-                                       16, 0, 0);
+      for (int i = 0; i < N; ++i) {
+        const int n = wave + i * NW;
+        const int slot = n * 64 + lane;
+        const int r = slot / UNITS, up = slot % UNITS;
+        row[i] = r;
+        off[i] = (unsigned)(r * D + 8 * (up ^ swz(tr, r))) * 2u;
+      }
     }
-  }
+    __device__ void load(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total, int wave) const {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(g + r0 * D);
+      if (r0 + 64 <= rows_total) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]),
+                                           reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                               reinterpret_cast<uintptr_t>(lds) + (wave + i * NW) * 1024),
+                                           16, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const long long gr = r0 + row[i];
+          const long long back = gr < rows_total ? 0 : gr - (rows_total - 1);  // rows to step back
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i] - back * (D * 2)),
+                                           reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                               reinterpret_cast<uintptr_t>(lds) + (wave + i * NW) * 1024),
+                                           16, 0, 0);
+        }
+      }
+    }
+  };
 
-  // Byte offset of the row fragment of step t for lane (c, grp): row pi(c),
-  // dims 16 t + 8 grp .. +7.  Rows 32 k further are + 32 k ROW_BYTES.
+  // Register-staged tile load into a rows-swizzled tile: NT threads fetch
+  // rows [r0, r0 + 64) into CH 16-byte registers each, then store them.  Rows
+  // past rows_total read row rows_total - 1.
+  template <int NT>
+  struct Stage {
+    static constexpr int CH = 64 * UNITS / NT;
+    static_assert(CH >= 1 && 64 * UNITS % NT == 0, "threads must divide the tile");
+    u32x4 r[CH];
+    __device__ void load(const uint16_t* g, long long r0, long long rows_total, int tid) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int id = tid + i * NT;
+        const int row = id / UNITS, u = id % UNITS;
+        long long gr = r0 + row;
+        gr = gr < rows_total ? gr : rows_total - 1;
+        r[i] = ld_global16(g + gr * D + 8 * u);
+      }
+    }
+    __device__ void store(unsigned char* lds, int tid) const {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int id = tid + i * NT;
+        const int row = id / UNITS, u = id % UNITS;
+        st_lds16(lds, off_rows(row, u), r[i]);
+      }
+    }
+  };
+
+  // Byte offset of the row fragment of step t for lane (c, grp) in a
+  // rows-swizzled tile: row pi(c), dims 16 t + 8 grp .. +7.  Rows 32 k
+  // further are + 32 k ROW_BYTES.
   __device__ static int row_off(int c, int grp, int t) {
     const int r = swap_bits23(c);
     return r * ROW_BYTES + (((2 * t + grp) ^ swz_rows(r)) << 4);
   }
 
-  // Byte offset of the first transposing read of the fragment T[8 grp + e][32 db + c]
-  // (e = 0..7) for lane l; the second read is 4 rows further, and row
-  // blocks 16 k further are + 16 k ROW_BYTES.
-  __device__ static int tr_off(int lane, int db) {
+  // Byte offset of the first transposing read of the fragment
+  // T[r0 + 8 grp + e][32 db + c] (e = 0..7) for lane l; the second read is 4
+  // rows further.  tr_off: tr-swizzled tile, r0 = 0 (multiples of 16 are
+  // + r0 ROW_BYTES).  tr_off_rows: rows-swizzled tile, r0 = 16 u16 (multiples
+  // of 32 are + r0 ROW_BYTES).
+  __device__ static int tr_off_sw(int lane, int db, int r0, bool tr) {
     const int gi = lane >> 4, s = lane & 15;
-    const int row = 8 * (gi >> 1) + (s >> 2);
+    const int row = r0 + 8 * (gi >> 1) + (s >> 2);
     const int x = 4 * db + 2 * (gi & 1) + ((s & 3) >> 1);
-    return row * ROW_BYTES + ((x ^ swz_tr(row)) << 4) + ((s & 1) << 3);
+    return row * ROW_BYTES + ((x ^ swz(tr, row)) << 4) + ((s & 1) << 3);
   }
+  __device__ static int tr_off(int lane, int db) { return tr_off_sw(lane, db, 0, true); }
+  __device__ static int tr_off_rows(int lane, int db, int u16) { return tr_off_sw(lane, db, 16 * u16, false); }
 };
 
 // Transposed fragment through inline assembly.  The compiler does not see
