@@ -336,7 +336,6 @@ constexpr int kBN = 64;
 template <int D, int HP>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   using T = SwzTile<D>;  // K tiles are read both ways, V tiles by rows: rows swizzle
-  using TR = LdsTile<D>;
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
   constexpr int NW = kDqWaves;
@@ -355,6 +354,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const long long q_start = (long long)qt * SPAN;
   const long long wq0 = q_start + (long long)(wave / HP) * 32;
   const long long qrow = wq0 + c;
+  const int qrow_i = (int)qrow;
+  const int klim = (int)N;
   const float sl = a.scale * kLog2e;
   const long long hb = (bz * a.Hq + h) * N;
   const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
@@ -363,8 +364,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   long long kv_end = N;
   if (a.causal) kv_end = min(N, q_start + SPAN);
   const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
-  const long long wq_last = min(wq0 + 32, N) - 1;
-  const bool wave_live = wq0 < N;
+  const int n_sub = 2 * n_tiles;  // 32-key sub-tiles
 
   typename T::template AsyncLoader<NW> ld;
   ld.init(wave, lane, false);
@@ -372,15 +372,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
     ld.load(buf, kbase, (long long)j * kBN, N, wave);
     ld.load(buf + T::BYTES, vbase, (long long)j * kBN, N, wave);
   };
-  int roff[KT], toff[DB][2];
-#pragma unroll
-  for (int t = 0; t < KT; ++t) roff[t] = T::row_off(c, grp, t);
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) toff[db][u] = T::tr_off_rows(lane, db, u);
   if (n_tiles > 0) issue(0, smem0);
 
+  // Q and dO of this lane's query row as B operands (reduction over D)
   bf16x8 qf[KT], of[KT];
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
@@ -392,7 +386,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
     qf[t] = as_bf16x8(x);
     of[t] = as_bf16x8(y);
   }
-  const float lse2 = qrow < N ? a.lse[hb + qrow] * kLog2e : INFINITY;
+  const float lse2 = qrow < N ? a.lse[hb + qrow] * kLog2e : INFINITY;  // rows past N: P = 0
   const float dvv = qrow < N ? a.delta[hb + qrow] : 0.f;
 
   f32x16 acc[DB];
@@ -400,74 +394,152 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
-  bf16x8 dsb[4];  // dS^T of the previous tile, pending its product
-  bool prev_active = false;
+  bf16x8 dsb[2];  // dS^T of the previous sub-tile, waiting for its product (zero: no-op)
+  dsb[0] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  dsb[1] = dsb[0];
+  // per-lane LDS offsets: K / V row fragments per step, K^T fragments per
+  // column block and 16-row half of a 32-row block
+  int roff[KT], toff[DB][2];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) roff[t] = T::row_off(c, grp, t);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) toff[db][u] = T::tr_off_rows(lane, db, u);
 
-  auto dq_product = [&](const unsigned char* buf) __attribute__((always_inline)) {
+  // dQ^T += K^T dS^T for the previous sub-tile: K^T fragments of its 32 keys
+  // (transposing reads through inline assembly, so no wait for the direct
+  // loads in flight), then the products
+  auto dq_frags = [&](const unsigned char* kb, int half, u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+    const unsigned base = (unsigned)reinterpret_cast<uintptr_t>(kb);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        f[db][u] = tr_frag_asm_at<T::ROW_BYTES>(base, toff[db][u] + 32 * half * T::ROW_BYTES);
+  };
+  auto dq_products = [&](u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+    if constexpr (DB == 4) {
+      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+      lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
+    } else {
+      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[db] = mfma32x32x16(TR::tr_frag_at(buf, toff[db][u & 1] + (u >> 1) * 32 * T::ROW_BYTES), dsb[u], acc[db]);
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), dsb[0], acc[db]);
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), dsb[1], acc[db]);
     }
   };
 
-  wait_vmem();
-  __syncthreads();
-
-  auto step = [&](int j, const unsigned char* prev, const unsigned char* cur, unsigned char* nxt) __attribute__((always_inline)) {
-    if (prev_active) dq_product(prev);
-    if (j + 1 < n_tiles) issue(j + 1, nxt);
-    const long long kt = (long long)j * kBN;
-    const bool active = wave_live && !(a.causal && kt > wq_last);
-    prev_active = active;
-    if (active) {
-      const bool need_mask = (kt + kBN > N) || (a.causal && kt + kBN - 1 > wq0);
+  // One step t of the pipeline over 32-key sub-tiles: K^T reads of sub-tile
+  // t-1, S^T = K Q^T and dP^T = V dO^T of sub-tile t (tile in cur, half
+  // `half`), then dQ of sub-tile t-1 next to the elementwise step of t.
+  auto step = [&](auto masked_tag, int t, const unsigned char* cur, int half, const unsigned char* prev,
+                  int phalf) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    u32x4 f[DB][2];
+    dq_frags(prev, phalf, f);
+    f32x16 s, dp;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[v] = 0.f;
-          dp[v] = 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          const int o = roff[t] + kb * 32 * T::ROW_BYTES;
-          s = mfma32x32x16(as_bf16x8(ld_lds16(cur, o)), qf[t], s);
-          dp = mfma32x32x16(as_bf16x8(ld_lds16(cur + T::BYTES, o)), of[t], dp);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float ds[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int v = 8 * u + e;
-            float p = fast_exp2(__builtin_fmaf(s[v], sl, -lse2));
-            if (need_mask) {
-              const int kk = (int)kt + kb * 32 + acc_row_pi(v, grp);
-              if (kk >= (int)N || (a.causal && kk > (int)qrow)) p = 0.f;
-            }
-            ds[e] = p * (dp[v] - dvv);
-          }
-          dsb[2 * kb + u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-        }
-      }
+    for (int v = 0; v < 16; ++v) {
+      s[v] = 0.f;
+      dp[v] = 0.f;
     }
-    wait_vmem();
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      const int o = roff[kk] + 32 * half * T::ROW_BYTES;
+      s = mfma32x32x16(as_bf16x8(ld_lds16(cur, o)), qf[kk], s);
+      dp = mfma32x32x16(as_bf16x8(ld_lds16(cur + T::BYTES, o)), of[kk], dp);
+    }
+    dq_products(f);
+    float ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float p = fast_exp2(__builtin_fmaf(s[v], sl, -lse2));
+      if (MASKED) {
+        const int key = 32 * t + acc_row_pi(v, grp);
+        if (key >= klim || (a.causal && key > qrow_i)) p = 0.f;
+      }
+      ds[v] = p * (dp[v] - dvv);
+    }
+    dsb[0] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    dsb[1] = pack_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+    // S / dP products first, then each dQ product next to a slice of the
+    // elementwise step
+    constexpr int NMF = 2 * DB;
+    constexpr int VPM = (80 + NMF - 1) / NMF;
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KT, 0);
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    }
+    // keep dS here, next to the products it should overlap (otherwise it may
+    // be sunk past the next step's load branch)
+    {
+      u32x4 d0 = as_u32x4(dsb[0]), d1 = as_u32x4(dsb[1]);
+      asm volatile("" : "+v"(d0), "+v"(d1));
+      dsb[0] = as_bf16x8(d0);
+      dsb[1] = as_bf16x8(d1);
+    }
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    wait_vmem();  // this wave's part of the next tile has landed in LDS
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 3 <= n_tiles; j += 3) {
-    step(j, smem2, smem0, smem1);
-    step(j + 1, smem0, smem1, smem2);
-    step(j + 2, smem1, smem2, smem0);
-  }
-  if (j < n_tiles) step(j, smem2, smem0, smem1);
-  if (j + 1 < n_tiles) step(j + 1, smem0, smem1, smem2);
-  if (prev_active) {
-    const int r = (n_tiles - 1) % 3;
-    dq_product(r == 0 ? smem0 : (r == 1 ? smem1 : smem2));
+  auto buf = [&](int i) __attribute__((always_inline)) {
+    const int r = i % 3;
+    return r == 0 ? smem0 : (r == 1 ? smem1 : smem2);
+  };
+
+  // Tiles [0, n_full) need no element mask for any wave of the workgroup.
+  long long full_keys = N;
+  if (a.causal) full_keys = min(full_keys, q_start + 1);
+  const int n_full = (int)min((long long)n_tiles, full_keys / kBN);
+
+  // Schedule: tile j lives in buffer j % 3 and is read in steps 2j .. 2j+2.
+  // Odd steps t issue the direct loads of tile (t+3)/2 (its buffer was last
+  // read in step t-1, before the barrier that ended it); even steps end with
+  // a barrier after which tile t/2+1 is resident.  Past the last tile the
+  // loads repeat it into the free buffer.
+  if (n_tiles > 0) {
+    wait_vmem();
+    __syncthreads();
+    issue(min(1, n_tiles - 1), smem1);
+    // step 0: no previous sub-tile (dS is zero; the fragments come from
+    // tile 0, finite data)
+    if (n_full > 0) step(std::false_type{}, 0, smem0, 0, smem0, 0);
+    else step(std::true_type{}, 0, smem0, 0, smem0, 0);
+    sync();
+    int t = 1;
+    for (; t + 6 <= 2 * n_full; t += 6) {
+      const int j0 = (t - 1) / 2;  // multiple of 3
+      issue(min(j0 + 2, n_tiles - 1), smem2);
+      step(std::false_type{}, t, smem0, 1, smem0, 0);
+      step(std::false_type{}, t + 1, smem1, 0, smem0, 1);
+      sync();
+      issue(min(j0 + 3, n_tiles - 1), smem0);
+      step(std::false_type{}, t + 2, smem1, 1, smem1, 0);
+      step(std::false_type{}, t + 3, smem2, 0, smem1, 1);
+      sync();
+      issue(min(j0 + 4, n_tiles - 1), smem1);
+      step(std::false_type{}, t + 4, smem2, 1, smem2, 0);
+      step(std::false_type{}, t + 5, smem0, 0, smem2, 1);
+      sync();
+    }
+    for (; t < n_sub; ++t) {
+      if (t & 1) issue(min((t + 3) / 2, n_tiles - 1), buf((t + 3) / 2));
+      step(std::true_type{}, t, buf(t / 2), t & 1, buf((t - 1) / 2), (t - 1) & 1);
+      if (!(t & 1)) sync();
+    }
+    // dQ of the last sub-tile
+    {
+      u32x4 f[DB][2];
+      dq_frags(buf(n_tiles - 1), 1, f);
+      dq_products(f);
+    }
+    wait_vmem();  // no direct load may still be in flight when the workgroup ends
   }
 
   if (qrow < N) {
