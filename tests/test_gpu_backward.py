@@ -44,7 +44,7 @@ def check_grads(got, ref, what):
 
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 257, 1000])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G,causal", [(1, True), (4, True), (2, False)])
+@pytest.mark.parametrize("G,causal", [(1, True), (2, True), (4, True), (2, False)])
 def test_bwd_small_sweep(gpu, N, D, G, causal):
     Hkv = 2
     d = make_qkv(1, Hkv * G, Hkv, N, D, seed=200 + N + D + G, with_do=True)

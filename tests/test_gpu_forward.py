@@ -34,7 +34,7 @@ def run_fwd(d, causal=True, q_pos0=0, k_pos0=0, out_f32=False, scale=None):
 
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 128, 129, 1000, 1024])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G,causal", [(1, True), (4, True), (1, False), (4, False)])
+@pytest.mark.parametrize("G,causal", [(1, True), (2, True), (4, True), (1, False), (4, False)])
 def test_fwd_small_sweep(gpu, N, D, G, causal):
     Hkv = 2
     d = make_qkv(1, Hkv * G, Hkv, N, D, seed=100 + N + D + G)
