@@ -50,7 +50,7 @@ enum {
   ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. D not 64/128) */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_ALIAS = 5,       /* an output overlaps an input */
-  ATTN_ERR_WORKSPACE = 6,   /* backward workspace missing or too small */
+  ATTN_ERR_WORKSPACE = 6,   /* workspace missing or too small */
   ATTN_ERR_HIP = 7          /* the HIP runtime reported an error */
 };
 
@@ -77,6 +77,38 @@ enum { ATTN_BF16 = 0, ATTN_FP32 = 1 };
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
              int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal,
              int64_t q_pos0, int64_t k_pos0, void* hip_stream);
+
+/*
+ * attn_fwd_splitkv_workspace_size -- bytes of device workspace attn_fwd_splitkv
+ * needs for the same arguments: fp32 partial outputs and log-sum-exps of every
+ * key range, n * B*Hq*Nq*(D + 1) floats for n ranges (n_splits > 0: that many;
+ * n_splits <= 0: the number attn_fwd_splitkv chooses).  Returns 0 for invalid
+ * sizes or n_splits > 64.
+ */
+size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,
+                                       int n_splits);
+
+/*
+ * attn_fwd_splitkv -- attn_fwd with the keys split into ranges that run side by
+ * side, for short sequences where one workgroup per query block leaves most
+ * of the GPU idle and the longest row sets the time.
+ *
+ * Same arguments, layouts, masking and results as attn_fwd with o in bf16
+ * (up to fp32 rounding order).  The keys are cut into n contiguous ranges of
+ * whole 64-key tiles; each range's attention (fp32 O and LSE) is the partial
+ * attention of "So funktioniert Kontextparallelität" for one KV block, and the
+ * ranges are combined by the attn_partial_merge rule.  n_splits in [1, 64]
+ * fixes n; n_splits <= 0 lets the library choose (about two non-empty
+ * workgroups per compute unit).  The workspace (caller-owned, >=
+ * attn_fwd_splitkv_workspace_size bytes, 16-byte aligned, not overlapping
+ * any argument) is scratch; its contents on return are unspecified.
+ * Deterministic.  Errors as attn_fwd, plus ATTN_ERR_WORKSPACE and
+ * ATTN_ERR_UNSUPPORTED for n_splits > 64.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal,
+                     int64_t q_pos0, int64_t k_pos0, int n_splits, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
 
 /*
  * attn_partial_merge -- log-sum-exp merge of partial attention results.

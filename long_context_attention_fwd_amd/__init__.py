@@ -21,6 +21,8 @@ import threading
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_splitkv",
+    "attn_fwd_splitkv_workspace_size",
     "attn_partial_merge",
     "attn_bwd",
     "attn_bwd_workspace_size",
@@ -59,6 +61,9 @@ _L = ctypes.c_int64
 _F = ctypes.c_float
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P]),
+    "attn_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _L, _I, _I, _I]),
+    "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P, ctypes.c_size_t,
+                              _P]),
     "attn_partial_merge": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _L, _I, _P]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
@@ -155,6 +160,42 @@ def attn_fwd(q, k, v, *, causal: bool = True, scale: float | None = None, q_pos0
     _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           ATTN_FP32 if out_dtype == torch.float32 else ATTN_BF16, lse.data_ptr(),
                           B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, q_pos0, k_pos0, _stream(q)))
+    return o, lse
+
+
+def attn_fwd_splitkv_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, causal: bool = True,
+                                    n_splits: int = 0) -> int:
+    return int(lib().attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, D, 1 if causal else 0, n_splits))
+
+
+def attn_fwd_splitkv(q, k, v, *, causal: bool = True, scale: float | None = None, q_pos0: int = 0,
+                     k_pos0: int = 0, n_splits: int = 0, workspace=None, o=None, lse=None):
+    """attn_fwd with the keys split into ranges that run side by side (for
+    short sequences); returns (o bf16 [B,Hq,Nq,D], lse [B,Hq,Nq] float32).
+    ``n_splits`` <= 0 lets the library choose the number of ranges."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    if o is None:
+        o = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=q.device)
+    _need(o, "o", torch.bfloat16, 4)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Hq, Nq, D) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("o / lse have the wrong shape")
+    need = attn_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, D, causal, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, q_pos0, k_pos0, n_splits,
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
     return o, lse
 
 

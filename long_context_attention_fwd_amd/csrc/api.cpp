@@ -20,6 +20,8 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+constexpr int kMaxSplits = 64;  // key ranges of attn_fwd_splitkv
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -81,55 +83,122 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int Hq,
-             int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0, int64_t k_pos0,
-             void* hip_stream) {
-  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "attn_fwd: q, k, v, o and lse must be non-null");
+}  // extern "C"
+
+namespace {
+
+// Validation shared by attn_fwd and attn_fwd_splitkv; fills the kernel
+// arguments on success.
+int fwd_check(const char* name, const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+              int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0,
+              int64_t k_pos0, lcattn::FwdArgs* a) {
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "%s: q, k, v, o and lse must be non-null", name);
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || D < 1)
-    return fail(ATTN_ERR_SHAPE, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%lld Nk=%lld D=%d)", B, Hq,
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%lld Nk=%lld D=%d)", name, B, Hq,
                 Hkv, (long long)Nq, (long long)Nk, D);
-  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "attn_fwd: Hkv=%d does not divide Hq=%d", Hkv, Hq);
-  if (q_pos0 < 0 || k_pos0 < 0) return fail(ATTN_ERR_SHAPE, "attn_fwd: position offsets must be >= 0");
-  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: D=%d (supported: 64, 128)", D);
+  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "%s: Hkv=%d does not divide Hq=%d", name, Hkv, Hq);
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(ATTN_ERR_SHAPE, "%s: position offsets must be >= 0", name);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", name, D);
   if (o_dtype != ATTN_BF16 && o_dtype != ATTN_FP32)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: o_dtype=%d (ATTN_BF16 or ATTN_FP32)", o_dtype);
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: o_dtype=%d (ATTN_BF16 or ATTN_FP32)", name, o_dtype);
   if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: scale must be finite and > 0");
-  if (Hq / Hkv > 1 && Hq > 65535 * 4) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: too many heads");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: scale must be finite and > 0", name);
+  if (Hq / Hkv > 1 && Hq > 65535 * 4) return fail(ATTN_ERR_UNSUPPORTED, "%s: too many heads", name);
   int64_t nq_el, nk_el, nl;
   if (!elems(&nq_el, {B, Hq, Nq, D}) || !elems(&nk_el, {B, Hkv, Nk, D}) || !elems(&nl, {B, Hq, Nq}) ||
       nq_el > (INT64_MAX / 8))
-    return fail(ATTN_ERR_SHAPE, "attn_fwd: tensor sizes overflow");
+    return fail(ATTN_ERR_SHAPE, "%s: tensor sizes overflow", name);
   if (Nq >= INT32_MAX || Nk >= INT32_MAX || B > 65535 || Hq > 65535)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: sequence lengths must be < 2^31, B and Hq <= 65535");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: sequence lengths must be < 2^31, B and Hq <= 65535", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return fail(ATTN_ERR_ALIGN, "attn_fwd: pointers must be 16-byte aligned");
+    return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
   const size_t ob = (size_t)nq_el * (o_dtype == ATTN_FP32 ? 4 : 2);
   const size_t lb = (size_t)nl * 4;
   const void* ins[3] = {q, k, v};
   const size_t inb[3] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2};
   for (int i = 0; i < 3; ++i)
     if (overlap(o, ob, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]))
-      return fail(ATTN_ERR_ALIAS, "attn_fwd: outputs overlap inputs");
-  if (overlap(o, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "attn_fwd: o overlaps lse");
+      return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
+  if (overlap(o, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "%s: o overlaps lse", name);
 
+  a->q = static_cast<const uint16_t*>(q);
+  a->k = static_cast<const uint16_t*>(k);
+  a->v = static_cast<const uint16_t*>(v);
+  a->o = o;
+  a->lse = lse;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->G = Hq / Hkv;
+  a->Nq = Nq;
+  a->Nk = Nk;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->causal = causal ? 1 : 0;
+  a->q_pos0 = q_pos0;
+  a->k_pos0 = k_pos0;
+  return ATTN_OK;
+}
+
+// Workspace bytes of attn_fwd_splitkv for n key ranges: fp32 partial O, then
+// fp32 partial LSE.  0 on overflow.
+size_t splitkv_bytes(int B, int Hq, int64_t Nq, int D, int n) {
+  int64_t el;
+  if (!elems(&el, {n, B, Hq, Nq, D + 1}) || el > INT64_MAX / 4) return 0;
+  return (size_t)el * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int Hq,
+             int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0, int64_t k_pos0,
+             void* hip_stream) {
   lcattn::FwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = o;
-  a.lse = lse;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = Hq / Hkv;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.causal = causal ? 1 : 0;
-  a.q_pos0 = q_pos0;
-  a.k_pos0 = k_pos0;
+  const int st = fwd_check("attn_fwd", q, k, v, o, o_dtype, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0,
+                           k_pos0, &a);
+  if (st != ATTN_OK) return st;
   return hip_status(lcattn::launch_attn_fwd(a, B, D, o_dtype == ATTN_FP32, static_cast<hipStream_t>(hip_stream)),
                     "attn_fwd launch");
+}
+
+size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,
+                                       int n_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1 || n_splits > kMaxSplits) return 0;
+  return splitkv_bytes(B, Hq, Nq, D, lcattn::fwd_split_count(B, Hq, Hkv, Nq, Nk, causal, n_splits));
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0, int64_t k_pos0,
+                     int n_splits, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  lcattn::FwdArgs a;
+  const int st = fwd_check("attn_fwd_splitkv", q, k, v, o, ATTN_BF16, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal,
+                           q_pos0, k_pos0, &a);
+  if (st != ATTN_OK) return st;
+  if (n_splits > kMaxSplits)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv: n_splits=%d (at most %d)", n_splits, kMaxSplits);
+  const int n = lcattn::fwd_split_count(B, Hq, Hkv, Nq, Nk, causal, n_splits);
+  if ((int64_t)B * n > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv: B * n_splits must be <= 65535");
+  const size_t need = splitkv_bytes(B, Hq, Nq, D, n);
+  if (need == 0) return fail(ATTN_ERR_SHAPE, "attn_fwd_splitkv: workspace size overflows");
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "attn_fwd_splitkv: workspace of %zu bytes needed", need);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "attn_fwd_splitkv: workspace must be 16-byte aligned");
+  int64_t nq_el, nk_el, nl;
+  elems(&nq_el, {B, Hq, Nq, D});
+  elems(&nk_el, {B, Hkv, Nk, D});
+  elems(&nl, {B, Hq, Nq});
+  const void* bufs[5] = {q, k, v, o, lse};
+  const size_t sizes[5] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2, (size_t)nq_el * 2,
+                           (size_t)nl * 4};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(workspace, need, bufs[i], sizes[i]))
+      return fail(ATTN_ERR_ALIAS, "attn_fwd_splitkv: workspace overlaps an input or output");
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = o_parts + (size_t)n * nq_el;
+  return hip_status(lcattn::launch_attn_fwd_splitkv(a, B, D, n, o_parts, lse_parts,
+                                                    static_cast<hipStream_t>(hip_stream)),
+                    "attn_fwd_splitkv launch");
 }
 
 int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_parts, int n_parts, void* o,

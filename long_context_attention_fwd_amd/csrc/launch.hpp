@@ -25,9 +25,25 @@ struct FwdArgs {
   float scale_log2;  // softmax scale times log2(e)
   int causal;
   long long q_pos0, k_pos0;
+  // split of the keys: workgroup z = s * B + b covers key tiles
+  // [s * split_tiles, (s + 1) * split_tiles) and writes part s of o / lse,
+  // part_stride elements apart in o (part_stride / D in lse)
+  int n_splits = 1;
+  int split_tiles = 1 << 30;
+  long long part_stride = 0;
+  int B = 1;  // batch (grid z = split * B + batch)
 };
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int B, int D, bool out_f32, hipStream_t stream);
+
+// Forward over n_splits key ranges side by side (fp32 partials in o_parts /
+// lse_parts, [n_splits, B, Hq, Nq(, D)]), then their LSE merge into o (bf16)
+// and lse.
+hipError_t launch_attn_fwd_splitkv(const FwdArgs& a, int B, int D, int n_splits, float* o_parts, float* lse_parts,
+                                   hipStream_t stream);
+// Number of key ranges for attn_fwd_splitkv: n_splits if > 0, else about
+// enough for two non-empty workgroups per compute unit.
+int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits);
 
 hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
                                 uint16_t* o, float* lse, long long rows, int D, hipStream_t stream);

@@ -35,7 +35,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_partial_merge",
+    for n in ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
+              "attn_bwd_workspace_size", "attn_partial_merge",
               "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -70,6 +71,33 @@ def fwd(L, **kw):
 def test_fwd_rejects(L, kw, status):
     assert fwd(L, **kw) == status
     assert L.attn_last_error()
+
+
+def splitkv(L, **kw):
+    args = dict(q=A, k=B_, v=C_, o=D_, lse=E_, B=1, Hq=4, Hkv=1, Nq=128, Nk=128, D=128, scale=0.125, causal=1,
+                q_pos0=0, k_pos0=0, n_splits=2, ws=F_, ws_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return L.attn_fwd_splitkv(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(B=0), 2), (dict(Hq=4, Hkv=3), 2), (dict(D=96), 3), (dict(n_splits=65), 3),
+    (dict(ws=None), 6), (dict(ws_bytes=100), 6), (dict(ws=F_ + 8), 4), (dict(ws=A), 5), (dict(o=A), 5),
+    (dict(B=2000, n_splits=64), 3),
+])
+def test_splitkv_rejects(L, kw, status):
+    assert splitkv(L, **kw) == status
+    assert L.attn_last_error()
+
+
+def test_splitkv_workspace_size(L):
+    # n ranges of fp32 partial O and LSE: n * B*Hq*Nq*(D+1) floats
+    assert L.attn_fwd_splitkv_workspace_size(1, 4, 1, 128, 128, 128, 1, 2) == 2 * 4 * 128 * 129 * 4
+    assert L.attn_fwd_splitkv_workspace_size(1, 4, 1, 128, 128, 128, 1, 65) == 0
+    assert L.attn_fwd_splitkv_workspace_size(1, 4, 3, 128, 128, 128, 1, 2) == 0
+    auto = L.attn_fwd_splitkv_workspace_size(1, 4, 4, 4096, 4096, 64, 1, 0)
+    per_range = 4 * 4096 * 65 * 4
+    assert auto % per_range == 0 and 1 <= auto // per_range <= 64
 
 
 def merge(L, **kw):
