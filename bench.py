@@ -331,10 +331,51 @@ def main():
         "roofline": roofline,
         "device": torch.cuda.get_device_name(dev),
     }
+    props = torch.cuda.get_device_properties(dev)
+    out["device_info"] = {"name": props.name, "compute_units": props.multi_processor_count,
+                          "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip}
+    if not args.profile_steps:
+        out["short_sequence_forward"] = short_forward(lc, torch, dev)
 
     if not args.no_cpu_baseline and not args.profile_steps:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def short_forward(lc, torch, dev, iters=20):
+    """The glossary example's forward shape ([1, 4, 4096, 64], causal), timed
+    apart from the step: attn_fwd, and attn_fwd_splitkv with the library's
+    choice of key ranges.  One workgroup per 256 query rows gives only 64
+    workgroups here, so the longest row sets attn_fwd's time."""
+    import numpy as np
+    from long_context_attention_fwd_amd.inputs import WORKLOADS, make_workload_inputs
+    w = WORKLOADS["listing_4k"]
+    d = make_workload_inputs(w)
+    q, k, v = (torch.from_numpy(d[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in "qkv")
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(lc.attn_fwd_splitkv_workspace_size(B, Hq, Hkv, N, N, D, True, 0), dtype=torch.uint8,
+                     device=dev)
+    flops = fwd_flops(B, Hq, N, D)
+    res = {"workload": w.name, "shape": [B, Hq, N, D], "causal": True}
+    calls = {"attn_fwd": lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse),
+             "attn_fwd_splitkv": lambda: lc.attn_fwd_splitkv(q, k, v, scale=w.scale, workspace=ws, o=o, lse=lse)}
+    for name, fn in calls.items():
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        res[name] = {"us": round(1e3 * ms, 2), "TFLOP/s": round(flops / ms / 1e9, 2),
+                     "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def cpu_baseline(w, budget_s):
