@@ -79,6 +79,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, 
              int64_t q_pos0, int64_t k_pos0, void* hip_stream);
 
 /*
+ * attn_fwd_strided -- attn_fwd on tensors given by element strides, so that
+ * attention can read a Ulysses shard in the token-major layout the exchange
+ * delivers ([N, H, D] rows: token stride H*D, head stride D) and write O the
+ * same way, without a separate relayout pass.
+ *
+ * q_strides, kv_strides, o_strides: host arrays of 3 element strides (batch,
+ * head, token) of q, of k and v (shared), and of o; the D elements of a row
+ * are contiguous.  Every stride keeps rows 16-byte aligned (a multiple of 8
+ * for bf16, of 4 for fp32 o); token strides are >= D and < 2^24; o's rows
+ * must not overlap one another (ATTN_ERR_ALIAS), and o, lse must not overlap
+ * the address ranges of q, k, v.  lse stays contiguous [B, Hq, Nq].  Results
+ * are bit-identical to attn_fwd on the same values.  Otherwise as attn_fwd.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                     int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal,
+                     int64_t q_pos0, int64_t k_pos0, const int64_t* q_strides, const int64_t* kv_strides,
+                     const int64_t* o_strides, void* hip_stream);
+
+/*
  * attn_fwd_splitkv_workspace_size -- bytes of device workspace attn_fwd_splitkv
  * needs for the same arguments: fp32 partial outputs and log-sum-exps of every
  * key range, n * B*Hq*Nq*(D + 1) floats for n ranges (n_splits > 0: that many;

@@ -21,6 +21,7 @@ import threading
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_strided",
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_size",
     "attn_partial_merge",
@@ -61,6 +62,7 @@ _L = ctypes.c_int64
 _F = ctypes.c_float
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P]),
+    "attn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P, _P, _P, _P]),
     "attn_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _L, _I, _I, _I]),
     "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P, ctypes.c_size_t,
                               _P]),
@@ -116,13 +118,16 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _need(t, name, dtype=None, dims=None):
+def _need(t, name, dtype=None, dims=None, strided=False):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() >= 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -160,6 +165,43 @@ def attn_fwd(q, k, v, *, causal: bool = True, scale: float | None = None, q_pos0
     _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           ATTN_FP32 if out_dtype == torch.float32 else ATTN_BF16, lse.data_ptr(),
                           B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, q_pos0, k_pos0, _stream(q)))
+    return o, lse
+
+
+def attn_fwd_strided(q, k, v, *, causal: bool = True, scale: float | None = None, q_pos0: int = 0,
+                     k_pos0: int = 0, out_dtype=None, o=None, lse=None):
+    """attn_fwd on [B, H, N, D] views with any batch / head / token strides
+    (the last dimension contiguous), e.g. heads of a token-major [N, H, D]
+    shard; returns (o, lse).  ``o`` may be such a view too (default: a new
+    contiguous tensor)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4, strided=True)
+    _need(k, "k", torch.bfloat16, 4, strided=True)
+    _need(v, "v", torch.bfloat16, 4, strided=True)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    if tuple(v.stride()) != tuple(k.stride()):
+        raise ValueError("k and v must have the same strides")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if o is None:
+        o = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q.device)
+    _need(o, "o", out_dtype, 4, strided=True)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Hq, Nq, D) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("o / lse have the wrong shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    arr = ctypes.c_int64 * 3
+    qs, ks, os_ = arr(*q.stride()[:3]), arr(*k.stride()[:3]), arr(*o.stride()[:3])
+    _check(lib().attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  ATTN_FP32 if out_dtype == torch.float32 else ATTN_BF16, lse.data_ptr(),
+                                  B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, q_pos0, k_pos0,
+                                  qs, ks, os_, _stream(q)))
     return o, lse
 
 

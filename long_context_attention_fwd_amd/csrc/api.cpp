@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <utility>
 
 #include "launch.hpp"
 
@@ -91,7 +92,7 @@ namespace {
 // arguments on success.
 int fwd_check(const char* name, const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
               int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0,
-              int64_t k_pos0, lcattn::FwdArgs* a) {
+              int64_t k_pos0, lcattn::FwdArgs* a, bool contiguous = true) {
   if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL, "%s: q, k, v, o and lse must be non-null", name);
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || D < 1)
     return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%lld Nk=%lld D=%d)", name, B, Hq,
@@ -112,14 +113,16 @@ int fwd_check(const char* name, const void* q, const void* k, const void* v, voi
     return fail(ATTN_ERR_UNSUPPORTED, "%s: sequence lengths must be < 2^31, B and Hq <= 65535", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
-  const size_t ob = (size_t)nq_el * (o_dtype == ATTN_FP32 ? 4 : 2);
-  const size_t lb = (size_t)nl * 4;
-  const void* ins[3] = {q, k, v};
-  const size_t inb[3] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2};
-  for (int i = 0; i < 3; ++i)
-    if (overlap(o, ob, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]))
-      return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
-  if (overlap(o, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "%s: o overlaps lse", name);
+  if (contiguous) {
+    const size_t ob = (size_t)nq_el * (o_dtype == ATTN_FP32 ? 4 : 2);
+    const size_t lb = (size_t)nl * 4;
+    const void* ins[3] = {q, k, v};
+    const size_t inb[3] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2};
+    for (int i = 0; i < 3; ++i)
+      if (overlap(o, ob, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]))
+        return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
+    if (overlap(o, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "%s: o overlaps lse", name);
+  }
 
   a->q = static_cast<const uint16_t*>(q);
   a->k = static_cast<const uint16_t*>(k);
@@ -135,6 +138,48 @@ int fwd_check(const char* name, const void* q, const void* k, const void* v, voi
   a->causal = causal ? 1 : 0;
   a->q_pos0 = q_pos0;
   a->k_pos0 = k_pos0;
+  return ATTN_OK;
+}
+
+// Strides (batch, head, token; elements) of a [B, H, N, D] tensor whose head
+// dimension is contiguous.  Every row starts 16-byte aligned; the token
+// stride is at least D and below 2^24 (per-lane tile offsets are 32-bit); an output's
+// rows must not overlap one another.  *span = elements from the first to one
+// past the last element.
+int stride_check(const char* name, const char* what, const int64_t* st, int B, int H, int64_t N, int D,
+                 int elem_bytes, bool output, int64_t* span) {
+  if (!st) return fail(ATTN_ERR_NULL, "%s: %s strides must be non-null", name, what);
+  const int64_t cnt[3] = {B, H, N};
+  int64_t sp = D;
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(ATTN_ERR_SHAPE, "%s: %s strides must be >= 0", name, what);
+    if ((st[i] * elem_bytes) % 16)
+      return fail(ATTN_ERR_ALIGN, "%s: %s strides must keep rows 16-byte aligned", name, what);
+    int64_t ext;
+    if (!mul_ok(cnt[i] - 1, st[i], &ext) || ext > INT64_MAX / 4 - sp)
+      return fail(ATTN_ERR_SHAPE, "%s: %s extent overflows", name, what);
+    sp += ext;
+  }
+  if (st[2] < D) return fail(ATTN_ERR_SHAPE, "%s: %s token stride must be >= D", name, what);
+  if (st[2] >= (int64_t(1) << 24))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: %s token stride must be < 2^24 elements", name, what);
+  if (output) {
+    // sort the dimensions of more than one element by stride; each must step
+    // past everything inside it
+    int64_t s2[3], c2[3];
+    int m = 0;
+    for (int i = 0; i < 3; ++i)
+      if (cnt[i] > 1) { s2[m] = st[i]; c2[m] = cnt[i]; ++m; }
+    for (int i = 0; i < m; ++i)
+      for (int j = i + 1; j < m; ++j)
+        if (s2[j] < s2[i]) { std::swap(s2[i], s2[j]); std::swap(c2[i], c2[j]); }
+    int64_t inner = D;
+    for (int i = 0; i < m; ++i) {
+      if (s2[i] < inner) return fail(ATTN_ERR_ALIAS, "%s: %s rows overlap one another", name, what);
+      inner = s2[i] * c2[i];
+    }
+  }
+  *span = sp;
   return ATTN_OK;
 }
 
@@ -159,6 +204,37 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, 
   if (st != ATTN_OK) return st;
   return hip_status(lcattn::launch_attn_fwd(a, B, D, o_dtype == ATTN_FP32, static_cast<hipStream_t>(hip_stream)),
                     "attn_fwd launch");
+}
+
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse, int B, int Hq,
+                     int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0,
+                     int64_t k_pos0, const int64_t* q_strides, const int64_t* kv_strides, const int64_t* o_strides,
+                     void* hip_stream) {
+  lcattn::FwdArgs a;
+  const char* name = "attn_fwd_strided";
+  int st = fwd_check(name, q, k, v, o, o_dtype, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0, k_pos0, &a,
+                     false);
+  if (st != ATTN_OK) return st;
+  const int ob = o_dtype == ATTN_FP32 ? 4 : 2;
+  int64_t qsp, ksp, osp;
+  if ((st = stride_check(name, "q", q_strides, B, Hq, Nq, D, 2, false, &qsp)) != ATTN_OK) return st;
+  if ((st = stride_check(name, "k/v", kv_strides, B, Hkv, Nk, D, 2, false, &ksp)) != ATTN_OK) return st;
+  if ((st = stride_check(name, "o", o_strides, B, Hq, Nq, D, ob, true, &osp)) != ATTN_OK) return st;
+  int64_t nl;
+  elems(&nl, {B, Hq, Nq});
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {(size_t)qsp * 2, (size_t)ksp * 2, (size_t)ksp * 2};
+  for (int i = 0; i < 3; ++i)
+    if (overlap(o, (size_t)osp * ob, ins[i], inb[i]) || overlap(lse, (size_t)nl * 4, ins[i], inb[i]))
+      return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
+  if (overlap(o, (size_t)osp * ob, lse, (size_t)nl * 4)) return fail(ATTN_ERR_ALIAS, "%s: o overlaps lse", name);
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = q_strides[i];
+    a.ks[i] = kv_strides[i];
+    a.os[i] = o_strides[i];
+  }
+  return hip_status(lcattn::launch_attn_fwd(a, B, D, o_dtype == ATTN_FP32, static_cast<hipStream_t>(hip_stream)),
+                    "attn_fwd_strided launch");
 }
 
 size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,

@@ -92,9 +92,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   const long long q_start = (long long)qt * SPAN;
   const long long wq0 = q_start + (long long)(wave / HP) * QW;
 
-  const uint16_t* qh = a.q + (bz * a.Hq + h) * a.Nq * D;
-  const uint16_t* kh = a.k + (bz * a.Hkv + kvh) * a.Nk * D;
-  const uint16_t* vh = a.v + (bz * a.Hkv + kvh) * a.Nk * D;
+  const uint16_t* qh = a.q + bz * a.qs[0] + h * a.qs[1];
+  const uint16_t* kh = a.k + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* vh = a.v + bz * a.ks[0] + kvh * a.ks[1];
 
   // keys the workgroup can see
   long long kv_end = a.Nk;
@@ -112,8 +112,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   const int klim = (int)min(a.Nk, (long long)INT32_MAX);
 
   typename T::template AsyncLoader<kWaves> kload, vload;
-  kload.init(wave, lane, false);
-  vload.init(wave, lane, true);
+  kload.init(wave, lane, false, a.ks[2]);
+  vload.init(wave, lane, true, a.ks[2]);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
     kload.load(buf, kh, (long long)(j0 + j) * kBN, a.Nk, wave);
     vload.load(buf + T::BYTES, vh, (long long)(j0 + j) * kBN, a.Nk, wave);
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < a.Nq) x = ld_global16(qh + row * D + 16 * t + 8 * grp);
+      if (row < a.Nq) x = ld_global16(qh + row * a.qs[2] + 16 * t + 8 * grp);
       qf[t] = as_bf16x8(x);
     }
   }
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const float lse = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
     if (row < a.Nq) {
-      const long long obase = split * a.part_stride + ((bz * a.Hq + h) * a.Nq + row) * D;
+      const long long obase = split * a.part_stride + bz * a.os[0] + h * a.os[1] + row * a.os[2];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -382,6 +382,16 @@ hipError_t launch_hp(const FwdArgs& a, int B, hipStream_t stream) {
 hipError_t launch_attn_fwd(const FwdArgs& a0, int B, int D, bool out_f32, hipStream_t stream) {
   FwdArgs a = a0;
   a.B = B;
+  auto contiguous = [&](long long (&st)[3], int H, long long N) {
+    if (st[0] == 0 && st[1] == 0 && st[2] == 0) {
+      st[2] = D;
+      st[1] = N * D;
+      st[0] = H * N * D;
+    }
+  };
+  contiguous(a.qs, a.Hq, a.Nq);
+  contiguous(a.ks, a.Hkv, a.Nk);
+  contiguous(a.os, a.Hq, a.Nq);
   if (D == 64) return out_f32 ? launch_hp<64, 1, true>(a, B, stream) : launch_hp<64, 1, false>(a, B, stream);
   return out_f32 ? launch_hp<128, 1, true>(a, B, stream) : launch_hp<128, 1, false>(a, B, stream);
 }
@@ -410,6 +420,7 @@ hipError_t launch_attn_fwd_splitkv(const FwdArgs& a0, int B, int D, int n_splits
   const long long tiles = (a.Nk + kBN - 1) / kBN;
   a.o = o_parts;
   a.lse = lse_parts;
+  a.os[0] = a.os[1] = a.os[2] = 0;  // partials: contiguous [B, Hq, Nq, D]
   a.n_splits = n_splits;
   a.split_tiles = (int)((tiles + n_splits - 1) / n_splits);
   a.part_stride = (long long)B * a.Hq * a.Nq * D;

@@ -270,18 +270,21 @@ struct SwzTile {
     static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
     unsigned off[N];  // byte offset of this lane's unit within the tile (global side)
     int row[N];       // tile row of that unit
-    __device__ void init(int wave, int lane, bool tr) {
+    long long rs;     // elements between consecutive rows of the matrix (>= D)
+    // row_stride < 2^24 (checked on the host) keeps the offsets in 32 bits
+    __device__ void init(int wave, int lane, bool tr, long long row_stride = D) {
+      rs = row_stride;
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const int n = wave + i * NW;
         const int slot = n * 64 + lane;
         const int r = slot / UNITS, up = slot % UNITS;
         row[i] = r;
-        off[i] = (unsigned)(r * D + 8 * (up ^ swz(tr, r))) * 2u;
+        off[i] = (unsigned)(r * row_stride + 8 * (up ^ swz(tr, r))) * 2u;
       }
     }
     __device__ void load(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total, int wave) const {
-      const unsigned char* base = reinterpret_cast<const unsigned char*>(g + r0 * D);
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(g + r0 * rs);
       if (r0 + 64 <= rows_total) {
 #pragma unroll
         for (int i = 0; i < N; ++i)
@@ -294,7 +297,7 @@ struct SwzTile {
         for (int i = 0; i < N; ++i) {
           const long long gr = r0 + row[i];
           const long long back = gr < rows_total ? 0 : gr - (rows_total - 1);  // rows to step back
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i] - back * (D * 2)),
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i] - back * rs * 2),
                                            reinterpret_cast<__attribute__((address_space(3))) void*>(
                                                reinterpret_cast<uintptr_t>(lds) + (wave + i * NW) * 1024),
                                            16, 0, 0);

@@ -32,8 +32,12 @@ struct FwdArgs {
   int split_tiles = 1 << 30;
   long long part_stride = 0;
   int B = 1;  // batch (grid z = split * B + batch)
+  // element strides (batch, head, token) of q, of k and v, and of o; the
+  // head dimension is contiguous.  Zero: contiguous [B, H, N, D].
+  long long qs[3] = {0, 0, 0}, ks[3] = {0, 0, 0}, os[3] = {0, 0, 0};
 };
 
+// (strides left at zero are filled in for contiguous [B, H, N, D] tensors)
 hipError_t launch_attn_fwd(const FwdArgs& a, int B, int D, bool out_f32, hipStream_t stream);
 
 // Forward over n_splits key ranges side by side (fp32 partials in o_parts /

@@ -35,7 +35,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
+    for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_partial_merge",
               "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
         assert n in names, names
@@ -98,6 +98,25 @@ def test_splitkv_workspace_size(L):
     auto = L.attn_fwd_splitkv_workspace_size(1, 4, 4, 4096, 4096, 64, 1, 0)
     per_range = 4 * 4096 * 65 * 4
     assert auto % per_range == 0 and 1 <= auto // per_range <= 64
+
+
+def strided(L, qs=(0, 128, 4096), ks=(0, 128, 512), os_=(0, 128, 512), **kw):
+    arr = ctypes.c_int64 * 3
+    args = dict(q=A, k=B_, v=C_, o=D_, o_dtype=0, lse=E_, B=1, Hq=4, Hkv=1, Nq=128, Nk=128, D=128,
+                scale=0.125, causal=1, q_pos0=0, k_pos0=0, qs=arr(*qs) if qs else None,
+                ks=arr(*ks) if ks else None, os_=arr(*os_) if os_ else None, stream=None)
+    args.update(kw)
+    return L.attn_fwd_strided(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), 1), (dict(os_=None), 1), (dict(qs=(0, -128, 4096)), 2), (dict(qs=(0, 128, 4100)), 4),
+    (dict(ks=(0, 0, 64)), 2), (dict(ks=(0, 0, 1 << 24)), 3), (dict(os_=(0, 64, 512)), 5),
+    (dict(os_=(0, 128, 128)), 5), (dict(o=A + 256), 5), (dict(D=96), 3),
+])
+def test_strided_rejects(L, kw, status):
+    assert strided(L, **kw) == status
+    assert L.attn_last_error()
 
 
 def merge(L, **kw):
