@@ -336,10 +336,33 @@ def main():
                           "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip}
     if not args.profile_steps:
         out["short_sequence_forward"] = short_forward(lc, torch, dev)
+        # shard 0's heads read straight from the token-major input, no relayout
+        qv = xs["q"].view(N, Hq, D)[:, :hq].permute(1, 0, 2).unsqueeze(0)
+        kv_ = xs["k"].view(N, Hkv, D)[:, :hkv].permute(1, 0, 2).unsqueeze(0)
+        vv = xs["v"].view(N, Hkv, D)[:, :hkv].permute(1, 0, 2).unsqueeze(0)
+        o_tm = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
+        ms = time_calls(torch, lambda: lc.attn_fwd_strided(qv, kv_, vv, causal=True, scale=scale, o=o_tm, lse=lse))
+        out["token_major_forward"] = {"call": "attn_fwd_strided on shard 0's heads of the token-major input",
+                                      "ms": round(ms, 4), "TFLOP/s": round(tflops(f_fwd, ms), 2),
+                                      "frac_peak": round(tflops(f_fwd, ms) / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline and not args.profile_steps:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def time_calls(torch, fn, iters=10, warmup=3):
+    """Average ms of fn() over iters calls on the current stream (events)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
 
 
 def short_forward(lc, torch, dev, iters=20):
@@ -363,16 +386,7 @@ def short_forward(lc, torch, dev, iters=20):
     calls = {"attn_fwd": lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse),
              "attn_fwd_splitkv": lambda: lc.attn_fwd_splitkv(q, k, v, scale=w.scale, workspace=ws, o=o, lse=lse)}
     for name, fn in calls.items():
-        for _ in range(5):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
+        ms = time_calls(torch, fn, iters, 5)
         res[name] = {"us": round(1e3 * ms, 2), "TFLOP/s": round(flops / ms / 1e9, 2),
                      "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
     return res
