@@ -98,6 +98,26 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int o
                      const int64_t* o_strides, void* hip_stream);
 
 /*
+ * attn_fwd_accumulate -- one step of a streaming ring on one GPU: attention of
+ * q against one KV block, merged in place into a running result.
+ *
+ * o_acc [B, Hq, Nq, D] float and lse_acc [B, Hq, Nq] float hold the running
+ * attention of q over the KV blocks of the previous calls.  With first != 0
+ * they are overwritten with this block's result (as attn_fwd with ATTN_FP32
+ * output); otherwise this block's (O_b, LSE_b) is merged into them by the
+ * attn_partial_merge rule ("So funktioniert Kontextparallelität": combining
+ * partial attention over disjoint key blocks gives full attention), which
+ * replaces the per-block partial buffers and the separate merge pass of the
+ * ring.  o_final (optional, bf16 [B, Hq, Nq, D]) also receives the merged O
+ * rounded to bf16, for the last block.  k, v, k_pos0 describe the block
+ * (global positions as in attn_fwd).  Calls on the same o_acc must be
+ * ordered (one stream).  Otherwise as attn_fwd.
+ */
+int attn_fwd_accumulate(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, void* o_final,
+                        int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal,
+                        int64_t q_pos0, int64_t k_pos0, int first, void* hip_stream);
+
+/*
  * attn_fwd_splitkv_workspace_size -- bytes of device workspace attn_fwd_splitkv
  * needs for the same arguments: fp32 partial outputs and log-sum-exps of every
  * key range, n * B*Hq*Nq*(D + 1) floats for n ranges (n_splits > 0: that many;

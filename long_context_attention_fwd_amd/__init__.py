@@ -22,6 +22,7 @@ import threading
 __all__ = [
     "attn_fwd",
     "attn_fwd_strided",
+    "attn_fwd_accumulate",
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_size",
     "attn_partial_merge",
@@ -63,6 +64,7 @@ _F = ctypes.c_float
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P]),
     "attn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P, _P, _P, _P]),
+    "attn_fwd_accumulate": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P]),
     "attn_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _L, _I, _I, _I]),
     "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P, ctypes.c_size_t,
                               _P]),
@@ -203,6 +205,34 @@ def attn_fwd_strided(q, k, v, *, causal: bool = True, scale: float | None = None
                                   B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, q_pos0, k_pos0,
                                   qs, ks, os_, _stream(q)))
     return o, lse
+
+
+def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, *, first: bool, causal: bool = True, scale: float | None = None,
+                        q_pos0: int = 0, k_pos0: int = 0, o_final=None):
+    """One streaming-ring step: attention of q against the KV block (k, v)
+    merged in place into the running fp32 (o_acc, lse_acc) (overwritten when
+    ``first``); ``o_final`` (bf16, optional) also receives the merged O."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(o_acc, "o_acc", torch.float32, 4)
+    _need(lse_acc, "lse_acc", torch.float32, 3)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    if tuple(o_acc.shape) != (B, Hq, Nq, D) or tuple(lse_acc.shape) != (B, Hq, Nq):
+        raise ValueError("o_acc / lse_acc have the wrong shape")
+    if o_final is not None:
+        _need(o_final, "o_final", torch.bfloat16, 4)
+        if tuple(o_final.shape) != (B, Hq, Nq, D):
+            raise ValueError("o_final has the wrong shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_fwd_accumulate(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_acc.data_ptr(), lse_acc.data_ptr(),
+                                     None if o_final is None else o_final.data_ptr(), B, Hq, Hkv, Nq, Nk, D, scale,
+                                     1 if causal else 0, q_pos0, k_pos0, 1 if first else 0, _stream(q)))
+    return o_acc, lse_acc
 
 
 def attn_fwd_splitkv_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, causal: bool = True,

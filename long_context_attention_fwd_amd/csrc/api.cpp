@@ -237,6 +237,32 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int o
                     "attn_fwd_strided launch");
 }
 
+int attn_fwd_accumulate(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, void* o_final,
+                        int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal,
+                        int64_t q_pos0, int64_t k_pos0, int first, void* hip_stream) {
+  lcattn::FwdArgs a;
+  const char* name = "attn_fwd_accumulate";
+  const int st = fwd_check(name, q, k, v, o_acc, ATTN_FP32, lse_acc, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0,
+                           k_pos0, &a);
+  if (st != ATTN_OK) return st;
+  if (o_final) {
+    if (!aligned16(o_final)) return fail(ATTN_ERR_ALIGN, "%s: o_final must be 16-byte aligned", name);
+    int64_t nq_el, nk_el, nl;
+    elems(&nq_el, {B, Hq, Nq, D});
+    elems(&nk_el, {B, Hkv, Nk, D});
+    elems(&nl, {B, Hq, Nq});
+    const void* bufs[5] = {q, k, v, o_acc, lse_acc};
+    const size_t sizes[5] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2, (size_t)nq_el * 4,
+                             (size_t)nl * 4};
+    for (int i = 0; i < 5; ++i)
+      if (overlap(o_final, (size_t)nq_el * 2, bufs[i], sizes[i]))
+        return fail(ATTN_ERR_ALIAS, "%s: o_final overlaps another argument", name);
+  }
+  a.accum = first ? 0 : 1;
+  a.o_final = static_cast<uint16_t*>(o_final);
+  return hip_status(lcattn::launch_attn_fwd(a, B, D, true, static_cast<hipStream_t>(hip_stream)), "attn_fwd_accumulate launch");
+}
+
 size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,
                                        int n_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1 || n_splits > kMaxSplits) return 0;

@@ -341,21 +341,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     const float lse = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
     if (row < a.Nq) {
       const long long obase = split * a.part_stride + bz * a.os[0] + h * a.os[1] + row * a.os[2];
+      const long long lidx = split * (a.part_stride / D) + (bz * a.Hq + h) * a.Nq + row;
+      // weights of the running result and of this call's in the merged one
+      // (a streaming ring step: the merge of "So funktioniert
+      // Kontextparallelität", one KV block at a time)
+      float w_old = 0.f, w_new = inv, lse_out = lse;
+      if (OUT_F32 && a.accum) {
+        const float l_old = a.lse[lidx];  // read by both lane groups before either writes
+        if (lse == -INFINITY) {
+          w_old = 1.f;
+          w_new = 0.f;
+          lse_out = l_old;
+        } else if (l_old != -INFINITY) {
+          const float M = fmaxf(l_old, lse);
+          const float e_old = fast_exp2((l_old - M) * kLog2e), e_new = fast_exp2((lse - M) * kLog2e);
+          const float r = 1.0f / (e_old + e_new);
+          w_old = e_old * r;
+          w_new = e_new * r * inv;
+          lse_out = M + fast_log2(e_old + e_new) * kLn2;
+        }
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d = db * 32 + 8 * jj + 4 * grp;
-          const float o0 = acc[db][4 * jj + 0] * inv, o1 = acc[db][4 * jj + 1] * inv;
-          const float o2 = acc[db][4 * jj + 2] * inv, o3 = acc[db][4 * jj + 3] * inv;
+          float o0 = acc[db][4 * jj + 0] * w_new, o1 = acc[db][4 * jj + 1] * w_new;
+          float o2 = acc[db][4 * jj + 2] * w_new, o3 = acc[db][4 * jj + 3] * w_new;
           if (OUT_F32) {
+            float* op = static_cast<float*>(a.o) + obase + d;
+            if (a.accum) {
+              const f32x4 prev = *reinterpret_cast<const f32x4*>(op);
+              o0 += w_old * prev[0];
+              o1 += w_old * prev[1];
+              o2 += w_old * prev[2];
+              o3 += w_old * prev[3];
+            }
             f32x4 w = {o0, o1, o2, o3};
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + obase + d) = w;
+            *reinterpret_cast<f32x4*>(op) = w;
+            if (a.o_final)
+              *reinterpret_cast<u32x2*>(a.o_final + ((bz * a.Hq + h) * a.Nq + row) * D + d) =
+                  pack_bf16x4_bits(o0, o1, o2, o3);
           } else {
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + obase + d) = pack_bf16x4_bits(o0, o1, o2, o3);
           }
         }
-      if (grp == 0) a.lse[split * (a.part_stride / D) + (bz * a.Hq + h) * a.Nq + row] = lse;
+      if (grp == 0) a.lse[lidx] = lse_out;
     }
   }
 }

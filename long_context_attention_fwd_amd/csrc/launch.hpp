@@ -35,6 +35,12 @@ struct FwdArgs {
   // element strides (batch, head, token) of q, of k and v, and of o; the
   // head dimension is contiguous.  Zero: contiguous [B, H, N, D].
   long long qs[3] = {0, 0, 0}, ks[3] = {0, 0, 0}, os[3] = {0, 0, 0};
+  // fp32 output only: accum != 0 merges this call's result into the running
+  // (o, lse) already there (log-sum-exp rule) instead of overwriting them;
+  // o_final, if set, also receives the (merged) O rounded to bf16,
+  // contiguous [B, Hq, Nq, D]
+  int accum = 0;
+  uint16_t* o_final = nullptr;
 };
 
 // (strides left at zero are filled in for contiguous [B, H, N, D] tensors)

@@ -35,7 +35,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
+    for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_partial_merge",
               "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
         assert n in names, names
@@ -116,6 +116,22 @@ def strided(L, qs=(0, 128, 4096), ks=(0, 128, 512), os_=(0, 128, 512), **kw):
 ])
 def test_strided_rejects(L, kw, status):
     assert strided(L, **kw) == status
+    assert L.attn_last_error()
+
+
+def accumulate(L, **kw):
+    args = dict(q=A, k=B_, v=C_, o=D_, lse=E_, o_final=F_, B=1, Hq=4, Hkv=1, Nq=128, Nk=128, D=128, scale=0.125,
+                causal=1, q_pos0=0, k_pos0=0, first=0, stream=None)
+    args.update(kw)
+    return L.attn_fwd_accumulate(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(Nk=0), 2), (dict(D=96), 3), (dict(o_final=F_ + 8), 4),
+    (dict(o_final=A + 1024), 5), (dict(o=A), 5),
+])
+def test_accumulate_rejects(L, kw, status):
+    assert accumulate(L, **kw) == status
     assert L.attn_last_error()
 
 
