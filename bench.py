@@ -345,6 +345,19 @@ def main():
         out["token_major_forward"] = {"call": "attn_fwd_strided on shard 0's heads of the token-major input",
                                       "ms": round(ms, 4), "TFLOP/s": round(tflops(f_fwd, ms), 2),
                                       "frac_peak": round(tflops(f_fwd, ms) / PEAK_BF16_TFLOPS, 4)}
+        # the ring streamed into one running result (blocks one after another)
+        o_acc = o_parts[0]
+        q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))
+
+        def streamed():
+            for i, a in enumerate(range(0, N, blk)):
+                lc.attn_fwd_accumulate(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], o_acc, lse_parts[0],
+                                       first=(i == 0), causal=True, scale=scale, k_pos0=a,
+                                       o_final=o_ring if a + blk >= N else None)
+        ms = time_calls(torch, streamed)
+        out["ring_streamed"] = {"call": f"{n_blk} x attn_fwd_accumulate (running fp32 O, LSE; bf16 O from the last)",
+                                "ms": round(ms, 4), "TFLOP/s": round(tflops(f_ring, ms), 2),
+                                "frac_peak": round(tflops(f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline and not args.profile_steps:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
