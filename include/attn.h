@@ -193,6 +193,62 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int64_t N, int D, float scale, int causal, void* hip_stream);
 
 /*
+ * attn_bwd_delta -- Dv_i = <dO_i, O_i> in fp32 for every query row: the
+ * per-row term of dS that attn_bwd_block takes as an input.  o, d_o
+ * [B, Hq, Nq, D] bf16 (o the final output of the forward, after every KV
+ * block); delta [B, Hq, Nq] float, caller-owned, must not overlap o or d_o.
+ * D in {64, 128}; 16-byte aligned pointers.
+ */
+int attn_bwd_delta(const void* o, const void* d_o, float* delta, int B, int Hq, int64_t Nq, int D,
+                   void* hip_stream);
+
+/*
+ * attn_bwd_block_workspace_size -- bytes of device workspace attn_bwd_block
+ * needs: 0 when Hq == Hkv, else per-query-head fp32 partials of dK and dV
+ * (2 * B*Hq*Nk*D floats).  Returns 0 also for invalid sizes.
+ */
+size_t attn_bwd_block_workspace_size(int B, int Hq, int Hkv, int64_t Nk, int D);
+
+/*
+ * attn_bwd_block -- the backward of one ring step: the gradients that flow
+ * through one KV block's part of the attention of q ("So funktioniert
+ * Kontextparallelität" on the "Context Parallelism" glossary page: each
+ * device attends its queries to one KV block at a time).  Because the
+ * forward's full attention is the LSE-merge of the per-block partials, P over
+ * block b is exp(scale q_i.k_j - LSE_i) with the global LSE, and
+ *   dS_ij = P_ij (dO_i.v_j - Dv_i)   (Dv from attn_bwd_delta on the final O),
+ *   dq_i += scale sum_{j in b} dS_ij k_j,
+ *   dk_j  = scale sum_i dS_ij q_i,   dv_j = sum_i P_ij dO_i   (j in b),
+ * so summing dq over the blocks, and running every block, gives attn_bwd's
+ * gradients exactly up to rounding.
+ *
+ * q, d_o [B, Hq, Nq, D] bf16; lse, delta [B, Hq, Nq] float (global LSE of the
+ * forward over all blocks, and Dv); k, v [B, Hkv, Nk, D] bf16: the block.
+ * Positions are global as in attn_fwd (q_pos0, k_pos0): key j is visible to
+ * query i iff k_pos0 + j <= q_pos0 + i when causal.
+ *
+ * Outputs, each optional but at least one of dq_acc / dq and one of the pairs
+ * (dk_acc, dv_acc) / (dk, dv):
+ *   dq_acc [B, Hq, Nq, D] float: overwritten with this block's dq, or, with
+ *     dq_accumulate != 0, this block's dq added to it (a ring over blocks);
+ *   dq [B, Hq, Nq, D] bf16: the value dq_acc holds after the call rounded to
+ *     bf16 (or, without dq_acc, this block's dq);
+ *   dk_acc, dv_acc [B, Hkv, Nk, D] float: the same for dk, dv with
+ *     dkv_accumulate (a block whose gradients arrive from several query
+ *     shards); dk, dv [B, Hkv, Nk, D] bf16: rounded copies.
+ * Keys that no query sees get zero gradients.  Requires Nq, Nk < 2^30;
+ * workspace >= attn_bwd_block_workspace_size bytes (may be null when that
+ * is 0; contents unspecified on return); outputs must not overlap inputs or
+ * one another.  Calls accumulating into the same buffers must be ordered
+ * (one stream).  Deterministic.  Otherwise as attn_bwd.
+ */
+int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                   const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D,
+                   float scale, int causal, int64_t q_pos0, int64_t k_pos0, int dq_accumulate, int dkv_accumulate,
+                   void* hip_stream);
+
+/*
  * seq_to_head_relayout -- the Ulysses all-to-all's data movement on one GPU.
  *
  * in  [P, N/P, H, D]: shard p holds tokens p*N/P .. (p+1)*N/P - 1, all heads.

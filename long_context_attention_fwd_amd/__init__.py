@@ -28,6 +28,9 @@ __all__ = [
     "attn_partial_merge",
     "attn_bwd",
     "attn_bwd_workspace_size",
+    "attn_bwd_delta",
+    "attn_bwd_block",
+    "attn_bwd_block_workspace_size",
     "seq_to_head_relayout",
     "head_to_seq_relayout",
     "trace_enable",
@@ -71,6 +74,10 @@ _SIGS = {
     "attn_partial_merge": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _L, _I, _P]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
+    "attn_bwd_delta": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
+    "attn_bwd_block_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
+    "attn_bwd_block": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                            _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _I, _P]),
     "seq_to_head_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
     "head_to_seq_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
     "attn_trace_enable": (_I, [_I]),
@@ -321,6 +328,78 @@ def attn_bwd(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = 
                           workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D, scale,
                           1 if causal else 0, _stream(q)))
     return dq, dk, dv
+
+
+def attn_bwd_delta(o, do, *, delta=None):
+    """Dv = <do_i, o_i> per query row (fp32 [B, Hq, Nq]) for attn_bwd_block."""
+    torch = _torch()
+    _need(o, "o", torch.bfloat16, 4)
+    _need(do, "do", torch.bfloat16, 4)
+    if tuple(do.shape) != tuple(o.shape):
+        raise ValueError("do must be shaped like o")
+    B, Hq, Nq, D = o.shape
+    delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=o.device) if delta is None else delta
+    _need(delta, "delta", torch.float32, 3)
+    if tuple(delta.shape) != (B, Hq, Nq):
+        raise ValueError("delta must be [B, Hq, Nq]")
+    _check(lib().attn_bwd_delta(o.data_ptr(), do.data_ptr(), delta.data_ptr(), B, Hq, Nq, D, _stream(o)))
+    return delta
+
+
+def attn_bwd_block_workspace_size(B: int, Hq: int, Hkv: int, Nk: int, D: int) -> int:
+    return int(lib().attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D))
+
+
+def attn_bwd_block(q, k, v, do, lse, delta, *, causal: bool = True, scale: float | None = None,
+                   q_pos0: int = 0, k_pos0: int = 0, dq_acc=None, dq_accumulate: bool = False,
+                   dk_acc=None, dv_acc=None, dkv_accumulate: bool = False, dq=None, dk=None, dv=None,
+                   workspace=None):
+    """Gradients through one KV block (k, v at global position k_pos0) of the
+    attention of q, given the global lse and Dv (attn_bwd_delta).  fp32
+    accumulators are overwritten, or added to with the *_accumulate flags;
+    bf16 dq / dk / dv, when given, receive rounded copies.  Returns
+    (dq_acc or dq, dk_acc or dk, dv_acc or dv)."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
+        _need(t, name, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(delta, "delta", torch.float32, 3)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(do.shape) != tuple(q.shape):
+        raise ValueError("do must be shaped like q")
+    if tuple(k.shape) != (B, Hkv, Nk, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, Nk, D]")
+    if tuple(lse.shape) != (B, Hq, Nq) or tuple(delta.shape) != (B, Hq, Nq):
+        raise ValueError("lse and delta must be [B, Hq, Nq]")
+    for t, name, dt, shape in ((dq_acc, "dq_acc", torch.float32, q.shape), (dq, "dq", torch.bfloat16, q.shape),
+                               (dk_acc, "dk_acc", torch.float32, k.shape), (dv_acc, "dv_acc", torch.float32, k.shape),
+                               (dk, "dk", torch.bfloat16, k.shape), (dv, "dv", torch.bfloat16, k.shape)):
+        if t is not None:
+            _need(t, name, dt, 4)
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} has the wrong shape")
+    if dq_acc is None and dq is None:
+        dq = torch.empty_like(q)
+    if dk_acc is None and dk is None:
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+    def ptr(t):
+        return t.data_ptr() if t is not None else 0
+
+    _check(lib().attn_bwd_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                delta.data_ptr(), ptr(dq_acc), ptr(dk_acc), ptr(dv_acc), ptr(dq), ptr(dk), ptr(dv),
+                                ws_ptr, ws_bytes, B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, int(q_pos0),
+                                int(k_pos0), 1 if dq_accumulate else 0, 1 if dkv_accumulate else 0, _stream(q)))
+    return (dq_acc if dq_acc is not None else dq, dk_acc if dk_acc is not None else dk,
+            dv_acc if dv_acc is not None else dv)
 
 
 def _relayout(fn_name, x, P, out, to_head):

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <algorithm>
 #include <utility>
 
 #include "launch.hpp"
@@ -332,7 +333,7 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D) {
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv) return 0;
   int64_t el;
   if (!elems(&el, {B, Hq, N, D}) || el > INT64_MAX / 16) return 0;
-  return (size_t)lcattn::bwd_workspace_bytes(B, Hq, Hkv, N, D);
+  return (size_t)lcattn::bwd_workspace_bytes(B, Hq, Hkv, N, N, D);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -378,13 +379,113 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.delta = static_cast<float*>(workspace);
+  a.part = a.delta + lcattn::bwd_delta_floats(B, Hq, N);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = Hq / Hkv;
-  a.N = N;
+  a.Nq = N;
+  a.Nk = N;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
   return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd launch");
+}
+
+int attn_bwd_delta(const void* o, const void* d_o, float* delta, int B, int Hq, int64_t Nq, int D,
+                   void* hip_stream) {
+  if (!o || !d_o || !delta) return fail(ATTN_ERR_NULL, "attn_bwd_delta: pointers must be non-null");
+  if (B < 1 || Hq < 1 || Nq < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "attn_bwd_delta: sizes must be >= 1");
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_delta: D=%d (supported: 64, 128)", D);
+  int64_t el, rows;
+  if (!elems(&el, {B, Hq, Nq, D}) || !elems(&rows, {B, Hq, Nq}) || el > INT64_MAX / 8 ||
+      (rows * (D / 8) + 255) / 256 > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "attn_bwd_delta: tensor sizes overflow");
+  if (!aligned16(o) || !aligned16(d_o) || !aligned16(delta))
+    return fail(ATTN_ERR_ALIGN, "attn_bwd_delta: pointers must be 16-byte aligned");
+  if (overlap(delta, (size_t)rows * 4, o, (size_t)el * 2) || overlap(delta, (size_t)rows * 4, d_o, (size_t)el * 2))
+    return fail(ATTN_ERR_ALIAS, "attn_bwd_delta: delta overlaps an input");
+  return hip_status(lcattn::launch_bwd_delta(static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(d_o),
+                                             delta, rows, D, static_cast<hipStream_t>(hip_stream)),
+                    "attn_bwd_delta launch");
+}
+
+size_t attn_bwd_block_workspace_size(int B, int Hq, int Hkv, int64_t Nk, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nk < 1 || D < 1 || Hq % Hkv) return 0;
+  int64_t el;
+  if (!elems(&el, {B, Hq, Nk, D}) || el > INT64_MAX / 16) return 0;
+  return (size_t)lcattn::bwd_part_floats(B, Hq, Hkv, Nk, D) * 4;
+}
+
+int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                   const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D,
+                   float scale, int causal, int64_t q_pos0, int64_t k_pos0, int dq_accumulate, int dkv_accumulate,
+                   void* hip_stream) {
+  const char* name = "attn_bwd_block";
+  if (!q || !k || !v || !d_o || !lse || !delta)
+    return fail(ATTN_ERR_NULL, "%s: q, k, v, d_o, lse and delta must be non-null", name);
+  if (!dq_acc && !dq) return fail(ATTN_ERR_NULL, "%s: dq_acc or dq must be set", name);
+  if (!dk_acc != !dv_acc || !dk != !dv)
+    return fail(ATTN_ERR_NULL, "%s: dk_acc and dv_acc (and dk and dv) are set together", name);
+  if (!dk_acc && !dk) return fail(ATTN_ERR_NULL, "%s: dk_acc/dv_acc or dk/dv must be set", name);
+  if ((dq_accumulate && !dq_acc) || (dkv_accumulate && !dk_acc))
+    return fail(ATTN_ERR_NULL, "%s: accumulating needs the fp32 accumulators", name);
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || D < 1)
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
+  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "%s: Hkv=%d does not divide Hq=%d", name, Hkv, Hq);
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(ATTN_ERR_SHAPE, "%s: position offsets must be >= 0", name);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", name, D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(ATTN_ERR_UNSUPPORTED, "%s: scale must be > 0", name);
+  int64_t nq_el, nk_el, nl, hk_el;
+  if (!elems(&nq_el, {B, Hq, Nq, D}) || !elems(&nk_el, {B, Hkv, Nk, D}) || !elems(&nl, {B, Hq, Nq}) ||
+      !elems(&hk_el, {B, Hq, Nk, D}) || nq_el > INT64_MAX / 8 || hk_el > INT64_MAX / 16)
+    return fail(ATTN_ERR_SHAPE, "%s: tensor sizes overflow", name);
+  if (Nq >= (int64_t(1) << 30) || Nk >= (int64_t(1) << 30) || B > 65535 || Hq > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: Nq and Nk must be < 2^30, B and Hq <= 65535", name);
+  const size_t need = attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", name, need, workspace_bytes);
+  const void* all[13] = {q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, dq, dk, dv, need ? workspace : nullptr};
+  for (int i = 0; i < 13; ++i)
+    if (all[i] && !aligned16(all[i])) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
+  const size_t qb = (size_t)nq_el * 2, kb = (size_t)nk_el * 2, lb = (size_t)nl * 4;
+  const void* ins[6] = {q, k, v, d_o, lse, delta};
+  const size_t inb[6] = {qb, kb, kb, qb, lb, lb};
+  const void* outs[7] = {dq_acc, dk_acc, dv_acc, dq, dk, dv, need ? workspace : nullptr};
+  const size_t outb[7] = {qb * 2, kb * 2, kb * 2, qb, kb, kb, need};
+  for (int i = 0; i < 7; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outb[i], ins[j], inb[j])) return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
+    for (int j = i + 1; j < 7; ++j)
+      if (outs[j] && overlap(outs[i], outb[i], outs[j], outb[j]))
+        return fail(ATTN_ERR_ALIAS, "%s: outputs overlap", name);
+  }
+  lcattn::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = nullptr;  // Dv is given
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = const_cast<float*>(delta);
+  a.part = static_cast<float*>(workspace);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  a.dpos = (int)std::max(-Nq, std::min(q_pos0 - k_pos0, Nk));
+  a.dq_mode = dq_acc ? (dq_accumulate ? 2 : 1) : 0;
+  a.dq_acc = dq_acc;
+  a.dkv_mode = dk_acc ? (dkv_accumulate ? 2 : 1) : 0;
+  a.dk_acc = dk_acc;
+  a.dv_acc = dv_acc;
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd_block launch");
 }
 
 static int relayout(const char* name, bool to_head, const void* in, void* out, int P, int64_t N, int H, int D,

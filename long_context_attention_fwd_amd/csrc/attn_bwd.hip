@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
-  const long long N = a.N;
+  const long long Nq = a.Nq, Nk = a.Nk;
   const long long bz = blockIdx.z;
   const int h = blockIdx.y;               // query head
   const int kvh = h / a.G;
@@ -100,27 +100,29 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   const int key = (int)(kw0 + c);         // this lane's key
   const float sl = a.scale * kLog2e;
 
-  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
-  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * N * D;
-  const long long hb = (bz * a.Hq + h) * N;
+  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * Nk * D;
+  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * Nk * D;
+  const long long hb = (bz * a.Hq + h) * Nq;
   const uint16_t* qbase = a.q + hb * D;
   const uint16_t* obase = a.d_o + hb * D;
   const float* lbase = a.lse + hb;
   const float* dbase = a.delta + hb;
 
-  const long long first_tile = a.causal ? kt0 / kBQ : 0;
-  const int n_tiles = (int)((N + kBQ - 1) / kBQ - first_tile);
+  // the first query that sees this workgroup's first key (kt0 <= i + dpos)
+  const long long q_first = a.causal ? max(0LL, kt0 - a.dpos) : 0;
+  const long long first_tile = q_first / kBQ;
+  const int n_tiles = q_first >= Nq ? 0 : (int)((Nq + kBQ - 1) / kBQ - first_tile);
 
   // global -> registers -> LDS staging of one query tile
   typename T::template Stage<NT> qst, ost;
   float lv = 0.f;
   auto fetch = [&](int i) __attribute__((always_inline)) {
     const long long r0 = (first_tile + i) * kBQ;
-    qst.load(qbase, r0, N, tid);
-    ost.load(obase, r0, N, tid);
+    qst.load(qbase, r0, Nq, tid);
+    ost.load(obase, r0, Nq, tid);
     if (tid < 2 * kBQ) {
       long long row = r0 + (tid & (kBQ - 1));
-      row = row < N ? row : N - 1;
+      row = row < Nq ? row : Nq - 1;
       lv = tid < kBQ ? lbase[row] * kLog2e : dbase[row];
     }
   };
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < N) {
+    if (key < Nk) {
       x = ld_global16(kbase + (long long)key * D + 16 * t + 8 * grp);
       y = ld_global16(vbase + (long long)key * D + 16 * t + 8 * grp);
     }
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
         float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lv2));
         if (MASKED) {
           const int qrow = (int)qt0 + r0 + e;
-          pe = (qrow >= (int)N || (a.causal && qrow < key)) ? 0.f : pe;
+          pe = (qrow >= (int)Nq || (a.causal && qrow < key - a.dpos)) ? 0.f : pe;
         }
         p[e] = pe;
         ds[e] = pe * (dp[8 * u + e] - dvv);
@@ -260,8 +262,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
     __syncthreads();
   };
   // masked tiles: those that hold the diagonal of some wave's keys, and the tail
-  const int head = a.causal ? (int)min((long long)n_tiles, (kt0 + BK - first_tile * kBQ + kBQ - 1) / kBQ) : 0;
-  const bool tail = (N % kBQ) != 0;
+  // (tiles holding a query below the workgroup's last key + 1 - dpos)
+  const int head = a.causal ? (int)max(0LL, min((long long)n_tiles,
+                                                (kt0 + BK - a.dpos - first_tile * kBQ + kBQ - 1) / kBQ))
+                            : 0;
+  const bool tail = (Nq % kBQ) != 0;
   const int body_end = max(head, n_tiles - (tail ? 1 : 0));
   int i = 0;
   for (; i < head; ++i) step(std::true_type{}, i);
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
       }
   }
 
-  if (key < N) {
+  if (key < Nk) {
 #pragma unroll
     for (int dbk = 0; dbk < DB; ++dbk)
 #pragma unroll
@@ -289,31 +294,45 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
         const float k0 = dk_acc[dbk][4 * j] * a.scale, k1 = dk_acc[dbk][4 * j + 1] * a.scale;
         const float k2 = dk_acc[dbk][4 * j + 2] * a.scale, k3 = dk_acc[dbk][4 * j + 3] * a.scale;
         if (PARTIAL) {
-          const long long base = (hb + key) * D + d;
+          const long long base = ((bz * a.Hq + h) * Nk + key) * D + d;
           const f32x4 wk = {k0, k1, k2, k3};
           const f32x4 wv = {dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2],
                             dv_acc[dbk][4 * j + 3]};
           *reinterpret_cast<f32x4*>(dk_part + base) = wk;
           *reinterpret_cast<f32x4*>(dv_part + base) = wv;
         } else {
-          const long long base = ((bz * a.Hkv + kvh) * N + key) * D + d;
-          *reinterpret_cast<u32x2*>(a.dk + base) = pack_bf16x4_bits(k0, k1, k2, k3);
-          *reinterpret_cast<u32x2*>(a.dv + base) = pack_bf16x4_bits(
-              dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2], dv_acc[dbk][4 * j + 3]);
+          const long long base = ((bz * a.Hkv + kvh) * Nk + key) * D + d;
+          f32x4 wk = {k0, k1, k2, k3};
+          f32x4 wv = {dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2], dv_acc[dbk][4 * j + 3]};
+          if (a.dkv_mode != 0) {
+            f32x4* pk = reinterpret_cast<f32x4*>(a.dk_acc + base);
+            f32x4* pv = reinterpret_cast<f32x4*>(a.dv_acc + base);
+            if (a.dkv_mode == 2) {  // this call's part added to the running dK, dV
+              wk += *pk;
+              wv += *pv;
+            }
+            *pk = wk;
+            *pv = wv;
+          }
+          if (a.dk) {
+            *reinterpret_cast<u32x2*>(a.dk + base) = pack_bf16x4_bits(wk[0], wk[1], wk[2], wk[3]);
+            *reinterpret_cast<u32x2*>(a.dv + base) = pack_bf16x4_bits(wv[0], wv[1], wv[2], wv[3]);
+          }
         }
       }
   }
 }
 
-// dK[b, kvh] = sum over the G query heads of the group of the fp32 partials.
-// One thread per 4 elements.
+// dK[b, kvh] = sum over the G query heads of the group of the fp32 partials,
+// written (or added) as the dK, dV modes of the arguments say.  One thread per
+// 4 elements.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ dk_part,
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const float* __restrict__ dk_part,
                                                               const float* __restrict__ dv_part,
-                                                              uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                                                              int G, long long kv_heads_total, long long N) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // over kv_heads_total * N * D / 4
-  const long long per_head = N * D / 4;
+                                                              long long kv_heads_total) {
+  const int G = a.G;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // over kv_heads_total * Nk * D / 4
+  const long long per_head = a.Nk * D / 4;
   if (idx >= kv_heads_total * per_head) return;
   const long long hk = idx / per_head;        // flattened (b, kvh)
   const long long rem = idx - hk * per_head;  // 4-element slot within the head
@@ -323,8 +342,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __res
     sk += *reinterpret_cast<const f32x4*>(dk_part + src);
     sv += *reinterpret_cast<const f32x4*>(dv_part + src);
   }
-  *reinterpret_cast<u32x2*>(dk + idx * 4) = pack_bf16x4_bits(sk[0], sk[1], sk[2], sk[3]);
-  *reinterpret_cast<u32x2*>(dv + idx * 4) = pack_bf16x4_bits(sv[0], sv[1], sv[2], sv[3]);
+  if (a.dkv_mode != 0) {
+    f32x4* pk = reinterpret_cast<f32x4*>(a.dk_acc + idx * 4);
+    f32x4* pv = reinterpret_cast<f32x4*>(a.dv_acc + idx * 4);
+    if (a.dkv_mode == 2) {
+      sk += *pk;
+      sv += *pv;
+    }
+    *pk = sk;
+    *pv = sv;
+  }
+  if (a.dk) {
+    *reinterpret_cast<u32x2*>(a.dk + idx * 4) = pack_bf16x4_bits(sk[0], sk[1], sk[2], sk[3]);
+    *reinterpret_cast<u32x2*>(a.dv + idx * 4) = pack_bf16x4_bits(sv[0], sv[1], sv[2], sv[3]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
-  const long long N = a.N;
+  const long long Nq = a.Nq, Nk = a.Nk;
   const long long bz = blockIdx.z;
   const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest causal rows first
   const int h = blockIdx.y * HP + (wave % HP);
@@ -355,22 +386,23 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const long long wq0 = q_start + (long long)(wave / HP) * 32;
   const long long qrow = wq0 + c;
   const int qrow_i = (int)qrow;
-  const int klim = (int)N;
+  const int klim = (int)Nk;
   const float sl = a.scale * kLog2e;
-  const long long hb = (bz * a.Hq + h) * N;
-  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * N * D;
-  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * N * D;
+  const long long hb = (bz * a.Hq + h) * Nq;
+  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * Nk * D;
+  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * Nk * D;
 
-  long long kv_end = N;
-  if (a.causal) kv_end = min(N, q_start + SPAN);
+  // keys the workgroup can see
+  long long kv_end = Nk;
+  if (a.causal) kv_end = max(0LL, min(Nk, min(q_start + SPAN, Nq) + a.dpos));
   const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
   const int n_sub = 2 * n_tiles;  // 32-key sub-tiles
 
   typename T::template AsyncLoader<NW> ld;
   ld.init(wave, lane, false);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    ld.load(buf, kbase, (long long)j * kBN, N, wave);
-    ld.load(buf + T::BYTES, vbase, (long long)j * kBN, N, wave);
+    ld.load(buf, kbase, (long long)j * kBN, Nk, wave);
+    ld.load(buf + T::BYTES, vbase, (long long)j * kBN, Nk, wave);
   };
   if (n_tiles > 0) issue(0, smem0);
 
@@ -379,15 +411,15 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (qrow < N) {
+    if (qrow < Nq) {
       x = ld_global16(a.q + (hb + qrow) * D + 16 * t + 8 * grp);
       y = ld_global16(a.d_o + (hb + qrow) * D + 16 * t + 8 * grp);
     }
     qf[t] = as_bf16x8(x);
     of[t] = as_bf16x8(y);
   }
-  const float lse2 = qrow < N ? a.lse[hb + qrow] * kLog2e : INFINITY;  // rows past N: P = 0
-  const float dvv = qrow < N ? a.delta[hb + qrow] : 0.f;
+  const float lse2 = qrow < Nq ? a.lse[hb + qrow] * kLog2e : INFINITY;  // rows past Nq: P = 0
+  const float dvv = qrow < Nq ? a.delta[hb + qrow] : 0.f;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -459,7 +491,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
       float p = fast_exp2(__builtin_fmaf(s[v], sl, -lse2));
       if (MASKED) {
         const int key = 32 * t + acc_row_pi(v, grp);
-        if (key >= klim || (a.causal && key > qrow_i)) p = 0.f;
+        if (key >= klim || (a.causal && key > qrow_i + a.dpos)) p = 0.f;
       }
       ds[v] = p * (dp[v] - dvv);
     }
@@ -494,8 +526,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   };
 
   // Tiles [0, n_full) need no element mask for any wave of the workgroup.
-  long long full_keys = N;
-  if (a.causal) full_keys = min(full_keys, q_start + 1);
+  long long full_keys = Nk;
+  if (a.causal) full_keys = max(0LL, min(full_keys, q_start + 1 + a.dpos));
   const int n_full = (int)min((long long)n_tiles, full_keys / kBN);
 
   // Schedule: tile j lives in buffer j % 3 and is read in steps 2j .. 2j+2.
@@ -542,46 +574,58 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
     wait_vmem();  // no direct load may still be in flight when the workgroup ends
   }
 
-  if (qrow < N) {
+  if (qrow < Nq) {
     const long long base = (hb + qrow) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d = db * 32 + 8 * jj + 4 * grp;
-        *reinterpret_cast<u32x2*>(a.dq + base + d) =
-            pack_bf16x4_bits(acc[db][4 * jj] * a.scale, acc[db][4 * jj + 1] * a.scale,
-                             acc[db][4 * jj + 2] * a.scale, acc[db][4 * jj + 3] * a.scale);
+        f32x4 g = {acc[db][4 * jj] * a.scale, acc[db][4 * jj + 1] * a.scale, acc[db][4 * jj + 2] * a.scale,
+                   acc[db][4 * jj + 3] * a.scale};
+        if (a.dq_mode != 0) {
+          f32x4* p = reinterpret_cast<f32x4*>(a.dq_acc + base + d);
+          if (a.dq_mode == 2) g += *p;  // this KV block's part added to the running dQ
+          *p = g;
+        }
+        if (a.dq) *reinterpret_cast<u32x2*>(a.dq + base + d) = pack_bf16x4_bits(g[0], g[1], g[2], g[3]);
       }
   }
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
-  const long long rows = (long long)B * a.Hq * a.N;
+hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, hipStream_t stream) {
   const long long threads = rows * (D / 8);
-  LCATTN_LAUNCH("bwd_delta_kernel", (bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.o,
-                     a.d_o, a.delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 kgrid((unsigned)((a.N + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
+  LCATTN_LAUNCH("bwd_delta_kernel", (bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                stream, o, d_o, delta, rows);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
+  hipError_t e;
+  if (a.o) {
+    e = launch_delta<D>(a.o, a.d_o, a.delta, (long long)B * a.Hq * a.Nq, stream);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 kgrid((unsigned)((a.Nk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
   if (a.G == 1) {
     LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, nullptr, nullptr);
   } else {
-    float* dk_part = a.delta + bwd_delta_floats(B, a.Hq, a.N);
-    float* dv_part = dk_part + (long long)B * a.Hq * a.N * D;
+    float* dk_part = a.part;
+    float* dv_part = dk_part + (long long)B * a.Hq * a.Nk * D;
     LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, dk_part, dv_part);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long slots = (long long)B * a.Hkv * a.N * D / 4;
-    LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream,
-                       dk_part, dv_part, a.dk, a.dv, a.G, (long long)B * a.Hkv, a.N);
+    const long long slots = (long long)B * a.Hkv * a.Nk * D / 4;
+    LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
+                  dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
   const long long span = (kDqWaves / HP) * 32;
-  const int n_qt = (int)((a.N + span - 1) / span);
+  const int n_qt = (int)((a.Nq + span - 1) / span);
   dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
   if (HP == 4)
     LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
@@ -594,19 +638,26 @@ hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
 
 }  // namespace
 
-long long bwd_delta_floats(int B, int Hq, long long N) {
+long long bwd_delta_floats(int B, int Hq, long long Nq) {
   // Dv rows, padded to a multiple of 64 floats (256 bytes)
-  return ((long long)B * Hq * N + 63) / 64 * 64;
+  return ((long long)B * Hq * Nq + 63) / 64 * 64;
 }
 
-long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long N, int D) {
-  long long f = bwd_delta_floats(B, Hq, N);
-  if (Hq != Hkv) f += 2LL * B * Hq * N * D;  // per-query-head dK, dV partials
-  return f * 4;
+long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D) {
+  return Hq != Hkv ? 2LL * B * Hq * Nk * D : 0;  // per-query-head dK, dV partials
+}
+
+long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D) {
+  return (bwd_delta_floats(B, Hq, Nq) + bwd_part_floats(B, Hq, Hkv, Nk, D)) * 4;
 }
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream) {
   return D == 64 ? launch_d<64>(a, B, stream) : launch_d<128>(a, B, stream);
+}
+
+hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, int D,
+                            hipStream_t stream) {
+  return D == 64 ? launch_delta<64>(o, d_o, delta, rows, stream) : launch_delta<128>(o, d_o, delta, rows, stream);
 }
 
 }  // namespace lcattn

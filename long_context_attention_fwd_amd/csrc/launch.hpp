@@ -68,19 +68,40 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;  // workspace: <dO_i, O_i> per query row, then the dK/dV partials
+  // <dO_i, O_i> per query row (fp32): written by the launch first when o is
+  // set, else given
+  float* delta;
+  float* part;  // grouped-query attention: per-query-head fp32 dK, dV partials
   int Hq, Hkv, G;
-  long long N;
+  long long Nq, Nk;  // query rows; keys (the whole sequence, or one KV block)
   float scale;
   int causal;
+  // q_pos0 - k_pos0: key j is visible to query i iff j <= i + dpos (causal);
+  // clamped to [-Nq, Nk], which keeps every mask sum in the int range for
+  // Nq, Nk < 2^30
+  int dpos = 0;
+  // dQ output: 0 -> bf16 dq only; 1 -> fp32 dq_acc overwritten; 2 -> added
+  // into dq_acc (a ring over KV blocks); with 1 and 2, dq (bf16) also
+  // receives the accumulated value if set
+  int dq_mode = 0;
+  float* dq_acc = nullptr;
+  // dK, dV output, the same three modes on dk_acc / dv_acc (fp32) with dk, dv
+  // (bf16) optional when set
+  int dkv_mode = 0;
+  float* dk_acc = nullptr;
+  float* dv_acc = nullptr;
 };
 
 // Backward workspace: Dv per query row (fp32, padded to 64 floats), then, for
 // grouped-query attention (Hq != Hkv), per-query-head fp32 partials of dK and
-// dV ([B, Hq, N, D] each).
-long long bwd_delta_floats(int B, int Hq, long long N);
-long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long N, int D);
+// dV ([B, Hq, Nk, D] each).
+long long bwd_delta_floats(int B, int Hq, long long Nq);
+long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D);
+long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream);
+// Dv_i = <dO_i, O_i> for rows query rows of width D
+hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, int D,
+                            hipStream_t stream);
 
 }  // namespace lcattn

@@ -20,6 +20,7 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_backward_sampled,
     attention_backward_row_support,
+    attention_backward_block,
     seq_to_head,
     head_to_seq,
 )

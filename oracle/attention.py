@@ -53,6 +53,7 @@ __all__ = [
     "attention_backward",
     "attention_backward_sampled",
     "attention_backward_row_support",
+    "attention_backward_block",
     "seq_to_head",
     "head_to_seq",
 ]
@@ -322,6 +323,55 @@ def attention_backward_sampled(q, k, v, do, scale, q_rows, kv_rows, causal=True,
                 dS = P * (do[b, h, rb] @ v[b, kh, kv_rows].T - dv[b, h, rb][:, None])
                 dK[b, kh] += s * (dS.T @ q[b, h, rb])
                 dV[b, kh] += P.T @ do[b, h, rb]
+    return dQ, dK, dV
+
+
+def attention_backward_block(q, k, v, do, lse, dv, scale, causal=True, q_pos0=0, k_pos0=0):
+    """Gradients through one KV block of the attention of a query shard (the
+    backward of one step of the ring of "So funktioniert Kontextparallelität").
+
+    q, do [B, Hq, Nq, D]: the shard's queries at global positions
+    q_pos0 .. q_pos0+Nq-1 and their output gradients.  k, v [B, Hkv, Nk, D]:
+    one KV block at positions k_pos0 .. k_pos0+Nk-1.  lse, dv [B, Hq, Nq]: the
+    shard's LSE over every key of the sequence and Dv_i = <dO_i, O_i> of its
+    final output.  Softmax over a disjoint union of key sets shares one
+    normaliser, so over this block P_ij = exp(s q_i.k_j - LSE_i) with the
+    global LSE, dS_ij = P_ij (<dO_i, V_j> - Dv_i), and
+    dQ_i = s sum_j dS_ij K_j (this block's term), dK_j = s sum_i dS_ij Q_i,
+    dV_j = sum_i P_ij dO_i.  Returns (dQ, dK, dV), float64.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    lse = np.asarray(lse, dtype=np.float64)
+    dv = np.asarray(dv, dtype=np.float64)
+    B, Hq, Hkv, D = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    Nq, Nk = q.shape[2], k.shape[2]
+    if do.shape != q.shape or lse.shape != (B, Hq, Nq) or dv.shape != (B, Hq, Nq):
+        raise ValueError("do like q; lse and dv [B, Hq, Nq]")
+    s = np.float64(scale)
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    rows = np.arange(Nq, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // G
+            for rb in _row_batches(rows, Nk):
+                qpos = np.int64(q_pos0) + rb
+                nvis = _visible_keys(causal, int(qpos.max()), k_pos0, Nk)
+                if nvis == 0:
+                    continue
+                S = scores(q[b, h, rb], k[b, kh, :nvis], scale, causal, qpos, k_pos0)
+                with np.errstate(invalid="ignore"):
+                    P = np.exp(S - lse[b, h, rb][:, None])
+                P[np.isneginf(S)] = 0.0  # masked entries (also rows whose LSE is -inf)
+                dS = P * (do[b, h, rb] @ v[b, kh, :nvis].T - dv[b, h, rb][:, None])
+                dQ[b, h, rb] = s * (dS @ k[b, kh, :nvis])
+                dK[b, kh, :nvis] += s * (dS.T @ q[b, h, rb])
+                dV[b, kh, :nvis] += P.T @ do[b, h, rb]
     return dQ, dK, dV
 
 

@@ -36,7 +36,8 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
-              "attn_bwd_workspace_size", "attn_partial_merge",
+              "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
+              "attn_partial_merge",
               "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -170,6 +171,50 @@ def bwd(L, **kw):
 ])
 def test_bwd_rejects(L, kw, status):
     assert bwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, B_, C_, 1, 8, 1024, 128), 1), ((A, B_, C_, 1, 8, 0, 128), 2), ((A, B_, C_, 1, 8, 1024, 96), 3),
+    ((A, B_, C_ + 4, 1, 8, 1024, 128), 4), ((A, B_, A + 1024, 1, 8, 1024, 128), 5),
+])
+def test_bwd_delta_rejects(L, args, status):
+    assert L.attn_bwd_delta(*args, None) == status
+
+
+def test_bwd_block_workspace_size(L):
+    assert L.attn_bwd_block_workspace_size(1, 8, 8, 4096, 128) == 0          # no group: no partials
+    assert L.attn_bwd_block_workspace_size(1, 8, 2, 4096, 128) == 2 * 8 * 4096 * 128 * 4
+    assert L.attn_bwd_block_workspace_size(1, 8, 3, 4096, 128) == 0
+    assert L.attn_bwd_block_workspace_size(1, 8, 8, 0, 128) == 0
+
+
+def bwd_block(L, **kw):
+    n = 1 << 24
+    args = dict(q=A, k=A + n, v=A + 2 * n, do=A + 3 * n, lse=A + 4 * n, delta=A + 5 * n, dq_acc=A + 6 * n,
+                dk_acc=A + 7 * n, dv_acc=A + 8 * n, dq=A + 9 * n, dk=A + 10 * n, dv=A + 11 * n, ws=A + 12 * n,
+                ws_bytes=1 << 24, B=1, Hq=8, Hkv=2, Nq=1024, Nk=512, D=128, scale=0.088, causal=1, q_pos0=512,
+                k_pos0=0, dq_accumulate=1, dkv_accumulate=0, stream=None)
+    args.update(kw)
+    return L.attn_bwd_block(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(delta=None), 1),
+    (dict(dq_acc=None, dq=None), 1),
+    (dict(dk_acc=None), 1),                                   # dk_acc and dv_acc come together
+    (dict(dk=None), 1),
+    (dict(dk_acc=None, dv_acc=None, dk=None, dv=None), 1),
+    (dict(dq_acc=None), 1),                                   # accumulate without the fp32 dQ
+    (dict(Nk=0), 2), (dict(Hkv=3), 2), (dict(q_pos0=-1), 2),
+    (dict(D=32), 3), (dict(scale=0.0), 3), (dict(Nq=1 << 30), 3),
+    (dict(ws=None), 6), (dict(ws_bytes=1000), 6),
+    (dict(dv=A + (11 << 24) + 8), 4),
+    (dict(dq_acc=A + (1 << 24) + 64), 5),                    # dq_acc overlaps k
+    (dict(dk=A + (7 << 24)), 5),                              # dk overlaps dk_acc
+])
+def test_bwd_block_rejects(L, kw, status):
+    assert bwd_block(L, **kw) == status
+    assert L.attn_last_error()
 
 
 @pytest.mark.parametrize("fn", ["seq_to_head_relayout", "head_to_seq_relayout"])

@@ -353,6 +353,99 @@ def test_backward_row_support_matches_full_with_masked_do():
 
 
 # ---------------------------------------------------------------------------
+# backward of one ring step: gradients through one KV block
+# ---------------------------------------------------------------------------
+def check_block_backward_vs_torch(Hq=4, Hkv=2, N=30, D=8, causal=True, shards=(0, 11, 30), blocks=(0, 7, 19, 30),
+                                  seed=21):
+    """Query shards against KV blocks, each block a separate leaf of torch's
+    autograd over SDPA with an explicit mask of global positions: the oracle's
+    per-(shard, block) gradients must sum to torch's gradients of each shard's
+    loss, and a block's dK/dV from one shard must equal torch's gradient of
+    that shard's loss with respect to that block."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    d = make_qkv(1, Hq, Hkv, N, D, seed=seed, with_do=True)
+    q, k, v, do = (oracle.bf16_bits_to_f64(d[n]) for n in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(D)
+    G = Hq // Hkv
+    worst = 0.0
+    for a, b in zip(shards[:-1], shards[1:]):
+        O, L = oracle.attention_forward(q, k, v, s, causal, rows=np.arange(a, b))
+        Dv = np.einsum("bhnd,bhnd->bhn", do[:, :, a:b], O)
+        tq = torch.from_numpy(q[:, :, a:b].copy()).requires_grad_()
+        tk = [torch.from_numpy(k[:, :, c:e].copy()).requires_grad_() for c, e in zip(blocks[:-1], blocks[1:])]
+        tv = [torch.from_numpy(v[:, :, c:e].copy()).requires_grad_() for c, e in zip(blocks[:-1], blocks[1:])]
+        kk = torch.cat(tk, dim=2).repeat_interleave(G, dim=1)
+        vv = torch.cat(tv, dim=2).repeat_interleave(G, dim=1)
+        mask = None
+        if causal:
+            mask = torch.arange(N)[None, :] <= torch.arange(a, b)[:, None]
+        o = F.scaled_dot_product_attention(tq, kk, vv, attn_mask=mask, scale=s)
+        (o * torch.from_numpy(do[:, :, a:b].copy())).sum().backward()
+        dq_sum = np.zeros_like(q[:, :, a:b])
+        for i, (c, e) in enumerate(zip(blocks[:-1], blocks[1:])):
+            bq, bk, bv = oracle.attention_backward_block(q[:, :, a:b], k[:, :, c:e], v[:, :, c:e], do[:, :, a:b], L,
+                                                         Dv, s, causal, q_pos0=a, k_pos0=c)
+            dq_sum += bq
+            worst = max(worst, np.abs(bk - tk[i].grad.numpy()).max(), np.abs(bv - tv[i].grad.numpy()).max())
+        worst = max(worst, np.abs(dq_sum - tq.grad.numpy()).max())
+    return worst
+
+
+@pytest.mark.parametrize("Hq,Hkv,causal", [(4, 2, True), (2, 2, False), (4, 1, True)])
+def test_block_backward_matches_torch_autograd(Hq, Hkv, causal):
+    assert check_block_backward_vs_torch(Hq, Hkv, causal=causal) < 1e-12
+
+
+def test_block_backward_sums_to_full_backward():
+    """Every (query shard, KV block) pair: dQ summed over blocks and dK, dV
+    summed over shards give attention_backward's gradients."""
+    d = make_qkv(2, 4, 2, 77, 8, seed=22, with_do=True)
+    q, k, v, do = (oracle.bf16_bits_to_f64(d[n]) for n in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(8)
+    O, L, dQ, dK, dV = oracle.attention_backward(q, k, v, do, s)
+    Dv = np.einsum("bhnd,bhnd->bhn", do, O)
+    cuts = [0, 13, 40, 64, 77]
+    gq, gk, gv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for a, b in zip(cuts[:-1], cuts[1:]):          # query shard
+        for c, e in zip(cuts[:-1], cuts[1:]):      # KV block
+            bq, bk, bv = oracle.attention_backward_block(q[:, :, a:b], k[:, :, c:e], v[:, :, c:e], do[:, :, a:b],
+                                                         L[:, :, a:b], Dv[:, :, a:b], s, True, a, c)
+            if c > b - 1:                          # block entirely after the shard: no gradient
+                assert not bq.any() and not bk.any() and not bv.any()
+            gq[:, :, a:b] += bq
+            gk[:, :, c:e] += bk
+            gv[:, :, c:e] += bv
+    assert np.abs(gq - dQ).max() < 1e-12
+    assert np.abs(gk - dK).max() < 1e-12 and np.abs(gv - dV).max() < 1e-12
+
+
+def test_block_backward_whole_sequence_is_full_backward():
+    d = make_qkv(1, 2, 1, 40, 8, seed=23, with_do=True)
+    s = 0.3
+    O, L, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s)
+    Dv = np.einsum("bhnd,bhnd->bhn", oracle.bf16_bits_to_f64(d["do"]), O)
+    bq, bk, bv = oracle.attention_backward_block(d["q"], d["k"], d["v"], d["do"], L, Dv, s)
+    assert np.abs(bq - dQ).max() < 1e-12 and np.abs(bk - dK).max() < 1e-12 and np.abs(bv - dV).max() < 1e-12
+
+
+def test_planted_block_backward_mistakes_are_caught(monkeypatch):
+    orig = oa.attention_backward_block
+
+    def local_lse(q, k, v, do, lse, dv, scale, causal=True, q_pos0=0, k_pos0=0):
+        # the block's own LSE instead of the global one
+        _, lb = oa.attention_forward(q, k, v, scale, causal, q_pos0, k_pos0)
+        return orig(q, k, v, do, lb, dv, scale, causal, q_pos0, k_pos0)
+
+    def shifted(q, k, v, do, lse, dv, scale, causal=True, q_pos0=0, k_pos0=0):
+        return orig(q, k, v, do, lse, dv, scale, causal, q_pos0, k_pos0 + 1)   # off-by-one block position
+
+    for bad in (local_lse, shifted):
+        monkeypatch.setattr(oracle, "attention_backward_block", bad)
+        assert check_block_backward_vs_torch() > 1e-3
+
+
+# ---------------------------------------------------------------------------
 # relayout: a transpose of the flattened token and head indices
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("P,N,H,D", [(8, 64, 32, 4), (8, 64, 8, 4), (4, 12, 4, 2), (2, 6, 6, 3)])
