@@ -358,6 +358,26 @@ def main():
         out["ring_streamed"] = {"call": f"{n_blk} x attn_fwd_accumulate (running fp32 O, LSE; bf16 O from the last)",
                                 "ms": round(ms, 4), "TFLOP/s": round(tflops(f_ring, ms), 2),
                                 "frac_peak": round(tflops(f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
+        # the ring's backward: Dv once, then one attn_bwd_block per KV block
+        # (fp32 dQ accumulated in place, bf16 dQ from the last; each block's
+        # dK, dV in bf16), against the same global LSE
+        dq_acc = o_parts[1]
+        delta = torch.empty_like(lse)
+        ws_blk = torch.empty(max(16, lc.attn_bwd_block_workspace_size(1, hq, hkv, blk, D)), dtype=torch.uint8,
+                             device=dev)
+        do0 = heads["do"][0:1]
+
+        def ring_backward():
+            lc.attn_bwd_delta(o, do0, delta=delta)
+            for i, a in enumerate(range(0, N, blk)):
+                lc.attn_bwd_block(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], do0, lse, delta, causal=True,
+                                  scale=scale, k_pos0=a, dq_acc=dq_acc, dq_accumulate=i > 0,
+                                  dq=dq if a + blk >= N else None, dk=dk[:, :, a:a + blk], dv=dv[:, :, a:a + blk],
+                                  workspace=ws_blk)
+        ms = time_calls(torch, ring_backward)
+        out["ring_backward"] = {"call": f"attn_bwd_delta + {n_blk} x attn_bwd_block (fp32 dQ accumulated)",
+                                "ms": round(ms, 4), "TFLOP/s": round(tflops(2.5 * f_ring, ms), 2),
+                                "frac_peak": round(tflops(2.5 * f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline and not args.profile_steps:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
