@@ -62,6 +62,7 @@ namespace {
 constexpr int kWaves = 8;      // two waves per SIMD: one's softmax overlaps the other's MFMAs
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;         // keys per tile
+constexpr float kSlack = 8.f;   // lazy rescale: P <= 2^kSlack before the final division
 
 template <int D, int QB, int HP, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
@@ -162,8 +163,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
 
   // Online softmax of one sub-tile: S^T (one query per lane, 16 of its 32
   // keys; the other 16 sit in lane ^ 32) -> P packed as the B operand of the
-  // next PV product, the running max / sum, and the rescale factor alpha.
-  auto softmax = [&](auto masked_tag, f32x16 s, int t, float& alpha) __attribute__((always_inline)) {
+  // next PV product, and this sub-tile's part of the row sum (psum).  The
+  // reference maximum m_run moves only when a scaled score exceeds it by
+  // more than kSlack (log2 units): P stays <= 2^kSlack, exact after the
+  // final division, and the rescale of O and the sum (m_old -> m_run) is
+  // rare after the first tiles.
+  auto softmax = [&](auto masked_tag, f32x16 s, int t, float& m_old, float& psum) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if (MASKED) {
       const int kt = kBN * j0 + 32 * t;
@@ -182,10 +187,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max with lane ^ 32
     }
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
-    m_run = m_new;
+    const float m_cand = fmaxf(m_run, mx * a.scale_log2);
+    m_old = m_run;
+    m_run = m_cand > m_run + kSlack ? m_cand : m_run;
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     }
     pf[0] = pack_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
     pf[1] = pack_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
-    l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
+    psum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   // One step t of the pipeline over 32-key sub-tiles:
@@ -225,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
       acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), pf[0], acc[db]);
       acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), pf[1], acc[db]);
     }
-    float alpha;
-    softmax(masked_tag, s_cur, t, alpha);
+    float m_old, psum;
+    softmax(masked_tag, s_cur, t, m_old, psum);
     constexpr int NM = KT + 2 * DB;
     constexpr int VPM = (72 + NM - 1) / NM;
 #pragma unroll
@@ -238,17 +243,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     // are sunk past it, out of reach of the MFMAs they should overlap)
     {
       u32x4 p0 = as_u32x4(pf[0]), p1 = as_u32x4(pf[1]);
-      asm volatile("" : "+v"(p0), "+v"(p1), "+v"(l_run));
+      asm volatile("" : "+v"(p0), "+v"(p1), "+v"(psum));
       pf[0] = as_bf16x8(p0);
       pf[1] = as_bf16x8(p1);
     }
-    // the accumulator now holds PV up to t-1: bring it to the new maximum
-    if (__any(alpha != 1.f)) {
+    // the accumulator now holds PV up to t-1: bring it and the sum to the new
+    // reference maximum
+    if (__any(m_run != m_old)) {
+      const float alpha = m_run != m_old ? fast_exp2(m_old - m_run) : 1.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+      l_run *= alpha;
     }
+    l_run += psum;
     return s_next;
   };
   auto sync = [&]() __attribute__((always_inline)) {
@@ -279,10 +288,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     f32x16 s = s_sub(smem0, 0);
     // step 0: nothing to multiply with V yet
     {
-      float alpha;
+      float m_old, psum;
       const f32x16 s_next = s_sub(smem0, 1);
-      if (n_full > 0) softmax(std::false_type{}, s, 0, alpha);
-      else softmax(std::true_type{}, s, 0, alpha);
+      if (n_full > 0) softmax(std::false_type{}, s, 0, m_old, psum);
+      else softmax(std::true_type{}, s, 0, m_old, psum);
+      l_run = psum;
       s = s_next;
     }
     sync();
