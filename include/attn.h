@@ -255,16 +255,38 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
  * out [P, H/P, N, D]: rank r holds heads r*H/P .. (r+1)*H/P - 1, all tokens.
  * out[r, h', n, :] = in[n / (N/P), n % (N/P), r*(H/P) + h', :] -- the
  * transpose [N, H, D] -> [H, N, D].  A bit copy of elem_bytes-wide words
- * (2 for bf16, 4 for float).  Requires P | N, P | H (H >= P), D*elem_bytes a
- * multiple of 16; in and out must not overlap.  For key/value tensors pass
- * H = Hkv.
+ * (2 for bf16, 4 for float).  Requires P | N, D*elem_bytes 16 times a power
+ * of two, and P | H -- or, for fewer heads than ranks (key/value heads of
+ * grouped-query attention, H < P), H | P: then each head is replicated to
+ * the P/H consecutive ranks whose query heads read it, out [P, 1, N, D] with
+ * out[r, 0, n, :] = in[n / (N/P), n % (N/P), r / (P/H), :].  in and out must
+ * not overlap.  For key/value tensors pass H = Hkv.
  */
 int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
                          void* hip_stream);
 
-/* head_to_seq_relayout -- the inverse: in [P, H/P, N, D] -> out [P, N/P, H, D]. */
+/*
+ * head_to_seq_relayout -- the inverse: in [P, H/P, N, D] -> out [P, N/P, H, D]
+ * (P | H; replicated heads, H < P, are ATTN_ERR_UNSUPPORTED here: their
+ * gradients must be summed, see head_to_seq_reduce).
+ */
 int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
                          void* hip_stream);
+
+/*
+ * head_to_seq_reduce -- the inverse exchange of gradients of heads that
+ * several ranks shared: with R = P/H ranks per head when H < P (else R = 1),
+ * in [P, max(1, H/P), N, D] (flattened: [H*R, N, D], rank-major), out
+ * [P, N/P, H, D] bf16 with out[n / (N/P), n % (N/P), h, :] = the sum over
+ * i < R of in[h*R + i, n, :], added in fp32 in the order i = 0, 1, ... and
+ * rounded once to bf16 (nearest even).  A key/value head read by the query
+ * heads of R ranks gets the sum of their dK (dV) parts, which is its
+ * gradient.  in_dtype ATTN_BF16 or ATTN_FP32 (e.g. attn_bwd_block's fp32
+ * accumulators); R = 1 is the plain inverse relayout with a conversion.
+ * Requires P | N, H | P or P | H, D a multiple of 8; in and out must not
+ * overlap.
+ */
+int head_to_seq_reduce(const void* in, int in_dtype, void* out, int P, int64_t N, int H, int D, void* hip_stream);
 
 /*
  * Measurement hook (not part of the computation).  While enabled, every

@@ -33,6 +33,7 @@ __all__ = [
     "attn_bwd_block_workspace_size",
     "seq_to_head_relayout",
     "head_to_seq_relayout",
+    "head_to_seq_reduce",
     "trace_enable",
     "trace_collect",
     "AttnError",
@@ -75,6 +76,7 @@ _SIGS = {
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
     "attn_bwd_delta": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
+    "head_to_seq_reduce": (_I, [_P, _I, _P, _I, _L, _I, _I, _P]),
     "attn_bwd_block_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd_block": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                             _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _I, _P]),
@@ -411,7 +413,7 @@ def _relayout(fn_name, x, P, out, to_head):
     if to_head:
         Pp, T, H, D = x.shape
         N = Pp * T
-        shape = (Pp, H // Pp if Pp else 0, N, D)
+        shape = (Pp, max(1, H // Pp) if Pp else 0, N, D)  # H < P: one replicated head per rank
     else:
         Pp, Hp, N, D = x.shape
         H = Pp * Hp
@@ -433,6 +435,27 @@ def seq_to_head_relayout(x, P: int, *, out=None):
 def head_to_seq_relayout(y, P: int, *, out=None):
     """[P, H/P, N, D] -> [P, N/P, H, D] (bit copy)."""
     return _relayout("head_to_seq_relayout", y, P, out, False)
+
+
+def head_to_seq_reduce(y, P: int, H: int, *, out=None):
+    """[P, max(1, H/P), N, D] (bf16 or fp32) -> [P, N/P, H, D] bf16, summing
+    the P/H replicas of each head when H < P (gradients of shared key/value
+    heads)."""
+    torch = _torch()
+    _need(y, "y", (torch.bfloat16, torch.float32), 4)
+    Pp, Hr, N, D = y.shape
+    if Pp != P:
+        raise ValueError(f"leading dimension must be P={P}")
+    if Hr != max(1, H // P):
+        raise ValueError(f"dimension 1 must be max(1, H/P) = {max(1, H // P)}")
+    if out is None:
+        out = torch.empty((P, N // P if P else 0, H, D), dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", torch.bfloat16, 4)
+    if tuple(out.shape) != (P, N // P, H, D):
+        raise ValueError("out must be [P, N/P, H, D]")
+    dt = ATTN_FP32 if y.dtype == torch.float32 else ATTN_BF16
+    _check(lib().head_to_seq_reduce(y.data_ptr(), dt, out.data_ptr(), P, N, H, D, _stream(y)))
+    return out
 
 
 def trace_enable(on: bool = True) -> None:

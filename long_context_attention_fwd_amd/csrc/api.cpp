@@ -493,24 +493,30 @@ static int relayout(const char* name, bool to_head, const void* in, void* out, i
   if (!in || !out) return fail(ATTN_ERR_NULL, "%s: null pointer", name);
   if (P < 1 || N < 1 || H < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
   if (N % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide N=%lld", name, P, (long long)N);
-  if (H < P) return fail(ATTN_ERR_UNSUPPORTED, "%s: H=%d < P=%d needs head replication", name, H, P);
-  if (H % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide H=%d", name, P, H);
+  if (H < P && !to_head)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: H=%d < P=%d: replicated heads are summed by head_to_seq_reduce", name, H,
+                P);
+  if (H < P && P % H) return fail(ATTN_ERR_SHAPE, "%s: H=%d does not divide P=%d", name, H, P);
+  if (H >= P && H % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide H=%d", name, P, H);
+  const int rep = H < P ? P / H : 1;  // ranks that share one head
   if (elem_bytes != 2 && elem_bytes != 4) return fail(ATTN_ERR_UNSUPPORTED, "%s: elem_bytes must be 2 or 4", name);
   const int64_t row_bytes = (int64_t)D * elem_bytes;
   if (row_bytes % 16 || ((row_bytes / 16) & (row_bytes / 16 - 1)))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: D*elem_bytes=%lld must be 16 times a power of two", name,
                 (long long)row_bytes);
-  int64_t units;
-  if (!elems(&units, {N, H, row_bytes / 16}) || units >= (int64_t(1) << 32))
+  int64_t units, out_units;
+  if (!elems(&units, {N, H, row_bytes / 16}) || !elems(&out_units, {N, H, rep, row_bytes / 16}) ||
+      out_units >= (int64_t(1) << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: tensor has 2^32 or more 16-byte units", name);
   if (!aligned16(in) || !aligned16(out)) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
-  const size_t bytes = (size_t)units * 16;
-  if (overlap(in, bytes, out, bytes)) return fail(ATTN_ERR_ALIAS, "%s: in and out overlap", name);
+  if (overlap(in, (size_t)units * 16, out, (size_t)out_units * 16))
+    return fail(ATTN_ERR_ALIAS, "%s: in and out overlap", name);
   // seq->head: out[h][n] = in[n][h] (A = H, Bn = N); head->seq: out[n][h] = in[h][n].
   const unsigned A = to_head ? (unsigned)H : (unsigned)N;
   const unsigned Bn = to_head ? (unsigned)N : (unsigned)H;
   return hip_status(
-      lcattn::launch_transpose_rows(in, out, A, Bn, (unsigned)row_bytes, static_cast<hipStream_t>(hip_stream)),
+      lcattn::launch_transpose_rows(in, out, A, Bn, (unsigned)row_bytes, (unsigned)rep,
+                                    static_cast<hipStream_t>(hip_stream)),
       name);
 }
 
@@ -522,6 +528,28 @@ int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int
 int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
                          void* hip_stream) {
   return relayout("head_to_seq_relayout", false, in, out, P, N, H, D, elem_bytes, hip_stream);
+}
+
+int head_to_seq_reduce(const void* in, int in_dtype, void* out, int P, int64_t N, int H, int D, void* hip_stream) {
+  const char* name = "head_to_seq_reduce";
+  if (!in || !out) return fail(ATTN_ERR_NULL, "%s: null pointer", name);
+  if (P < 1 || N < 1 || H < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
+  if (N % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide N=%lld", name, P, (long long)N);
+  if (H < P ? P % H : H % P) return fail(ATTN_ERR_SHAPE, "%s: H=%d and P=%d: one must divide the other", name, H, P);
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: in_dtype=%d (ATTN_BF16 or ATTN_FP32)", name, in_dtype);
+  if (D % 8) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d must be a multiple of 8", name, D);
+  const int rep = H < P ? P / H : 1;
+  int64_t out_el, in_el;
+  if (!elems(&out_el, {N, H, D}) || !elems(&in_el, {N, H, rep, D}) || in_el > INT64_MAX / 8 ||
+      (out_el / 8 + 255) / 256 > INT32_MAX)
+    return fail(ATTN_ERR_SHAPE, "%s: tensor sizes overflow", name);
+  if (!aligned16(in) || !aligned16(out)) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
+  if (overlap(in, (size_t)in_el * (in_dtype == ATTN_FP32 ? 4 : 2), out, (size_t)out_el * 2))
+    return fail(ATTN_ERR_ALIAS, "%s: in and out overlap", name);
+  return hip_status(lcattn::launch_sum_replicas(in, in_dtype == ATTN_FP32, static_cast<uint16_t*>(out), H, N, D, rep,
+                                                static_cast<hipStream_t>(hip_stream)),
+                    name);
 }
 
 }  // extern "C"

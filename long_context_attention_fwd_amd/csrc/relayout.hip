@@ -27,15 +27,17 @@ namespace lcattn {
 constexpr int kRelayoutThreads = 256;
 constexpr int kRelayoutUnroll = 4;
 
-// out[a, b, :] = in[b, a, :] for rows of 2^units_log2 16-byte units, a in
-// [0, A), b in [0, Bn).  Tile (a-tile, b-tile) = blockIdx.x split as
-// (blockIdx.x / nbt, blockIdx.x % nbt); TA = 2^ta_log2, TB = 2^tb_log2 rows.
-// A * Bn * units < 2^32 is checked on the host.
+// out[a * rep + i, b, :] = in[b, a, :] (i < rep) for rows of 2^units_log2
+// 16-byte units, a in [0, A), b in [0, Bn): rep > 1 replicates every a-row
+// block (a key/value head shared by rep ranks).  Tile (a-tile, b-tile) =
+// blockIdx.x split as (blockIdx.x / nbt, blockIdx.x % nbt); TA = 2^ta_log2,
+// TB = 2^tb_log2 rows.  A * rep * Bn * units < 2^32 is checked on the host.
 __global__ __launch_bounds__(kRelayoutThreads) void transpose_rows_kernel(const u32x4* __restrict__ in,
                                                                             u32x4* __restrict__ out,
                                                                             unsigned A, unsigned Bn,
                                                                             unsigned units_log2, unsigned ta_log2,
-                                                                            unsigned tb_log2, unsigned nbt) {
+                                                                            unsigned tb_log2, unsigned nbt,
+                                                                            unsigned rep) {
   const unsigned bt = blockIdx.x % nbt, at = blockIdx.x / nbt;
   const unsigned a0 = at << ta_log2, b0 = bt << tb_log2;
   const unsigned umask = (1u << units_log2) - 1u, tbmask = (1u << tb_log2) - 1u;
@@ -50,17 +52,60 @@ __global__ __launch_bounds__(kRelayoutThreads) void transpose_rows_kernel(const 
       const unsigned r = k >> units_log2;  // row in the tile, b fastest
       const unsigned a = a0 + (r >> tb_log2), b = b0 + (r & tbmask);
       ok[i] = k < per && a < A && b < Bn;
-      dst[i] = ((a * Bn + b) << units_log2) | (k & umask);
+      dst[i] = ((a * rep * Bn + b) << units_log2) | (k & umask);
       if (ok[i]) vals[i] = __builtin_nontemporal_load(in + (((b * A + a) << units_log2) | (k & umask)));
     }
+    for (unsigned c = 0; c < rep; ++c) {
+      const unsigned step = (c * Bn) << units_log2;  // c-th copy of the a-row block
 #pragma unroll
-    for (int i = 0; i < kRelayoutUnroll; ++i)
-      if (ok[i]) __builtin_nontemporal_store(vals[i], out + dst[i]);
+      for (int i = 0; i < kRelayoutUnroll; ++i)
+        if (ok[i]) __builtin_nontemporal_store(vals[i], out + dst[i] + step);
+    }
   }
 }
 
+// out[b, a, :] = sum over i < rep of in[a * rep + i, b, :] for rows of D
+// elements (bf16 or fp32 in, summed in fp32 in order i = 0, 1, ..., bf16 out
+// rounded to nearest even): the inverse exchange of gradients of a
+// key/value head that rep ranks shared (rep = 1: the transpose with a
+// conversion).  One thread per 8 output elements.
+template <bool IN_F32>
+__global__ __launch_bounds__(256) void sum_replicas_kernel(const void* __restrict__ in, uint16_t* __restrict__ out,
+                                                           long long A, long long Bn, int D, int rep) {
+  const long long units = (long long)D / 8;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // over Bn * A * units
+  if (idx >= Bn * A * units) return;
+  const long long u = idx % units, ab = idx / units;
+  const long long a = ab % A, b = ab / A;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < rep; ++i) {
+    const long long src = ((a * rep + i) * Bn + b) * D + 8 * u;
+    if (IN_F32) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(in) + src);
+      const f32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += x[e];
+        acc[4 + e] += y[e];
+      }
+    } else {
+      const u32x4 x = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(in) + src));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(x[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(x[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  const u32x2 lo = pack_bf16x4_bits(acc[0], acc[1], acc[2], acc[3]);
+  const u32x2 hi = pack_bf16x4_bits(acc[4], acc[5], acc[6], acc[7]);
+  const u32x4 o = {lo[0], lo[1], hi[0], hi[1]};
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + idx * 8));
+}
+
 hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned Bn, unsigned row_bytes,
-                                 hipStream_t stream) {
+                                 unsigned rep, hipStream_t stream) {
   unsigned units = row_bytes / 16, lg = 0;
   while ((1u << lg) < units) ++lg;
   // 4 x 4 rows, with more b rows when rows are short, so a tile is at least
@@ -71,7 +116,20 @@ hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned
   const unsigned nbt = (Bn + (1u << tb_lg) - 1) >> tb_lg;
   const unsigned nat = (A + (1u << ta_lg) - 1) >> ta_lg;
   LCATTN_LAUNCH("transpose_rows_kernel", transpose_rows_kernel, dim3(nbt * nat), dim3(kRelayoutThreads), 0, stream,
-                static_cast<const u32x4*>(in), static_cast<u32x4*>(out), A, Bn, lg, ta_lg, tb_lg, nbt);
+                static_cast<const u32x4*>(in), static_cast<u32x4*>(out), A, Bn, lg, ta_lg, tb_lg, nbt, rep);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long long A, long long Bn, int D, int rep,
+                               hipStream_t stream) {
+  const long long threads = A * Bn * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (in_f32)
+    LCATTN_LAUNCH("sum_replicas_kernel", (sum_replicas_kernel<true>), grid, dim3(256), 0, stream, in, out, A, Bn, D,
+                  rep);
+  else
+    LCATTN_LAUNCH("sum_replicas_kernel", (sum_replicas_kernel<false>), grid, dim3(256), 0, stream, in, out, A, Bn, D,
+                  rep);
   return hipGetLastError();
 }
 

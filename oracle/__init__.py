@@ -23,4 +23,5 @@ from .attention import (  # noqa: F401
     attention_backward_block,
     seq_to_head,
     head_to_seq,
+    head_to_seq_sum,
 )

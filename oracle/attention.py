@@ -56,6 +56,7 @@ __all__ = [
     "attention_backward_block",
     "seq_to_head",
     "head_to_seq",
+    "head_to_seq_sum",
 ]
 
 _ROW_BATCH_ELEMS = 1 << 25  # score elements per batch of rows (256 MiB in fp64)
@@ -422,15 +423,26 @@ def attention_backward_row_support(q, k, v, do, scale, support, kv_rows=None, ca
 def seq_to_head(x, P: int) -> np.ndarray:
     """in [P, N/P, H, D] (shard p holds tokens p*N/P ...) -> out [P, H/P, N, D]
     (rank r holds heads r*H/P ...):  out[r, h', n, :] =
-    in[n // (N/P), n mod (N/P), r*(H/P) + h', :].  Bit copy (any dtype)."""
+    in[n // (N/P), n mod (N/P), r*(H/P) + h', :].  Bit copy (any dtype).
+
+    Fewer heads than ranks (H < P, H | P; key/value heads of grouped-query
+    attention): rank r's query heads read head r // (P/H), so that head is
+    what it receives: out [P, 1, N, D], out[r, 0, n, :] =
+    in[n // (N/P), n mod (N/P), r // (P/H), :]."""
     x = np.asarray(x)
     Pp, T, H, D = x.shape
-    if Pp != P or H % P:
-        raise ValueError("shape must be [P, N/P, H, D] with P | H")
-    Hp = H // P
+    if Pp != P or (H % P if H >= P else P % H):
+        raise ValueError("shape must be [P, N/P, H, D] with P | H or H | P")
     N = P * T
     n = np.arange(N)
     src_p, src_t = n // T, n % T
+    if H < P:
+        R = P // H
+        out = np.empty((P, 1, N, D), dtype=x.dtype)
+        for r in range(P):
+            out[r, 0] = x[src_p, src_t, r // R]
+        return out
+    Hp = H // P
     out = np.empty((P, Hp, N, D), dtype=x.dtype)
     for r in range(P):
         for hh in range(Hp):
@@ -452,4 +464,27 @@ def head_to_seq(y, P: int) -> np.ndarray:
     for p in range(P):
         for h in range(H):
             out[p, :, h] = y[h // Hp, h % Hp, p * T + t]
+    return out
+
+
+def head_to_seq_sum(y, P: int, H: int) -> np.ndarray:
+    """Inverse exchange of gradients (float64 values): in [P, max(1, H/P), N, D]
+    -> out [P, N/P, H, D].  For H >= P it is ``head_to_seq`` on the values.
+    For H < P each head was replicated to R = P/H ranks (``seq_to_head``), so
+    its gradient is the sum of theirs: out[p, t, h, :] = sum over i < R of
+    in[h*R + i, 0, p*(N/P) + t, :]."""
+    y = _as_f64(y)
+    Pp, Hr, N, D = y.shape
+    if Pp != P or N % P or (H % P if H >= P else P % H) or Hr != max(1, H // P):
+        raise ValueError("shape must be [P, max(1, H/P), N, D] with P | N and P | H or H | P")
+    if H >= P:
+        return head_to_seq(y, P)
+    R = P // H
+    T = N // P
+    out = np.zeros((P, T, H, D))
+    t = np.arange(T)
+    for p in range(P):
+        for h in range(H):
+            for i in range(R):
+                out[p, :, h] += y[h * R + i, 0, p * T + t]
     return out

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
-              "attn_partial_merge",
+              "attn_partial_merge", "head_to_seq_reduce",
               "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -221,7 +221,6 @@ def test_bwd_block_rejects(L, kw, status):
 @pytest.mark.parametrize("args,status", [
     ((None, B_, 8, 4096, 32, 128, 2), 1),
     ((A, B_, 8, 4095, 32, 128, 2), 2),
-    ((A, B_, 8, 4096, 4, 128, 2), 3),      # H < P needs head replication
     ((A, B_, 8, 4096, 12, 128, 2), 2),
     ((A, B_, 8, 4096, 32, 128, 3), 3),
     ((A, B_, 8, 4096, 32, 12, 2), 3),
@@ -230,6 +229,28 @@ def test_bwd_block_rejects(L, kw, status):
 ])
 def test_relayout_rejects(L, fn, args, status):
     assert getattr(L, fn)(*args, None) == status
+
+
+def test_relayout_shared_heads(L):
+    # H < P: replication is valid for seq->head only when H divides P; the
+    # plain inverse refuses replicated heads (their gradients must be summed)
+    assert L.seq_to_head_relayout(A, B_, 8, 4096, 3, 128, 2, None) == 2
+    assert L.seq_to_head_relayout(A + 4 * 4096 * 256 - 16, A, 8, 4096, 4, 128, 2, None) == 5  # replicated out reaches in
+    assert L.head_to_seq_relayout(A, B_, 8, 4096, 4, 128, 2, None) == 3
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 0, B_, 8, 4096, 4, 128), 1),
+    ((A, 0, B_, 8, 4095, 4, 128), 2),
+    ((A, 0, B_, 8, 4096, 3, 128), 2),
+    ((A, 0, B_, 8, 4096, 12, 128), 2),
+    ((A, 2, B_, 8, 4096, 4, 128), 3),
+    ((A, 0, B_, 8, 4096, 4, 12), 3),
+    ((A + 8, 0, B_, 8, 4096, 4, 128), 4),
+    ((A, 1, A + 1024, 8, 4096, 4, 128), 5),
+])
+def test_head_to_seq_reduce_rejects(L, args, status):
+    assert L.head_to_seq_reduce(*args, None) == status
 
 
 def test_binding_raises_on_missing_gpu_tensors():

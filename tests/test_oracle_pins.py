@@ -457,6 +457,58 @@ def test_relayout_is_transpose_and_round_trips(P, N, H, D):
     assert np.array_equal(oracle.head_to_seq(y, P), x)
 
 
+@pytest.mark.parametrize("P,N,H,D", [(8, 64, 4, 4), (8, 64, 1, 4), (4, 12, 2, 2), (8, 64, 2, 8)])
+def test_relayout_replicates_shared_heads(P, N, H, D):
+    """H < P: every head goes to the P/H ranks after one another (np.repeat
+    of the transpose), i.e. rank r gets the key/value head its query heads
+    h = r*(Hq/P) .. read under the grouped-query map h // (Hq/H)."""
+    x = _rng(16).integers(0, 1 << 16, size=(P, N // P, H, D), dtype=np.uint16)
+    y = oracle.seq_to_head(x, P)
+    want = np.repeat(np.transpose(x.reshape(N, H, D), (1, 0, 2)), P // H, axis=0)[:, None]
+    assert np.array_equal(y, want)
+    Hq = 4 * P  # 4 query heads per rank
+    for r in range(P):
+        assert all((r * 4 + j) // (Hq // H) == r // (P // H) for j in range(4))
+
+
+def adjoint_gap(P, N, H, D, seed=17):
+    r = _rng(seed)
+    x = r.standard_normal((P, N // P, H, D))
+    y = r.standard_normal((P, max(1, H // P), N, D))
+    lhs = float((oracle.seq_to_head(x, P) * y).sum())
+    rhs = float((x * oracle.head_to_seq_sum(y, P, H)).sum())
+    return abs(lhs - rhs) / max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("P,N,H,D", [(8, 64, 4, 4), (8, 64, 1, 4), (4, 12, 8, 2), (2, 6, 6, 3)])
+def test_head_to_seq_sum_is_adjoint_of_seq_to_head(P, N, H, D):
+    """<seq_to_head(x), y> = <x, head_to_seq_sum(y)> for all x, y: the sum is
+    the transpose of the (replicating) exchange, which is what the gradient
+    of a shared head needs; for H >= P it is the inverse relayout."""
+    assert adjoint_gap(P, N, H, D) < 1e-9
+    if H >= P:
+        y = _rng(19).standard_normal((P, H // P, N, D))
+        assert np.array_equal(oracle.head_to_seq_sum(y, P, H), oracle.head_to_seq(y, P))
+
+
+def test_head_to_seq_sum_planted_mistake_is_caught(monkeypatch):
+    """Replicas summed from the wrong ranks (interleaved r % H instead of
+    r // (P/H)) must break the adjoint identity."""
+    def bad(y, P, H):
+        y = np.asarray(y, dtype=np.float64)
+        T = y.shape[2] // P
+        out = np.zeros((P, T, H, y.shape[3]))
+        for p in range(P):
+            for h in range(H):
+                for i in range(P // H):
+                    out[p, :, h] += y[i * H + h, 0, p * T:(p + 1) * T]
+        return out
+
+    assert adjoint_gap(8, 16, 2, 2) < 1e-9
+    monkeypatch.setattr(oracle, "head_to_seq_sum", bad)
+    assert adjoint_gap(8, 16, 2, 2) > 1e-6
+
+
 def test_sample_rows_contains_boundaries():
     r = sample_rows(32768, seed=3, count=256, block=8192)
     assert len(r) == 256 and len(np.unique(r)) == 256
