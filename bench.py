@@ -378,10 +378,48 @@ def main():
         out["ring_backward"] = {"call": f"attn_bwd_delta + {n_blk} x attn_bwd_block (fp32 dQ accumulated)",
                                 "ms": round(ms, 4), "TFLOP/s": round(tflops(2.5 * f_ring, ms), 2),
                                 "frac_peak": round(tflops(2.5 * f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
+        out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops)
 
     if not args.no_cpu_baseline and not args.profile_steps:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
+    """Shard 0's causal attention as a Pr-rank ring over 2*Pr chunks, every
+    rank's every step timed on this GPU: the ring waits for the slowest rank
+    at each step, so its critical path is the sum over steps of the maximum
+    over ranks.  Contiguous sharding against zigzag (rank r holds chunks r
+    and 2*Pr-1-r)."""
+    from long_context_attention_fwd_amd.ring import SCHEMES, rank_chunks, ring_forward
+    C = N // (2 * Pr)
+    q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))
+    cq = [q0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    ck = [k0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    cv = [v0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    o_acc = [torch.empty((1, hq, C, D), dtype=torch.float32, device=dev) for _ in range(2)]
+    lse = [torch.empty((1, hq, C), dtype=torch.float32, device=dev) for _ in range(2)]
+    o_fin = [torch.empty((1, hq, C, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    res = {"ranks": Pr, "chunk_tokens": C, "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair"}
+    for scheme in SCHEMES:
+        t = [[0.0] * Pr for _ in range(Pr)]
+        for r in range(Pr):
+            qs = [cq[c] for c in rank_chunks(r, Pr, scheme)]
+
+            def kv(src, scheme=scheme):
+                return tuple((ck[c], cv[c]) for c in rank_chunks(src, Pr, scheme))
+            for st in range(Pr):
+                t[r][st] = time_calls(torch, lambda: ring_forward(qs, kv, r, Pr, C, o_acc=o_acc, lse_acc=lse,
+                                                                  o_final=o_fin, scheme=scheme, scale=scale,
+                                                                  steps={st}))
+        crit = sum(max(t[r][s] for r in range(Pr)) for s in range(Pr))
+        # a real ring runs the ranks on Pr GPUs at once: aggregate over the
+        # ranks, and per rank (one GPU)
+        res[scheme] = {"critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
+                       "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
+                       "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
+                       "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
+    return res
 
 
 def time_calls(torch, fn, iters=10, warmup=3):

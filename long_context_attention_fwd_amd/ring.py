@@ -1,0 +1,79 @@
+"""Ring schedules over the library's calls (host-side ordering only; every
+piece of arithmetic runs in the library's kernels).
+
+Ring attention ("Context Parallelism", Ultralytics glossary, section "So
+funktioniert Kontextparallelität"): every rank keeps its queries and, over P
+steps, receives every rank's key/value block; the partial attention of its
+queries against each block is merged into a running result.  Here the
+sequence is cut into 2P chunks of C tokens and a rank holds two of them:
+
+* ``contiguous``: rank r holds chunks 2r and 2r+1.  Under the causal mask
+  rank P-1 attends to every earlier chunk and rank 0 to its own only, so the
+  ring's steps wait for the busiest rank.
+* ``zigzag``: rank r holds chunks r and 2P-1-r, one early and one late, so
+  every rank does the same causal work at every step (the load-balanced
+  sharding named as the ring's next step).
+
+A step's calls are the (query chunk, key chunk) pairs with at least one
+visible key; each is one ``attn_fwd_accumulate`` with the chunks' global
+positions, so the kernel's own mask handles the rest.
+"""
+
+from __future__ import annotations
+
+SCHEMES = ("contiguous", "zigzag")
+
+
+def rank_chunks(rank: int, P: int, scheme: str = "zigzag") -> tuple[int, int]:
+    """The two chunk indices (of 2P) that rank ``rank`` holds, in order."""
+    if not 0 <= rank < P:
+        raise ValueError(f"rank {rank} out of [0, {P})")
+    if scheme == "zigzag":
+        return (rank, 2 * P - 1 - rank)
+    if scheme == "contiguous":
+        return (2 * rank, 2 * rank + 1)
+    raise ValueError(f"scheme must be one of {SCHEMES}")
+
+
+def ring_schedule(rank: int, P: int, scheme: str = "zigzag", causal: bool = True):
+    """The calls of one rank's ring in order: tuples (step, src, qi, ki) --
+    at ``step`` the rank holds the key/value chunks of rank ``src`` =
+    (rank - step) mod P, and query chunk ``qi`` (0 or 1 of its own pair)
+    attends to key chunk ``ki`` of src's pair.  Pairs whose keys all lie
+    after the queries (causal) are left out."""
+    mine = rank_chunks(rank, P, scheme)
+    calls = []
+    for step in range(P):
+        src = (rank - step) % P
+        theirs = rank_chunks(src, P, scheme)
+        for qi, qc in enumerate(mine):
+            for ki, kc in enumerate(theirs):
+                if not causal or kc <= qc:
+                    calls.append((step, src, qi, ki))
+    return calls
+
+
+def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_acc, o_final=None,
+                 scheme: str = "zigzag", causal: bool = True, scale: float | None = None, steps=None):
+    """Run rank ``rank``'s ring on this GPU.
+
+    q_chunks: the rank's two query chunks, [B, Hq, C, D] bf16 each.
+    kv_chunks(src): ((k, v), (k, v)) of rank src's two chunks, [B, Hkv, C, D].
+    o_acc, lse_acc: per query chunk, the fp32 running (O, LSE); o_final (per
+    query chunk, optional) receives the bf16 O on that chunk's last call.
+    steps: restrict to these ring steps (for timing one step); None = all.
+    """
+    from . import attn_fwd_accumulate
+
+    calls = ring_schedule(rank, P, scheme, causal)
+    mine = rank_chunks(rank, P, scheme)
+    last = {qi: max(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
+    first_call = {qi: min(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
+    for i, (step, src, qi, ki) in enumerate(calls):
+        if steps is not None and step not in steps:
+            continue
+        k, v = kv_chunks(src)[ki]
+        kc = rank_chunks(src, P, scheme)[ki]
+        attn_fwd_accumulate(q_chunks[qi], k, v, o_acc[qi], lse_acc[qi], first=(i == first_call[qi]),
+                            causal=causal, scale=scale, q_pos0=mine[qi] * C, k_pos0=kc * C,
+                            o_final=(o_final[qi] if o_final is not None and i == last[qi] else None))

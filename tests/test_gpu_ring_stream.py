@@ -76,3 +76,34 @@ def test_ring_stream_32k_blocks(gpu):
     O, L = oracle.attention_forward(d["q"], d["k"], d["v"], w.scale, True, rows=rows)
     idx = torch.from_numpy(rows).cuda()
     check_forward(f64_of(o[:, :, idx]), f64_of(lse[:, :, idx]), O, L, "stream vs oracle")
+
+
+@pytest.mark.parametrize("scheme", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("P,C,G", [(4, 256, 4), (2, 300, 1), (8, 64, 2)])
+def test_ring_sharding_schemes(gpu, scheme, P, C, G):
+    """Every rank's ring (its two chunks of the 2P, each chunk pair one
+    attn_fwd_accumulate with global positions) against the oracle's full
+    causal attention at that rank's rows."""
+    import torch
+    from long_context_attention_fwd_amd.ring import rank_chunks, ring_forward
+    N, D, Hkv = 2 * P * C, 128, 1
+    d = make_qkv(1, Hkv * G, Hkv, N, D, seed=700 + P + C + G)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    s = sdpa_scale(D)
+
+    def chunk(t, c):
+        return t[:, :, c * C:(c + 1) * C].contiguous()
+
+    kv = {r: tuple((chunk(k, c), chunk(v, c)) for c in rank_chunks(r, P, scheme)) for r in range(P)}
+    for r in range(P):
+        mine = rank_chunks(r, P, scheme)
+        qs = [chunk(q, c) for c in mine]
+        o_acc = [poisoned((1, Hkv * G, C, D), torch.float32) for _ in mine]
+        lse = [poisoned((1, Hkv * G, C), torch.float32) for _ in mine]
+        o = [poisoned((1, Hkv * G, C, D), torch.bfloat16) for _ in mine]
+        ring_forward(qs, lambda src: kv[src], r, P, C, o_acc=o_acc, lse_acc=lse, o_final=o, scheme=scheme, scale=s)
+        torch.cuda.synchronize()
+        for i, c in enumerate(mine):
+            rows = np.arange(c * C, (c + 1) * C)
+            O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, True, rows=rows)
+            check_forward(f64_of(o[i]), f64_of(lse[i]), O, L, f"{scheme} P={P} rank {r} chunk {c}")
