@@ -123,14 +123,16 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
     if (tid < 2 * kBQ) {
       long long row = r0 + (tid & (kBQ - 1));
       row = row < Nq ? row : Nq - 1;
-      lv = tid < kBQ ? lbase[row] * kLog2e : dbase[row];
+      // no arithmetic on the loaded value here: using it would wait for
+      // every load in flight, the tile prefetch included
+      lv = (tid < kBQ ? lbase : dbase)[row];
     }
   };
   auto deposit = [&](int i) __attribute__((always_inline)) {
     unsigned char* b = buf(i);
     qst.store(b, tid);
     ost.store(b + T::BYTES, tid);
-    if (tid < 2 * kBQ) reinterpret_cast<float*>(b + 2 * T::BYTES)[tid] = lv;
+    if (tid < 2 * kBQ) reinterpret_cast<float*>(b + 2 * T::BYTES)[tid] = tid < kBQ ? lv * kLog2e : lv;
   };
   if (n_tiles > 0) fetch(0);
 
@@ -166,6 +168,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   const typename T::TrAddr ta = T::tr_addr(lane);
 
   if (n_tiles > 0) deposit(0);
+  // K and V of this lane in registers before the loop: otherwise the first
+  // product of every tile waits for that tile's prefetch as well
+  wait_vmem();
   __syncthreads();
 
   // One 32-row query block of the tile in cur (rows qb*32 ..): S, dP (MFMA),
