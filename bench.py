@@ -400,7 +400,11 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
     o_acc = [torch.empty((1, hq, C, D), dtype=torch.float32, device=dev) for _ in range(2)]
     lse = [torch.empty((1, hq, C), dtype=torch.float32, device=dev) for _ in range(2)]
     o_fin = [torch.empty((1, hq, C, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    res = {"ranks": Pr, "chunk_tokens": C, "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair"}
+    # one call after another: a chunk call fills a quarter of this GPU here,
+    # so running the two chunks' calls side by side would measure launch
+    # overlap rather than each rank's causal work
+    res = {"ranks": Pr, "chunk_tokens": C,
+           "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair, in sequence"}
     for scheme in SCHEMES:
         t = [[0.0] * Pr for _ in range(Pr)]
         for r in range(Pr):

@@ -54,7 +54,8 @@ def ring_schedule(rank: int, P: int, scheme: str = "zigzag", causal: bool = True
 
 
 def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_acc, o_final=None,
-                 scheme: str = "zigzag", causal: bool = True, scale: float | None = None, steps=None):
+                 scheme: str = "zigzag", causal: bool = True, scale: float | None = None, steps=None,
+                 streams=None):
     """Run rank ``rank``'s ring on this GPU.
 
     q_chunks: the rank's two query chunks, [B, Hq, C, D] bf16 each.
@@ -62,18 +63,36 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
     o_acc, lse_acc: per query chunk, the fp32 running (O, LSE); o_final (per
     query chunk, optional) receives the bf16 O on that chunk's last call.
     steps: restrict to these ring steps (for timing one step); None = all.
+    streams: two torch streams (default priority); the calls of query chunk
+    i go to streams[i], so the two chunks' calls of a step run side by side
+    (each chunk's calls stay in order: they update the same running result).
+    The caller's stream waits for both at the end.
     """
+    import torch
+
     from . import attn_fwd_accumulate
 
     calls = ring_schedule(rank, P, scheme, causal)
     mine = rank_chunks(rank, P, scheme)
     last = {qi: max(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
     first_call = {qi: min(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
+    caller = torch.cuda.current_stream(q_chunks[0].device)
+    if streams is not None:
+        fork = torch.cuda.Event()
+        fork.record(caller)
+        for st in streams:
+            st.wait_event(fork)
     for i, (step, src, qi, ki) in enumerate(calls):
         if steps is not None and step not in steps:
             continue
         k, v = kv_chunks(src)[ki]
         kc = rank_chunks(src, P, scheme)[ki]
-        attn_fwd_accumulate(q_chunks[qi], k, v, o_acc[qi], lse_acc[qi], first=(i == first_call[qi]),
-                            causal=causal, scale=scale, q_pos0=mine[qi] * C, k_pos0=kc * C,
-                            o_final=(o_final[qi] if o_final is not None and i == last[qi] else None))
+        with torch.cuda.stream(streams[qi] if streams is not None else caller):
+            attn_fwd_accumulate(q_chunks[qi], k, v, o_acc[qi], lse_acc[qi], first=(i == first_call[qi]),
+                                causal=causal, scale=scale, q_pos0=mine[qi] * C, k_pos0=kc * C,
+                                o_final=(o_final[qi] if o_final is not None and i == last[qi] else None))
+    if streams is not None:
+        for st in streams:
+            join = torch.cuda.Event()
+            join.record(st)
+            caller.wait_event(join)

@@ -95,13 +95,15 @@ def test_ring_sharding_schemes(gpu, scheme, P, C, G):
         return t[:, :, c * C:(c + 1) * C].contiguous()
 
     kv = {r: tuple((chunk(k, c), chunk(v, c)) for c in rank_chunks(r, P, scheme)) for r in range(P)}
+    streams = [torch.cuda.Stream() for _ in range(2)]  # odd ranks run their two chunks side by side
     for r in range(P):
         mine = rank_chunks(r, P, scheme)
         qs = [chunk(q, c) for c in mine]
         o_acc = [poisoned((1, Hkv * G, C, D), torch.float32) for _ in mine]
         lse = [poisoned((1, Hkv * G, C), torch.float32) for _ in mine]
         o = [poisoned((1, Hkv * G, C, D), torch.bfloat16) for _ in mine]
-        ring_forward(qs, lambda src: kv[src], r, P, C, o_acc=o_acc, lse_acc=lse, o_final=o, scheme=scheme, scale=s)
+        ring_forward(qs, lambda src: kv[src], r, P, C, o_acc=o_acc, lse_acc=lse, o_final=o, scheme=scheme, scale=s,
+                     streams=streams if r % 2 else None)
         torch.cuda.synchronize()
         for i, c in enumerate(mine):
             rows = np.arange(c * C, (c + 1) * C)
