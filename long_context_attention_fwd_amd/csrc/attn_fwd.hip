@@ -62,7 +62,6 @@ namespace {
 constexpr int kWaves = 8;      // two waves per SIMD: one's softmax overlaps the other's MFMAs
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;         // keys per tile
-constexpr float kSlack = 8.f;   // lazy rescale: P <= 2^kSlack before the final division
 
 template <int D, int QB, int HP, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
@@ -163,11 +162,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
 
   // Online softmax of one sub-tile: S^T (one query per lane, 16 of its 32
   // keys; the other 16 sit in lane ^ 32) -> P packed as the B operand of the
-  // next PV product, and this sub-tile's part of the row sum (psum).  The
-  // reference maximum m_run moves only when a scaled score exceeds it by
-  // more than kSlack (log2 units): P stays <= 2^kSlack, exact after the
-  // final division, and the rescale of O and the sum (m_old -> m_run) is
-  // rare after the first tiles.
+  // next PV product, and this sub-tile's part of the row sum (psum), against
+  // the exact running maximum m_run (so a row's largest weight is exactly 1
+  // and carries no bf16 rounding).  The caller rescales O and the sum when
+  // m_run moved (m_old -> m_run).
   auto softmax = [&](auto masked_tag, f32x16 s, int t, float& m_old, float& psum) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if (MASKED) {
@@ -187,9 +185,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max with lane ^ 32
     }
-    const float m_cand = fmaxf(m_run, mx * a.scale_log2);
     m_old = m_run;
-    m_run = m_cand > m_run + kSlack ? m_cand : m_run;
+    m_run = fmaxf(m_run, mx * a.scale_log2);
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

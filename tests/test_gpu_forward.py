@@ -94,6 +94,10 @@ def test_fwd_peaky_softmax(gpu):
     o, lse = run_fwd(d)
     O, L = oracle.attention_forward(d["q"], d["k"], d["v"], sdpa_scale(128))
     check_forward(f64_of(o), f64_of(lse), O, L, "peaky", out_rounding=True)
+    # at this scale the reference's own bf16 rounding is 7.8e-3, so the plain
+    # 1e-2 gate still holds; it fails if a row's largest weight is rounded
+    # (a reference maximum that lags the true one)
+    assert np.abs(f64_of(o) - O).max() <= 1e-2
 
 
 def test_fwd_deterministic(gpu):
