@@ -94,6 +94,21 @@ def test_ring_backward_equals_full(gpu, N, D, G, causal):
     assert torch.equal(dq.view(torch.int16), dq_acc.to(torch.bfloat16).view(torch.int16))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_backward_batch(gpu, causal):
+    """B = 3 with grouped heads: the batch index of every kernel of the block
+    path (Dv, dK/dV with the per-head partials and their sum, dQ)."""
+    B, Hkv, G, N, D = 3, 2, 2, 500, 128
+    d = make_qkv(B, Hkv * G, Hkv, N, D, seed=650 + int(causal), with_do=True)
+    s = sdpa_scale(D)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lc.attn_fwd(q, k, v, causal=causal, scale=s)
+    delta = lc.attn_bwd_delta(o, do)
+    dq_acc, dq, dk, dv = ring_backward(q, k, v, do, lse, delta, [0, 128, 300, 500], s, causal)
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, causal)
+    check((dq, dk, dv), (dQ, dK, dV), f"batch ring causal={causal}")
+
+
 @pytest.mark.parametrize("G", [1, 4])
 def test_single_block_is_attn_bwd_bit_for_bit(gpu, G):
     """One block over the whole sequence with bf16 outputs runs attn_bwd's
