@@ -379,6 +379,7 @@ def main():
                                 "ms": round(ms, 4), "TFLOP/s": round(tflops(2.5 * f_ring, ms), 2),
                                 "frac_peak": round(tflops(2.5 * f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
         out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops)
+        out["long_shapes"] = long_shapes(lc, torch, dev)
 
     if not args.no_cpu_baseline and not args.profile_steps:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -464,6 +465,44 @@ def short_forward(lc, torch, dev, iters=20):
         ms = time_calls(torch, fn, iters, 5)
         res[name] = {"us": round(1e3 * ms, 2), "TFLOP/s": round(flops / ms / 1e9, 2),
                      "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
+def long_shapes(lc, torch, dev):
+    """The other two large workloads, timed apart from the step on inputs
+    drawn on the GPU (seeded normal, bf16): the 64K training shape
+    (8 heads, forward and backward) and the 512K-token forward of one
+    Ulysses share (4 query heads on 1 key/value head, inputs 0.5 N(0,1))."""
+    from long_context_attention_fwd_amd.inputs import WORKLOADS
+    res = {}
+    gen = torch.Generator(device=dev)
+
+    def draw(shape, seed, amp=1.0):
+        gen.manual_seed(seed)
+        return (amp * torch.randn(shape, generator=gen, device=dev)).to(torch.bfloat16)
+
+    w = WORKLOADS["train_64k"]
+    q, k, v, do = (draw((w.B, h, w.N, w.D), w.seed * 10 + i) for i, h in enumerate((w.Hq, w.Hkv, w.Hkv, w.Hq)))
+    o, lse = lc.attn_fwd(q, k, v, scale=w.scale)
+    ws = torch.empty(lc.attn_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.D), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    f = fwd_flops(w.B, w.Hq, w.N, w.D)
+    t_f = time_calls(torch, lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse), 3, 1)
+    t_b = time_calls(torch, lambda: lc.attn_bwd(q, k, v, o, do, lse, scale=w.scale, workspace=ws, dq=dq, dk=dk,
+                                                dv=dv), 3, 1)
+    res[w.name] = {"shape": [w.B, w.Hq, w.N, w.D], "fwd_ms": round(t_f, 3), "fwd_TFLOP/s": round(f / t_f / 1e9, 1),
+                   "bwd_ms": round(t_b, 3), "bwd_TFLOP/s": round(2.5 * f / t_b / 1e9, 1),
+                   "bwd_frac_peak": round(2.5 * f / t_b / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, do, o, lse, ws, dq, dk, dv
+    w = WORKLOADS["ulysses_512k"]
+    q = draw((w.B, w.Hq, w.N, w.D), w.seed * 10, w.amp)
+    k = draw((w.B, w.Hkv, w.N, w.D), w.seed * 10 + 1, w.amp)
+    v = draw((w.B, w.Hkv, w.N, w.D), w.seed * 10 + 2, w.amp)
+    o, lse = lc.attn_fwd(q, k, v, scale=w.scale)
+    f = fwd_flops(w.B, w.Hq, w.N, w.D)
+    t_f = time_calls(torch, lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse), 2, 1)
+    res[w.name] = {"shape": [w.B, w.Hq, w.N, w.D], "kv_heads": w.Hkv, "fwd_ms": round(t_f, 2),
+                   "fwd_TFLOP/s": round(f / t_f / 1e9, 1), "fwd_frac_peak": round(f / t_f / 1e9 / PEAK_BF16_TFLOPS, 4)}
     return res
 
 
