@@ -79,8 +79,8 @@ def test_ring_stream_32k_blocks(gpu):
 
 
 @pytest.mark.parametrize("scheme", ["zigzag", "contiguous"])
-@pytest.mark.parametrize("P,C,G", [(4, 256, 4), (2, 300, 1), (8, 64, 2)])
-def test_ring_sharding_schemes(gpu, scheme, P, C, G):
+@pytest.mark.parametrize("P,C,G,causal", [(4, 256, 4, True), (2, 300, 1, True), (8, 64, 2, True), (4, 100, 2, False)])
+def test_ring_sharding_schemes(gpu, scheme, P, C, G, causal):
     """Every rank's ring (its two chunks of the 2P, each chunk pair one
     attn_fwd_accumulate with global positions) against the oracle's full
     causal attention at that rank's rows."""
@@ -103,9 +103,9 @@ def test_ring_sharding_schemes(gpu, scheme, P, C, G):
         lse = [poisoned((1, Hkv * G, C), torch.float32) for _ in mine]
         o = [poisoned((1, Hkv * G, C, D), torch.bfloat16) for _ in mine]
         ring_forward(qs, lambda src: kv[src], r, P, C, o_acc=o_acc, lse_acc=lse, o_final=o, scheme=scheme, scale=s,
-                     streams=streams if r % 2 else None)
+                     causal=causal, streams=streams if r % 2 else None)
         torch.cuda.synchronize()
         for i, c in enumerate(mine):
             rows = np.arange(c * C, (c + 1) * C)
-            O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, True, rows=rows)
+            O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, causal, rows=rows)
             check_forward(f64_of(o[i]), f64_of(lse[i]), O, L, f"{scheme} P={P} rank {r} chunk {c}")
