@@ -99,34 +99,9 @@ struct LdsTile {
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int UNITS = D / 8;          // 16-byte units per row
   static constexpr int BYTES = 64 * ROW_BYTES;  // one 64-row tile
-  static constexpr int LOADS = BYTES / (64 * 16);  // wave-wide 1 KiB direct loads per tile
 
   // Byte offset of 16-byte unit u of row r.
   __device__ static int off(int r, int u) { return r * ROW_BYTES + ((u ^ tile_swz(r)) << 4); }
-
-  // Issue the direct global->LDS loads of rows [r0, r0 + 64) of a row-major
-  // [rows_total, D] bf16 matrix.  Wave w of NW waves issues loads w, w+NW, ...;
-  // load n fills LDS bytes [n KiB, n KiB + 1 KiB), lane i its 16 bytes at
-  // 16 i.  Rows past rows_total read row rows_total - 1 instead (finite data
-  // that the callers mask).
-  template <int NW>
-  __device__ static void load_async(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total,
-                                    int wave, int lane) {
-    static_assert(LOADS % NW == 0, "tile loads split evenly over the waves");
-#pragma unroll
-    for (int i = 0; i < LOADS / NW; ++i) {
-      const int n = wave + i * NW;
-      const int slot = n * 64 + lane;
-      const int r = slot / UNITS, up = slot % UNITS;
-      const int u = up ^ tile_swz(r);
-      long long gr = r0 + r;
-      gr = gr < rows_total ? gr : rows_total - 1;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + gr * D + 8 * u),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(lds) + n * 1024),
-                                       16, 0, 0);
-    }
-  }
 
   // Per-lane base offsets for the row fragments of rows r + 32k (k any) and
   // steps t: unit (2t + grp) ^ f(r) = 8 (t >> 2) + ((2 (t & 3)) ^ (grp ^ f(r)))
@@ -204,29 +179,6 @@ struct LdsTile {
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o +
                                                                    4 * ROW_BYTES));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  }
-
-  // (a) A operand reducing over D: row r (already in pi order), step t.
-  __device__ static bf16x8 row_frag(const unsigned char* lds, int r, int t, int grp) {
-    return as_bf16x8(ld_lds16(lds, off(r, 2 * t + grp)));
-  }
-
-  // (b) A operand reducing over tile rows: lane (c, grp) receives
-  // T[r0 + 8 grp + e][d0 + c] for e = 0..7 (r0 a multiple of 8, d0 of 32).
-  __device__ static bf16x8 tr_frag(const unsigned char* lds, int r0, int d0, int lane) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int gi = lane >> 4, s = lane & 15;
-    const int row = r0 + 8 * (gi >> 1) + (s >> 2);
-    const int col = d0 + 16 * (gi & 1) + 4 * (s & 3);
-    const int o = off(row, col >> 3) + ((col & 7) << 1);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o +
-                                                                   4 * ROW_BYTES));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   }
