@@ -92,10 +92,15 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
   const long long Nq = a.Nq, Nk = a.Nk;
-  const long long bz = blockIdx.z;
-  const int h = blockIdx.y;               // query head
+  // XCD-aware order (neighbouring key tiles of one head share an XCD and its
+  // L2 while they stream the same query tiles: 14x less HBM traffic on the
+  // 32K shard)
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const long long bz = lin / (nx * ny);
+  const int h = (int)(lin / nx % ny);     // query head
   const int kvh = h / a.G;
-  const long long kt0 = (long long)blockIdx.x * BK;
+  const long long kt0 = (lin % nx) * BK;
   const long long kw0 = kt0 + 32 * wave;  // this wave's first key
   const int key = (int)(kw0 + c);         // this lane's key
   const float sl = a.scale * kLog2e;
@@ -383,10 +388,15 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, grp = lane >> 5;
   const long long Nq = a.Nq, Nk = a.Nk;
-  const long long bz = blockIdx.z;
-  const int qt = n_qtiles - 1 - (int)blockIdx.x;  // longest causal rows first
-  const int h = blockIdx.y * HP + (wave % HP);
-  const int kvh = (blockIdx.y * HP) / a.G;
+  // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
+  // they stream the same key/value tiles; longest causal rows first
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const int by = (int)(lin / nx % ny);
+  const long long bz = lin / (nx * ny);
+  const int qt = n_qtiles - 1 - (int)(lin % nx);
+  const int h = by * HP + (wave % HP);
+  const int kvh = (by * HP) / a.G;
   const long long q_start = (long long)qt * SPAN;
   const long long wq0 = q_start + (long long)(wave / HP) * 32;
   const long long qrow = wq0 + c;

@@ -84,11 +84,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   const int c = lane & 31, grp = lane >> 5;
   // longest causal rows first; key range (split) outermost, which dispatches
   // the first ranges of every query tile before the later, shorter ones
-  const int qt = n_qtiles - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y * HP + (wave % HP);
-  const int kvh = (blockIdx.y * HP) / a.G;
-  const long long bz = blockIdx.z % a.B;
-  const int split = (int)(blockIdx.z / a.B);
+  // XCD-aware order: neighbouring query tiles of one head group share an XCD
+  // and its L2 while they stream the same key/value tiles
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const int by = (int)(lin / nx % ny);
+  const long long bzs = lin / (nx * ny);
+  const int qt = n_qtiles - 1 - (int)(lin % nx);
+  const int h = by * HP + (wave % HP);
+  const int kvh = (by * HP) / a.G;
+  const long long bz = bzs % a.B;
+  const int split = (int)(bzs / a.B);
   const long long q_start = (long long)qt * SPAN;
   const long long wq0 = q_start + (long long)(wave / HP) * QW;
 

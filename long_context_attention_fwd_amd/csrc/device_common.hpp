@@ -336,4 +336,19 @@ __device__ __forceinline__ void lds_wait_frags(u32x4& a, u32x4& b, u32x4& c, u32
 // [6:4], lgkmcnt in [11:8]; 0x0F70 = vmcnt(0) with the other counters free.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// XCD-aware workgroup order.  The 8 XCDs of the chip take workgroups
+// round-robin by linear id, and each has its own L2.  Within every round of
+// 8 x 32 ids, XCD x is given 32 consecutive logical workgroups (neighbours
+// that stream the same tiles through its L2 at about the same time); an XCD
+// takes chunk x of even rounds and chunk 7 - x of odd ones, so that the long
+// and short workgroups of a longest-first order alternate on every XCD.
+// A bijection on [0, total); a last partial round keeps the identity.
+__device__ __forceinline__ long long xcd_order(long long lin, long long total) {
+  if (lin >= total / 256 * 256) return lin;
+  const long long round = lin / 256, x = lin % 8;
+  const long long chunk = (round & 1) ? 7 - x : x;
+  return round * 256 + chunk * 32 + (lin % 256) / 8;
+}
+
+
 }  // namespace lcattn
