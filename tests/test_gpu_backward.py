@@ -126,3 +126,37 @@ def test_bwd_train_64k_sampled(gpu):
     e_dk = grad_rel_err(f64_of(dk2), rk)
     e_dv = grad_rel_err(f64_of(dv2), rv)
     assert max(e_dq, e_dq2, e_dk, e_dv) <= GRAD_REL_TOL, (e_dq, e_dq2, e_dk, e_dv)
+
+
+def test_bwd_ulysses_shard_32k_sampled(gpu):
+    """The bench step's backward at its full size: shard 0 of the 32K-token
+    layer after the seq->head relayout (4 query heads on 1 key/value head, so
+    the per-head dK/dV partials and their sum), dO drawn like the bench's.
+    dQ at the sampled rows with the full dO; dK, dV at every key for a dO
+    zeroed outside the sampled rows."""
+    import torch
+    from long_context_attention_fwd_amd.inputs import normal_bf16
+    w = WORKLOADS["ulysses_shard_32k"]
+    d = make_workload_inputs(w)
+    d["do"] = normal_bf16(np.random.default_rng(w.seed + 17), (w.P, w.N // w.P, w.Hq, w.D))
+    heads = {n: lc.seq_to_head_relayout(to_dev(d[n]), w.P)[0:1].contiguous() for n in ("q", "k", "v", "do")}
+    ref = {n: oracle.seq_to_head(d[n], w.P)[0:1] for n in ("q", "k", "v", "do")}
+    rows = sample_rows(w.N, w.seed, 64)
+    idx = torch.from_numpy(rows).cuda()
+    o, lse = lc.attn_fwd(heads["q"], heads["k"], heads["v"], causal=True, scale=w.scale)
+    dq, _, _ = lc.attn_bwd(heads["q"], heads["k"], heads["v"], o, heads["do"], lse, causal=True, scale=w.scale)
+    do_r = torch.zeros_like(heads["do"])
+    do_r[:, :, idx] = heads["do"][:, :, idx]
+    _, dk, dv = lc.attn_bwd(heads["q"], heads["k"], heads["v"], o, do_r, lse, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    do_np = oracle.bf16_bits_to_f64(ref["do"])
+    mask = np.zeros(w.N, dtype=bool)
+    mask[rows] = True
+    do_np[:, :, ~mask] = 0.0
+    rq, rk, rv = oracle.attention_backward_row_support(ref["q"], ref["k"], ref["v"], do_np, w.scale, rows)
+    # dQ of a row depends only on that row's dO (and its LSE and Dv): the
+    # restricted dO gives the sampled rows of the full dQ
+    e_dq = grad_rel_err(f64_of(dq[:, :, idx]), rq)
+    e_dk = grad_rel_err(f64_of(dk), rk)
+    e_dv = grad_rel_err(f64_of(dv), rv)
+    assert max(e_dq, e_dk, e_dv) <= GRAD_REL_TOL, (e_dq, e_dk, e_dv)
