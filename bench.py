@@ -5,13 +5,14 @@ One step is one pass over the whole hot path on one GPU's Ulysses share of a
 Llama-3-8B-shaped layer (32 query / 8 key-value heads, D = 128, N = 32768
 tokens split P = 8 ways), with inputs already resident in HBM:
 
-  1. seq_to_head_relayout of Q, K, V, dO (all P shards)   -- the all-to-all's data movement
+  1. seq_to_head_relayout_batch of Q, K, V, dO (all P shards, one launch)
+     -- the all-to-all's data movement
   2. attn_fwd on shard 0 (4 query heads, 1 KV head, causal GQA, N = 32768)
   3. the ring form of the same forward: 4 partial attn_fwd calls over
      8192-key blocks (fp32 partials, run side by side on their own streams)
      + attn_partial_merge
   4. attn_bwd on shard 0 (from step 2's O and LSE)
-  5. head_to_seq_relayout of O, dQ, dK, dV
+  5. head_to_seq_relayout_batch of O, dQ, dK, dV (one launch)
 
 ``value`` is the attention work of the step (forward + ring forward +
 backward, algorithmic flops: masked pairs not counted) divided by the step
@@ -171,8 +172,9 @@ def main():
                 marks.append(e)
 
         mark()
-        for n in ("q", "k", "v", "do"):
-            lc.seq_to_head_relayout(xs[n], P, out=heads[n])
+        # one launch for the four tensors of the exchange
+        lc.seq_to_head_relayout_batch([xs[n] for n in ("q", "k", "v", "do")], P,
+                                      outs=[heads[n] for n in ("q", "k", "v", "do")])
         mark()
         q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
         lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
@@ -197,10 +199,7 @@ def main():
         mark()
         lc.attn_bwd(q0, k0, v0, o, do0, lse, causal=True, scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
         mark()
-        lc.head_to_seq_relayout(o_all, P, out=o_tok)
-        lc.head_to_seq_relayout(dq_all, P, out=dq_tok)
-        lc.head_to_seq_relayout(dk_all, P, out=dk_tok)
-        lc.head_to_seq_relayout(dv_all, P, out=dv_tok)
+        lc.head_to_seq_relayout_batch([o_all, dq_all, dk_all, dv_all], P, outs=[o_tok, dq_tok, dk_tok, dv_tok])
         mark()
         return marks
 

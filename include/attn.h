@@ -274,6 +274,27 @@ int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int
                          void* hip_stream);
 
 /*
+ * seq_to_head_relayout_batch / head_to_seq_relayout_batch -- the relayouts
+ * of several tensors in one launch: tensor j (j < n) is moved exactly as
+ * seq_to_head_relayout (head_to_seq_relayout) would move ins[j] into
+ * outs[j] with H = H[j]; P, N, D and elem_bytes are shared.  Ulysses
+ * exchanges the query, key and value matrices in one all-to-all step
+ * ("Million-Token-Kontexte im Training ...", section "Ulysses: Die Sequenz
+ * als Verteilungseinheit"); one launch over all of them (and dO, or O and
+ * the gradients on the way back) avoids the ramp-up and drain of a launch
+ * per tensor.  ins, outs and H
+ * are host arrays of n entries, 1 <= n <= ATTN_MAX_RELAYOUT_BATCH; each
+ * tensor is validated as in the single call (status and tensor index in
+ * attn_last_error), and no output may overlap any input or another output
+ * (ATTN_ERR_ALIAS).  Nothing is launched on any error.
+ */
+#define ATTN_MAX_RELAYOUT_BATCH 8
+int seq_to_head_relayout_batch(int n, const void* const* ins, void* const* outs, const int* H, int P, int64_t N,
+                               int D, int elem_bytes, void* hip_stream);
+int head_to_seq_relayout_batch(int n, const void* const* ins, void* const* outs, const int* H, int P, int64_t N,
+                               int D, int elem_bytes, void* hip_stream);
+
+/*
  * head_to_seq_reduce -- the inverse exchange of gradients of heads that
  * several ranks shared: with R = P/H ranks per head when H < P (else R = 1),
  * in [P, max(1, H/P), N, D] (flattened: [H*R, N, D], rank-major), out

@@ -33,6 +33,8 @@ __all__ = [
     "attn_bwd_block_workspace_size",
     "seq_to_head_relayout",
     "head_to_seq_relayout",
+    "seq_to_head_relayout_batch",
+    "head_to_seq_relayout_batch",
     "head_to_seq_reduce",
     "trace_enable",
     "trace_collect",
@@ -82,6 +84,8 @@ _SIGS = {
                             _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _I, _P]),
     "seq_to_head_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
     "head_to_seq_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
+    "seq_to_head_relayout_batch": (_I, [_I, _P, _P, _P, _I, _L, _I, _I, _P]),
+    "head_to_seq_relayout_batch": (_I, [_I, _P, _P, _P, _I, _L, _I, _I, _P]),
     "attn_trace_enable": (_I, [_I]),
     "attn_trace_collect": (_I, [ctypes.c_char_p, _I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I), _I]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
@@ -404,7 +408,9 @@ def attn_bwd_block(q, k, v, do, lse, delta, *, causal: bool = True, scale: float
             dv_acc if dv_acc is not None else dv)
 
 
-def _relayout(fn_name, x, P, out, to_head):
+def _relayout_shape(x, P, out, to_head):
+    """(N, H, D, element bytes, out) of one relayout operand, allocating out
+    when it is None."""
     torch = _torch()
     _need(x, "x", None, 4)
     if x.dtype not in (torch.bfloat16, torch.float16, torch.float32, torch.int16):
@@ -423,8 +429,32 @@ def _relayout(fn_name, x, P, out, to_head):
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
     _need(out, "out", x.dtype, 4)
+    return N, H, D, eb, out
+
+
+def _relayout(fn_name, x, P, out, to_head):
+    N, H, D, eb, out = _relayout_shape(x, P, out, to_head)
     _check(getattr(lib(), fn_name)(x.data_ptr(), out.data_ptr(), P, N, H, D, eb, _stream(x)))
     return out
+
+
+def _relayout_batch(fn_name, xs, P, outs, to_head):
+    xs = list(xs)
+    if not 1 <= len(xs) <= 8:
+        raise ValueError("a batch holds 1 to 8 tensors")
+    outs = [None] * len(xs) if outs is None else list(outs)
+    if len(outs) != len(xs):
+        raise ValueError("outs must have one entry per input")
+    shapes = [_relayout_shape(x, P, o, to_head) for x, o in zip(xs, outs)]
+    N, _, D, eb, _ = shapes[0]
+    if any((n, d, e) != (N, D, eb) for n, _, d, e, _ in shapes):
+        raise ValueError("the tensors of a batch share N, D and the element size")
+    n = len(xs)
+    ins = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    ptrs = (ctypes.c_void_p * n)(*[s[4].data_ptr() for s in shapes])
+    heads = (ctypes.c_int * n)(*[s[1] for s in shapes])
+    _check(getattr(lib(), fn_name)(n, ins, ptrs, heads, P, N, D, eb, _stream(xs[0])))
+    return [s[4] for s in shapes]
 
 
 def seq_to_head_relayout(x, P: int, *, out=None):
@@ -435,6 +465,17 @@ def seq_to_head_relayout(x, P: int, *, out=None):
 def head_to_seq_relayout(y, P: int, *, out=None):
     """[P, H/P, N, D] -> [P, N/P, H, D] (bit copy)."""
     return _relayout("head_to_seq_relayout", y, P, out, False)
+
+
+def seq_to_head_relayout_batch(xs, P: int, *, outs=None):
+    """seq_to_head_relayout of every tensor of xs (1 to 8, same N, D and
+    element size, any H) in one launch; returns the outputs."""
+    return _relayout_batch("seq_to_head_relayout_batch", xs, P, outs, True)
+
+
+def head_to_seq_relayout_batch(ys, P: int, *, outs=None):
+    """head_to_seq_relayout of every tensor of ys in one launch."""
+    return _relayout_batch("head_to_seq_relayout_batch", ys, P, outs, False)
 
 
 def head_to_seq_reduce(y, P: int, H: int, *, out=None):

@@ -28,8 +28,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 # The forward's row maximum is a chain of fmaxf; without NaN semantics the
 # compiler drops the quieting of each operand (NaN inputs still reach the
-# output through exp2 and the products).
-PER_FILE = {"attn_fwd.hip": ["-fno-honor-nans"]}
+# output through exp2 and the products).  Without signed zeros it drops the
+# 0 + x that starts each partial row sum (the sign of a zero sum does not
+# matter: a row's sum is positive or the row is empty).
+PER_FILE = {"attn_fwd.hip": ["-fno-honor-nans", "-fno-signed-zeros"]}
 
 
 def _compile(src: str) -> str:

@@ -488,8 +488,9 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
   return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd_block launch");
 }
 
-static int relayout(const char* name, bool to_head, const void* in, void* out, int P, int64_t N, int H, int D,
-                    int elem_bytes, void* hip_stream) {
+// Validates one tensor of a relayout and fills its job; returns a status.
+static int relayout_job(const char* name, bool to_head, const void* in, void* out, int P, int64_t N, int H, int D,
+                        int elem_bytes, lcattn::TransposeJob* job, size_t* in_bytes, size_t* out_bytes) {
   if (!in || !out) return fail(ATTN_ERR_NULL, "%s: null pointer", name);
   if (P < 1 || N < 1 || H < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
   if (N % P) return fail(ATTN_ERR_SHAPE, "%s: P=%d does not divide N=%lld", name, P, (long long)N);
@@ -512,12 +513,58 @@ static int relayout(const char* name, bool to_head, const void* in, void* out, i
   if (overlap(in, (size_t)units * 16, out, (size_t)out_units * 16))
     return fail(ATTN_ERR_ALIAS, "%s: in and out overlap", name);
   // seq->head: out[h][n] = in[n][h] (A = H, Bn = N); head->seq: out[n][h] = in[h][n].
-  const unsigned A = to_head ? (unsigned)H : (unsigned)N;
-  const unsigned Bn = to_head ? (unsigned)N : (unsigned)H;
-  return hip_status(
-      lcattn::launch_transpose_rows(in, out, A, Bn, (unsigned)row_bytes, (unsigned)rep,
-                                    static_cast<hipStream_t>(hip_stream)),
-      name);
+  job->in = in;
+  job->out = out;
+  job->A = to_head ? (unsigned)H : (unsigned)N;
+  job->Bn = to_head ? (unsigned)N : (unsigned)H;
+  job->rep = (unsigned)rep;
+  *in_bytes = (size_t)units * 16;
+  *out_bytes = (size_t)out_units * 16;
+  return ATTN_OK;
+}
+
+static int relayout(const char* name, bool to_head, const void* in, void* out, int P, int64_t N, int H, int D,
+                    int elem_bytes, void* hip_stream) {
+  lcattn::TransposeJob job;
+  size_t ib, ob;
+  const int st = relayout_job(name, to_head, in, out, P, N, H, D, elem_bytes, &job, &ib, &ob);
+  if (st != ATTN_OK) return st;
+  return hip_status(lcattn::launch_transpose_rows_batch(&job, 1, (unsigned)(D * elem_bytes),
+                                                        static_cast<hipStream_t>(hip_stream)),
+                    name);
+}
+
+static_assert(ATTN_MAX_RELAYOUT_BATCH == lcattn::kMaxRelayoutBatch, "batch limit of the header and the kernel");
+
+static int relayout_batch(const char* name, bool to_head, int n, const void* const* ins, void* const* outs,
+                          const int* H, int P, int64_t N, int D, int elem_bytes, void* hip_stream) {
+  if (!ins || !outs || !H) return fail(ATTN_ERR_NULL, "%s: null array", name);
+  if (n < 1 || n > ATTN_MAX_RELAYOUT_BATCH)
+    return fail(ATTN_ERR_SHAPE, "%s: n=%d tensors (1 .. %d)", name, n, ATTN_MAX_RELAYOUT_BATCH);
+  lcattn::TransposeJob jobs[ATTN_MAX_RELAYOUT_BATCH];
+  size_t ib[ATTN_MAX_RELAYOUT_BATCH], ob[ATTN_MAX_RELAYOUT_BATCH];
+  unsigned long long blocks = 0;
+  for (int j = 0; j < n; ++j) {
+    const int st = relayout_job(name, to_head, ins[j], outs[j], P, N, H[j], D, elem_bytes, &jobs[j], &ib[j], &ob[j]);
+    if (st != ATTN_OK) {
+      char detail[sizeof(g_last_error)];
+      snprintf(detail, sizeof(detail), "%s", g_last_error);
+      return fail(st, "%s (tensor %d)", detail, j);
+    }
+    blocks += (unsigned long long)jobs[j].A * jobs[j].Bn;  // >= the workgroups of the job
+  }
+  if (blocks > 0xFFFFFFFFull) return fail(ATTN_ERR_UNSUPPORTED, "%s: too many rows in one launch", name);
+  // every output is written while every input is still being read
+  for (int j = 0; j < n; ++j)
+    for (int i = 0; i < n; ++i) {
+      if (i != j && overlap(ins[i], ib[i], outs[j], ob[j]))
+        return fail(ATTN_ERR_ALIAS, "%s: output %d overlaps input %d", name, j, i);
+      if (i < j && overlap(outs[i], ob[i], outs[j], ob[j]))
+        return fail(ATTN_ERR_ALIAS, "%s: outputs %d and %d overlap", name, i, j);
+    }
+  return hip_status(lcattn::launch_transpose_rows_batch(jobs, n, (unsigned)(D * elem_bytes),
+                                                        static_cast<hipStream_t>(hip_stream)),
+                    name);
 }
 
 int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
@@ -528,6 +575,16 @@ int seq_to_head_relayout(const void* in, void* out, int P, int64_t N, int H, int
 int head_to_seq_relayout(const void* in, void* out, int P, int64_t N, int H, int D, int elem_bytes,
                          void* hip_stream) {
   return relayout("head_to_seq_relayout", false, in, out, P, N, H, D, elem_bytes, hip_stream);
+}
+
+int seq_to_head_relayout_batch(int n, const void* const* ins, void* const* outs, const int* H, int P, int64_t N,
+                               int D, int elem_bytes, void* hip_stream) {
+  return relayout_batch("seq_to_head_relayout_batch", true, n, ins, outs, H, P, N, D, elem_bytes, hip_stream);
+}
+
+int head_to_seq_relayout_batch(int n, const void* const* ins, void* const* outs, const int* H, int P, int64_t N,
+                               int D, int elem_bytes, void* hip_stream) {
+  return relayout_batch("head_to_seq_relayout_batch", false, n, ins, outs, H, P, N, D, elem_bytes, hip_stream);
 }
 
 int head_to_seq_reduce(const void* in, int in_dtype, void* out, int P, int64_t N, int H, int D, void* hip_stream) {

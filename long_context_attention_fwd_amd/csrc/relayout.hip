@@ -27,18 +27,39 @@ namespace lcattn {
 constexpr int kRelayoutThreads = 256;
 constexpr int kRelayoutUnroll = 4;
 
+// One tensor of a batched relayout, as the kernel sees it (passed by value).
+struct RelayoutJob {
+  const void* in;
+  void* out;
+  unsigned A, Bn, rep;
+  unsigned nbt;    // b-tiles per a-tile
+  unsigned first;  // first workgroup of this job
+};
+struct RelayoutBatch {
+  RelayoutJob job[kMaxRelayoutBatch];
+  int n;
+  unsigned units_log2, ta_log2, tb_log2;
+};
+
 // out[a * rep + i, b, :] = in[b, a, :] (i < rep) for rows of 2^units_log2
-// 16-byte units, a in [0, A), b in [0, Bn): rep > 1 replicates every a-row
-// block (a key/value head shared by rep ranks).  Tile (a-tile, b-tile) =
-// blockIdx.x split as (blockIdx.x / nbt, blockIdx.x % nbt); TA = 2^ta_log2,
-// TB = 2^tb_log2 rows.  A * rep * Bn * units < 2^32 is checked on the host.
-__global__ __launch_bounds__(kRelayoutThreads) void transpose_rows_kernel(const u32x4* __restrict__ in,
-                                                                            u32x4* __restrict__ out,
-                                                                            unsigned A, unsigned Bn,
-                                                                            unsigned units_log2, unsigned ta_log2,
-                                                                            unsigned tb_log2, unsigned nbt,
-                                                                            unsigned rep) {
-  const unsigned bt = blockIdx.x % nbt, at = blockIdx.x / nbt;
+// 16-byte units, a in [0, A), b in [0, Bn), for each job of a batch (the
+// tensors that one exchange moves together, e.g. Q, K, V and dO): rep > 1
+// replicates every a-row block (a key/value head shared by rep ranks).  The
+// jobs' tiles are numbered one after another; job j owns workgroups
+// [first, first + nat * nbt) and tile (a-tile, b-tile) = (w / nbt, w % nbt)
+// of its local index w.  TA = 2^ta_log2, TB = 2^tb_log2 rows.
+// A * rep * Bn * units < 2^32 per job is checked on the host.
+__global__ __launch_bounds__(kRelayoutThreads) void transpose_rows_kernel(RelayoutBatch jobs) {
+  // the job of this workgroup (uniform: a scalar scan of at most 8 entries)
+  int j = 0;
+  while (j + 1 < jobs.n && blockIdx.x >= jobs.job[j + 1].first) ++j;
+  const RelayoutJob& J = jobs.job[j];
+  const u32x4* __restrict__ in = static_cast<const u32x4*>(J.in);
+  u32x4* __restrict__ out = static_cast<u32x4*>(J.out);
+  const unsigned A = J.A, Bn = J.Bn, rep = J.rep, nbt = J.nbt;
+  const unsigned units_log2 = jobs.units_log2, ta_log2 = jobs.ta_log2, tb_log2 = jobs.tb_log2;
+  const unsigned w = blockIdx.x - J.first;
+  const unsigned bt = w % nbt, at = w / nbt;
   const unsigned a0 = at << ta_log2, b0 = bt << tb_log2;
   const unsigned umask = (1u << units_log2) - 1u, tbmask = (1u << tb_log2) - 1u;
   const unsigned per = 1u << (ta_log2 + tb_log2 + units_log2);  // units in the tile
@@ -104,8 +125,7 @@ __global__ __launch_bounds__(256) void sum_replicas_kernel(const void* __restric
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + idx * 8));
 }
 
-hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned Bn, unsigned row_bytes,
-                                 unsigned rep, hipStream_t stream) {
+hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned row_bytes, hipStream_t stream) {
   unsigned units = row_bytes / 16, lg = 0;
   while ((1u << lg) < units) ++lg;
   // 4 x 4 rows, with more b rows when rows are short, so a tile is at least
@@ -113,11 +133,34 @@ hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned
   const unsigned ta_lg = 2;
   unsigned tb_lg = 2;
   while ((1u << (ta_lg + tb_lg + lg)) < (unsigned)kRelayoutThreads) ++tb_lg;
-  const unsigned nbt = (Bn + (1u << tb_lg) - 1) >> tb_lg;
-  const unsigned nat = (A + (1u << ta_lg) - 1) >> ta_lg;
-  LCATTN_LAUNCH("transpose_rows_kernel", transpose_rows_kernel, dim3(nbt * nat), dim3(kRelayoutThreads), 0, stream,
-                static_cast<const u32x4*>(in), static_cast<u32x4*>(out), A, Bn, lg, ta_lg, tb_lg, nbt, rep);
+  RelayoutBatch b{};
+  b.n = n;
+  b.units_log2 = lg;
+  b.ta_log2 = ta_lg;
+  b.tb_log2 = tb_lg;
+  unsigned long long blocks = 0;
+  for (int j = 0; j < n; ++j) {
+    RelayoutJob& J = b.job[j];
+    J.in = jobs[j].in;
+    J.out = jobs[j].out;
+    J.A = jobs[j].A;
+    J.Bn = jobs[j].Bn;
+    J.rep = jobs[j].rep;
+    J.nbt = (J.Bn + (1u << tb_lg) - 1) >> tb_lg;
+    J.first = (unsigned)blocks;
+    blocks += (unsigned long long)J.nbt * ((J.A + (1u << ta_lg) - 1) >> ta_lg);
+  }
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  LCATTN_LAUNCH("transpose_rows_kernel", transpose_rows_kernel, dim3((unsigned)blocks), dim3(kRelayoutThreads), 0,
+                stream, b);
   return hipGetLastError();
+}
+
+hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned Bn, unsigned row_bytes,
+                                 unsigned rep, hipStream_t stream) {
+  const TransposeJob job{in, out, A, Bn, rep};
+  return launch_transpose_rows_batch(&job, 1, row_bytes, stream);
 }
 
 hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long long A, long long Bn, int D, int rep,

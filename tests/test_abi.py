@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
-              "seq_to_head_relayout", "head_to_seq_relayout", "attn_status_string", "attn_last_error"):
+              "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
+              "head_to_seq_relayout_batch", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
 
@@ -237,6 +238,39 @@ def test_relayout_shared_heads(L):
     assert L.seq_to_head_relayout(A, B_, 8, 4096, 3, 128, 2, None) == 2
     assert L.seq_to_head_relayout(A + 4 * 4096 * 256 - 16, A, 8, 4096, 4, 128, 2, None) == 5  # replicated out reaches in
     assert L.head_to_seq_relayout(A, B_, 8, 4096, 4, 128, 2, None) == 3
+
+
+def batch_call(L, fn, ins, outs, heads, P=8, N=4096, D=128, eb=2):
+    n = len(ins)
+    arr = lambda t, xs: (t * max(1, n))(*xs) if xs is not None else None
+    return getattr(L, fn)(n, arr(ctypes.c_void_p, ins), arr(ctypes.c_void_p, outs), arr(ctypes.c_int, heads),
+                          P, N, D, eb, None)
+
+
+MiB = 1 << 20
+
+
+@pytest.mark.parametrize("fn", ["seq_to_head_relayout_batch", "head_to_seq_relayout_batch"])
+def test_relayout_batch_rejects(L, fn):
+    # tensors of [8, 512, H, 128] bf16: 1 MiB per 8 heads
+    ins, outs, heads = [A, B_, C_], [D_, E_, F_], [32, 8, 8]
+    assert getattr(L, fn)(3, None, None, None, 8, 4096, 128, 2, None) == 1
+    assert batch_call(L, fn, [], [], [], ) == 2                          # n = 0
+    assert batch_call(L, fn, [A] * 9, [B_] * 9, [32] * 9) == 2            # n > 8
+    assert batch_call(L, fn, [A, None], [D_, E_], [32, 8]) == 1           # a null tensor
+    assert batch_call(L, fn, ins, outs, [32, 12, 8]) == 2                 # P does not divide H of tensor 1
+    assert b"tensor 1" in L.attn_last_error()
+    assert batch_call(L, fn, [A, B_ + 2], [D_, E_], [32, 8]) == 4         # misaligned
+    assert batch_call(L, fn, [A, B_], [D_, A + 64], [32, 8]) == 5         # output 1 overlaps input 0
+    assert batch_call(L, fn, [A, B_], [D_, D_ + 2 * MiB], [32, 8]) == 5   # outputs 0 and 1 overlap
+    assert batch_call(L, fn, [A], [B_], [32], N=4095) == 2
+    assert batch_call(L, fn, [A], [B_], [32], eb=3) == 3
+
+
+def test_relayout_batch_shared_heads(L):
+    # replication only on the way to heads; the inverse refuses it as the single call does
+    assert batch_call(L, "seq_to_head_relayout_batch", [A, B_], [D_, E_], [32, 3]) == 2
+    assert batch_call(L, "head_to_seq_relayout_batch", [A, B_], [D_, E_], [32, 4]) == 3
 
 
 @pytest.mark.parametrize("args,status", [

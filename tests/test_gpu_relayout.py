@@ -52,6 +52,58 @@ def test_relayout_ulysses_shard_32k_full(gpu):
         del xd, y, back
 
 
+def test_relayout_batch_ulysses_shard_32k_full(gpu):
+    """Q, K, V and dO of the 32K layer moved to head shards in one launch and
+    back in another: every element against the oracle, and the round trip."""
+    import torch
+    w = WORKLOADS["ulysses_shard_32k"]
+    d = make_workload_inputs(w)
+    d["do"] = np.random.default_rng(w.seed + 17).integers(0, 1 << 16, size=d["q"].shape, dtype=np.uint16)
+    names = ("q", "k", "v", "do")
+    xs = [to_dev(d[n]) for n in names]
+    outs = [torch.full((w.P, x.shape[2] // w.P, w.N, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+            for x in xs]
+    ys = lc.seq_to_head_relayout_batch(xs, w.P, outs=outs)
+    backs = lc.head_to_seq_relayout_batch(ys, w.P)
+    torch.cuda.synchronize()
+    for n, x, y, b in zip(names, xs, ys, backs):
+        assert y.data_ptr() == outs[names.index(n)].data_ptr()
+        assert np.array_equal(bits_of(y), oracle.seq_to_head(d[n], w.P)), n
+        assert torch.equal(b.view(torch.int16), x.view(torch.int16)), n
+
+
+@pytest.mark.parametrize("P,T,heads,D,elem", [
+    (8, 8, (32, 8, 8, 4, 2, 1, 16, 8), 128, 2),   # eight tensors, three of them replicated (H < P)
+    (4, 25, (4, 8, 2), 64, 2),                     # ragged: 100 tokens, 64-dim rows
+    (2, 3, (6, 2), 64, 4),                          # fp32 words
+    (1, 17, (3,), 128, 2),                          # one tensor, one rank
+])
+def test_relayout_batch_matches_single_calls(gpu, P, T, heads, D, elem):
+    import torch
+    rng = np.random.default_rng(P * 1000 + T)
+    dt = torch.bfloat16 if elem == 2 else torch.float32
+    xs, hs = [], []
+    for H in heads:
+        x = rng.integers(0, 1 << (8 * elem), size=(P, T, H, D), dtype=np.uint16 if elem == 2 else np.uint32)
+        xs.append(x)
+        hs.append(torch.from_numpy(x.view(np.int16 if elem == 2 else np.int32)).cuda().view(dt))
+    ys = lc.seq_to_head_relayout_batch(hs, P)
+    torch.cuda.synchronize()
+    it = torch.int16 if elem == 2 else torch.int32
+    for x, h, y in zip(xs, hs, ys):
+        single = lc.seq_to_head_relayout(h, P)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(it), single.view(it))
+        want = oracle.seq_to_head(x, P)
+        assert np.array_equal(y.cpu().view(it).numpy().view(want.dtype), want)
+    plain = [i for i, H in enumerate(heads) if H >= P and H % P == 0]
+    if plain:
+        backs = lc.head_to_seq_relayout_batch([ys[i] for i in plain], P)
+        torch.cuda.synchronize()
+        for i, b in zip(plain, backs):
+            assert np.array_equal(b.cpu().view(it).numpy().view(xs[i].dtype), xs[i])
+
+
 # ---------------------------------------------------------------------------
 # fewer key/value heads than ranks: replication out, summed gradients back
 # ---------------------------------------------------------------------------
