@@ -73,11 +73,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   static_assert(QB == 1, "one block of 32 query rows per wave");
   static_assert(kBN == 64, "LdsTile holds 64 rows");
 
-  // Three buffers, each a K tile followed by a V tile (row-major, swizzled),
-  // as separate objects so the compiler can tell them apart.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * T::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * T::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem2[2 * T::BYTES];
+  // LDS: the K tiles of the three pipeline buffers, then their V tiles
+  // (row-major, swizzled), in one object so that every fragment read is a
+  // lane-constant address plus an immediate offset below 64 KiB.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[6 * T::BYTES];
+  constexpr int KB = T::BYTES;      // bytes of one tile
+  constexpr int VREG = 3 * T::BYTES;  // start of the V tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -120,11 +121,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   typename T::template AsyncLoader<kWaves> kload, vload;
   kload.init(wave, lane, false, a.ks[2]);
   vload.init(wave, lane, true, a.ks[2]);
-  auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    kload.load(buf, kh, (long long)(j0 + j) * kBN, a.Nk, wave);
-    vload.load(buf + T::BYTES, vh, (long long)(j0 + j) * kBN, a.Nk, wave);
+  // the wave index in a scalar register: the LDS side of a direct load is
+  // then scalar arithmetic
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int j, int b) __attribute__((always_inline)) {
+    const long long r0 = (long long)(j0 + j) * kBN;
+    if (r0 + kBN <= a.Nk) {  // uniform: every row of the tile exists
+      kload.load_full(smem + b * KB, kh, r0, wave_s);
+      vload.load_full(smem + VREG + b * KB, vh, r0, wave_s);
+    } else {
+      kload.load(smem + b * KB, kh, r0, a.Nk, wave_s);
+      vload.load(smem + VREG + b * KB, vh, r0, a.Nk, wave_s);
+    }
   };
-  if (n_tiles > 0) issue(0, smem0);
+  if (n_tiles > 0) issue(0, 0);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds its query row's dims
   // 16t + 8*grp .. +7 for every reduction step t.
@@ -148,31 +158,78 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   bf16x8 pf[2];  // P of the sub-tile waiting for its PV product (zero: no-op)
   pf[0] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   pf[1] = pf[0];
-  // per-lane LDS offsets of the K row fragments and the V^T fragments
-  int koff[KT], voff[DB];
+  // per-lane LDS addresses of the K row fragments (in the K tile of buffer 0)
+  // and of the V^T fragments (in the V tile of buffer 0); a sub-tile adds an
+  // offset: (buffer) * KB + (half) * 32 rows
+  const unsigned lds0 = (unsigned)reinterpret_cast<uintptr_t>(smem);
+  unsigned koff[KT], voff[DB];
 #pragma unroll
-  for (int t = 0; t < KT; ++t) koff[t] = T::row_off(c, grp, t);
+  for (int t = 0; t < KT; ++t) koff[t] = lds0 + T::row_off(c, grp, t);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) voff[db] = T::tr_off(lane, db);
+  for (int db = 0; db < DB; ++db) voff[db] = lds0 + VREG + T::tr_off(lane, db);
 
-  // S^T of the 32 keys in half kh of the K tile in buf (rows in pi order)
-  auto s_sub = [&](const unsigned char* buf, int khalf) __attribute__((always_inline)) {
+  // Fragment reads of one 32-key sub-tile at byte offset `off` from buffer 0:
+  // a compile-time offset (std::integral_constant) becomes the immediate of
+  // each read, a run-time one is added to the address.
+  auto read_k = [&](auto off, u32x4 (&kf)[KT]) __attribute__((always_inline)) {
+    if constexpr (std::is_integral_v<decltype(off)>) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) kf[t] = lds_read16_rt(koff[t] + off);
+    } else {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) kf[t] = lds_read16_imm<decltype(off)::value>(koff[t]);
+    }
+  };
+  auto read_v = [&](auto off, u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+    if constexpr (std::is_integral_v<decltype(off)>) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f[db][0] = tr_frag_asm_at<T::ROW_BYTES>(voff[db], off);
+        f[db][1] = tr_frag_asm_at<T::ROW_BYTES>(voff[db], off + 16 * T::ROW_BYTES);
+      }
+    } else {
+      constexpr int O = decltype(off)::value;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f[db][0] = tr_frag_asm_imm<O, T::ROW_BYTES>(voff[db]);
+        f[db][1] = tr_frag_asm_imm<O + 16 * T::ROW_BYTES, T::ROW_BYTES>(voff[db]);
+      }
+    }
+  };
+  auto wait_k = [&](u32x4 (&kf)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < KT; t += 4) lds_wait_frags(kf[t], kf[t + 1], kf[t + 2], kf[t + 3]);
+  };
+  auto wait_v = [&](u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; db += 2) lds_wait_frags(f[db][0], f[db][1], f[db + 1][0], f[db + 1][1]);
+  };
+  // S^T of one sub-tile from its K fragments (rows in pi order)
+  auto s_mfma = [&](u32x4 (&kf)[KT]) __attribute__((always_inline)) {
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.f;
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-      s = mfma32x32x16(as_bf16x8(ld_lds16(buf, koff[t] + 32 * khalf * T::ROW_BYTES)), qf[t], s);
+    for (int t = 0; t < KT; ++t) s = mfma32x32x16(as_bf16x8(kf[t]), qf[t], s);
     return s;
   };
+  auto pv_mfma = [&](u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), pf[0], acc[db]);
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), pf[1], acc[db]);
+    }
+  };
 
-  // Online softmax of one sub-tile: S^T (one query per lane, 16 of its 32
-  // keys; the other 16 sit in lane ^ 32) -> P packed as the B operand of the
-  // next PV product, and this sub-tile's part of the row sum (psum), against
-  // the exact running maximum m_run (so a row's largest weight is exactly 1
-  // and carries no bf16 rounding).  The caller rescales O and the sum when
-  // m_run moved (m_old -> m_run).
-  auto softmax = [&](auto masked_tag, f32x16 s, int t, float& m_old, float& psum) __attribute__((always_inline)) {
+  // Online softmax of one sub-tile in three parts: S^T (one query per lane,
+  // 16 of its 32 keys; the other 16 sit in lane ^ 32) -> the row maximum
+  // (masked tiles mask s in place; updates m_run, returns the reference
+  // used by the exponentials), the weights exp2(s * scale - m) in place, and
+  // P packed as the B operand of the next PV product with this sub-tile's
+  // part of the row sum.  The maximum is exact, so a row's largest weight is
+  // exactly 1 and carries no bf16 rounding; the caller rescales O and the
+  // sum when m_run moved.
+  auto row_max = [&](auto masked_tag, f32x16& s, int t, float& m_old) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if (MASKED) {
       const int kt = kBN * j0 + 32 * t;
@@ -193,65 +250,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
     }
     m_old = m_run;
     m_run = fmaxf(m_run, mx * a.scale_log2);
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    // a row with no visible key so far keeps m_run = -inf; its weights are
+    // exp2(-inf) = 0 against reference 0 (an unmasked sub-tile has a visible
+    // key in every row, so m_run is finite there)
+    if (MASKED) return (m_run == -INFINITY) ? 0.f : m_run;
+    return m_run;
+  };
+  auto weights = [&](f32x16& s, float m_use) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, -m_use));
-      ls[v & 3] += s[v];
-    }
+    for (int v = 0; v < 16; ++v) s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, -m_use));
+  };
+  auto pack = [&](const f32x16& s) __attribute__((always_inline)) {
+    float ls[4] = {s[0], s[1], s[2], s[3]};
+#pragma unroll
+    for (int v = 4; v < 16; ++v) ls[v & 3] += s[v];
     pf[0] = pack_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
     pf[1] = pack_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
-    psum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
-
-  // One step t of the pipeline over 32-key sub-tiles:
-  //   MFMA: S(t+1) from the K half in (kbuf, kh); O^T += V^T P(t-1)^T from the
-  //         V half in (vbuf, vh)
-  //   VALU: softmax of S(t) -> P(t)
-  // The MFMA and VALU work is independent, so it is interleaved one MFMA at
-  // a time.  Returns S(t+1).
-  auto step = [&](auto masked_tag, int t, f32x16 s_cur, const unsigned char* kbuf, int khalf,
-                  const unsigned char* vbuf, int vhalf) __attribute__((always_inline)) {
-    // V^T fragments of the previous sub-tile (transposing reads, waited below)
-    const unsigned vbase = (unsigned)reinterpret_cast<uintptr_t>(vbuf + T::BYTES);
-    u32x4 f[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      f[db][0] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + 32 * vhalf * T::ROW_BYTES);
-      f[db][1] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + (32 * vhalf + 16) * T::ROW_BYTES);
-    }
-    const f32x16 s_next = s_sub(kbuf, khalf);
-    if constexpr (DB == 4) {
-      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
-      lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
-    } else {
-      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), pf[0], acc[db]);
-      acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), pf[1], acc[db]);
-    }
-    float m_old, psum;
-    softmax(masked_tag, s_cur, t, m_old, psum);
-    constexpr int NM = KT + 2 * DB;
-    constexpr int VPM = (72 + NM - 1) / NM;
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-    }
-    // keep P and the sum ahead of the rescale branch below (otherwise they
-    // are sunk past it, out of reach of the MFMAs they should overlap)
-    {
-      u32x4 p0 = as_u32x4(pf[0]), p1 = as_u32x4(pf[1]);
-      asm volatile("" : "+v"(p0), "+v"(p1), "+v"(psum));
-      pf[0] = as_bf16x8(p0);
-      pf[1] = as_bf16x8(p1);
-    }
-    // the accumulator now holds PV up to t-1: bring it and the sum to the new
-    // reference maximum
+  // the accumulator holds PV up to the previous sub-tile: bring it and the
+  // sum to the new reference maximum
+  auto rescale = [&](float m_old, float psum) __attribute__((always_inline)) {
     if (__any(m_run != m_old)) {
       const float alpha = m_run != m_old ? fast_exp2(m_old - m_run) : 1.f;
 #pragma unroll
@@ -261,22 +280,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
       l_run *= alpha;
     }
     l_run += psum;
+  };
+
+  auto pin16 = [&](f32x16& x) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]),
+                 "+v"(x[14]), "+v"(x[15]));
+  };
+
+  // One step t of the pipeline over 32-key sub-tiles, in phases that no
+  // instruction crosses:
+  //   [1] transposing reads of the V^T fragments of sub-tile t-1; row max of S(t)
+  //   [2] O^T += V^T P(t-1)^T (8 MFMAs), one at a time between the
+  //       exponentials of S(t) (independent VALU work)
+  //   [3] reads of the K fragments of sub-tile t+1 (all eight in flight at
+  //       once); row sum and bf16 P(t)
+  //   [4] S(t+1) = K Q^T (8 MFMAs); rescale when some row's maximum moved
+  // koff_t / voff_t: byte offsets of sub-tiles t+1 (K) and t-1 (V) from
+  // buffer 0 (compile-time in the unrolled loop).  Returns S(t+1).
+  auto step = [&](auto masked_tag, int t, f32x16 s_cur, auto koff_t, auto voff_t) __attribute__((always_inline)) {
+    u32x4 f[DB][2];
+    read_v(voff_t, f);
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out before the row max
+    float m_old;
+    const float m_use = row_max(masked_tag, s_cur, t, m_old);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_v(f);
+    pv_mfma(f);
+    weights(s_cur, m_use);
+    constexpr int NPV = 2 * DB;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 / NPV, 0);
+    }
+    // the weights are computed here, next to the PV products (otherwise they
+    // are sunk past the rescale branch below, out of reach of the MFMAs)
+    pin16(s_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 kf[KT];
+    read_k(koff_t, kf);
+    float psum = pack(s_cur);
+    {
+      u32x4 p0 = as_u32x4(pf[0]), p1 = as_u32x4(pf[1]);
+      asm volatile("" : "+v"(p0), "+v"(p1), "+v"(psum));
+      pf[0] = as_bf16x8(p0);
+      pf[1] = as_bf16x8(p1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_k(kf);
+    const f32x16 s_next = s_mfma(kf);
+    rescale(m_old, psum);
     return s_next;
   };
   auto sync = [&]() __attribute__((always_inline)) {
     wait_vmem();  // this wave's part of the next tile has landed in LDS
     __syncthreads();
   };
+  using std::integral_constant;
+  constexpr int H32 = 32 * T::ROW_BYTES;  // second half of a tile
 
   // Tiles [0, n_full) need no element mask for any wave of the workgroup:
   // every key precedes the workgroup's first query and lies inside Nk.
   long long full_keys = a.Nk;
   if (a.causal) full_keys = min(full_keys, max(0LL, a.q_pos0 + q_start - a.k_pos0 + 1));
   const int n_full = (int)min((long long)n_tiles, max(0LL, full_keys / kBN - j0));
-  auto buf = [&](int i) __attribute__((always_inline)) {
-    const int r = i % 3;
-    return r == 0 ? smem0 : (r == 1 ? smem1 : smem2);
-  };
 
   // Schedule: tile j lives in buffer j % 3.  Step t reads the K half of
   // sub-tile t+1 and the V half of sub-tile t-1; odd steps t issue the direct
@@ -287,61 +355,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   if (n_tiles > 0) {
     wait_vmem();
     __syncthreads();
-    issue(min(1, n_tiles - 1), smem1);
-    f32x16 s = s_sub(smem0, 0);
+    issue(min(1, n_tiles - 1), 1);
+    f32x16 s;
+    {
+      u32x4 kf[KT];
+      read_k(integral_constant<int, 0>{}, kf);
+      wait_k(kf);
+      s = s_mfma(kf);
+    }
     // step 0: nothing to multiply with V yet
     {
-      float m_old, psum;
-      const f32x16 s_next = s_sub(smem0, 1);
-      if (n_full > 0) softmax(std::false_type{}, s, 0, m_old, psum);
-      else softmax(std::true_type{}, s, 0, m_old, psum);
-      l_run = psum;
-      s = s_next;
+      float m_old;
+      const float m_use = n_full > 0 ? row_max(std::false_type{}, s, 0, m_old) : row_max(std::true_type{}, s, 0, m_old);
+      weights(s, m_use);
+      l_run = pack(s);
+      u32x4 kf[KT];
+      read_k(integral_constant<int, H32>{}, kf);
+      wait_k(kf);
+      s = s_mfma(kf);
     }
     sync();
     int t = 1;
     // unmasked steps, unrolled over the buffer pattern (period 6)
     for (; t + 6 <= 2 * n_full; t += 6) {
-      const int j0 = (t - 1) / 2;  // multiple of 3
-      issue(min(j0 + 2, n_tiles - 1), smem2);
-      s = step(std::false_type{}, t, s, smem1, 0, smem0, 0);
-      s = step(std::false_type{}, t + 1, s, smem1, 1, smem0, 1);
+      const int jb = (t - 1) / 2;  // multiple of 3
+      issue(min(jb + 2, n_tiles - 1), 2);
+      s = step(std::false_type{}, t, s, integral_constant<int, KB>{}, integral_constant<int, 0>{});
+      s = step(std::false_type{}, t + 1, s, integral_constant<int, KB + H32>{}, integral_constant<int, H32>{});
       sync();
-      issue(min(j0 + 3, n_tiles - 1), smem0);
-      s = step(std::false_type{}, t + 2, s, smem2, 0, smem1, 0);
-      s = step(std::false_type{}, t + 3, s, smem2, 1, smem1, 1);
+      issue(min(jb + 3, n_tiles - 1), 0);
+      s = step(std::false_type{}, t + 2, s, integral_constant<int, 2 * KB>{}, integral_constant<int, KB>{});
+      s = step(std::false_type{}, t + 3, s, integral_constant<int, 2 * KB + H32>{}, integral_constant<int, KB + H32>{});
       sync();
-      issue(min(j0 + 4, n_tiles - 1), smem1);
-      s = step(std::false_type{}, t + 4, s, smem0, 0, smem2, 0);
-      s = step(std::false_type{}, t + 5, s, smem0, 1, smem2, 1);
+      issue(min(jb + 4, n_tiles - 1), 1);
+      s = step(std::false_type{}, t + 4, s, integral_constant<int, 0>{}, integral_constant<int, 2 * KB>{});
+      s = step(std::false_type{}, t + 5, s, integral_constant<int, H32>{}, integral_constant<int, 2 * KB + H32>{});
       sync();
     }
-    // the rest (diagonal and tail tiles, and leftovers): buffers at run time
+    // the rest (diagonal and tail tiles, and leftovers): offsets at run time
     for (; t < n_sub; ++t) {
-      if (t & 1) issue(min((t + 3) / 2, n_tiles - 1), buf((t + 3) / 2));
-      s = step(std::true_type{}, t, s, buf((t + 1) / 2), (t + 1) & 1, buf((t - 1) / 2), (t - 1) & 1);
+      if (t & 1) issue(min((t + 3) / 2, n_tiles - 1), ((t + 3) / 2) % 3);
+      const int ko = ((t + 1) / 2 % 3) * KB + ((t + 1) & 1) * H32;
+      const int vo = ((t - 1) / 2 % 3) * KB + ((t - 1) & 1) * H32;
+      s = step(std::true_type{}, t, s, ko, vo);
       if (!(t & 1)) sync();
     }
     // PV of the last sub-tile
     {
-      const unsigned vbase = (unsigned)reinterpret_cast<uintptr_t>(buf(n_tiles - 1) + T::BYTES);
       u32x4 f[DB][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        f[db][0] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + 32 * T::ROW_BYTES);
-        f[db][1] = tr_frag_asm_at<T::ROW_BYTES>(vbase, voff[db] + 48 * T::ROW_BYTES);
-      }
-      if constexpr (DB == 4) {
-        lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
-        lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
-      } else {
-        lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), pf[0], acc[db]);
-        acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), pf[1], acc[db]);
-      }
+      read_v(((n_tiles - 1) % 3) * KB + H32, f);
+      wait_v(f);
+      pv_mfma(f);
     }
     wait_vmem();  // no direct load may still be in flight when the workgroup ends
   }

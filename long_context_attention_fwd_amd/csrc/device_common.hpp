@@ -235,15 +235,22 @@ struct SwzTile {
         off[i] = (unsigned)(r * row_stride + 8 * (up ^ swz(tr, r))) * 2u;
       }
     }
+    // A tile whose 64 rows all exist (r0 + 64 <= rows_total); wave must be
+    // wave-uniform in a scalar register (readfirstlane), so that only the
+    // per-lane offset is a vector value.
+    __device__ void load_full(unsigned char* lds, const uint16_t* g, long long r0, int wave) const {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(g + r0 * rs);
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]),
+                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                             reinterpret_cast<uintptr_t>(lds) + (wave + i * NW) * 1024),
+                                         16, 0, 0);
+    }
     __device__ void load(unsigned char* lds, const uint16_t* g, long long r0, long long rows_total, int wave) const {
       const unsigned char* base = reinterpret_cast<const unsigned char*>(g + r0 * rs);
       if (r0 + 64 <= rows_total) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + off[i]),
-                                           reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                               reinterpret_cast<uintptr_t>(lds) + (wave + i * NW) * 1024),
-                                           16, 0, 0);
+        load_full(lds, g, r0, wave);
       } else {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -320,6 +327,32 @@ __device__ __forceinline__ u32x4 tr_frag_asm_at(unsigned lds_base, int off) {
   const unsigned addr = lds_base + off;
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(addr));
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(4 * ROW_BYTES));
+  u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+  return r;
+}
+
+// 16-byte LDS read through inline assembly at a lane-constant address plus
+// an immediate offset (IMM < 64 KiB), or at a run-time address; as for
+// tr_frag_asm_at, the caller runs lds_wait_frags on the result before use.
+template <int IMM>
+__device__ __forceinline__ u32x4 lds_read16_imm(unsigned addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(IMM));
+  return r;
+}
+__device__ __forceinline__ u32x4 lds_read16_rt(unsigned addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// Transposed fragment (two transposing reads, the second 4 rows further) at a
+// lane-constant address plus an immediate offset (IMM + 4 ROW_BYTES < 64 KiB).
+template <int IMM, int ROW_BYTES>
+__device__ __forceinline__ u32x4 tr_frag_asm_imm(unsigned addr) {
+  u32x2 lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(IMM));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(IMM + 4 * ROW_BYTES));
   u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
   return r;
 }
