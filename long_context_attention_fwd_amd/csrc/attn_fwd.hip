@@ -26,14 +26,19 @@
 //    per-row XOR swizzle of 16-byte units.  K fragments are plain 16-byte
 //    reads; the V^T fragments of the PV product come from the row-major V tile
 //    through the transposing LDS read (ds_read_b64_tr_b16, two per fragment).
-//  * Pipeline over three LDS buffers: iteration j issues the direct loads of
-//    tile j+1, computes S(j) = K(j) Q^T, then the PV product of tile j-1 and
-//    the softmax of tile j (independent MFMA and VALU work), then one
-//    wait + barrier.  The transposing reads are issued through inline
-//    assembly with explicit lgkmcnt waits: the compiler cannot tell which
-//    LDS buffer such a read touches and would otherwise wait for the in-flight
-//    direct loads of tile j+1 before it.  The K reads are ordinary loads of
-//    distinct __shared__ objects, which it can tell apart.
+//    The three pipeline buffers sit in one LDS object (K tiles, then V
+//    tiles), so every fragment read is a lane-constant address plus an
+//    immediate offset: no address arithmetic in the loop.
+//  * Pipeline over 32-key sub-tiles; step t runs in phases that no
+//    instruction crosses: [1] transposing reads of the V^T fragments of
+//    sub-tile t-1, row max of S(t); [2] the 8 MFMAs of O^T += V^T P(t-1)^T,
+//    one at a time between the exponentials of S(t); [3] the 8 K fragment
+//    reads of sub-tile t+1 (all in flight at once), row sum and bf16 P(t);
+//    [4] the 8 MFMAs of S(t+1) = K Q^T.  Fragment reads are inline assembly
+//    with explicit lgkmcnt waits (the compiler would otherwise wait for the
+//    direct loads in flight, or read and wait for one K fragment at a time).
+//    Odd steps issue the direct loads of the tile two steps ahead, even steps
+//    end with one wait + barrier.
 //  * Tiles that need no element mask for any wave run in a straight-line loop
 //    unrolled over the three buffers; the diagonal and tail tiles run a masked
 //    copy with buffers chosen at run time.
@@ -43,10 +48,9 @@
 //    near one-hot rows).  The accumulator (64 registers per query block) is
 //    rescaled only when the maximum of some row in the wave has moved; late
 //    in a long row that is rare.
-//  * Causal: tiles past the workgroup's last query are never loaded, tiles
-//    past a wave's last query are skipped by that wave, and only tiles that
-//    straddle the diagonal (or the end of the keys) apply the element mask.
-//    Workgroups are issued longest-first.
+//  * Causal: tiles past the workgroup's last query are never loaded, and
+//    only tiles that straddle the diagonal (or the end of the keys) apply the
+//    element mask.  Workgroups are issued longest-first.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "trace.hpp"
