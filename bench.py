@@ -344,6 +344,21 @@ def main():
         out["token_major_forward"] = {"call": "attn_fwd_strided on shard 0's heads of the token-major input",
                                       "ms": round(ms, 4), "TFLOP/s": round(tflops(f_fwd, ms), 2),
                                       "frac_peak": round(tflops(f_fwd, ms) / PEAK_BF16_TFLOPS, 4)}
+        # its backward the same way: Q, K, V, O, dO read and dQ, dK, dV written token-major
+        def tm_heads(x, H, n):
+            return x.view(N, H, D)[:, :n].permute(1, 0, 2).unsqueeze(0)
+        o_tmb = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+        g_tm = [torch.empty((N, H, D), dtype=torch.bfloat16, device=dev) for H in (Hq, Hkv, Hkv)]
+        ov = tm_heads(o_tmb, Hq, hq)
+        lc.attn_fwd_strided(qv, kv_, vv, causal=True, scale=scale, o=ov, lse=lse)
+        dov = tm_heads(xs["do"], Hq, hq)
+        gq, gk, gv = tm_heads(g_tm[0], Hq, hq), tm_heads(g_tm[1], Hkv, hkv), tm_heads(g_tm[2], Hkv, hkv)
+        ms = time_calls(torch, lambda: lc.attn_bwd_strided(qv, kv_, vv, ov, dov, lse, causal=True, scale=scale,
+                                                           workspace=ws, dq=gq, dk=gk, dv=gv))
+        out["token_major_backward"] = {"call": "attn_bwd_strided on shard 0's heads of token-major Q, K, V, O, dO",
+                                       "ms": round(ms, 4), "TFLOP/s": round(tflops(f_bwd, ms), 2),
+                                       "frac_peak": round(tflops(f_bwd, ms) / PEAK_BF16_TFLOPS, 4)}
+        del o_tmb, g_tm
         # the ring streamed into one running result (blocks one after another)
         o_acc = o_parts[0]
         q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))

@@ -193,6 +193,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int64_t N, int D, float scale, int causal, void* hip_stream);
 
 /*
+ * attn_bwd_strided -- attn_bwd on tensors given by element strides, so that
+ * the backward of a Ulysses shard reads Q, K, V, O, dO in the token-major
+ * layout the exchange delivers ([N, H, D] rows: token stride H*D, head
+ * stride D; "Million-Token-Kontexte im Training ...", section "Ulysses: Die
+ * Sequenz als Verteilungseinheit") and writes dQ, dK, dV the same way,
+ * without relayout passes -- the backward counterpart of attn_fwd_strided.
+ *
+ * q_strides: host array of 3 element strides (batch, head, token) shared by
+ * q, o, d_o and dq; kv_strides: the same for k, v, dk and dv.  The D
+ * elements of a row are contiguous; every stride keeps rows 16-byte aligned
+ * (a multiple of 8), token strides are >= D and < 2^24, and the rows of dq
+ * (dk, dv) under these strides must not overlap one another (ATTN_ERR_ALIAS).
+ * lse [B, Hq, N] and the workspace stay contiguous.  Outputs must not
+ * overlap the address ranges of the inputs or one another.  Results are
+ * bit-identical to attn_bwd on the same values.  Otherwise as attn_bwd.
+ */
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                     int64_t N, int D, float scale, int causal, const int64_t* q_strides,
+                     const int64_t* kv_strides, void* hip_stream);
+
+/*
  * attn_bwd_delta -- Dv_i = <dO_i, O_i> in fp32 for every query row: the
  * per-row term of dS that attn_bwd_block takes as an input.  o, d_o
  * [B, Hq, Nq, D] bf16 (o the final output of the forward, after every KV

@@ -28,6 +28,7 @@ __all__ = [
     "attn_partial_merge",
     "attn_bwd",
     "attn_bwd_workspace_size",
+    "attn_bwd_strided",
     "attn_bwd_delta",
     "attn_bwd_block",
     "attn_bwd_block_workspace_size",
@@ -78,6 +79,8 @@ _SIGS = {
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
     "attn_bwd_delta": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
+    "attn_bwd_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I,
+                              _P, _P, _P]),
     "head_to_seq_reduce": (_I, [_P, _I, _P, _I, _L, _I, _I, _P]),
     "attn_bwd_block_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd_block": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
@@ -333,6 +336,47 @@ def attn_bwd(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = 
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D, scale,
                           1 if causal else 0, _stream(q)))
+    return dq, dk, dv
+
+
+def attn_bwd_strided(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = None, workspace=None,
+                     dq=None, dk=None, dv=None):
+    """attn_bwd on [B, H, N, D] views with any batch / head / token strides
+    (the last dimension contiguous), e.g. heads of token-major [N, H, D]
+    shards: q, o, do (and dq) share one stride set, k, v (and dk, dv)
+    another.  dq, dk, dv default to new tensors with the strides of q and k.
+    Returns (dq, dk, dv)."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _need(t, name, torch.bfloat16, 4, strided=True)
+    _need(lse, "lse", torch.float32, 3)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must be shaped like q")
+    if tuple(k.shape) != (B, Hkv, N, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, N, D]")
+    if tuple(o.stride()) != tuple(q.stride()) or tuple(do.stride()) != tuple(q.stride()):
+        raise ValueError("o and do must have the strides of q")
+    if tuple(v.stride()) != tuple(k.stride()):
+        raise ValueError("k and v must have the same strides")
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dv is None else dv
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", k)):
+        _need(t, name, torch.bfloat16, 4, strided=True)
+        if tuple(t.shape) != tuple(ref.shape) or tuple(t.stride()) != tuple(ref.stride()):
+            raise ValueError(f"{name} must have the shape and strides of {'q' if ref is q else 'k'}")
+    need = attn_bwd_workspace_size(B, Hq, Hkv, N, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    arr = ctypes.c_int64 * 3
+    qs, ks = arr(*q.stride()[:3]), arr(*k.stride()[:3])
+    _check(lib().attn_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D, scale,
+                                  1 if causal else 0, qs, ks, _stream(q)))
     return dq, dk, dv
 
 

@@ -336,37 +336,54 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D) {
   return (size_t)lcattn::bwd_workspace_bytes(B, Hq, Hkv, N, N, D);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
-             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-             int64_t N, int D, float scale, int causal, void* hip_stream) {
+// attn_bwd and attn_bwd_strided: validation and launch.  Null strides:
+// contiguous [B, H, N, D] tensors.
+static int bwd_entry(const char* name, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                     int Hq, int Hkv, int64_t N, int D, float scale, int causal, const int64_t* q_strides,
+                     const int64_t* kv_strides, void* hip_stream) {
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv)
-    return fail(ATTN_ERR_NULL, "attn_bwd: tensor pointers must be non-null");
-  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "attn_bwd: sizes must be >= 1");
-  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "attn_bwd: Hkv=%d does not divide Hq=%d", Hkv, Hq);
-  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: D=%d (supported: 64, 128)", D);
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: scale must be > 0");
+    return fail(ATTN_ERR_NULL, "%s: tensor pointers must be non-null", name);
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
+  if (Hq % Hkv) return fail(ATTN_ERR_SHAPE, "%s: Hkv=%d does not divide Hq=%d", name, Hkv, Hq);
+  if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", name, D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(ATTN_ERR_UNSUPPORTED, "%s: scale must be > 0", name);
   int64_t nq_el, nk_el, nl;
   if (!elems(&nq_el, {B, Hq, N, D}) || !elems(&nk_el, {B, Hkv, N, D}) || !elems(&nl, {B, Hq, N}) ||
       nq_el > INT64_MAX / 8)
-    return fail(ATTN_ERR_SHAPE, "attn_bwd: tensor sizes overflow");
+    return fail(ATTN_ERR_SHAPE, "%s: tensor sizes overflow", name);
   if (N >= INT32_MAX || B > 65535 || Hq > 65535)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: N must be < 2^31, B and Hq <= 65535");
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: N must be < 2^31, B and Hq <= 65535", name);
   const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, N, D);
   if (!workspace || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "attn_bwd: workspace needs %zu bytes, got %zu", need, workspace_bytes);
-  const void* ptrs[11] = {q, k, v, o, d_o, lse, dq, dk, dv, workspace, nullptr};
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", name, need, workspace_bytes);
+  const void* ptrs[10] = {q, k, v, o, d_o, lse, dq, dk, dv, workspace};
   for (int i = 0; i < 10; ++i)
-    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_ALIGN, "attn_bwd: pointers must be 16-byte aligned");
-  const size_t qb = (size_t)nq_el * 2, kb = (size_t)nk_el * 2, lb = (size_t)nl * 4;
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
+  // byte extents from each base (the whole tensor when contiguous)
+  size_t qb = (size_t)nq_el * 2, kb = (size_t)nk_el * 2;
+  const size_t lb = (size_t)nl * 4;
+  const bool strided = q_strides || kv_strides;
+  if (strided) {
+    int64_t qsp, ksp;
+    int st;
+    if ((st = stride_check(name, "q", q_strides, B, Hq, N, D, 2, false, &qsp)) != ATTN_OK) return st;
+    if ((st = stride_check(name, "k/v", kv_strides, B, Hkv, N, D, 2, false, &ksp)) != ATTN_OK) return st;
+    // the gradients take the strides of their inputs: their rows must not overlap
+    if ((st = stride_check(name, "dq", q_strides, B, Hq, N, D, 2, true, &qsp)) != ATTN_OK) return st;
+    if ((st = stride_check(name, "dk/dv", kv_strides, B, Hkv, N, D, 2, true, &ksp)) != ATTN_OK) return st;
+    qb = (size_t)qsp * 2;
+    kb = (size_t)ksp * 2;
+  }
   const void* ins[6] = {q, k, v, o, d_o, lse};
   const size_t inb[6] = {qb, kb, kb, qb, qb, lb};
   const void* outs[4] = {dq, dk, dv, workspace};
   const size_t outb[4] = {qb, kb, kb, need};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
-      if (overlap(outs[i], outb[i], ins[j], inb[j])) return fail(ATTN_ERR_ALIAS, "attn_bwd: outputs overlap inputs");
+      if (overlap(outs[i], outb[i], ins[j], inb[j])) return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
     for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outb[i], outs[j], outb[j])) return fail(ATTN_ERR_ALIAS, "attn_bwd: outputs overlap");
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return fail(ATTN_ERR_ALIAS, "%s: outputs overlap", name);
   }
   lcattn::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -387,7 +404,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.Nk = N;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
-  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd launch");
+  if (strided)
+    for (int i = 0; i < 3; ++i) {
+      a.qs[i] = q_strides[i];
+      a.ks[i] = kv_strides[i];
+    }
+  char what[64];
+  snprintf(what, sizeof(what), "%s launch", name);
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), what);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+             int64_t N, int D, float scale, int causal, void* hip_stream) {
+  return bwd_entry("attn_bwd", q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, D, scale,
+                   causal, nullptr, nullptr, hip_stream);
+}
+
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                     int64_t N, int D, float scale, int causal, const int64_t* q_strides,
+                     const int64_t* kv_strides, void* hip_stream) {
+  if (!q_strides || !kv_strides) return fail(ATTN_ERR_NULL, "attn_bwd_strided: strides must be non-null");
+  return bwd_entry("attn_bwd_strided", q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
+                   D, scale, causal, q_strides, kv_strides, hip_stream);
 }
 
 int attn_bwd_delta(const void* o, const void* d_o, float* delta, int B, int Hq, int64_t Nq, int D,

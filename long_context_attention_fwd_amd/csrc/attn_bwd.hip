@@ -44,20 +44,25 @@ namespace lcattn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Dv_i = <dO_i, O_i> (fp32), one thread per 8 elements
+// Dv_i = <dO_i, O_i> (fp32), one thread per 8 elements; row n of head h of
+// batch b (grid z = b, y = h) at element b*s0 + h*s1 + n*s2 of o and d_o,
+// Dv contiguous [B, H, N]
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
                                                         const uint16_t* __restrict__ d_o,
-                                                        float* __restrict__ delta, long long rows) {
+                                                        float* __restrict__ delta, long long N, long long s0,
+                                                        long long s1, long long s2) {
   constexpr int U = D / 8;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = idx / U;
+  const long long n = idx / U;
   const int u = (int)(idx % U);
+  const long long b = blockIdx.z, h = blockIdx.y;
   float s = 0.f;
-  if (row < rows) {
-    const u32x4 x = ld_global16(o + row * D + 8 * u);
-    const u32x4 y = ld_global16(d_o + row * D + 8 * u);
+  if (n < N) {
+    const long long off = b * s0 + h * s1 + n * s2 + 8 * u;
+    const u32x4 x = ld_global16(o + off);
+    const u32x4 y = ld_global16(d_o + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       s += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   }
 #pragma unroll
   for (int off = U / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && u == 0) delta[row] = s;
+  if (n < N && u == 0) delta[(b * gridDim.y + h) * N + n] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -75,7 +80,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 constexpr int kDkdvWaves = 4;
 constexpr int kBQ = 64;   // query rows per tile
 
-template <int D, bool PARTIAL>
+// DENSE: contiguous [B, H, N, D] tensors (row strides D known at compile
+// time); else the strides of a.
+template <int D, bool PARTIAL, bool DENSE>
 __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a, float* __restrict__ dk_part,
                                                                        float* __restrict__ dv_part) {
   using T = LdsTile<D>;
@@ -105,11 +112,12 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   const int key = (int)(kw0 + c);         // this lane's key
   const float sl = a.scale * kLog2e;
 
-  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * Nk * D;
-  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * Nk * D;
   const long long hb = (bz * a.Hq + h) * Nq;
-  const uint16_t* qbase = a.q + hb * D;
-  const uint16_t* obase = a.d_o + hb * D;
+  const long long kst = DENSE ? D : a.ks[2], qst_rows = DENSE ? D : a.qs[2];  // row strides
+  const uint16_t* kbase = DENSE ? a.k + (bz * a.Hkv + kvh) * Nk * D : a.k + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* vbase = DENSE ? a.v + (bz * a.Hkv + kvh) * Nk * D : a.v + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* qbase = DENSE ? a.q + hb * D : a.q + bz * a.qs[0] + h * a.qs[1];
+  const uint16_t* obase = DENSE ? a.d_o + hb * D : a.d_o + bz * a.qs[0] + h * a.qs[1];
   const float* lbase = a.lse + hb;
   const float* dbase = a.delta + hb;
 
@@ -123,8 +131,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   float lv = 0.f;
   auto fetch = [&](int i) __attribute__((always_inline)) {
     const long long r0 = (first_tile + i) * kBQ;
-    qst.load(qbase, r0, Nq, tid);
-    ost.load(obase, r0, Nq, tid);
+    if constexpr (DENSE) {
+      qst.load(qbase, r0, Nq, tid);
+      ost.load(obase, r0, Nq, tid);
+    } else {
+      qst.load(qbase, r0, Nq, tid, qst_rows);
+      ost.load(obase, r0, Nq, tid, qst_rows);
+    }
     if (tid < 2 * kBQ) {
       long long row = r0 + (tid & (kBQ - 1));
       row = row < Nq ? row : Nq - 1;
@@ -147,8 +160,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   for (int t = 0; t < KT; ++t) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (key < Nk) {
-      x = ld_global16(kbase + (long long)key * D + 16 * t + 8 * grp);
-      y = ld_global16(vbase + (long long)key * D + 16 * t + 8 * grp);
+      x = ld_global16(kbase + (long long)key * kst + 16 * t + 8 * grp);
+      y = ld_global16(vbase + (long long)key * kst + 16 * t + 8 * grp);
     }
     kf[t] = as_bf16x8(x);
     vf[t] = as_bf16x8(y);
@@ -311,7 +324,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
           *reinterpret_cast<f32x4*>(dk_part + base) = wk;
           *reinterpret_cast<f32x4*>(dv_part + base) = wv;
         } else {
-          const long long base = ((bz * a.Hkv + kvh) * Nk + key) * D + d;
+          const long long base = ((bz * a.Hkv + kvh) * Nk + key) * D + d;  // fp32 accumulators
+          const long long obf = DENSE ? base : bz * a.ks[0] + kvh * a.ks[1] + key * a.ks[2] + d;  // bf16 dk, dv
           f32x4 wk = {k0, k1, k2, k3};
           f32x4 wv = {dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2], dv_acc[dbk][4 * j + 3]};
           if (a.dkv_mode != 0) {
@@ -325,8 +339,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
             *pv = wv;
           }
           if (a.dk) {
-            *reinterpret_cast<u32x2*>(a.dk + base) = pack_bf16x4_bits(wk[0], wk[1], wk[2], wk[3]);
-            *reinterpret_cast<u32x2*>(a.dv + base) = pack_bf16x4_bits(wv[0], wv[1], wv[2], wv[3]);
+            *reinterpret_cast<u32x2*>(a.dk + obf) = pack_bf16x4_bits(wk[0], wk[1], wk[2], wk[3]);
+            *reinterpret_cast<u32x2*>(a.dv + obf) = pack_bf16x4_bits(wv[0], wv[1], wv[2], wv[3]);
           }
         }
       }
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const float* __restrict__ dk_part,
                                                               const float* __restrict__ dv_part,
-                                                              long long kv_heads_total) {
+                                                              long long kv_heads_total, bool dense) {
   const int G = a.G;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // over kv_heads_total * Nk * D / 4
   const long long per_head = a.Nk * D / 4;
@@ -363,8 +377,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const f
     *pv = sv;
   }
   if (a.dk) {
-    *reinterpret_cast<u32x2*>(a.dk + idx * 4) = pack_bf16x4_bits(sk[0], sk[1], sk[2], sk[3]);
-    *reinterpret_cast<u32x2*>(a.dv + idx * 4) = pack_bf16x4_bits(sv[0], sv[1], sv[2], sv[3]);
+    long long obf = idx * 4;  // contiguous
+    if (!dense) {
+      const long long b = hk / a.Hkv, kvh = hk % a.Hkv, key = rem / (D / 4);
+      obf = b * a.ks[0] + kvh * a.ks[1] + key * a.ks[2] + 4 * (rem % (D / 4));
+    }
+    *reinterpret_cast<u32x2*>(a.dk + obf) = pack_bf16x4_bits(sk[0], sk[1], sk[2], sk[3]);
+    *reinterpret_cast<u32x2*>(a.dv + obf) = pack_bf16x4_bits(sv[0], sv[1], sv[2], sv[3]);
   }
 }
 
@@ -374,7 +393,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const f
 constexpr int kDqWaves = 8;
 constexpr int kBN = 64;
 
-template <int D, int HP>
+// DENSE: contiguous [B, H, N, D] tensors (row strides D known at compile
+// time, which keeps the kernel within its registers); else the strides of a.
+template <int D, int HP, bool DENSE>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   using T = SwzTile<D>;  // K tiles are read both ways, V tiles by rows: rows swizzle
   constexpr int KT = D / 16;
@@ -404,8 +425,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const int klim = (int)Nk;
   const float sl = a.scale * kLog2e;
   const long long hb = (bz * a.Hq + h) * Nq;
-  const uint16_t* kbase = a.k + (bz * a.Hkv + kvh) * Nk * D;
-  const uint16_t* vbase = a.v + (bz * a.Hkv + kvh) * Nk * D;
+  const uint16_t* kbase = DENSE ? a.k + (bz * a.Hkv + kvh) * Nk * D : a.k + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* vbase = DENSE ? a.v + (bz * a.Hkv + kvh) * Nk * D : a.v + bz * a.ks[0] + kvh * a.ks[1];
 
   // keys the workgroup can see
   long long kv_end = Nk;
@@ -414,7 +435,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const int n_sub = 2 * n_tiles;  // 32-key sub-tiles
 
   typename T::template AsyncLoader<NW> ld;
-  ld.init(wave, lane, false);
+  ld.init(wave, lane, false, DENSE ? D : a.ks[2]);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
     ld.load(buf, kbase, (long long)j * kBN, Nk, wave);
     ld.load(buf + T::BYTES, vbase, (long long)j * kBN, Nk, wave);
@@ -427,8 +448,10 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   for (int t = 0; t < KT; ++t) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (qrow < Nq) {
-      x = ld_global16(a.q + (hb + qrow) * D + 16 * t + 8 * grp);
-      y = ld_global16(a.d_o + (hb + qrow) * D + 16 * t + 8 * grp);
+      const long long off =
+          (DENSE ? (hb + qrow) * D : bz * a.qs[0] + h * a.qs[1] + qrow * a.qs[2]) + 16 * t + 8 * grp;
+      x = ld_global16(a.q + off);
+      y = ld_global16(a.d_o + off);
     }
     qf[t] = as_bf16x8(x);
     of[t] = as_bf16x8(y);
@@ -590,7 +613,8 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   }
 
   if (qrow < Nq) {
-    const long long base = (hb + qrow) * D;
+    const long long base = (hb + qrow) * D;                                // fp32 accumulator
+    const long long obf = DENSE ? base : bz * a.qs[0] + h * a.qs[1] + qrow * a.qs[2];  // bf16 dq
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -603,38 +627,62 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
           if (a.dq_mode == 2) g += *p;  // this KV block's part added to the running dQ
           *p = g;
         }
-        if (a.dq) *reinterpret_cast<u32x2*>(a.dq + base + d) = pack_bf16x4_bits(g[0], g[1], g[2], g[3]);
+        if (a.dq) *reinterpret_cast<u32x2*>(a.dq + obf + d) = pack_bf16x4_bits(g[0], g[1], g[2], g[3]);
       }
   }
 }
 
 template <int D>
-hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, hipStream_t stream) {
-  const long long threads = rows * (D / 8);
-  LCATTN_LAUNCH("bwd_delta_kernel", (bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                stream, o, d_o, delta, rows);
+hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, int B, int H, long long N,
+                        const long long (&st)[3], hipStream_t stream) {
+  const long long threads = N * (D / 8);
+  LCATTN_LAUNCH("bwd_delta_kernel", (bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256), (unsigned)H,
+                                                                (unsigned)B),
+                dim3(256), 0, stream, o, d_o, delta, N, st[0], st[1], st[2]);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
+hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
   hipError_t e;
+  BwdArgs a = a0;
+  const bool dense = a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0 && a.ks[0] == 0 && a.ks[1] == 0 && a.ks[2] == 0;
+  if (a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0) {
+    a.qs[2] = D;
+    a.qs[1] = a.Nq * D;
+    a.qs[0] = a.Hq * a.Nq * D;
+  }
+  if (a.ks[0] == 0 && a.ks[1] == 0 && a.ks[2] == 0) {
+    a.ks[2] = D;
+    a.ks[1] = a.Nk * D;
+    a.ks[0] = a.Hkv * a.Nk * D;
+  }
   if (a.o) {
-    e = launch_delta<D>(a.o, a.d_o, a.delta, (long long)B * a.Hq * a.Nq, stream);
+    e = launch_delta<D>(a.o, a.d_o, a.delta, B, a.Hq, a.Nq, a.qs, stream);
     if (e != hipSuccess) return e;
   }
   const dim3 kgrid((unsigned)((a.Nk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
   if (a.G == 1) {
-    LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, nullptr, nullptr);
+    if (dense)
+      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
+                    nullptr, nullptr);
+    else
+      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
+                    nullptr, nullptr);
   } else {
     float* dk_part = a.part;
     float* dv_part = dk_part + (long long)B * a.Hq * a.Nk * D;
-    LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a, dk_part, dv_part);
+    if (dense)
+      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
+                    dk_part, dv_part);
+    else
+      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
+                    dk_part, dv_part);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long slots = (long long)B * a.Hkv * a.Nk * D / 4;
     LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
-                  dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv);
+                  dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv, dense);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -642,12 +690,21 @@ hipError_t launch_d(const BwdArgs& a, int B, hipStream_t stream) {
   const long long span = (kDqWaves / HP) * 32;
   const int n_qt = (int)((a.Nq + span - 1) / span);
   dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
-  if (HP == 4)
-    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-  else if (HP == 2)
-    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-  else
-    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+  if (dense) {
+    if (HP == 4)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    else if (HP == 2)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    else
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+  } else {
+    if (HP == 4)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, false>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    else if (HP == 2)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2, false>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+    else
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1, false>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
+  }
   return hipGetLastError();
 }
 
@@ -672,7 +729,9 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream) {
 
 hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, int D,
                             hipStream_t stream) {
-  return D == 64 ? launch_delta<64>(o, d_o, delta, rows, stream) : launch_delta<128>(o, d_o, delta, rows, stream);
+  const long long st[3] = {0, 0, D};  // contiguous rows
+  return D == 64 ? launch_delta<64>(o, d_o, delta, 1, 1, rows, st, stream)
+                 : launch_delta<128>(o, d_o, delta, 1, 1, rows, st, stream);
 }
 
 }  // namespace lcattn

@@ -142,22 +142,23 @@ struct LdsTile {
   }
 
   // Register-staged tile load: NT threads fetch rows [r0, r0 + 64) of a
-  // row-major [rows_total, D] matrix into CH 16-byte registers each, then store
-  // them into the swizzled LDS tile.  Rows past rows_total read row
-  // rows_total - 1 (finite data that the callers mask).
+  // row-major [rows_total, D] matrix (rows rs elements apart) into CH 16-byte
+  // registers each, then store them into the swizzled LDS tile.  Rows past
+  // rows_total read row rows_total - 1 (finite data that the callers mask).
   template <int NT>
   struct Stage {
     static constexpr int CH = 64 * UNITS / NT;
     static_assert(CH >= 1 && 64 * UNITS % NT == 0, "threads must divide the tile");
     u32x4 r[CH];
-    __device__ void load(const uint16_t* g, long long r0, long long rows_total, int tid) {
+    // rows rs elements apart (rs = D: a contiguous matrix)
+    __device__ void load(const uint16_t* g, long long r0, long long rows_total, int tid, long long rs = D) {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int id = tid + i * NT;
         const int row = id / UNITS, u = id % UNITS;
         long long gr = r0 + row;
         gr = gr < rows_total ? gr : rows_total - 1;
-        r[i] = ld_global16(g + gr * D + 8 * u);
+        r[i] = ld_global16(g + gr * rs + 8 * u);
       }
     }
     __device__ void store(unsigned char* lds, int tid) const {

@@ -101,6 +101,11 @@ struct BwdArgs {
   int dkv_mode = 0;
   float* dk_acc = nullptr;
   float* dv_acc = nullptr;
+  // element strides (batch, head, token) of q, o, d_o and dq (qs) and of k,
+  // v, dk and dv (ks); the head dimension is contiguous.  Zero: contiguous
+  // [B, H, N, D].  lse, the delta, the fp32 accumulators and the workspace
+  // are always contiguous.
+  long long qs[3] = {0, 0, 0}, ks[3] = {0, 0, 0};
 };
 
 // Backward workspace: Dv per query row (fp32, padded to 64 floats), then, for

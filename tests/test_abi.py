@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
-              "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
+              "attn_bwd_strided", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
               "head_to_seq_relayout_batch", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -118,6 +118,36 @@ def strided(L, qs=(0, 128, 4096), ks=(0, 128, 512), os_=(0, 128, 512), **kw):
 ])
 def test_strided_rejects(L, kw, status):
     assert strided(L, **kw) == status
+    assert L.attn_last_error()
+
+
+def bwd_strided(L, qs=(0, 128, 1024), ks=(0, 128, 256), **kw):
+    """Token-major shard of 8 query heads on 2 key/value heads, N = 1024, D = 128:
+    q, o, d_o, dq rows 2 KiB apart, k, v, dk, dv rows 512 B apart (each tensor
+    spans 2 MiB or 512 KiB from its base)."""
+    arr = ctypes.c_int64 * 3
+    n = 1 << 22
+    args = dict(q=A, k=A + n, v=A + 2 * n, o=A + 3 * n, do=A + 4 * n, lse=A + 5 * n, dq=A + 6 * n, dk=A + 7 * n,
+                dv=A + 8 * n, ws=A + 9 * n, ws_bytes=1 << 24, B=1, Hq=8, Hkv=2, N=1024, D=128, scale=0.088,
+                causal=1, qs=arr(*qs) if qs else None, ks=arr(*ks) if ks else None, stream=None)
+    args.update(kw)
+    return L.attn_bwd_strided(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), 1), (dict(ks=None), 1), (dict(dq=None), 1),
+    (dict(qs=(0, -128, 1024)), 2),            # negative stride
+    (dict(qs=(0, 128, 1028)), 4),             # rows not 16-byte aligned
+    (dict(ks=(0, 0, 64)), 2),                 # token stride < D
+    (dict(ks=(0, 128, 1 << 24)), 3),          # token stride beyond the kernels' offsets
+    (dict(qs=(0, 64, 1024)), 5),              # dq rows of neighbouring heads overlap
+    (dict(ks=(0, 0, 256)), 5),                # dk rows of the two heads coincide
+    (dict(dq=A + (1 << 22) + 4096), 5),       # dq overlaps k
+    (dict(dv=A + (7 << 22) + 256), 5),        # dv overlaps dk
+    (dict(ws=None), 6), (dict(D=96), 3), (dict(Hkv=3), 2),
+])
+def test_bwd_strided_rejects(L, kw, status):
+    assert bwd_strided(L, **kw) == status
     assert L.attn_last_error()
 
 
