@@ -420,7 +420,9 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
     # overlap rather than each rank's causal work
     res = {"ranks": Pr, "chunk_tokens": C,
            "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair, in sequence"}
-    for scheme in SCHEMES:
+    # "<scheme>_grouped": the calls of a step that read the same key/value
+    # chunk (one per query chunk) as one attn_fwd_accumulate_group launch
+    for scheme, grouped in [(sc, g) for g in (False, True) for sc in SCHEMES]:
         t = [[0.0] * Pr for _ in range(Pr)]
         for r in range(Pr):
             qs = [cq[c] for c in rank_chunks(r, Pr, scheme)]
@@ -430,14 +432,15 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
             for st in range(Pr):
                 t[r][st] = time_calls(torch, lambda: ring_forward(qs, kv, r, Pr, C, o_acc=o_acc, lse_acc=lse,
                                                                   o_final=o_fin, scheme=scheme, scale=scale,
-                                                                  steps={st}))
+                                                                  steps={st}, grouped=grouped))
         crit = sum(max(t[r][s] for r in range(Pr)) for s in range(Pr))
         # a real ring runs the ranks on Pr GPUs at once: aggregate over the
         # ranks, and per rank (one GPU)
-        res[scheme] = {"critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
-                       "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
-                       "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
-                       "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
+        res[scheme + ("_grouped" if grouped else "")] = {
+            "critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
+            "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
+            "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
+            "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
     return res
 
 

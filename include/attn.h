@@ -118,6 +118,36 @@ int attn_fwd_accumulate(const void* q, const void* k, const void* v, float* o_ac
                         int64_t q_pos0, int64_t k_pos0, int first, void* hip_stream);
 
 /*
+ * attn_fwd_accumulate_group -- up to ATTN_MAX_FWD_GROUP independent
+ * attn_fwd_accumulate calls in one launch.  In a ring step a rank's query
+ * chunks each attend to the key/value chunk that just arrived ("Context
+ * Parallelism", section "So funktioniert Kontextparallelität"); their
+ * running results are distinct, so the calls are independent, and one
+ * launch gives the GPU all their workgroups at once.  Each entry of calls (a
+ * host array of n) is one call with the meaning of attn_fwd_accumulate's
+ * arguments; B, Hq, Hkv, D, scale and causal are shared.  No call's outputs
+ * (o_acc, lse_acc, o_final) may overlap another call's outputs or inputs
+ * (ATTN_ERR_ALIAS): calls that update the same running result must be
+ * separate, ordered launches.  Results are bit-identical to the calls made
+ * one by one.  Every entry is validated before anything is launched; the
+ * status names the first failing entry in attn_last_error.
+ */
+#define ATTN_MAX_FWD_GROUP 4
+typedef struct {
+  const void* q;    /* [B, Hq, Nq, D] bf16 */
+  const void* k;    /* [B, Hkv, Nk, D] bf16 */
+  const void* v;    /* [B, Hkv, Nk, D] bf16 */
+  float* o_acc;     /* [B, Hq, Nq, D] float, running output */
+  float* lse_acc;   /* [B, Hq, Nq] float, running log-sum-exp */
+  void* o_final;    /* optional bf16 [B, Hq, Nq, D]: the merged O */
+  int64_t Nq, Nk;   /* query rows, keys of the block */
+  int64_t q_pos0, k_pos0;  /* global positions of the first query and key */
+  int first;        /* nonzero: overwrite o_acc, lse_acc instead of merging */
+} attn_accumulate_call;
+int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
+                              int causal, void* hip_stream);
+
+/*
  * attn_fwd_splitkv_workspace_size -- bytes of device workspace attn_fwd_splitkv
  * needs for the same arguments: fp32 partial outputs and log-sum-exps of every
  * key range, n * B*Hq*Nq*(D + 1) floats for n ranges (n_splits > 0: that many;

@@ -23,6 +23,7 @@ __all__ = [
     "attn_fwd",
     "attn_fwd_strided",
     "attn_fwd_accumulate",
+    "attn_fwd_accumulate_group",
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_size",
     "attn_partial_merge",
@@ -68,10 +69,19 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _L = ctypes.c_int64
 _F = ctypes.c_float
+class AccumulateCall(ctypes.Structure):
+    """One entry of attn_fwd_accumulate_group (mirrors attn_accumulate_call)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o_acc", ctypes.c_void_p), ("lse_acc", ctypes.c_void_p), ("o_final", ctypes.c_void_p),
+                ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64), ("q_pos0", ctypes.c_int64),
+                ("k_pos0", ctypes.c_int64), ("first", ctypes.c_int)]
+
+
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P]),
     "attn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P, _P, _P, _P]),
     "attn_fwd_accumulate": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P]),
+    "attn_fwd_accumulate_group": (_I, [_P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _L, _I, _I, _I]),
     "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P, ctypes.c_size_t,
                               _P]),
@@ -249,6 +259,44 @@ def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, *, first: bool, causal: bool = 
                                      None if o_final is None else o_final.data_ptr(), B, Hq, Hkv, Nq, Nk, D, scale,
                                      1 if causal else 0, q_pos0, k_pos0, 1 if first else 0, _stream(q)))
     return o_acc, lse_acc
+
+
+def attn_fwd_accumulate_group(calls, *, causal: bool = True, scale: float | None = None):
+    """Independent attn_fwd_accumulate calls (1 to 4) in one launch.  calls:
+    dicts with q, k, v, o_acc, lse_acc, first and optionally o_final,
+    q_pos0, k_pos0 (meanings as in attn_fwd_accumulate); B, Hq, Hkv, D are
+    shared.  The calls must not write what another call reads or writes."""
+    torch = _torch()
+    calls = list(calls)
+    if not 1 <= len(calls) <= 4:
+        raise ValueError("a group holds 1 to 4 calls")
+    B, Hq, _, D = calls[0]["q"].shape
+    Hkv = calls[0]["k"].shape[1]
+    arr = (AccumulateCall * len(calls))()
+    for i, c in enumerate(calls):
+        q, k, v, o_acc, lse_acc = c["q"], c["k"], c["v"], c["o_acc"], c["lse_acc"]
+        _need(q, "q", torch.bfloat16, 4)
+        _need(k, "k", torch.bfloat16, 4)
+        _need(v, "v", torch.bfloat16, 4)
+        _need(o_acc, "o_acc", torch.float32, 4)
+        _need(lse_acc, "lse_acc", torch.float32, 3)
+        Nq, Nk = q.shape[2], k.shape[2]
+        if (q.shape[0], q.shape[1], q.shape[3]) != (B, Hq, D) or tuple(k.shape) != (B, Hkv, Nk, D) \
+                or tuple(v.shape) != tuple(k.shape):
+            raise ValueError("the calls of a group share B, Hq, Hkv and D")
+        if tuple(o_acc.shape) != (B, Hq, Nq, D) or tuple(lse_acc.shape) != (B, Hq, Nq):
+            raise ValueError("o_acc / lse_acc have the wrong shape")
+        of = c.get("o_final")
+        if of is not None:
+            _need(of, "o_final", torch.bfloat16, 4)
+            if tuple(of.shape) != (B, Hq, Nq, D):
+                raise ValueError("o_final has the wrong shape")
+        arr[i] = AccumulateCall(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_acc.data_ptr(), lse_acc.data_ptr(),
+                                None if of is None else of.data_ptr(), Nq, Nk, int(c.get("q_pos0", 0)),
+                                int(c.get("k_pos0", 0)), 1 if c["first"] else 0)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_fwd_accumulate_group(arr, len(calls), B, Hq, Hkv, D, scale, 1 if causal else 0,
+                                           _stream(calls[0]["q"])))
 
 
 def attn_fwd_splitkv_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, causal: bool = True,

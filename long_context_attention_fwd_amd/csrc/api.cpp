@@ -264,6 +264,68 @@ int attn_fwd_accumulate(const void* q, const void* k, const void* v, float* o_ac
   return hip_status(lcattn::launch_attn_fwd(a, B, D, true, static_cast<hipStream_t>(hip_stream)), "attn_fwd_accumulate launch");
 }
 
+static_assert(ATTN_MAX_FWD_GROUP == lcattn::kMaxFwdGroup, "group limit of the header and the kernel");
+
+int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
+                              int causal, void* hip_stream) {
+  const char* name = "attn_fwd_accumulate_group";
+  if (!calls) return fail(ATTN_ERR_NULL, "%s: null call array", name);
+  if (n < 1 || n > ATTN_MAX_FWD_GROUP) return fail(ATTN_ERR_SHAPE, "%s: n=%d calls (1 .. %d)", name, n, ATTN_MAX_FWD_GROUP);
+  if ((int64_t)B * n > 65535) return fail(ATTN_ERR_UNSUPPORTED, "%s: B * n must be <= 65535", name);
+  lcattn::FwdArgs args[ATTN_MAX_FWD_GROUP];
+  // byte ranges of every call's inputs (q, k, v) and outputs (o_acc, lse_acc, o_final)
+  const void* in_p[ATTN_MAX_FWD_GROUP][3];
+  size_t in_b[ATTN_MAX_FWD_GROUP][3];
+  const void* out_p[ATTN_MAX_FWD_GROUP][3];
+  size_t out_b[ATTN_MAX_FWD_GROUP][3];
+  for (int c = 0; c < n; ++c) {
+    const attn_accumulate_call& x = calls[c];
+    int st = fwd_check(name, x.q, x.k, x.v, x.o_acc, ATTN_FP32, x.lse_acc, B, Hq, Hkv, x.Nq, x.Nk, D, scale, causal,
+                       x.q_pos0, x.k_pos0, &args[c]);
+    int64_t nq_el, nk_el, nl;
+    elems(&nq_el, {B, Hq, x.Nq, D});
+    elems(&nk_el, {B, Hkv, x.Nk, D});
+    elems(&nl, {B, Hq, x.Nq});
+    if (st == ATTN_OK && x.o_final) {
+      if (!aligned16(x.o_final)) st = fail(ATTN_ERR_ALIGN, "%s: o_final must be 16-byte aligned", name);
+      const void* bufs[5] = {x.q, x.k, x.v, x.o_acc, x.lse_acc};
+      const size_t sizes[5] = {(size_t)nq_el * 2, (size_t)nk_el * 2, (size_t)nk_el * 2, (size_t)nq_el * 4,
+                               (size_t)nl * 4};
+      for (int i = 0; st == ATTN_OK && i < 5; ++i)
+        if (overlap(x.o_final, (size_t)nq_el * 2, bufs[i], sizes[i]))
+          st = fail(ATTN_ERR_ALIAS, "%s: o_final overlaps another argument", name);
+    }
+    if (st != ATTN_OK) {
+      char detail[sizeof(g_last_error)];
+      snprintf(detail, sizeof(detail), "%s", g_last_error);
+      return fail(st, "%s (call %d)", detail, c);
+    }
+    in_p[c][0] = x.q; in_b[c][0] = (size_t)nq_el * 2;
+    in_p[c][1] = x.k; in_b[c][1] = (size_t)nk_el * 2;
+    in_p[c][2] = x.v; in_b[c][2] = (size_t)nk_el * 2;
+    out_p[c][0] = x.o_acc; out_b[c][0] = (size_t)nq_el * 4;
+    out_p[c][1] = x.lse_acc; out_b[c][1] = (size_t)nl * 4;
+    out_p[c][2] = x.o_final; out_b[c][2] = x.o_final ? (size_t)nq_el * 2 : 0;
+    args[c].accum = x.first ? 0 : 1;
+    args[c].o_final = static_cast<uint16_t*>(x.o_final);
+  }
+  for (int c = 0; c < n; ++c)
+    for (int d = 0; d < n; ++d) {
+      if (c == d) continue;
+      for (int i = 0; i < 3; ++i) {
+        if (!out_p[c][i]) continue;
+        for (int j = 0; j < 3; ++j) {
+          if (overlap(out_p[c][i], out_b[c][i], in_p[d][j], in_b[d][j]))
+            return fail(ATTN_ERR_ALIAS, "%s: outputs of call %d overlap inputs of call %d", name, c, d);
+          if (out_p[d][j] && overlap(out_p[c][i], out_b[c][i], out_p[d][j], out_b[d][j]))
+            return fail(ATTN_ERR_ALIAS, "%s: outputs of calls %d and %d overlap", name, c, d);
+        }
+      }
+    }
+  return hip_status(lcattn::launch_attn_fwd_group(args, n, B, D, static_cast<hipStream_t>(hip_stream)),
+                    "attn_fwd_accumulate_group launch");
+}
+
 size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,
                                        int n_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1 || n_splits > kMaxSplits) return 0;

@@ -67,8 +67,11 @@ constexpr int kWaves = 8;      // two waves per SIMD: one's softmax overlaps the
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;         // keys per tile
 
+// The kernel body: workgroup number lin (already in XCD-aware order) of a
+// grid of nx query tiles x ny head groups x (splits x batch).
 template <int D, int QB, int HP, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, long long lin, long long nx,
+                                              long long ny) {
   using T = SwzTile<D>;
   constexpr int KT = D / 16;       // reduction steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
@@ -91,11 +94,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   // the first ranges of every query tile before the later, shorter ones
   // XCD-aware order: neighbouring query tiles of one head group share an XCD
   // and its L2 while they stream the same key/value tiles
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
   const int by = (int)(lin / nx % ny);
   const long long bzs = lin / (nx * ny);
   const int qt = n_qtiles - 1 - (int)(lin % nx);
+  if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;
   const long long bz = bzs % a.B;
@@ -472,6 +474,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
   }
 }
 
+template <int D, int QB, int HP, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  attn_fwd_body<D, QB, HP, OUT_F32>(a, n_qtiles, lin, nx, ny);
+}
+
+// Independent calls in one launch (a ring step's query chunks against one
+// key/value chunk): grid z = call * B + batch; call c covers
+// n_qtiles[c] <= gridDim.x query tiles.
+struct FwdGroup {
+  FwdArgs a[kMaxFwdGroup];
+  int n_qtiles[kMaxFwdGroup];
+};
+
+template <int D, int QB, int HP, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_group_kernel(FwdGroup g, int B) {
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const long long per_call = nx * ny * B;
+  const int c = (int)(lin / per_call);
+  attn_fwd_body<D, QB, HP, OUT_F32>(g.a[c], g.n_qtiles[c], lin - c * per_call, nx, ny);
+}
+
 template <int D, int QB, int HP, bool F32>
 hipError_t launch_cfg(const FwdArgs& a, int B, hipStream_t stream) {
   constexpr int SPAN = (kWaves / HP) * 32 * QB;
@@ -489,7 +515,42 @@ hipError_t launch_hp(const FwdArgs& a, int B, hipStream_t stream) {
   return launch_cfg<D, QB, 1, F32>(a, B, stream);
 }
 
+template <int D, int HP>
+hipError_t launch_group_hp(FwdGroup& g, int n, int B, hipStream_t stream) {
+  constexpr int SPAN = (kWaves / HP) * 32;
+  long long nx = 0;
+  for (int c = 0; c < n; ++c) {
+    g.n_qtiles[c] = (int)((g.a[c].Nq + SPAN - 1) / SPAN);
+    nx = std::max<long long>(nx, g.n_qtiles[c]);
+  }
+  dim3 grid((unsigned)nx, (unsigned)(g.a[0].Hq / HP), (unsigned)(B * n));
+  LCATTN_LAUNCH("attn_fwd_kernel_fp32out", (attn_fwd_group_kernel<D, 1, HP, true>), grid, dim3(kThreads), 0, stream,
+                g, B);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_attn_fwd_group(const FwdArgs* calls, int n, int B, int D, hipStream_t stream) {
+  FwdGroup g{};
+  for (int c = 0; c < n; ++c) {
+    FwdArgs a = calls[c];
+    a.B = B;
+    a.qs[2] = D; a.qs[1] = a.Nq * D; a.qs[0] = a.Hq * a.Nq * D;
+    a.ks[2] = D; a.ks[1] = a.Nk * D; a.ks[0] = a.Hkv * a.Nk * D;
+    a.os[2] = D; a.os[1] = a.Nq * D; a.os[0] = a.Hq * a.Nq * D;
+    g.a[c] = a;
+  }
+  const int G = calls[0].G;
+  if (D == 64) {
+    if (G % 4 == 0) return launch_group_hp<64, 4>(g, n, B, stream);
+    if (G % 2 == 0) return launch_group_hp<64, 2>(g, n, B, stream);
+    return launch_group_hp<64, 1>(g, n, B, stream);
+  }
+  if (G % 4 == 0) return launch_group_hp<128, 4>(g, n, B, stream);
+  if (G % 2 == 0) return launch_group_hp<128, 2>(g, n, B, stream);
+  return launch_group_hp<128, 1>(g, n, B, stream);
+}
 
 hipError_t launch_attn_fwd(const FwdArgs& a0, int B, int D, bool out_f32, hipStream_t stream) {
   FwdArgs a = a0;

@@ -56,6 +56,10 @@ struct FwdArgs {
 
 // (strides left at zero are filled in for contiguous [B, H, N, D] tensors)
 hipError_t launch_attn_fwd(const FwdArgs& a, int B, int D, bool out_f32, hipStream_t stream);
+// Up to kMaxFwdGroup independent fp32-output calls (contiguous tensors, the
+// same B, Hq, Hkv, D, scale and mask kind) in one launch.
+constexpr int kMaxFwdGroup = 4;
+hipError_t launch_attn_fwd_group(const FwdArgs* calls, int n, int B, int D, hipStream_t stream);
 
 // Forward over n_splits key ranges side by side (fp32 partials in o_parts /
 // lse_parts, [n_splits, B, Hq, Nq(, D)]), then their LSE merge into o (bf16)

@@ -55,7 +55,7 @@ def ring_schedule(rank: int, P: int, scheme: str = "zigzag", causal: bool = True
 
 def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_acc, o_final=None,
                  scheme: str = "zigzag", causal: bool = True, scale: float | None = None, steps=None,
-                 streams=None):
+                 streams=None, grouped: bool = False):
     """Run rank ``rank``'s ring on this GPU.
 
     q_chunks: the rank's two query chunks, [B, Hq, C, D] bf16 each.
@@ -67,6 +67,9 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
     i go to streams[i], so the two chunks' calls of a step run side by side
     (each chunk's calls stay in order: they update the same running result).
     The caller's stream waits for both at the end.
+    grouped: the calls of a step that read the same key/value chunk (one per
+    query chunk: independent running results) go out as one
+    ``attn_fwd_accumulate_group`` launch instead (streams is then unused).
     """
     import torch
 
@@ -76,6 +79,24 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
     mine = rank_chunks(rank, P, scheme)
     last = {qi: max(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
     first_call = {qi: min(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
+    if grouped:
+        from . import attn_fwd_accumulate_group
+        for step in range(P):
+            if steps is not None and step not in steps:
+                continue
+            for ki in (0, 1):
+                group = []
+                for i, (st, src, qi, kk) in enumerate(calls):
+                    if st != step or kk != ki:
+                        continue
+                    k, v = kv_chunks(src)[ki]
+                    kc = rank_chunks(src, P, scheme)[ki]
+                    group.append(dict(q=q_chunks[qi], k=k, v=v, o_acc=o_acc[qi], lse_acc=lse_acc[qi],
+                                      first=(i == first_call[qi]), q_pos0=mine[qi] * C, k_pos0=kc * C,
+                                      o_final=(o_final[qi] if o_final is not None and i == last[qi] else None)))
+                if group:
+                    attn_fwd_accumulate_group(group, causal=causal, scale=scale)
+        return
     caller = torch.cuda.current_stream(q_chunks[0].device)
     if streams is not None:
         fork = torch.cuda.Event()

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
-              "attn_bwd_strided", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
+              "attn_bwd_strided", "attn_fwd_accumulate_group", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
               "head_to_seq_relayout_batch", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -119,6 +119,28 @@ def strided(L, qs=(0, 128, 4096), ks=(0, 128, 512), os_=(0, 128, 512), **kw):
 def test_strided_rejects(L, kw, status):
     assert strided(L, **kw) == status
     assert L.attn_last_error()
+
+
+def group_call(L, calls, n=None, B=1, Hq=4, Hkv=1, D=128, scale=0.125, causal=1):
+    arr = (lc.AccumulateCall * max(1, len(calls)))(*[lc.AccumulateCall(*c) for c in calls])
+    return L.attn_fwd_accumulate_group(arr if calls else None, len(calls) if n is None else n, B, Hq, Hkv, D, scale,
+                                       causal, None)
+
+
+def test_accumulate_group_rejects(L):
+    # call: q, k, v, o_acc, lse_acc, o_final, Nq, Nk, q_pos0, k_pos0, first (Nq = Nk = 128: q, o_acc 256 KiB apart)
+    c0 = (A, B_, C_, D_, E_, None, 128, 128, 0, 0, 1)
+    c1 = (A + (1 << 20), B_, C_, D_ + (1 << 20), E_ + (1 << 20), None, 128, 128, 128, 0, 0)
+    assert group_call(L, []) == 1
+    assert group_call(L, [c0], n=0) == 2
+    assert group_call(L, [c0] * 5) == 2
+    assert group_call(L, [c0, (None,) + c1[1:]]) == 1
+    assert b"call 1" in L.attn_last_error()
+    assert group_call(L, [c0, c1[:3] + (D_ + 64,) + c1[4:]]) == 5          # o_acc of call 1 overlaps call 0's
+    assert group_call(L, [c0, c1[:3] + (A + 512,) + c1[4:]]) == 5          # o_acc of call 1 overlaps q of call 0
+    assert group_call(L, [c0, c1[:5] + (F_ + 8,) + c1[6:]]) == 4           # misaligned o_final
+    assert group_call(L, [c0], D=96) == 3
+    assert group_call(L, [c0] * 4, B=20000) == 3                           # grid z = B * n too large
 
 
 def bwd_strided(L, qs=(0, 128, 1024), ks=(0, 128, 256), **kw):

@@ -109,3 +109,69 @@ def test_ring_sharding_schemes(gpu, scheme, P, C, G, causal):
             rows = np.arange(c * C, (c + 1) * C)
             O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, causal, rows=rows)
             check_forward(f64_of(o[i]), f64_of(lse[i]), O, L, f"{scheme} P={P} rank {r} chunk {c}")
+
+
+@pytest.mark.parametrize("scheme", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("P,C,G,causal,D", [(4, 256, 4, True, 128), (2, 300, 1, True, 64), (4, 100, 2, False, 128)])
+def test_ring_grouped_launches_match_calls(gpu, scheme, P, C, G, causal, D):
+    """One attn_fwd_accumulate_group launch per (step, key chunk) gives, bit
+    for bit, what the calls made one by one give, for every rank."""
+    import torch
+    from long_context_attention_fwd_amd.ring import rank_chunks, ring_forward
+    N, Hkv = 2 * P * C, 1
+    d = make_qkv(1, Hkv * G, Hkv, N, D, seed=900 + P + C + G + D)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    s = sdpa_scale(D)
+
+    def chunk(t, c):
+        return t[:, :, c * C:(c + 1) * C].contiguous()
+
+    kv = {r: tuple((chunk(k, c), chunk(v, c)) for c in rank_chunks(r, P, scheme)) for r in range(P)}
+    for r in range(P):
+        mine = rank_chunks(r, P, scheme)
+        qs = [chunk(q, c) for c in mine]
+        outs = []
+        for grouped in (False, True):
+            o_acc = [poisoned((1, Hkv * G, C, D), torch.float32) for _ in mine]
+            lse = [poisoned((1, Hkv * G, C), torch.float32) for _ in mine]
+            o = [poisoned((1, Hkv * G, C, D), torch.bfloat16) for _ in mine]
+            ring_forward(qs, lambda src: kv[src], r, P, C, o_acc=o_acc, lse_acc=lse, o_final=o, scheme=scheme,
+                         scale=s, causal=causal, grouped=grouped)
+            torch.cuda.synchronize()
+            outs.append((o, lse, o_acc))
+        for i in range(2):
+            for a, b in zip(outs[0], outs[1]):
+                assert torch.equal(a[i].view(torch.int32) if a[i].dtype == torch.float32 else a[i].view(torch.int16),
+                                   b[i].view(torch.int32) if b[i].dtype == torch.float32 else b[i].view(torch.int16)), \
+                    f"{scheme} P={P} rank {r} chunk {i}"
+        for i, c in enumerate(mine):
+            rows = np.arange(c * C, (c + 1) * C)
+            O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, causal, rows=rows)
+            check_forward(f64_of(outs[1][0][i]), f64_of(outs[1][1][i]), O, L, f"grouped {scheme} rank {r} chunk {c}")
+
+
+def test_accumulate_group_uneven_calls(gpu):
+    """Calls of different lengths and positions in one launch (the grid covers
+    the longest): each equal to its own attn_fwd_accumulate."""
+    import torch
+    D, G = 128, 4
+    d = make_qkv(1, G, 1, 1500, D, seed=77)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    s = sdpa_scale(D)
+    spec = [(0, 700, 0, 900), (700, 1500, 300, 1200), (1400, 1500, 0, 1500)]  # (q0, q1, k0, k1)
+    ref, grp = [], []
+    for q0, q1, k0, k1 in spec:
+        args = dict(q=q[:, :, q0:q1].contiguous(), k=k[:, :, k0:k1].contiguous(), v=v[:, :, k0:k1].contiguous(),
+                    q_pos0=q0, k_pos0=k0)
+        o1 = poisoned((1, G, q1 - q0, D), torch.float32)
+        l1 = poisoned((1, G, q1 - q0), torch.float32)
+        lc.attn_fwd_accumulate(args["q"], args["k"], args["v"], o1, l1, first=True, scale=s, q_pos0=q0, k_pos0=k0)
+        ref.append((o1, l1))
+        o2 = poisoned((1, G, q1 - q0, D), torch.float32)
+        l2 = poisoned((1, G, q1 - q0), torch.float32)
+        grp.append(dict(args, o_acc=o2, lse_acc=l2, first=True))
+    lc.attn_fwd_accumulate_group(grp, scale=s)
+    torch.cuda.synchronize()
+    for (o1, l1), g in zip(ref, grp):
+        assert torch.equal(o1.view(torch.int32), g["o_acc"].view(torch.int32))
+        assert torch.equal(l1.view(torch.int32), g["lse_acc"].view(torch.int32))
