@@ -444,18 +444,23 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
     return res
 
 
-def time_calls(torch, fn, iters=10, warmup=3):
-    """Average ms of fn() over iters calls on the current stream (events)."""
+def time_calls(torch, fn, iters=10, warmup=3, rounds=3):
+    """ms of fn() on the current stream (events): the median over rounds of
+    the average over iters calls, so that a one-off stall of the box does not
+    set the figure."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters
+    avgs = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        avgs.append(e0.elapsed_time(e1) / iters)
+    return sorted(avgs)[len(avgs) // 2]
 
 
 def short_forward(lc, torch, dev, iters=20):
