@@ -8,8 +8,8 @@ tokens split P = 8 ways), with inputs already resident in HBM:
   1. seq_to_head_relayout_batch of Q, K, V, dO (all P shards, one launch)
      -- the all-to-all's data movement
   2. attn_fwd on shard 0 (4 query heads, 1 KV head, causal GQA, N = 32768)
-  3. the ring form of the same forward: 4 partial attn_fwd calls over
-     8192-key blocks (fp32 partials, run side by side on their own streams)
+  3. the ring form of the same forward: 4 partial attention calls over
+     8192-key blocks (fp32 partials, one attn_fwd_accumulate_group launch)
      + attn_partial_merge
   4. attn_bwd on shard 0 (from step 2's O and LSE)
   5. head_to_seq_relayout_batch of O, dQ, dK, dV (one launch)
@@ -157,7 +157,10 @@ def main():
     ws = torch.empty(lc.attn_bwd_workspace_size(1, hq, hkv, N, D), dtype=torch.uint8, device=dev)
     scale = w.scale
     stream = torch.cuda.current_stream(dev)
-    ring_streams = [torch.cuda.Stream(dev) for _ in range(n_blk)]  # default priority
+    # the key/value blocks of the ring (views of shard 0's head-major K, V:
+    # contiguous, as a ring step receives them, since a shard has one KV head)
+    ring_blocks = [(a, heads["k"][0:1, :, a:a + blk], heads["v"][0:1, :, a:a + blk]) for a in range(0, N, blk)]
+    assert all(kb.is_contiguous() and vb.is_contiguous() for _, kb, vb in ring_blocks)
 
     names = ["relayout_in", "fwd", "ring_partials", "merge", "bwd", "relayout_out"]
     ev = {n: [] for n in names}
@@ -179,21 +182,14 @@ def main():
         q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
         lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
         mark()
-        # The ring's partials, one per KV block [a, a + blk).  All blocks are
-        # resident on this GPU and independent, so they run side by side on
-        # their own streams (a late block has work only for the last queries
-        # and alone would leave most CUs idle); the merge waits for all.
-        fork = torch.cuda.Event()
-        fork.record(stream)
-        for i, a in enumerate(range(0, N, blk)):
-            side = ring_streams[i]
-            side.wait_event(fork)
-            with torch.cuda.stream(side):
-                lc.attn_fwd(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], causal=True, scale=scale, k_pos0=a,
-                            out_dtype=torch.float32, o=o_parts[i], lse=lse_parts[i])
-            join = torch.cuda.Event()
-            join.record(side)
-            stream.wait_event(join)
+        # The ring's partials, one per KV block [a, a + blk), fp32 O and LSE
+        # each.  All blocks are resident on this GPU and the partials are
+        # independent, so the four calls go out as one grouped launch (a late
+        # block has work only for the last queries and alone would leave most
+        # CUs idle); the merge follows.
+        lc.attn_fwd_accumulate_group(
+            [dict(q=q0, k=kb, v=vb, o_acc=o_parts[i], lse_acc=lse_parts[i], first=True, k_pos0=a)
+             for i, (a, kb, vb) in enumerate(ring_blocks)], causal=True, scale=scale)
         mark()
         lc.attn_partial_merge(o_parts, lse_parts, o=o_ring, lse=lse_ring)
         mark()
@@ -264,11 +260,12 @@ def main():
     # algorithmic work of all its launches / its total time.  The backward's
     # five counted contractions are S, dP, dV, dK (dK/dV kernel) and dQ (dQ
     # kernel); the dQ kernel's recomputed S and dP are not counted.
-    OVERLAPPED = {"attn_fwd_kernel_fp32out"}
+    # kernels whose launches share the GPU with one another (none since the
+    # ring partials became one grouped launch)
+    OVERLAPPED = set()
     alg = {
         "attn_fwd_kernel": ("TFLOP/s", args.steps * f_fwd),
-        # the ring partials overlap one another, so their summed kernel time
-        # exceeds the wall time of that phase (see phases.ring_partials_x4)
+        # the ring partials: one grouped launch of four fp32-output calls
         "attn_fwd_kernel_fp32out": ("TFLOP/s", args.steps * f_ring),
         "bwd_dkdv_kernel": ("TFLOP/s", args.steps * 0.8 * f_bwd),
         "bwd_dq_kernel": ("TFLOP/s", args.steps * 0.2 * f_bwd),

@@ -87,3 +87,24 @@ def test_ring_blocks_32k(gpu):
              for a, b in zip(bounds[:-1], bounds[1:])]
     Om, Lm = oracle.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
     assert np.abs(Om - O).max() < 1e-12 and np.abs(Lm - L).max() < 1e-12
+
+
+def test_ring_blocks_32k_grouped_partials(gpu):
+    """The four 8192-key partials of the ring workload from one
+    attn_fwd_accumulate_group launch (the bench step's ring leg): bit-identical
+    to four attn_fwd calls, and merged within the gates of the full forward."""
+    import torch
+    w = WORKLOADS["ring_blocks_32k"]
+    d = make_workload_inputs(w)
+    q, k, v = (to_dev(d[x]) for x in "qkv")
+    blk = w.N // w.kv_blocks
+    bounds = [i * blk for i in range(w.kv_blocks + 1)]
+    o_ref, lse_ref = ring_partials(q, k, v, bounds, w.scale, torch.float32)
+    o_parts = poisoned(tuple(o_ref.shape), torch.float32)
+    lse_parts = poisoned(tuple(lse_ref.shape), torch.float32)
+    lc.attn_fwd_accumulate_group(
+        [dict(q=q, k=k[:, :, a:b].contiguous(), v=v[:, :, a:b].contiguous(), o_acc=o_parts[i], lse_acc=lse_parts[i],
+              first=True, k_pos0=a) for i, (a, b) in enumerate(zip(bounds[:-1], bounds[1:]))], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_parts.view(torch.int32), o_ref.view(torch.int32))
+    assert torch.equal(lse_parts.view(torch.int32), lse_ref.view(torch.int32))
