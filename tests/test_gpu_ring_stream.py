@@ -150,12 +150,13 @@ def test_ring_grouped_launches_match_calls(gpu, scheme, P, C, G, causal, D):
             check_forward(f64_of(outs[1][0][i]), f64_of(outs[1][1][i]), O, L, f"grouped {scheme} rank {r} chunk {c}")
 
 
-def test_accumulate_group_uneven_calls(gpu):
+@pytest.mark.parametrize("B", [1, 2])
+def test_accumulate_group_uneven_calls(gpu, B):
     """Calls of different lengths and positions in one launch (the grid covers
     the longest): each equal to its own attn_fwd_accumulate."""
     import torch
     D, G = 128, 4
-    d = make_qkv(1, G, 1, 1500, D, seed=77)
+    d = make_qkv(B, G, 1, 1500, D, seed=77 + B)
     q, k, v = (to_dev(d[n]) for n in "qkv")
     s = sdpa_scale(D)
     spec = [(0, 700, 0, 900), (700, 1500, 300, 1200), (1400, 1500, 0, 1500)]  # (q0, q1, k0, k1)
@@ -163,12 +164,12 @@ def test_accumulate_group_uneven_calls(gpu):
     for q0, q1, k0, k1 in spec:
         args = dict(q=q[:, :, q0:q1].contiguous(), k=k[:, :, k0:k1].contiguous(), v=v[:, :, k0:k1].contiguous(),
                     q_pos0=q0, k_pos0=k0)
-        o1 = poisoned((1, G, q1 - q0, D), torch.float32)
-        l1 = poisoned((1, G, q1 - q0), torch.float32)
+        o1 = poisoned((B, G, q1 - q0, D), torch.float32)
+        l1 = poisoned((B, G, q1 - q0), torch.float32)
         lc.attn_fwd_accumulate(args["q"], args["k"], args["v"], o1, l1, first=True, scale=s, q_pos0=q0, k_pos0=k0)
         ref.append((o1, l1))
-        o2 = poisoned((1, G, q1 - q0, D), torch.float32)
-        l2 = poisoned((1, G, q1 - q0), torch.float32)
+        o2 = poisoned((B, G, q1 - q0, D), torch.float32)
+        l2 = poisoned((B, G, q1 - q0), torch.float32)
         grp.append(dict(args, o_acc=o2, lse_acc=l2, first=True))
     lc.attn_fwd_accumulate_group(grp, scale=s)
     torch.cuda.synchronize()
