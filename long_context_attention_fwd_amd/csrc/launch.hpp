@@ -10,17 +10,18 @@
 
 namespace lcattn {
 
-// out[a, b, :] = in[b, a, :], rows of row_bytes (a power-of-two multiple of 16).
-hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned Bn, unsigned row_bytes,
-                                 unsigned rep, hipStream_t stream);
-// The same for up to kMaxRelayoutBatch tensors with rows of one size, in one launch.
+// out[a * rep + i, b, :] = in[b, a, :] (i < rep), rows of row_bytes (a
+// power-of-two multiple of 16), for up to kMaxRelayoutBatch tensors with rows
+// of one size, in one launch.
 constexpr int kMaxRelayoutBatch = 8;
 struct TransposeJob {
   const void* in;
   void* out;
   unsigned A, Bn, rep;
 };
-hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned row_bytes, hipStream_t stream);
+// a_fast: a-tiles fastest in the workgroup order (else b-tiles fastest)
+hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned row_bytes, bool a_fast,
+                                       hipStream_t stream);
 // out[b, a, :] = sum over i < rep of in[a * rep + i, b, :] (bf16 out)
 hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long long A, long long Bn, int D, int rep,
                                hipStream_t stream);

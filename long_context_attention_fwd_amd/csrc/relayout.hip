@@ -32,13 +32,16 @@ struct RelayoutJob {
   const void* in;
   void* out;
   unsigned A, Bn, rep;
-  unsigned nbt;    // b-tiles per a-tile
+  unsigned nbt, nat;  // b-tiles, a-tiles
   unsigned first;  // first workgroup of this job
 };
 struct RelayoutBatch {
   RelayoutJob job[kMaxRelayoutBatch];
   int n;
   unsigned units_log2, ta_log2, tb_log2;
+  // tile order within a job: a-tiles fastest (else b-tiles fastest); the
+  // launcher picks the order that walks the token-major side sequentially
+  unsigned a_fast;
 };
 
 // out[a * rep + i, b, :] = in[b, a, :] (i < rep) for rows of 2^units_log2
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kRelayoutThreads) void transpose_rows_kernel(Relayo
   const unsigned A = J.A, Bn = J.Bn, rep = J.rep, nbt = J.nbt;
   const unsigned units_log2 = jobs.units_log2, ta_log2 = jobs.ta_log2, tb_log2 = jobs.tb_log2;
   const unsigned w = blockIdx.x - J.first;
-  const unsigned bt = w % nbt, at = w / nbt;
+  const unsigned bt = jobs.a_fast ? w / J.nat : w % nbt, at = jobs.a_fast ? w % J.nat : w / nbt;
   const unsigned a0 = at << ta_log2, b0 = bt << tb_log2;
   const unsigned umask = (1u << units_log2) - 1u, tbmask = (1u << tb_log2) - 1u;
   const unsigned per = 1u << (ta_log2 + tb_log2 + units_log2);  // units in the tile
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(256) void sum_replicas_kernel(const void* __restric
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + idx * 8));
 }
 
-hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned row_bytes, hipStream_t stream) {
+hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned row_bytes, bool a_fast,
+                                       hipStream_t stream) {
   unsigned units = row_bytes / 16, lg = 0;
   while ((1u << lg) < units) ++lg;
   // 4 x 4 rows, with more b rows when rows are short, so a tile is at least
@@ -138,6 +142,7 @@ hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned
   b.units_log2 = lg;
   b.ta_log2 = ta_lg;
   b.tb_log2 = tb_lg;
+  b.a_fast = a_fast ? 1u : 0u;
   unsigned long long blocks = 0;
   for (int j = 0; j < n; ++j) {
     RelayoutJob& J = b.job[j];
@@ -147,20 +152,15 @@ hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned
     J.Bn = jobs[j].Bn;
     J.rep = jobs[j].rep;
     J.nbt = (J.Bn + (1u << tb_lg) - 1) >> tb_lg;
+    J.nat = (J.A + (1u << ta_lg) - 1) >> ta_lg;
     J.first = (unsigned)blocks;
-    blocks += (unsigned long long)J.nbt * ((J.A + (1u << ta_lg) - 1) >> ta_lg);
+    blocks += (unsigned long long)J.nbt * J.nat;
   }
   if (blocks == 0) return hipSuccess;
   if (blocks > 0xFFFFFFFFull) return hipErrorInvalidValue;
   LCATTN_LAUNCH("transpose_rows_kernel", transpose_rows_kernel, dim3((unsigned)blocks), dim3(kRelayoutThreads), 0,
                 stream, b);
   return hipGetLastError();
-}
-
-hipError_t launch_transpose_rows(const void* in, void* out, unsigned A, unsigned Bn, unsigned row_bytes,
-                                 unsigned rep, hipStream_t stream) {
-  const TransposeJob job{in, out, A, Bn, rep};
-  return launch_transpose_rows_batch(&job, 1, row_bytes, stream);
 }
 
 hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long long A, long long Bn, int D, int rep,
