@@ -443,7 +443,7 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
 
 def time_calls(torch, fn, iters=10, warmup=3, rounds=3):
     """ms of fn() on the current stream (events): the median over rounds of
-    the average over iters calls, so that a one-off stall of the box does not
+    the average over iters calls, so that a one-off stall of the machine does not
     set the figure."""
     for _ in range(warmup):
         fn()
