@@ -436,9 +436,18 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
 
   typename T::template AsyncLoader<NW> ld;
   ld.init(wave, lane, false, DENSE ? D : a.ks[2]);
+  // the wave index in a scalar register: the LDS side of a direct load is
+  // then scalar arithmetic; full tiles skip the row clamping
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    ld.load(buf, kbase, (long long)j * kBN, Nk, wave);
-    ld.load(buf + T::BYTES, vbase, (long long)j * kBN, Nk, wave);
+    const long long r0 = (long long)j * kBN;
+    if (r0 + kBN <= Nk) {
+      ld.load_full(buf, kbase, r0, wave_s);
+      ld.load_full(buf + T::BYTES, vbase, r0, wave_s);
+    } else {
+      ld.load(buf, kbase, r0, Nk, wave_s);
+      ld.load(buf + T::BYTES, vbase, r0, Nk, wave_s);
+    }
   };
   if (n_tiles > 0) issue(0, smem0);
 
