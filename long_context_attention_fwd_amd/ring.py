@@ -53,6 +53,22 @@ def ring_schedule(rank: int, P: int, scheme: str = "zigzag", causal: bool = True
     return calls
 
 
+def ring_groups(rank: int, P: int, scheme: str = "zigzag", causal: bool = True):
+    """The launches of one rank's ring when the calls of a step that read the
+    same key/value chunk go out together: a list of groups in launch order,
+    each a list of (index into ring_schedule's calls, call).  A group holds at
+    most one call per query chunk (their running results are distinct, so the
+    calls are independent), and every query chunk's calls keep their order."""
+    calls = ring_schedule(rank, P, scheme, causal)
+    groups = []
+    for step in range(P):
+        for ki in (0, 1):
+            g = [(i, c) for i, c in enumerate(calls) if c[0] == step and c[3] == ki]
+            if g:
+                groups.append(g)
+    return groups
+
+
 def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_acc, o_final=None,
                  scheme: str = "zigzag", causal: bool = True, scale: float | None = None, steps=None,
                  streams=None, grouped: bool = False):
@@ -81,21 +97,17 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
     first_call = {qi: min(i for i, c in enumerate(calls) if c[2] == qi) for qi in (0, 1)}
     if grouped:
         from . import attn_fwd_accumulate_group
-        for step in range(P):
-            if steps is not None and step not in steps:
+        for g in ring_groups(rank, P, scheme, causal):
+            if steps is not None and g[0][1][0] not in steps:
                 continue
-            for ki in (0, 1):
-                group = []
-                for i, (st, src, qi, kk) in enumerate(calls):
-                    if st != step or kk != ki:
-                        continue
-                    k, v = kv_chunks(src)[ki]
-                    kc = rank_chunks(src, P, scheme)[ki]
-                    group.append(dict(q=q_chunks[qi], k=k, v=v, o_acc=o_acc[qi], lse_acc=lse_acc[qi],
-                                      first=(i == first_call[qi]), q_pos0=mine[qi] * C, k_pos0=kc * C,
-                                      o_final=(o_final[qi] if o_final is not None and i == last[qi] else None)))
-                if group:
-                    attn_fwd_accumulate_group(group, causal=causal, scale=scale)
+            group = []
+            for i, (step, src, qi, ki) in g:
+                k, v = kv_chunks(src)[ki]
+                kc = rank_chunks(src, P, scheme)[ki]
+                group.append(dict(q=q_chunks[qi], k=k, v=v, o_acc=o_acc[qi], lse_acc=lse_acc[qi],
+                                  first=(i == first_call[qi]), q_pos0=mine[qi] * C, k_pos0=kc * C,
+                                  o_final=(o_final[qi] if o_final is not None and i == last[qi] else None)))
+            attn_fwd_accumulate_group(group, causal=causal, scale=scale)
         return
     caller = torch.cuda.current_stream(q_chunks[0].device)
     if streams is not None:

@@ -54,3 +54,43 @@ def test_zigzag_balances_every_step(P):
     crit_c = sum(max(c[r][s] for r in range(P)) for s in range(P))
     assert crit_z * P == total
     assert crit_c > crit_z
+
+
+@pytest.mark.parametrize("scheme", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_grouped_launches(scheme, P, causal):
+    """The grouped launches of a ring: every call exactly once; a group holds
+    calls of one step that read one key/value chunk, at most one per query
+    chunk (independent running results); each query chunk's calls keep the
+    order of the ungrouped schedule."""
+    from long_context_attention_fwd_amd.ring import ring_groups
+    for r in range(P):
+        calls = ring_schedule(r, P, scheme, causal)
+        groups = ring_groups(r, P, scheme, causal)
+        flat = [i for g in groups for i, _ in g]
+        assert sorted(flat) == list(range(len(calls)))
+        for g in groups:
+            assert 1 <= len(g) <= 2
+            assert len({c[0] for _, c in g}) == 1 and len({c[3] for _, c in g}) == 1  # one step, one KV chunk
+            assert len({c[2] for _, c in g}) == len(g)  # distinct query chunks
+            assert all(calls[i] == c for i, c in g)
+        for qi in (0, 1):
+            order = [i for i in flat if calls[i][2] == qi]
+            assert order == sorted(order)
+
+
+def test_zigzag_groups_per_step():
+    """Zigzag over 4 ranks (rank r holds chunks r and 7 - r): at step 0 the
+    two query chunks share the early key chunk (one launch of two) and the
+    late chunk attends to itself (one more); at step s >= 1 rank r receives
+    the chunks of rank r - s, and both query chunks see one of them (one
+    launch of two) when s <= r, else only the late query chunk sees both
+    (two launches that update the same running result, in order)."""
+    from long_context_attention_fwd_amd.ring import ring_groups
+    for r in range(4):
+        groups = ring_groups(r, 4, "zigzag", True)
+        sizes = [[len(g) for g in groups if g[0][1][0] == step] for step in range(4)]
+        assert sizes[0] == [2, 1]
+        for step in range(1, 4):
+            assert sizes[step] == ([2] if step <= r else [1, 1]), (r, step, sizes)
