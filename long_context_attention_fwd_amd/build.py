@@ -27,10 +27,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 # The forward's row maximum is a chain of fmaxf; without NaN semantics the
-# compiler drops the quieting of each operand (NaN inputs still reach the
-# output through exp2 and the products).  Without signed zeros it drops the
-# 0 + x that starts each partial row sum (the sign of a zero sum does not
-# matter: a row's sum is positive or the row is empty).
+# compiler drops the quieting of each operand.  The row maximum may then skip
+# a NaN score, but the NaN still reaches the row through exp2, the row sum and
+# the products, and the epilogue decides whether a row is empty from key
+# positions, never from the (then NaN) sum; the GPU tests feed NaN and Inf
+# inputs.  Without signed zeros the compiler drops the 0 + x that starts each
+# partial row sum (the sign of a zero sum does not matter: a row's sum is
+# positive or the row is empty).
 PER_FILE = {"attn_fwd.hip": ["-fno-honor-nans", "-fno-signed-zeros"]}
 
 

@@ -420,8 +420,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, lo
   {
     const long long row = wq0 + c;
     const float l = l_run + __shfl_xor(l_run, 32);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const float lse = l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
+    // A row is empty (O = 0, LSE = -inf) when the first key of this call's
+    // range is past the end of the keys or masked for it: decided from
+    // positions, not from l, so that NaN scores (l = NaN) give a NaN row
+    // instead of the empty-row result.
+    const int kfirst = kBN * j0;
+    const bool has_key = kfirst < klim && (!a.causal || kfirst - qrow <= dpos);
+    const float inv = has_key ? 1.0f / l : 0.f;
+    const float lse = has_key ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
     if (row < a.Nq) {
       const long long obase = split * a.part_stride + bz * a.os[0] + h * a.os[1] + row * a.os[2];
       const long long lidx = split * (a.part_stride / D) + (bz * a.Hq + h) * a.Nq + row;
@@ -431,12 +437,21 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, lo
       float w_old = 0.f, w_new = inv, lse_out = lse;
       if (OUT_F32 && a.accum) {
         const float l_old = a.lse[lidx];  // read by both lane groups before either writes
-        if (lse == -INFINITY) {
+        // This file is compiled without NaN semantics, under which the
+        // compiler may turn x == -inf into !(x > -inf) (true for NaN) or
+        // lse - max(l_old, lse) into min(0, lse - l_old) (which drops a NaN).
+        // So the emptiness of this call comes from key positions, that of
+        // the running result from its bit pattern, and the maximum from an
+        // opaque instruction: a NaN on either side stays NaN.
+        unsigned old_bits;
+        asm("v_mov_b32 %0, %1" : "=v"(old_bits) : "v"(l_old));
+        if (!has_key) {
           w_old = 1.f;
           w_new = 0.f;
           lse_out = l_old;
-        } else if (l_old != -INFINITY) {
-          const float M = fmaxf(l_old, lse);
+        } else if (old_bits != 0xff800000u) {  // the running result is not empty
+          float M;
+          asm("v_max_f32 %0, %1, %2" : "=v"(M) : "v"(l_old), "v"(lse));
           const float e_old = fast_exp2((l_old - M) * kLog2e), e_new = fast_exp2((lse - M) * kLog2e);
           const float r = 1.0f / (e_old + e_new);
           w_old = e_old * r;

@@ -9,7 +9,7 @@
 //   LSE = M + ln sum_b exp(LSE_b - M),  M = max_b LSE_b,
 //   O   = sum_b exp(LSE_b - LSE) O_b.
 // Parts with LSE_b = -inf weigh zero; rows empty in every part give O = 0,
-// LSE = -inf.
+// LSE = -inf.  A part with a NaN LSE makes the merged row NaN.
 //
 // Kernel: HBM bound.  One thread per (row, 8 consecutive head-dim elements);
 // the n_parts LSE values of a row are read by all of the row's threads (they
@@ -36,7 +36,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const void* __rest
   if (row >= rows) return;
 
   float m = -INFINITY;
-  for (int b = 0; b < n_parts; ++b) m = fmaxf(m, lse_parts[(long long)b * rows + row]);
+  bool nan = false;
+  for (int b = 0; b < n_parts; ++b) {
+    const float lb = lse_parts[(long long)b * rows + row];
+    nan |= lb != lb;
+    m = fmaxf(m, lb);  // ignores NaN operands
+  }
+  // a NaN part (NaN inputs reached it) makes the row NaN, also when every
+  // other part is empty: reference 0 lets exp(NaN - 0) carry it through
+  if (nan && m == -INFINITY) m = 0.f;
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float out_lse = -INFINITY;

@@ -79,3 +79,37 @@ def grad_rel_err(g_gpu, g_ref) -> float:
     g_gpu = np.asarray(g_gpu, dtype=np.float64)
     den = float(np.abs(g_ref).max())
     return float(np.abs(g_gpu - g_ref).max()) / (den if den > 0 else 1.0)
+
+
+def oracle_full_lse_delta(q, k, v, do, scale, causal=True, workers=None, chunk=2048):
+    """The oracle's fp64 LSE and Dv_i = <dO_i, O_i> for every query row of
+    every head, from ``oracle.attention_forward`` run over (head, row chunk)
+    tasks in a thread pool (rows are independent under the definition).
+    BLAS is held to one thread per task so the tasks run side by side.
+    q, k, v, do: float64 arrays [B, H, N, D] (decoded once by the caller).
+    Returns (lse [B, Hq, N], dv [B, Hq, N])."""
+    import concurrent.futures as cf
+    import os
+    from threadpoolctl import threadpool_limits
+
+    B, Hq, N, _ = q.shape
+    G = Hq // k.shape[1]
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    tasks = [(b, h, r0) for b in range(B) for h in range(Hq) for r0 in range(0, N, chunk)]
+    tasks.sort(key=lambda t: -t[2])  # longest causal rows first
+    lse = np.empty((B, Hq, N))
+    dv = np.empty((B, Hq, N))
+
+    def run(t):
+        b, h, r0 = t
+        rows = np.arange(r0, min(N, r0 + chunk))
+        kh = h // G
+        O, L = oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, kh:kh + 1], v[b:b + 1, kh:kh + 1],
+                                        scale, causal, rows=rows)
+        lse[b, h, rows] = L[0, 0]
+        dv[b, h, rows] = np.einsum("nd,nd->n", do[b, h, rows], O[0, 0])
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(run, tasks))
+    return lse, dv

@@ -160,3 +160,60 @@ def test_bwd_ulysses_shard_32k_sampled(gpu):
     e_dk = grad_rel_err(f64_of(dk), rk)
     e_dv = grad_rel_err(f64_of(dv), rv)
     assert max(e_dq, e_dk, e_dv) <= GRAD_REL_TOL, (e_dq, e_dk, e_dv)
+
+
+def test_bwd_train_64k_full_do(gpu):
+    """N = 65536, H = 8, D = 128 with the full dO: dQ at the 128 sampled query
+    rows and dK, dV at the key rows with the same 128 indices, against the
+    oracle with its own fp64 LSE and Dv for every query row (each sampled key
+    row is reached by its own query row and every later one, up to 65536
+    terms per element of dK and dV)."""
+    import time
+    import torch
+    from gpu_util import oracle_full_lse_delta
+    w = WORKLOADS["train_64k"]
+    d = make_workload_inputs(w)
+    s = w.scale
+    rows = sample_rows(w.N, w.seed, w.sampled_rows)
+    idx = torch.from_numpy(rows).cuda()
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s)
+    got = (f64_of(dq[:, :, idx]), f64_of(dk[:, :, idx]), f64_of(dv[:, :, idx]))
+    del q, k, v, do, o, lse, dq, dk, dv
+    f = {n: oracle.bf16_bits_to_f64(d[n]) for n in ("q", "k", "v", "do")}
+    t0 = time.perf_counter()
+    L, Dv = oracle_full_lse_delta(f["q"], f["k"], f["v"], f["do"], s)
+    t1 = time.perf_counter()
+    rq, rk, rv = oracle.attention_backward_sampled(f["q"], f["k"], f["v"], f["do"], s, rows, rows, True,
+                                                   lse=L, dv=Dv)
+    print(f"oracle: full fp64 LSE/Dv {t1 - t0:.1f} s, sampled gradients {time.perf_counter() - t1:.1f} s")
+    errs = [grad_rel_err(g, r) for g, r in zip(got, (rq, rk, rv))]
+    assert all(np.isfinite(g).all() for g in got)
+    assert max(errs) <= GRAD_REL_TOL, errs
+
+
+def test_bwd_ulysses_shard_32k_full_do(gpu):
+    """Shard 0 of the 32K-token layer (4 query heads on 1 key/value head: the
+    per-query-head dK/dV partials and their sum) with the full dO: dQ at 64
+    sampled rows, dK and dV at the key rows with the same indices, against the
+    oracle with its own fp64 LSE and Dv for every query row."""
+    import torch
+    from gpu_util import oracle_full_lse_delta
+    from long_context_attention_fwd_amd.inputs import normal_bf16
+    w = WORKLOADS["ulysses_shard_32k"]
+    d = make_workload_inputs(w)
+    d["do"] = normal_bf16(np.random.default_rng(w.seed + 17), (w.P, w.N // w.P, w.Hq, w.D))
+    heads = {n: lc.seq_to_head_relayout(to_dev(d[n]), w.P)[0:1].contiguous() for n in ("q", "k", "v", "do")}
+    rows = sample_rows(w.N, w.seed, 64)
+    idx = torch.from_numpy(rows).cuda()
+    o, lse = lc.attn_fwd(heads["q"], heads["k"], heads["v"], causal=True, scale=w.scale)
+    dq, dk, dv = lc.attn_bwd(heads["q"], heads["k"], heads["v"], o, heads["do"], lse, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    got = (f64_of(dq[:, :, idx]), f64_of(dk[:, :, idx]), f64_of(dv[:, :, idx]))
+    f = {n: oracle.bf16_bits_to_f64(oracle.seq_to_head(d[n], w.P)[0:1]) for n in ("q", "k", "v", "do")}
+    L, Dv = oracle_full_lse_delta(f["q"], f["k"], f["v"], f["do"], w.scale)
+    rq, rk, rv = oracle.attention_backward_sampled(f["q"], f["k"], f["v"], f["do"], w.scale, rows, rows, True,
+                                                   lse=L, dv=Dv)
+    errs = [grad_rel_err(g, r) for g, r in zip(got, (rq, rk, rv))]
+    assert all(np.isfinite(g).all() for g in got)
+    assert max(errs) <= GRAD_REL_TOL, errs
