@@ -223,6 +223,31 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int64_t N, int D, float scale, int causal, void* hip_stream);
 
 /*
+ * attn_bwd_noalloc -- attn_bwd without a workspace argument and without any
+ * device allocation, for callers that cannot allocate: code under HIP graph
+ * capture, tight training loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, layout and results as attn_bwd (the same kernels; outputs
+ * bit-identical), minus workspace / workspace_bytes.  The scratch those
+ * kernels need (attn_bwd_workspace_size bytes: Dv per query row, and for
+ * grouped-query attention per-query-head fp32 dK/dV partials) lives in a
+ * device array inside the library, attn_bwd_noalloc_max_scratch() bytes
+ * (160 MiB) per GPU, held from the first call on that GPU until the process
+ * ends.  A call that needs more returns ATTN_ERR_WORKSPACE before any GPU
+ * work.  The array serves the GPU of hip_stream; every call on one GPU
+ * shares it, so calls that may overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Nothing in it needs
+ * to start at zero.  The first call on a GPU looks up the array's device
+ * address (not a device allocation); an error there returns ATTN_ERR_HIP.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int64_t N, int D,
+                     float scale, int causal, void* hip_stream);
+
+/* Bytes of scratch attn_bwd_noalloc holds per GPU (its size limit). */
+size_t attn_bwd_noalloc_max_scratch(void);
+
+/*
  * attn_bwd_strided -- attn_bwd on tensors given by element strides, so that
  * the backward of a Ulysses shard reads Q, K, V, O, dO in the token-major
  * layout the exchange delivers ([N, H, D] rows: token stride H*D, head

@@ -88,6 +88,8 @@ _SIGS = {
     "attn_partial_merge": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _L, _I, _P]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
+    "attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _I, _F, _I, _P]),
+    "attn_bwd_noalloc_max_scratch": (ctypes.c_size_t, []),
     "attn_bwd_delta": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
     "attn_bwd_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I,
                               _P, _P, _P]),
@@ -384,6 +386,41 @@ def attn_bwd(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = 
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), B, Hq, Hkv, N, D, scale,
                           1 if causal else 0, _stream(q)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc_max_scratch() -> int:
+    """Bytes of scratch attn_bwd_noalloc holds per GPU (its size limit)."""
+    return int(lib().attn_bwd_noalloc_max_scratch())
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = None,
+                     dq=None, dk=None, dv=None):
+    """attn_bwd with no workspace: the library's own per-GPU scratch serves
+    its kernels, so the call allocates nothing when dq, dk, dv are given
+    (usable under graph capture).  Calls that may overlap on one GPU share
+    that scratch and must be serialised.  Returns (dq, dk, dv)."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _need(t, name, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must be shaped like q")
+    if tuple(k.shape) != (B, Hkv, N, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, N, D]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _need(t, name, torch.bfloat16, 4)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{name} has the wrong shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, D,
+                                  scale, 1 if causal else 0, _stream(q)))
     return dq, dk, dv
 
 

@@ -403,7 +403,7 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D) {
 static int bwd_entry(const char* name, const void* q, const void* k, const void* v, const void* o, const void* d_o,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
                      int Hq, int Hkv, int64_t N, int D, float scale, int causal, const int64_t* q_strides,
-                     const int64_t* kv_strides, void* hip_stream) {
+                     const int64_t* kv_strides, void* hip_stream, bool use_scratch = false) {
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv)
     return fail(ATTN_ERR_NULL, "%s: tensor pointers must be non-null", name);
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return fail(ATTN_ERR_SHAPE, "%s: sizes must be >= 1", name);
@@ -417,9 +417,14 @@ static int bwd_entry(const char* name, const void* q, const void* k, const void*
   if (N >= INT32_MAX || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: N must be < 2^31, B and Hq <= 65535", name);
   const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, N, D);
-  if (!workspace || workspace_bytes < need)
+  if (use_scratch) {
+    if (need > lcattn::kNoAllocScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE, "%s: needs %zu bytes of scratch; the library holds %zu per GPU", name, need,
+                  lcattn::kNoAllocScratchBytes);
+  } else if (!workspace || workspace_bytes < need) {
     return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", name, need, workspace_bytes);
-  const void* ptrs[10] = {q, k, v, o, d_o, lse, dq, dk, dv, workspace};
+  }
+  const void* ptrs[10] = {q, k, v, o, d_o, lse, dq, dk, dv, use_scratch ? q : workspace};
   for (int i = 0; i < 10; ++i)
     if (!aligned16(ptrs[i])) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
   // byte extents from each base (the whole tensor when contiguous)
@@ -439,13 +444,18 @@ static int bwd_entry(const char* name, const void* q, const void* k, const void*
   }
   const void* ins[6] = {q, k, v, o, d_o, lse};
   const size_t inb[6] = {qb, kb, kb, qb, qb, lb};
-  const void* outs[4] = {dq, dk, dv, workspace};
-  const size_t outb[4] = {qb, kb, kb, need};
+  // the library's scratch is memory of its own, apart from every caller buffer
+  const void* outs[4] = {dq, dk, dv, use_scratch ? nullptr : workspace};
+  const size_t outb[4] = {qb, kb, kb, use_scratch ? 0 : need};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlap(outs[i], outb[i], ins[j], inb[j])) return fail(ATTN_ERR_ALIAS, "%s: outputs overlap inputs", name);
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outb[i], outs[j], outb[j])) return fail(ATTN_ERR_ALIAS, "%s: outputs overlap", name);
+  }
+  if (use_scratch) {  // every argument is valid: now the GPU's copy of the scratch
+    const hipError_t e = lcattn::noalloc_scratch(static_cast<hipStream_t>(hip_stream), &workspace);
+    if (e != hipSuccess) return hip_status(e, "attn_bwd_noalloc scratch");
   }
   lcattn::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -482,6 +492,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return bwd_entry("attn_bwd", q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, D, scale,
                    causal, nullptr, nullptr, hip_stream);
 }
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int64_t N, int D, float scale, int causal,
+                     void* hip_stream) {
+  return bwd_entry("attn_bwd_noalloc", q, k, v, o, d_o, lse, dq, dk, dv, nullptr, 0, B, Hq, Hkv, N, D, scale, causal,
+                   nullptr, nullptr, hip_stream, true);
+}
+
+size_t attn_bwd_noalloc_max_scratch(void) { return lcattn::kNoAllocScratchBytes; }
 
 int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,

@@ -36,6 +36,7 @@
 #include "launch.hpp"
 #include "trace.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 
@@ -718,6 +719,46 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free backward (attn_bwd_noalloc): the same Dv and
+// per-query-head dK/dV partials as the caller's workspace of attn_bwd, in a
+// file-scope device array.  Every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as memory:
+// its device address comes from hipGetSymbolAddress, once per device with
+// that device current, and is kept per device.  Nothing in it must start at
+// zero (every word a launch reads was written earlier in the same launch
+// sequence); calls that overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (e2 != hipSuccess) return e2;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 long long bwd_delta_floats(int B, int Hq, long long Nq) {
   // Dv rows, padded to a multiple of 64 floats (256 bytes)

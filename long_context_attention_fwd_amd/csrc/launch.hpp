@@ -121,6 +121,13 @@ long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D);
 long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream);
+
+// The allocation-free backward's scratch: kNoAllocScratchBytes of device
+// memory per GPU, held by the library until the process ends.  *ptr receives
+// the device address of the copy on the GPU that `stream` belongs to (looked
+// up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(160) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 // Dv_i = <dO_i, O_i> for rows query rows of width D
 hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, int D,
                             hipStream_t stream);

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
-              "attn_bwd_strided", "attn_fwd_accumulate_group", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
+              "attn_bwd_strided", "attn_bwd_noalloc", "attn_bwd_noalloc_max_scratch", "attn_fwd_accumulate_group", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
               "head_to_seq_relayout_batch", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -224,6 +224,38 @@ def bwd(L, **kw):
 ])
 def test_bwd_rejects(L, kw, status):
     assert bwd(L, **kw) == status
+
+
+def bwd_noalloc(L, **kw):
+    n = 1 << 22
+    args = dict(q=A, k=A + n, v=A + 2 * n, o=A + 3 * n, do=A + 4 * n, lse=A + 5 * n, dq=A + 6 * n, dk=A + 7 * n,
+                dv=A + 8 * n, B=1, Hq=8, Hkv=8, N=1024, D=128, scale=0.088, causal=1, stream=None)
+    args.update(kw)
+    return L.attn_bwd_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), 1), (dict(N=0), 2), (dict(Hkv=3), 2), (dict(D=32), 3), (dict(scale=-1.0), 3),
+    (dict(dk=A + 8), 4), (dict(dq=A), 5),
+    # scratch beyond the library's per-GPU array: Dv + fp32 partials of 4 x 16 query heads
+    (dict(B=4, Hq=16, Hkv=4, N=32768), 6),
+])
+def test_bwd_noalloc_rejects(L, kw, status):
+    """Every check runs on the host before the scratch lookup (the first GPU
+    call), so bad arguments fail here without a GPU."""
+    assert bwd_noalloc(L, **kw) == status
+
+
+def test_bwd_noalloc_limit(L):
+    cap = L.attn_bwd_noalloc_max_scratch()
+    assert cap == 160 << 20
+    # the two backward shapes of the workloads fit: the 64K training shape
+    # (8 heads, Dv only) and the 32K Ulysses shard (4 query heads on 1 KV head)
+    assert L.attn_bwd_workspace_size(1, 8, 8, 65536, 128) <= cap
+    assert L.attn_bwd_workspace_size(1, 4, 1, 32768, 128) <= cap
+    assert L.attn_bwd_workspace_size(4, 16, 4, 32768, 128) > cap
+    assert bwd_noalloc(L, B=4, Hq=16, Hkv=4, N=32768) == 6
+    assert b"scratch" in L.attn_last_error()
 
 
 @pytest.mark.parametrize("args,status", [
