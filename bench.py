@@ -1,24 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the long-context causal attention hot path on one MI355X.
 
-One step is one pass over the whole hot path on one GPU's Ulysses share of a
-Llama-3-8B-shaped layer (32 query / 8 key-value heads, D = 128, N = 32768
-tokens split P = 8 ways), with inputs already resident in HBM:
+Headline step (``value``): one training pass of causal attention at the
+largest single-GPU workload, ``train_64k`` (B = 1, 8 heads, N = 65536,
+D = 128, seeded bf16 N(0,1) inputs already resident in HBM):
 
-  1. seq_to_head_relayout_batch of Q, K, V, dO (all P shards, one launch)
-     -- the all-to-all's data movement
-  2. attn_fwd on shard 0 (4 query heads, 1 KV head, causal GQA, N = 32768)
-  3. the ring form of the same forward: 4 partial attention calls over
-     8192-key blocks (fp32 partials, one attn_fwd_accumulate_group launch)
-     + attn_partial_merge
-  4. attn_bwd on shard 0 (from step 2's O and LSE)
-  5. head_to_seq_relayout_batch of O, dQ, dK, dV (one launch)
+  attn_fwd (O, LSE)  ->  attn_bwd (dQ, dK, dV from the forward's O and LSE)
 
-``value`` is the attention work of the step (forward + ring forward +
-backward, algorithmic flops: masked pairs not counted) divided by the step
-time.  The per-kernel breakdown, the roofline of the dominant kernel and the
-oracle's CPU rate on a bounded sample of the same workload are printed in the
-same JSON line.
+``value`` = algorithmic flops of the step (forward 2 B H D N (N+1), backward
+2.5x that; masked pairs are not counted) / step time.  ``roofline`` is the
+dominant kernel of that step (most GPU time), timed with HIP events around
+each of its launches over the timed steps.
+
+Legs timed apart from the step, each with the roofline of its kernels
+(``rooflines``): the glossary example's 4K shape (forward, plain and
+split-KV), one Ulysses shard of a 32K-token layer (relayout GB/s, forward,
+the four ring partials + merge, backward, inverse relayout), the ring workload
+at its configured shape (8 heads, four 8192-key fp32 partials + the 609 MB
+merge), the 512K-token forward of one Ulysses share, and the backward of the
+64K shape again from the other legs' viewpoint.  ``cpu_baseline`` times the
+fp64 oracle on the host cores on bounded samples of every workload.
+
+``--only WORKLOAD`` runs one workload alone (for a profiler: its kernels and
+nothing else).
 """
 
 from __future__ import annotations
@@ -26,8 +30,8 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
+import platform
 import sys
 import time
 
@@ -36,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBPS = 8000.0
+WORKLOAD_NAMES = ("train_64k", "listing_4k", "ulysses_shard_32k", "ring_blocks_32k", "ulysses_512k")
 
 
 def fwd_flops(B, Hq, N, D):
@@ -50,27 +55,32 @@ def pair_flops_block(Hq, D, N, a, b):
     return 4.0 * Hq * D * pairs
 
 
+KERNEL_SOURCES = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip",
+                  "bwd_delta_kernel": "attn_bwd.hip", "bwd_dkdv_reduce_kernel": "attn_bwd.hip",
+                  "attn_fwd_kernel": "attn_fwd.hip", "attn_fwd_kernel_fp32out": "attn_fwd.hip",
+                  "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}
+
+
 def kernel_source_digest(name):
     """sha256 of the sources a kernel is compiled from (to tell whether
     committed counter figures still describe it)."""
-    csrc = os.path.join(ROOT, "long_context_attention_fwd_amd", "csrc")
-    files = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip", "attn_fwd_kernel": "attn_fwd.hip",
-             "attn_fwd_kernel_fp32out": "attn_fwd.hip",
-             "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}.get(name)
-    if files is None:
+    f = KERNEL_SOURCES.get(name)
+    if f is None:
         return None
+    csrc = os.path.join(ROOT, "long_context_attention_fwd_amd", "csrc")
     h = hashlib.sha256()
-    for f in (files, "device_common.hpp"):
-        with open(os.path.join(csrc, f), "rb") as fh:
+    for fn in (f, "device_common.hpp"):
+        with open(os.path.join(csrc, fn), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when
-    there is none or the kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+def measured_traffic(name, workload):
+    """HBM bytes per launch of kernel ``name`` on ``workload`` from the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by
+    a copy of known size), or None when there is none or the kernel's
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -89,356 +99,49 @@ def measured_traffic(name):
         return None
 
 
-def parse():
-    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
-    p.add_argument("--profile-steps", action="store_true", help="short run for rocprofv3 (no CPU leg)")
-    return p.parse_args()
+def tflops(f, ms):
+    return f / (ms * 1e-3) / 1e12
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share only: this build runs no collectives, so --gpus must be 1",
-              file=sys.stderr)
-        sys.exit(2)
+def gbps(b, ms):
+    return b / (ms * 1e-3) / 1e9
 
-    import numpy as np
-    import torch
 
-    import long_context_attention_fwd_amd as lc
-    from long_context_attention_fwd_amd.inputs import WORKLOADS, make_workload_inputs, normal_bf16
+def roofline_entry(kernel, traced, work_per_launch, unit, workload):
+    """Roofline of one kernel from its traced launches: algorithmic work per
+    launch / average launch duration, against the MI355X peak of its bound."""
+    tot_ms, calls = traced[kernel]
+    avg_ms = tot_ms / calls
+    mfma = unit == "TFLOP/s"
+    achieved = tflops(work_per_launch, avg_ms) if mfma else gbps(work_per_launch, avg_ms)
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBPS
+    ent = {"bound": "mfma" if mfma else "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+           "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(achieved / peak, 4), "traffic": None,
+           "avg_launch_us": round(1e3 * avg_ms, 2), "launches": calls, "algorithmic_per_launch": work_per_launch}
+    t = measured_traffic(kernel, workload)
+    if t is not None:
+        ent["traffic"] = t["read_bytes"] + t["write_bytes"]
+        ent["traffic_detail"] = t
+    return ent
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    w = WORKLOADS["ulysses_shard_32k"]
-    P, N, D, Hq, Hkv = w.P, w.N, w.D, w.Hq, w.Hkv
-    hq, hkv = Hq // P, Hkv // P  # one shard's heads: 4 and 1
 
-    # ---- inputs, resident in HBM before timing ------------------------------
-    d = make_workload_inputs(w)
-    rng = np.random.default_rng(w.seed + 17)
-    d["do"] = normal_bf16(rng, (P, N // P, Hq, D))
-
-    def dev_bf16(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    xs = {k: dev_bf16(v) for k, v in d.items()}
-    del d
-    heads = {"q": torch.empty((P, hq, N, D), dtype=torch.bfloat16, device=dev),
-             "do": torch.empty((P, hq, N, D), dtype=torch.bfloat16, device=dev),
-             "k": torch.empty((P, hkv, N, D), dtype=torch.bfloat16, device=dev),
-             "v": torch.empty((P, hkv, N, D), dtype=torch.bfloat16, device=dev)}
-    # token-major outputs of the inverse relayout.  Shard 0's results are
-    # written straight into slot 0 of the head-major buffers; the inverse
-    # relayout moves all P shards' bytes, as the exchange would.
-    o_all = torch.zeros((P, hq, N, D), dtype=torch.bfloat16, device=dev)
-    dq_all = torch.zeros_like(o_all)
-    dk_all = torch.zeros((P, hkv, N, D), dtype=torch.bfloat16, device=dev)
-    dv_all = torch.zeros_like(dk_all)
-    o, dq, dk, dv = o_all[0:1], dq_all[0:1], dk_all[0:1], dv_all[0:1]
-    lse = torch.empty((1, hq, N), dtype=torch.float32, device=dev)
-    o_tok = torch.empty((P, N // P, Hq, D), dtype=torch.bfloat16, device=dev)
-    dq_tok = torch.empty_like(o_tok)
-    dk_tok = torch.empty((P, N // P, Hkv, D), dtype=torch.bfloat16, device=dev)
-    dv_tok = torch.empty_like(dk_tok)
-    n_blk = 4
-    blk = N // n_blk
-    o_parts = torch.empty((n_blk, 1, hq, N, D), dtype=torch.float32, device=dev)
-    lse_parts = torch.empty((n_blk, 1, hq, N), dtype=torch.float32, device=dev)
-    o_ring = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
-    lse_ring = torch.empty_like(lse)
-    ws = torch.empty(lc.attn_bwd_workspace_size(1, hq, hkv, N, D), dtype=torch.uint8, device=dev)
-    scale = w.scale
-    stream = torch.cuda.current_stream(dev)
-    # the key/value blocks of the ring (views of shard 0's head-major K, V:
-    # contiguous, as a ring step receives them, since a shard has one KV head)
-    ring_blocks = [(a, heads["k"][0:1, :, a:a + blk], heads["v"][0:1, :, a:a + blk]) for a in range(0, N, blk)]
-    assert all(kb.is_contiguous() and vb.is_contiguous() for _, kb, vb in ring_blocks)
-
-    names = ["relayout_in", "fwd", "ring_partials", "merge", "bwd", "relayout_out"]
-    ev = {n: [] for n in names}
-
-    def step(record):
-        marks = []
-
-        def mark():
-            if record:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                marks.append(e)
-
-        mark()
-        # one launch for the four tensors of the exchange
-        lc.seq_to_head_relayout_batch([xs[n] for n in ("q", "k", "v", "do")], P,
-                                      outs=[heads[n] for n in ("q", "k", "v", "do")])
-        mark()
-        q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
-        lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
-        mark()
-        # The ring's partials, one per KV block [a, a + blk), fp32 O and LSE
-        # each.  All blocks are resident on this GPU and the partials are
-        # independent, so the four calls go out as one grouped launch (a late
-        # block has work only for the last queries and alone would leave most
-        # CUs idle); the merge follows.
-        lc.attn_fwd_accumulate_group(
-            [dict(q=q0, k=kb, v=vb, o_acc=o_parts[i], lse_acc=lse_parts[i], first=True, k_pos0=a)
-             for i, (a, kb, vb) in enumerate(ring_blocks)], causal=True, scale=scale)
-        mark()
-        lc.attn_partial_merge(o_parts, lse_parts, o=o_ring, lse=lse_ring)
-        mark()
-        lc.attn_bwd(q0, k0, v0, o, do0, lse, causal=True, scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
-        mark()
-        lc.head_to_seq_relayout_batch([o_all, dq_all, dk_all, dv_all], P, outs=[o_tok, dq_tok, dk_tok, dv_tok])
-        mark()
-        return marks
-
+def traced_calls(lc, torch, fn, iters, warmup):
+    """fn() warmup times, then iters times with every library kernel
+    bracketed by HIP events; returns (ms per call from events around all
+    iters, {kernel: (total_ms, launches)})."""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    all_marks = []
-    torch.cuda.synchronize()
-    lc.trace_collect()          # drop records of the warmup
-    lc.trace_enable(True)       # every library kernel bracketed by HIP events
-    t_start.record(stream)
-    for _ in range(args.steps):
-        all_marks.append(step(True))
-    t_end.record(stream)
+    lc.trace_collect()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lc.trace_enable(True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
     torch.cuda.synchronize()
     lc.trace_enable(False)
-    traced = lc.trace_collect()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    per = {n: 0.0 for n in names}
-    for marks in all_marks:
-        for i, n in enumerate(names):
-            per[n] += marks[i].elapsed_time(marks[i + 1])
-    per = {n: v / args.steps for n, v in per.items()}
-
-    B = 1
-    f_fwd = fwd_flops(B, hq, N, D)
-    f_ring = sum(pair_flops_block(hq, D, N, a, a + blk) for a in range(0, N, blk))
-    f_bwd = 2.5 * f_fwd
-    attn_flops = f_fwd + f_ring + f_bwd
-    relayout_in_bytes = 2 * 2 * (xs["q"].numel() + xs["k"].numel() + xs["v"].numel() + xs["do"].numel())
-    relayout_out_bytes = 2 * 2 * (o_all.numel() + dq_all.numel() + dk_all.numel() + dv_all.numel())
-    merge_bytes = o_parts.numel() * 4 + lse_parts.numel() * 4 + o_ring.numel() * 2 + lse_ring.numel() * 4
-
-    def tflops(f, ms):
-        return f / (ms * 1e-3) / 1e12
-
-    def gbps(b, ms):
-        return b / (ms * 1e-3) / 1e9
-
-    kernels = {
-        "fwd": {"ms": per["fwd"], "TFLOP/s": tflops(f_fwd, per["fwd"]),
-                "frac_peak": tflops(f_fwd, per["fwd"]) / PEAK_BF16_TFLOPS},
-        "ring_partials_x4": {"ms": per["ring_partials"], "TFLOP/s": tflops(f_ring, per["ring_partials"]),
-                             "frac_peak": tflops(f_ring, per["ring_partials"]) / PEAK_BF16_TFLOPS},
-        "merge": {"ms": per["merge"], "GB/s": gbps(merge_bytes, per["merge"]),
-                  "frac_peak": gbps(merge_bytes, per["merge"]) / PEAK_HBM_GBPS},
-        "bwd": {"ms": per["bwd"], "TFLOP/s": tflops(f_bwd, per["bwd"]),
-                "frac_peak": tflops(f_bwd, per["bwd"]) / PEAK_BF16_TFLOPS},
-        "relayout_seq_to_head_qkvdo": {"ms": per["relayout_in"], "GB/s": gbps(relayout_in_bytes, per["relayout_in"]),
-                                       "frac_peak": gbps(relayout_in_bytes, per["relayout_in"]) / PEAK_HBM_GBPS},
-        "relayout_head_to_seq_o_grads": {"ms": per["relayout_out"],
-                                         "GB/s": gbps(relayout_out_bytes, per["relayout_out"]),
-                                         "frac_peak": gbps(relayout_out_bytes, per["relayout_out"]) / PEAK_HBM_GBPS},
-    }
-    # Per GPU kernel, from the library's HIP events over the timed region:
-    # algorithmic work of all its launches / its total time.  The backward's
-    # five counted contractions are S, dP, dV, dK (dK/dV kernel) and dQ (dQ
-    # kernel); the dQ kernel's recomputed S and dP are not counted.
-    # kernels whose launches share the GPU with one another (none since the
-    # ring partials became one grouped launch)
-    OVERLAPPED = set()
-    alg = {
-        "attn_fwd_kernel": ("TFLOP/s", args.steps * f_fwd),
-        # the ring partials: one grouped launch of four fp32-output calls
-        "attn_fwd_kernel_fp32out": ("TFLOP/s", args.steps * f_ring),
-        "bwd_dkdv_kernel": ("TFLOP/s", args.steps * 0.8 * f_bwd),
-        "bwd_dq_kernel": ("TFLOP/s", args.steps * 0.2 * f_bwd),
-        "transpose_rows_kernel": ("GB/s", args.steps * (relayout_in_bytes + relayout_out_bytes)),
-        "merge_kernel": ("GB/s", args.steps * merge_bytes),
-        "bwd_delta_kernel": ("GB/s", args.steps * 2 * 2 * o_ring.numel() + args.steps * 4 * lse.numel()),
-        "bwd_dkdv_reduce_kernel": ("GB/s", args.steps * (2 * 4 * hq + 2 * 2 * hkv) * N * D),
-    }
-    gpu_kernels = {}
-    for name, (tot_ms, calls) in traced.items():
-        unit, work = alg.get(name, (None, None))
-        ent = {"calls_per_step": calls / args.steps, "avg_us": round(1e3 * tot_ms / calls, 2),
-               "share_of_step": round(tot_ms / total_ms, 4)}
-        if unit == "TFLOP/s":
-            ent["TFLOP/s"] = round(tflops(work, tot_ms), 2)
-            ent["frac_peak"] = round(tflops(work, tot_ms) / PEAK_BF16_TFLOPS, 4)
-        elif unit == "GB/s":
-            ent["GB/s"] = round(gbps(work, tot_ms), 1)
-            ent["frac_peak"] = round(gbps(work, tot_ms) / PEAK_HBM_GBPS, 4)
-        if name in OVERLAPPED:
-            ent["overlapped"] = True  # launches share the GPU: avg_us is not one launch's own time
-        gpu_kernels[name] = ent
-    # The dominant kernel is the one with the most time among kernels that run
-    # alone, so that its launch duration is its own.
-    dom = max((n for n in traced if n not in OVERLAPPED), key=lambda n: traced[n][0])
-    tot_ms, calls = traced[dom]
-    unit, work = alg[dom]
-    mfma = unit == "TFLOP/s"
-    achieved = tflops(work, tot_ms) if mfma else gbps(work, tot_ms)
-    peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBPS
-    roofline = {"bound": "mfma" if mfma else "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": None, "avg_launch_us": round(1e3 * tot_ms / calls, 2),
-                "algorithmic_per_launch": work / calls}
-    t = measured_traffic(dom)
-    if t is not None:
-        roofline["traffic"] = t["read_bytes"] + t["write_bytes"]
-        roofline["traffic_detail"] = t
-
-    out = {
-        "metric": "causal attention TFLOP/s fwd/bwd at 1 GPU + % bf16 MFMA peak; relayout GB/s",
-        "value": round(tflops(attn_flops, ms_step), 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded i.i.d. N(0,1) bf16 (numpy PCG64), no dataset or weights",
-        "config": {"workload": w.name, "P": P, "N": N, "Hq_total": Hq, "Hkv_total": Hkv, "D": D,
-                   "shard_heads_q": hq, "shard_heads_kv": hkv, "causal": True, "ring_blocks": n_blk,
-                   "step": "relayout q,k,v,dO -> fwd -> 4 partial fwd + merge -> bwd -> relayout o,dq,dk,dv"},
-        "phases": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                   for k, v in kernels.items()},
-        "gpu_kernels": gpu_kernels,
-        "roofline": roofline,
-        "device": torch.cuda.get_device_name(dev),
-    }
-    props = torch.cuda.get_device_properties(dev)
-    out["device_info"] = {"name": props.name, "compute_units": props.multi_processor_count,
-                          "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip}
-    if not args.profile_steps:
-        out["short_sequence_forward"] = short_forward(lc, torch, dev)
-        # shard 0's heads read straight from the token-major input, no relayout
-        qv = xs["q"].view(N, Hq, D)[:, :hq].permute(1, 0, 2).unsqueeze(0)
-        kv_ = xs["k"].view(N, Hkv, D)[:, :hkv].permute(1, 0, 2).unsqueeze(0)
-        vv = xs["v"].view(N, Hkv, D)[:, :hkv].permute(1, 0, 2).unsqueeze(0)
-        o_tm = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
-        ms = time_calls(torch, lambda: lc.attn_fwd_strided(qv, kv_, vv, causal=True, scale=scale, o=o_tm, lse=lse))
-        out["token_major_forward"] = {"call": "attn_fwd_strided on shard 0's heads of the token-major input",
-                                      "ms": round(ms, 4), "TFLOP/s": round(tflops(f_fwd, ms), 2),
-                                      "frac_peak": round(tflops(f_fwd, ms) / PEAK_BF16_TFLOPS, 4)}
-        # its backward the same way: Q, K, V, O, dO read and dQ, dK, dV written token-major
-        def tm_heads(x, H, n):
-            return x.view(N, H, D)[:, :n].permute(1, 0, 2).unsqueeze(0)
-        o_tmb = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
-        g_tm = [torch.empty((N, H, D), dtype=torch.bfloat16, device=dev) for H in (Hq, Hkv, Hkv)]
-        ov = tm_heads(o_tmb, Hq, hq)
-        lc.attn_fwd_strided(qv, kv_, vv, causal=True, scale=scale, o=ov, lse=lse)
-        dov = tm_heads(xs["do"], Hq, hq)
-        gq, gk, gv = tm_heads(g_tm[0], Hq, hq), tm_heads(g_tm[1], Hkv, hkv), tm_heads(g_tm[2], Hkv, hkv)
-        ms = time_calls(torch, lambda: lc.attn_bwd_strided(qv, kv_, vv, ov, dov, lse, causal=True, scale=scale,
-                                                           workspace=ws, dq=gq, dk=gk, dv=gv))
-        out["token_major_backward"] = {"call": "attn_bwd_strided on shard 0's heads of token-major Q, K, V, O, dO",
-                                       "ms": round(ms, 4), "TFLOP/s": round(tflops(f_bwd, ms), 2),
-                                       "frac_peak": round(tflops(f_bwd, ms) / PEAK_BF16_TFLOPS, 4)}
-        del o_tmb, g_tm
-        # the ring streamed into one running result (blocks one after another)
-        o_acc = o_parts[0]
-        q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))
-
-        def streamed():
-            for i, a in enumerate(range(0, N, blk)):
-                lc.attn_fwd_accumulate(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], o_acc, lse_parts[0],
-                                       first=(i == 0), causal=True, scale=scale, k_pos0=a,
-                                       o_final=o_ring if a + blk >= N else None)
-        ms = time_calls(torch, streamed)
-        out["ring_streamed"] = {"call": f"{n_blk} x attn_fwd_accumulate (running fp32 O, LSE; bf16 O from the last)",
-                                "ms": round(ms, 4), "TFLOP/s": round(tflops(f_ring, ms), 2),
-                                "frac_peak": round(tflops(f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
-        # the ring's backward: Dv once, then one attn_bwd_block per KV block
-        # (fp32 dQ accumulated in place, bf16 dQ from the last; each block's
-        # dK, dV in bf16), against the same global LSE
-        dq_acc = o_parts[1]
-        delta = torch.empty_like(lse)
-        ws_blk = torch.empty(max(16, lc.attn_bwd_block_workspace_size(1, hq, hkv, blk, D)), dtype=torch.uint8,
-                             device=dev)
-        do0 = heads["do"][0:1]
-
-        def ring_backward():
-            lc.attn_bwd_delta(o, do0, delta=delta)
-            for i, a in enumerate(range(0, N, blk)):
-                lc.attn_bwd_block(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], do0, lse, delta, causal=True,
-                                  scale=scale, k_pos0=a, dq_acc=dq_acc, dq_accumulate=i > 0,
-                                  dq=dq if a + blk >= N else None, dk=dk[:, :, a:a + blk], dv=dv[:, :, a:a + blk],
-                                  workspace=ws_blk)
-        ms = time_calls(torch, ring_backward)
-        out["ring_backward"] = {"call": f"attn_bwd_delta + {n_blk} x attn_bwd_block (fp32 dQ accumulated)",
-                                "ms": round(ms, 4), "TFLOP/s": round(tflops(2.5 * f_ring, ms), 2),
-                                "frac_peak": round(tflops(2.5 * f_ring, ms) / PEAK_BF16_TFLOPS, 4)}
-        out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops)
-        out["long_shapes"] = long_shapes(lc, torch, dev)
-
-    if not args.no_cpu_baseline and not args.profile_steps:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
-
-
-def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, tflops, Pr=4):
-    """Shard 0's causal attention as a Pr-rank ring over 2*Pr chunks, every
-    rank's every step timed on this GPU: the ring waits for the slowest rank
-    at each step, so its critical path is the sum over steps of the maximum
-    over ranks.  Contiguous sharding against zigzag (rank r holds chunks r
-    and 2*Pr-1-r)."""
-    from long_context_attention_fwd_amd.ring import SCHEMES, rank_chunks, ring_forward
-    C = N // (2 * Pr)
-    q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))
-    cq = [q0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
-    ck = [k0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
-    cv = [v0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
-    o_acc = [torch.empty((1, hq, C, D), dtype=torch.float32, device=dev) for _ in range(2)]
-    lse = [torch.empty((1, hq, C), dtype=torch.float32, device=dev) for _ in range(2)]
-    o_fin = [torch.empty((1, hq, C, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    # one call after another: a chunk call fills a quarter of this GPU here,
-    # so running the two chunks' calls side by side would measure launch
-    # overlap rather than each rank's causal work
-    res = {"ranks": Pr, "chunk_tokens": C,
-           "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair, in sequence"}
-    # "<scheme>_grouped": the calls of a step that read the same key/value
-    # chunk (one per query chunk) as one attn_fwd_accumulate_group launch
-    for scheme, grouped in [(sc, g) for g in (False, True) for sc in SCHEMES]:
-        t = [[0.0] * Pr for _ in range(Pr)]
-        for r in range(Pr):
-            qs = [cq[c] for c in rank_chunks(r, Pr, scheme)]
-
-            def kv(src, scheme=scheme):
-                return tuple((ck[c], cv[c]) for c in rank_chunks(src, Pr, scheme))
-            for st in range(Pr):
-                t[r][st] = time_calls(torch, lambda: ring_forward(qs, kv, r, Pr, C, o_acc=o_acc, lse_acc=lse,
-                                                                  o_final=o_fin, scheme=scheme, scale=scale,
-                                                                  steps={st}, grouped=grouped))
-        crit = sum(max(t[r][s] for r in range(Pr)) for s in range(Pr))
-        # a real ring runs the ranks on Pr GPUs at once: aggregate over the
-        # ranks, and per rank (one GPU)
-        res[scheme + ("_grouped" if grouped else "")] = {
-            "critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
-            "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
-            "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
-            "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
-    return res
+    return e0.elapsed_time(e1) / iters, lc.trace_collect()
 
 
 def time_calls(torch, fn, iters=10, warmup=3, rounds=3):
@@ -460,98 +163,693 @@ def time_calls(torch, fn, iters=10, warmup=3, rounds=3):
     return sorted(avgs)[len(avgs) // 2]
 
 
-def short_forward(lc, torch, dev, iters=20):
-    """The glossary example's forward shape ([1, 4, 4096, 64], causal), timed
-    apart from the step: attn_fwd, and attn_fwd_splitkv with the library's
-    choice of key ranges.  One workgroup per 256 query rows gives only 64
-    workgroups here, so the longest row sets attn_fwd's time."""
+_HOST_INPUTS = {}
+
+
+def host_inputs(name):
+    """Seeded bf16 bit patterns of a workload (the same arrays the oracle
+    baseline decodes), drawn once per run."""
+    from long_context_attention_fwd_amd.inputs import WORKLOADS, make_workload_inputs, normal_bf16
+    if name not in _HOST_INPUTS:
+        w = WORKLOADS[name]
+        d = make_workload_inputs(w)
+        if name == "ulysses_shard_32k":  # the shard step's backward needs dO, drawn token-major like q
+            import numpy as np
+            d["do"] = normal_bf16(np.random.default_rng(w.seed + 17), (w.P, w.N // w.P, w.Hq, w.D))
+        _HOST_INPUTS[name] = d
+    return _HOST_INPUTS[name]
+
+
+def to_dev(torch, bits, dev):
     import numpy as np
-    from long_context_attention_fwd_amd.inputs import WORKLOADS, make_workload_inputs
-    w = WORKLOADS["listing_4k"]
-    d = make_workload_inputs(w)
-    q, k, v = (torch.from_numpy(d[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in "qkv")
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    p.add_argument("--only", choices=WORKLOAD_NAMES, help="run one workload alone (for a profiler)")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="with --only: first one elementwise kernel of known traffic (1 GiB fp32 read, 1 GiB "
+                        "written), the reference for scaling the profiler's byte counters")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the shard leg's extra variants (token-major, streamed ring, ring sharding)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# headline: the 64K training step
+# ---------------------------------------------------------------------------
+def train_64k(lc, torch, dev, steps, warmup):
+    from long_context_attention_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["train_64k"]
+    d = host_inputs(w.name)
+    q, k, v, do = (to_dev(torch, d[n], dev) for n in ("q", "k", "v", "do"))
     B, Hq, N, D = q.shape
-    Hkv = k.shape[1]
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
-    ws = torch.empty(lc.attn_fwd_splitkv_workspace_size(B, Hq, Hkv, N, N, D, True, 0), dtype=torch.uint8,
-                     device=dev)
-    flops = fwd_flops(B, Hq, N, D)
-    res = {"workload": w.name, "shape": [B, Hq, N, D], "causal": True}
-    calls = {"attn_fwd": lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse),
-             "attn_fwd_splitkv": lambda: lc.attn_fwd_splitkv(q, k, v, scale=w.scale, workspace=ws, o=o, lse=lse)}
-    for name, fn in calls.items():
-        ms = time_calls(torch, fn, iters, 5)
-        res[name] = {"us": round(1e3 * ms, 2), "TFLOP/s": round(flops / ms / 1e9, 2),
-                     "frac_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
-    return res
-
-
-def long_shapes(lc, torch, dev):
-    """The other two large workloads, timed apart from the step on inputs
-    drawn on the GPU (seeded normal, bf16): the 64K training shape
-    (8 heads, forward and backward) and the 512K-token forward of one
-    Ulysses share (4 query heads on 1 key/value head, inputs 0.5 N(0,1))."""
-    from long_context_attention_fwd_amd.inputs import WORKLOADS
-    res = {}
-    gen = torch.Generator(device=dev)
-
-    def draw(shape, seed, amp=1.0):
-        gen.manual_seed(seed)
-        return (amp * torch.randn(shape, generator=gen, device=dev)).to(torch.bfloat16)
-
-    w = WORKLOADS["train_64k"]
-    q, k, v, do = (draw((w.B, h, w.N, w.D), w.seed * 10 + i) for i, h in enumerate((w.Hq, w.Hkv, w.Hkv, w.Hq)))
-    o, lse = lc.attn_fwd(q, k, v, scale=w.scale)
-    ws = torch.empty(lc.attn_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.D), dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    f = fwd_flops(w.B, w.Hq, w.N, w.D)
-    t_f = time_calls(torch, lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse), 3, 1)
-    t_b = time_calls(torch, lambda: lc.attn_bwd(q, k, v, o, do, lse, scale=w.scale, workspace=ws, dq=dq, dk=dk,
-                                                dv=dv), 3, 1)
-    res[w.name] = {"shape": [w.B, w.Hq, w.N, w.D], "fwd_ms": round(t_f, 3), "fwd_TFLOP/s": round(f / t_f / 1e9, 1),
-                   "bwd_ms": round(t_b, 3), "bwd_TFLOP/s": round(2.5 * f / t_b / 1e9, 1),
-                   "bwd_frac_peak": round(2.5 * f / t_b / 1e9 / PEAK_BF16_TFLOPS, 4)}
-    del q, k, v, do, o, lse, ws, dq, dk, dv
-    w = WORKLOADS["ulysses_512k"]
-    q = draw((w.B, w.Hq, w.N, w.D), w.seed * 10, w.amp)
-    k = draw((w.B, w.Hkv, w.N, w.D), w.seed * 10 + 1, w.amp)
-    v = draw((w.B, w.Hkv, w.N, w.D), w.seed * 10 + 2, w.amp)
-    o, lse = lc.attn_fwd(q, k, v, scale=w.scale)
-    f = fwd_flops(w.B, w.Hq, w.N, w.D)
-    t_f = time_calls(torch, lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse), 2, 1)
-    res[w.name] = {"shape": [w.B, w.Hq, w.N, w.D], "kv_heads": w.Hkv, "fwd_ms": round(t_f, 2),
-                   "fwd_TFLOP/s": round(f / t_f / 1e9, 1), "fwd_frac_peak": round(f / t_f / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    ws = torch.empty(lc.attn_bwd_workspace_size(B, Hq, w.Hkv, N, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    f_fwd = fwd_flops(B, Hq, N, D)
+    f_bwd = 2.5 * f_fwd
+
+    def step(record):
+        marks = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
+        mark()
+        lc.attn_fwd(q, k, v, causal=True, scale=w.scale, o=o, lse=lse)
+        mark()
+        lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        mark()
+        return marks
+
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    lc.trace_collect()  # drop the warmup's records
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    all_marks = []
+    torch.cuda.synchronize()
+    lc.trace_enable(True)
+    t0.record(stream)
+    for _ in range(steps):
+        all_marks.append(step(True))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    lc.trace_enable(False)
+    tr = lc.trace_collect()
+    ms_step = t0.elapsed_time(t1) / steps
+    ph = [sum(m[i].elapsed_time(m[i + 1]) for m in all_marks) / steps for i in range(2)]
+    work = {"attn_fwd_kernel": ("TFLOP/s", f_fwd), "bwd_dkdv_kernel": ("TFLOP/s", 0.8 * f_bwd),
+            "bwd_dq_kernel": ("TFLOP/s", 0.2 * f_bwd),
+            "bwd_delta_kernel": ("GB/s", 2 * 2 * B * Hq * N * D + 4 * B * Hq * N)}
+    gpu_kernels = {}
+    for name, (tot, calls) in tr.items():
+        ent = {"calls_per_step": calls / steps, "avg_us": round(1e3 * tot / calls, 2),
+               "share_of_step": round(tot / (ms_step * steps), 4)}
+        if name in work:
+            unit, wk = work[name]
+            rate = tflops(wk, tot / calls) if unit == "TFLOP/s" else gbps(wk, tot / calls)
+            ent[unit] = round(rate, 2)
+            ent["frac_peak"] = round(rate / (PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBPS), 4)
+        gpu_kernels[name] = ent
+    dom = max(tr, key=lambda n: tr[n][0])
+    rl = {n: roofline_entry(n, tr, work[n][1], work[n][0], w.name) for n in work if n in tr}
+    res = {
+        "value": round(tflops(f_fwd + f_bwd, ms_step), 3), "ms_per_step": round(ms_step, 4),
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": w.Hkv, "N": N, "D": D, "causal": True,
+                   "seed": w.seed, "step": "attn_fwd -> attn_bwd (dQ, dK, dV from the forward's O and LSE)",
+                   "algorithmic_flops_per_step": f_fwd + f_bwd},
+        "phases": {"fwd": {"ms": round(ph[0], 4), "TFLOP/s": round(tflops(f_fwd, ph[0]), 2),
+                           "frac_peak": round(tflops(f_fwd, ph[0]) / PEAK_BF16_TFLOPS, 4)},
+                   "bwd": {"ms": round(ph[1], 4), "TFLOP/s": round(tflops(f_bwd, ph[1]), 2),
+                           "frac_peak": round(tflops(f_bwd, ph[1]) / PEAK_BF16_TFLOPS, 4)}},
+        "gpu_kernels": gpu_kernels,
+        "roofline": rl[dom],
+        "rooflines": {f"{w.name}.{n}": r for n, r in rl.items()},
+    }
     return res
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the same shard:
-    forward attention of the last rows of shard 0 (4 query heads, 1 KV head),
-    in chunks of 256 rows until the time budget is spent."""
+# ---------------------------------------------------------------------------
+# legs
+# ---------------------------------------------------------------------------
+def leg_listing_4k(lc, torch, dev, iters=50, warmup=10):
+    """The glossary example's forward shape ([1, 4, 4096, 64], causal):
+    attn_fwd, and attn_fwd_splitkv with the library's choice of key ranges
+    (one workgroup per 256 query rows gives only 64 workgroups here, so the
+    longest row sets attn_fwd's time)."""
+    from long_context_attention_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["listing_4k"]
+    d = host_inputs(w.name)
+    q, k, v = (to_dev(torch, d[n], dev) for n in "qkv")
+    B, Hq, N, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(lc.attn_fwd_splitkv_workspace_size(B, Hq, w.Hkv, N, N, D, True, 0), dtype=torch.uint8,
+                     device=dev)
+    f = fwd_flops(B, Hq, N, D)
+    res = {"workload": w.name, "shape": [B, Hq, N, D], "causal": True, "algorithmic_flops": f}
+    rls = {}
+    for name, fn in (("attn_fwd", lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse)),
+                     ("attn_fwd_splitkv", lambda: lc.attn_fwd_splitkv(q, k, v, scale=w.scale, workspace=ws, o=o,
+                                                                      lse=lse))):
+        ms, tr = traced_calls(lc, torch, fn, iters, warmup)
+        ms_plain = time_calls(torch, fn, iters, warmup)  # without the per-launch events
+        res[name] = {"us": round(1e3 * ms_plain, 2), "TFLOP/s": round(tflops(f, ms_plain), 2),
+                     "frac_peak": round(tflops(f, ms_plain) / PEAK_BF16_TFLOPS, 4),
+                     "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in tr.items()}}
+        kern = "attn_fwd_kernel" if name == "attn_fwd" else "attn_fwd_kernel_fp32out"
+        rls[f"{w.name}.{name}"] = roofline_entry(kern, tr, f, "TFLOP/s", w.name)
+    return res, rls
+
+
+def leg_ulysses_512k(lc, torch, dev, iters=3, warmup=1):
+    """The 512K-token forward of one Ulysses share: 4 query heads on 1
+    key/value head, seeded inputs 0.5 N(0,1)."""
+    from long_context_attention_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["ulysses_512k"]
+    d = host_inputs(w.name)
+    q, k, v = (to_dev(torch, d[n], dev) for n in "qkv")
+    B, Hq, N, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    f = fwd_flops(B, Hq, N, D)
+    ms, tr = traced_calls(lc, torch, lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse), iters, warmup)
+    res = {"workload": w.name, "shape": [B, Hq, N, D], "kv_heads": w.Hkv, "ms": round(ms, 3),
+           "TFLOP/s": round(tflops(f, ms), 2), "frac_peak": round(tflops(f, ms) / PEAK_BF16_TFLOPS, 4),
+           "algorithmic_flops": f}
+    return res, {f"{w.name}.attn_fwd": roofline_entry("attn_fwd_kernel", tr, f, "TFLOP/s", w.name)}
+
+
+def leg_ring_blocks_32k(lc, torch, dev, iters=10, warmup=2):
+    """The ring workload at its configured shape: B = 1, 8 heads (8 KV heads),
+    N = 32768, four contiguous 8192-key blocks: the four partial forwards
+    (fp32 O and LSE per block, one grouped launch: they are independent) and
+    attn_partial_merge of the four fp32 partials (609 MB of HBM traffic), and
+    the full attn_fwd for comparison."""
+    from long_context_attention_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["ring_blocks_32k"]
+    d = host_inputs(w.name)
+    q, k, v = (to_dev(torch, d[n], dev) for n in "qkv")
+    B, H, N, D = q.shape
+    nb = w.kv_blocks
+    blk = N // nb
+    kb = [k[:, :, a:a + blk].contiguous() for a in range(0, N, blk)]
+    vb = [v[:, :, a:a + blk].contiguous() for a in range(0, N, blk)]
+    o_parts = torch.empty((nb, B, H, N, D), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((nb, B, H, N), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    f_parts = sum(pair_flops_block(H, D, N, a, a + blk) for a in range(0, N, blk))
+    merge_bytes = o_parts.numel() * 4 + lse_parts.numel() * 4 + o.numel() * 2 + lse.numel() * 4
+
+    def partials():
+        lc.attn_fwd_accumulate_group([dict(q=q, k=kb[i], v=vb[i], o_acc=o_parts[i], lse_acc=lse_parts[i], first=True,
+                                           k_pos0=i * blk) for i in range(nb)], causal=True, scale=w.scale)
+    ms_p, tr_p = traced_calls(lc, torch, partials, iters, warmup)
+    ms_m, tr_m = traced_calls(lc, torch, lambda: lc.attn_partial_merge(o_parts, lse_parts, o=o, lse=lse), iters,
+                              warmup)
+    ms_f, tr_f = traced_calls(lc, torch, lambda: lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse), iters, warmup)
+    res = {"workload": w.name, "shape": [B, H, N, D], "kv_blocks": nb,
+           "partials_x4": {"ms": round(ms_p, 4), "TFLOP/s": round(tflops(f_parts, ms_p), 2),
+                           "frac_peak": round(tflops(f_parts, ms_p) / PEAK_BF16_TFLOPS, 4)},
+           "merge": {"ms": round(ms_m, 4), "bytes": merge_bytes, "GB/s": round(gbps(merge_bytes, ms_m), 1),
+                     "frac_peak": round(gbps(merge_bytes, ms_m) / PEAK_HBM_GBPS, 4)},
+           "partials_plus_merge_ms": round(ms_p + ms_m, 4),
+           "full_attn_fwd": {"ms": round(ms_f, 4), "TFLOP/s": round(tflops(f_parts, ms_f), 2),
+                             "frac_peak": round(tflops(f_parts, ms_f) / PEAK_BF16_TFLOPS, 4)}}
+    rls = {f"{w.name}.partials": roofline_entry("attn_fwd_kernel_fp32out", tr_p, f_parts, "TFLOP/s", w.name),
+           f"{w.name}.merge": roofline_entry("merge_kernel", tr_m, merge_bytes, "GB/s", w.name),
+           f"{w.name}.attn_fwd": roofline_entry("attn_fwd_kernel", tr_f, f_parts, "TFLOP/s", w.name)}
+    return res, rls
+
+
+def leg_ulysses_shard_32k(lc, torch, dev, steps, warmup, extras):
+    """One GPU's Ulysses share of a Llama-3-8B-shaped layer (32 query / 8
+    key-value heads, D = 128, N = 32768 split P = 8 ways), the whole path in
+    one step:
+      1. seq_to_head_relayout_batch of Q, K, V, dO (all P shards, one launch)
+      2. attn_fwd on shard 0 (4 query heads, 1 KV head, causal GQA)
+      3. the ring form of the same forward: 4 partial calls over 8192-key
+         blocks (fp32, one grouped launch) + attn_partial_merge
+      4. attn_bwd on shard 0 (from step 2's O and LSE)
+      5. head_to_seq_relayout_batch of O, dQ, dK, dV (one launch)"""
+    from long_context_attention_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["ulysses_shard_32k"]
+    P, N, D, Hq, Hkv = w.P, w.N, w.D, w.Hq, w.Hkv
+    hq, hkv = Hq // P, Hkv // P
+    d = host_inputs(w.name)
+    xs = {n: to_dev(torch, d[n], dev) for n in ("q", "k", "v", "do")}
+    heads = {"q": torch.empty((P, hq, N, D), dtype=torch.bfloat16, device=dev),
+             "do": torch.empty((P, hq, N, D), dtype=torch.bfloat16, device=dev),
+             "k": torch.empty((P, hkv, N, D), dtype=torch.bfloat16, device=dev),
+             "v": torch.empty((P, hkv, N, D), dtype=torch.bfloat16, device=dev)}
+    # shard 0's results go straight into slot 0 of the head-major buffers; the
+    # inverse relayout moves all P shards' bytes, as the exchange would
+    o_all = torch.zeros((P, hq, N, D), dtype=torch.bfloat16, device=dev)
+    dq_all = torch.zeros_like(o_all)
+    dk_all = torch.zeros((P, hkv, N, D), dtype=torch.bfloat16, device=dev)
+    dv_all = torch.zeros_like(dk_all)
+    o, dq, dk, dv = o_all[0:1], dq_all[0:1], dk_all[0:1], dv_all[0:1]
+    lse = torch.empty((1, hq, N), dtype=torch.float32, device=dev)
+    o_tok = torch.empty((P, N // P, Hq, D), dtype=torch.bfloat16, device=dev)
+    dq_tok = torch.empty_like(o_tok)
+    dk_tok = torch.empty((P, N // P, Hkv, D), dtype=torch.bfloat16, device=dev)
+    dv_tok = torch.empty_like(dk_tok)
+    n_blk = 4
+    blk = N // n_blk
+    o_parts = torch.empty((n_blk, 1, hq, N, D), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((n_blk, 1, hq, N), dtype=torch.float32, device=dev)
+    o_ring = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
+    lse_ring = torch.empty_like(lse)
+    ws = torch.empty(lc.attn_bwd_workspace_size(1, hq, hkv, N, D), dtype=torch.uint8, device=dev)
+    scale = w.scale
+    stream = torch.cuda.current_stream(dev)
+    ring_blocks = [(a, heads["k"][0:1, :, a:a + blk], heads["v"][0:1, :, a:a + blk]) for a in range(0, N, blk)]
+    assert all(kb.is_contiguous() and vb.is_contiguous() for _, kb, vb in ring_blocks)
+    names = ["relayout_in", "fwd", "ring_partials", "merge", "bwd", "relayout_out"]
+
+    def step(record):
+        marks = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
+        mark()
+        lc.seq_to_head_relayout_batch([xs[n] for n in ("q", "k", "v", "do")], P,
+                                      outs=[heads[n] for n in ("q", "k", "v", "do")])
+        mark()
+        q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
+        lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
+        mark()
+        lc.attn_fwd_accumulate_group(
+            [dict(q=q0, k=kb, v=vb, o_acc=o_parts[i], lse_acc=lse_parts[i], first=True, k_pos0=a)
+             for i, (a, kb, vb) in enumerate(ring_blocks)], causal=True, scale=scale)
+        mark()
+        lc.attn_partial_merge(o_parts, lse_parts, o=o_ring, lse=lse_ring)
+        mark()
+        lc.attn_bwd(q0, k0, v0, o, do0, lse, causal=True, scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        mark()
+        lc.head_to_seq_relayout_batch([o_all, dq_all, dk_all, dv_all], P, outs=[o_tok, dq_tok, dk_tok, dv_tok])
+        mark()
+        return marks
+
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    lc.trace_collect()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    all_marks = []
+    lc.trace_enable(True)
+    t0.record(stream)
+    for _ in range(steps):
+        all_marks.append(step(True))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    lc.trace_enable(False)
+    tr = lc.trace_collect()
+    ms_step = t0.elapsed_time(t1) / steps
+    per = {n: sum(m[i].elapsed_time(m[i + 1]) for m in all_marks) / steps for i, n in enumerate(names)}
+    f_fwd = fwd_flops(1, hq, N, D)
+    f_ring = sum(pair_flops_block(hq, D, N, a, a + blk) for a in range(0, N, blk))
+    f_bwd = 2.5 * f_fwd
+    rel_in = 2 * 2 * sum(xs[n].numel() for n in ("q", "k", "v", "do"))
+    rel_out = 2 * 2 * (o_all.numel() + dq_all.numel() + dk_all.numel() + dv_all.numel())
+    merge_bytes = o_parts.numel() * 4 + lse_parts.numel() * 4 + o_ring.numel() * 2 + lse_ring.numel() * 4
+
+    def ph(ms, f=None, b=None):
+        if f is not None:
+            return {"ms": round(ms, 4), "TFLOP/s": round(tflops(f, ms), 2),
+                    "frac_peak": round(tflops(f, ms) / PEAK_BF16_TFLOPS, 4)}
+        return {"ms": round(ms, 4), "GB/s": round(gbps(b, ms), 1), "frac_peak": round(gbps(b, ms) / PEAK_HBM_GBPS, 4)}
+    res = {"workload": w.name, "P": P, "N": N, "shard_heads_q": hq, "shard_heads_kv": hkv, "D": D,
+           "step": "relayout q,k,v,dO -> fwd -> 4 partial fwd + merge -> bwd -> relayout o,dq,dk,dv",
+           "ms_per_step": round(ms_step, 4),
+           "attention_TFLOP/s": round(tflops(f_fwd + f_ring + f_bwd, ms_step), 2),
+           "phases": {"relayout_seq_to_head_qkvdo": ph(per["relayout_in"], b=rel_in),
+                      "fwd": ph(per["fwd"], f=f_fwd), "ring_partials_x4": ph(per["ring_partials"], f=f_ring),
+                      "merge": ph(per["merge"], b=merge_bytes), "bwd": ph(per["bwd"], f=f_bwd),
+                      "relayout_head_to_seq_o_grads": ph(per["relayout_out"], b=rel_out)}}
+    rls = {f"{w.name}.relayout": roofline_entry("transpose_rows_kernel", tr, (rel_in + rel_out) / 2, "GB/s", w.name),
+           f"{w.name}.attn_fwd": roofline_entry("attn_fwd_kernel", tr, f_fwd, "TFLOP/s", w.name),
+           f"{w.name}.ring_partials": roofline_entry("attn_fwd_kernel_fp32out", tr, f_ring, "TFLOP/s", w.name),
+           f"{w.name}.merge": roofline_entry("merge_kernel", tr, merge_bytes, "GB/s", w.name),
+           f"{w.name}.bwd_dkdv_kernel": roofline_entry("bwd_dkdv_kernel", tr, 0.8 * f_bwd, "TFLOP/s", w.name),
+           f"{w.name}.bwd_dq_kernel": roofline_entry("bwd_dq_kernel", tr, 0.2 * f_bwd, "TFLOP/s", w.name)}
+    if extras:
+        res.update(shard_extras(lc, torch, dev, w, xs, heads, o, dq, dk, dv, lse, o_parts, lse_parts, o_ring, ws,
+                                f_fwd, f_ring, f_bwd))
+    return res, rls
+
+
+def shard_extras(lc, torch, dev, w, xs, heads, o, dq, dk, dv, lse, o_parts, lse_parts, o_ring, ws, f_fwd, f_ring,
+                 f_bwd):
+    """Variants of the shard's attention: read token-major without a relayout
+    (forward and backward), the ring streamed into one running result, the
+    ring's backward, and ring sharding over 4 ranks."""
+    P, N, D, Hq, Hkv = w.P, w.N, w.D, w.Hq, w.Hkv
+    hq, hkv = Hq // P, Hkv // P
+    scale = w.scale
+    blk = N // 4
+    out = {}
+
+    def r(ms, f):
+        return {"ms": round(ms, 4), "TFLOP/s": round(tflops(f, ms), 2),
+                "frac_peak": round(tflops(f, ms) / PEAK_BF16_TFLOPS, 4)}
+    qv = xs["q"].view(N, Hq, D)[:, :hq].permute(1, 0, 2).unsqueeze(0)
+    kv_ = xs["k"].view(N, Hkv, D)[:, :hkv].permute(1, 0, 2).unsqueeze(0)
+    vv = xs["v"].view(N, Hkv, D)[:, :hkv].permute(1, 0, 2).unsqueeze(0)
+    o_tm = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
+    ms = time_calls(torch, lambda: lc.attn_fwd_strided(qv, kv_, vv, causal=True, scale=scale, o=o_tm, lse=lse))
+    out["token_major_forward"] = {"call": "attn_fwd_strided on shard 0's heads of the token-major input", **r(ms, f_fwd)}
+
+    def tm_heads(x, H, n):
+        return x.view(N, H, D)[:, :n].permute(1, 0, 2).unsqueeze(0)
+    o_tmb = torch.empty((N, Hq, D), dtype=torch.bfloat16, device=dev)
+    g_tm = [torch.empty((N, H, D), dtype=torch.bfloat16, device=dev) for H in (Hq, Hkv, Hkv)]
+    ov = tm_heads(o_tmb, Hq, hq)
+    lc.attn_fwd_strided(qv, kv_, vv, causal=True, scale=scale, o=ov, lse=lse)
+    dov = tm_heads(xs["do"], Hq, hq)
+    gq, gk, gv = tm_heads(g_tm[0], Hq, hq), tm_heads(g_tm[1], Hkv, hkv), tm_heads(g_tm[2], Hkv, hkv)
+    ms = time_calls(torch, lambda: lc.attn_bwd_strided(qv, kv_, vv, ov, dov, lse, causal=True, scale=scale,
+                                                       workspace=ws, dq=gq, dk=gk, dv=gv))
+    out["token_major_backward"] = {"call": "attn_bwd_strided on shard 0's heads of token-major Q, K, V, O, dO",
+                                   **r(ms, f_bwd)}
+    del o_tmb, g_tm
+    o_acc = o_parts[0]
+    q0, k0, v0, do0 = (heads[n][0:1] for n in ("q", "k", "v", "do"))
+
+    def streamed():
+        for i, a in enumerate(range(0, N, blk)):
+            lc.attn_fwd_accumulate(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], o_acc, lse_parts[0],
+                                   first=(i == 0), causal=True, scale=scale, k_pos0=a,
+                                   o_final=o_ring if a + blk >= N else None)
+    out["ring_streamed"] = {"call": "4 x attn_fwd_accumulate (running fp32 O, LSE; bf16 O from the last)",
+                            **r(time_calls(torch, streamed), f_ring)}
+    lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
+    dq_acc = o_parts[1]
+    delta = torch.empty_like(lse)
+    ws_blk = torch.empty(max(16, lc.attn_bwd_block_workspace_size(1, hq, hkv, blk, D)), dtype=torch.uint8,
+                         device=dev)
+
+    def ring_backward():
+        lc.attn_bwd_delta(o, do0, delta=delta)
+        for i, a in enumerate(range(0, N, blk)):
+            lc.attn_bwd_block(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], do0, lse, delta, causal=True,
+                              scale=scale, k_pos0=a, dq_acc=dq_acc, dq_accumulate=i > 0,
+                              dq=dq if a + blk >= N else None, dk=dk[:, :, a:a + blk], dv=dv[:, :, a:a + blk],
+                              workspace=ws_blk)
+    out["ring_backward"] = {"call": "attn_bwd_delta + 4 x attn_bwd_block (fp32 dQ accumulated)",
+                            **r(time_calls(torch, ring_backward), 2.5 * f_ring)}
+    out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd)
+    return out
+
+
+def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, Pr=4):
+    """Shard 0's causal attention as a Pr-rank ring over 2*Pr chunks, every
+    rank's every step timed on this GPU: the ring waits for the slowest rank
+    at each step, so its critical path is the sum over steps of the maximum
+    over ranks.  Contiguous sharding against zigzag (rank r holds chunks r
+    and 2*Pr-1-r)."""
+    from long_context_attention_fwd_amd.ring import SCHEMES, rank_chunks, ring_forward
+    C = N // (2 * Pr)
+    q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))
+    cq = [q0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    ck = [k0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    cv = [v0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    o_acc = [torch.empty((1, hq, C, D), dtype=torch.float32, device=dev) for _ in range(2)]
+    lse = [torch.empty((1, hq, C), dtype=torch.float32, device=dev) for _ in range(2)]
+    o_fin = [torch.empty((1, hq, C, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    res = {"ranks": Pr, "chunk_tokens": C,
+           "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair, in sequence"}
+    for scheme, grouped in [(sc, g) for g in (False, True) for sc in SCHEMES]:
+        t = [[0.0] * Pr for _ in range(Pr)]
+        for r in range(Pr):
+            qs = [cq[c] for c in rank_chunks(r, Pr, scheme)]
+
+            def kv(src, scheme=scheme):
+                return tuple((ck[c], cv[c]) for c in rank_chunks(src, Pr, scheme))
+            for st in range(Pr):
+                t[r][st] = time_calls(torch, lambda: ring_forward(qs, kv, r, Pr, C, o_acc=o_acc, lse_acc=lse,
+                                                                  o_final=o_fin, scheme=scheme, scale=scale,
+                                                                  steps={st}, grouped=grouped))
+        crit = sum(max(t[r][s] for r in range(Pr)) for s in range(Pr))
+        res[scheme + ("_grouped" if grouped else "")] = {
+            "critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
+            "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
+            "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
+            "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
+    return res
+
+
+# ---------------------------------------------------------------------------
+# the oracle on the host cores
+# ---------------------------------------------------------------------------
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _blas_config():
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')} ({b.get('openblas configuration', '').strip()})"
+    except Exception:  # noqa: BLE001 -- reporting only
+        return "unknown"
+
+
+def _run_tasks(tasks, fn, workers):
+    """fn over tasks in a thread pool, BLAS held to one thread per task (the
+    tasks are independent query rows of the oracle's definition)."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        if workers == 1:
+            return [fn(t) for t in tasks]
+        with cf.ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, tasks))
+
+
+def _chunks(rows, n):
+    return [rows[i:i + n] for i in range(0, len(rows), n)]
+
+
+def cpu_baseline():
+    """The fp64 oracle as it stands (oracle/attention.py, untuned) on the host
+    cores, per workload, on the work the parity tests give it: the 4K shape in
+    full (all threads, and one thread), 256 sampled query rows of every head
+    for the 32K shard, the 32K ring (partials + merge) and the 512K share, and
+    for the 64K training shape the full fp64 forward (LSE and Dv of every row)
+    plus the gradients at 128 sampled rows.  Independent query rows run in a
+    thread pool with BLAS held to one thread per task.  Rates are algorithmic
+    flops (as on the GPU) per second; full-workload times at those rates are
+    extrapolations and labelled so."""
     import numpy as np
 
     import oracle
-    from long_context_attention_fwd_amd.inputs import make_workload_inputs
+    from long_context_attention_fwd_amd.inputs import WORKLOADS, sample_rows
 
-    d = make_workload_inputs(w)
-    ref = {n: oracle.seq_to_head(d[n], w.P)[0:1] for n in "qkv"}
-    N, D, hq = w.N, w.D, w.Hq // w.P
-    done_rows, flops, t_used = 0, 0.0, 0.0
-    end = N
-    while t_used < budget_s and end > 0:
-        rows = np.arange(max(0, end - 256), end)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    per = {}
+
+    def f64(bits):
+        return oracle.bf16_bits_to_f64(bits)
+
+    def rows_flops(rows, nh, D):  # forward flops of causal rows (all keys up to the row)
+        return 4.0 * nh * D * float((np.asarray(rows) + 1).sum())
+
+    def fwd_rows(q, k, v, s, G, k_pos0=0):
+        def run(t):
+            h, rows = t
+            return oracle.attention_forward(q[:, h:h + 1], k[:, h // G:h // G + 1], v[:, h // G:h // G + 1], s, True,
+                                            0, k_pos0, rows=rows)
+        return run
+
+    # listing_4k: every row and head, all threads and one thread
+    w = WORKLOADS["listing_4k"]
+    d = host_inputs(w.name)
+    q, k, v = (f64(d[n]) for n in "qkv")
+    G = w.Hq // w.Hkv
+    tasks = [(h, r) for h in range(w.Hq) for r in _chunks(np.arange(w.N)[::-1].copy(), 256)]
+    f = fwd_flops(1, w.Hq, w.N, w.D)
+    for n_thr in (workers, 1):
         t0 = time.perf_counter()
-        oracle.attention_forward(ref["q"], ref["k"], ref["v"], w.scale, True, rows=rows)
-        t_used += time.perf_counter() - t0
-        flops += 4.0 * hq * D * float((rows + 1).sum())
-        done_rows += len(rows)
-        end -= 256
-    cores = len(os.sched_getaffinity(0))
-    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 forward of the last {done_rows} query rows x {hq} heads of shard 0 "
-                      f"(N={N}, D={D}); {t_used:.1f} s of CPU work",
-            "seconds": round(t_used, 2)}
+        _run_tasks(tasks, fwd_rows(q, k, v, w.scale, G), n_thr)
+        dt = time.perf_counter() - t0
+        per[f"{w.name}" + ("" if n_thr > 1 else "_1thread")] = {
+            "work": "fp64 forward, every row and head", "threads": n_thr, "seconds": round(dt, 3),
+            "GFLOP/s": round(f / dt / 1e9, 2), "algorithmic_flops": f}
+
+    # ulysses_shard_32k: 256 sampled rows x 4 heads of shard 0 (the oracle's own relayout)
+    w = WORKLOADS["ulysses_shard_32k"]
+    d = host_inputs(w.name)
+    ref = {n: f64(oracle.seq_to_head(d[n], w.P)[0:1]) for n in "qkv"}
+    hq = w.Hq // w.P
+    rows = sample_rows(w.N, w.seed, w.sampled_rows)
+    tasks = [(h, r) for h in range(hq) for r in _chunks(rows[::-1].copy(), 16)]
+    t0 = time.perf_counter()
+    _run_tasks(tasks, fwd_rows(ref["q"], ref["k"], ref["v"], w.scale, hq), workers)
+    dt = time.perf_counter() - t0
+    fs = rows_flops(rows, hq, w.D)
+    full = fwd_flops(1, hq, w.N, w.D)
+    per[w.name] = {"work": f"fp64 forward, {len(rows)} sampled rows x {hq} heads of shard 0", "threads": workers,
+                   "seconds": round(dt, 3), "GFLOP/s": round(fs / dt / 1e9, 2), "algorithmic_flops": fs,
+                   "extrapolated_full_forward_s": round(full / (fs / dt), 1)}
+
+    # ring_blocks_32k: 256 sampled rows x 8 heads, four 8192-key partials + merge
+    w = WORKLOADS["ring_blocks_32k"]
+    d = host_inputs(w.name)
+    q, k, v = (f64(d[n]) for n in "qkv")
+    blk = w.N // w.kv_blocks
+    rows = sample_rows(w.N, w.seed, w.sampled_rows, block=blk)
+
+    def ring_rows(t):
+        h, rr = t
+        parts = [oracle.attention_forward(q[:, h:h + 1], k[:, h:h + 1, a:a + blk], v[:, h:h + 1, a:a + blk], w.scale,
+                                          True, 0, a, rows=rr) for a in range(0, w.N, blk)]
+        return oracle.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    tasks = [(h, r) for h in range(w.Hq) for r in _chunks(rows[::-1].copy(), 16)]
+    t0 = time.perf_counter()
+    _run_tasks(tasks, ring_rows, workers)
+    dt = time.perf_counter() - t0
+    fs = rows_flops(rows, w.Hq, w.D)
+    full = fwd_flops(1, w.Hq, w.N, w.D)
+    per[w.name] = {"work": f"fp64 partials over 4 key blocks + LSE merge, {len(rows)} sampled rows x {w.Hq} heads",
+                   "threads": workers, "seconds": round(dt, 3), "GFLOP/s": round(fs / dt / 1e9, 2),
+                   "algorithmic_flops": fs, "extrapolated_full_partials_s": round(full / (fs / dt), 1)}
+    del q, k, v
+
+    # ulysses_512k: 256 sampled rows x 4 heads
+    w = WORKLOADS["ulysses_512k"]
+    d = host_inputs(w.name)
+    q, k, v = (f64(d[n]) for n in "qkv")
+    rows = sample_rows(w.N, w.seed, w.sampled_rows)
+    tasks = [(h, r) for h in range(w.Hq) for r in _chunks(rows[::-1].copy(), 8)]
+    t0 = time.perf_counter()
+    _run_tasks(tasks, fwd_rows(q, k, v, w.scale, w.Hq // w.Hkv), workers)
+    dt = time.perf_counter() - t0
+    fs = rows_flops(rows, w.Hq, w.D)
+    full = fwd_flops(1, w.Hq, w.N, w.D)
+    per[w.name] = {"work": f"fp64 forward, {len(rows)} sampled rows x {w.Hq} heads", "threads": workers,
+                   "seconds": round(dt, 3), "GFLOP/s": round(fs / dt / 1e9, 2), "algorithmic_flops": fs,
+                   "extrapolated_full_forward_s": round(full / (fs / dt), 1)}
+    del q, k, v
+
+    # train_64k: full fp64 forward (LSE, Dv of every row) + gradients at 128 sampled rows
+    w = WORKLOADS["train_64k"]
+    d = host_inputs(w.name)
+    q, k, v, do = (f64(d[n]) for n in ("q", "k", "v", "do"))
+    rows = sample_rows(w.N, w.seed, w.sampled_rows)
+    L = np.empty((1, w.Hq, w.N))
+    Dv = np.empty((1, w.Hq, w.N))
+
+    def fwd_task(t):
+        h, rr = t
+        O, l = oracle.attention_forward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w.scale, True, rows=rr)
+        L[0, h, rr] = l[0, 0]
+        Dv[0, h, rr] = np.einsum("nd,nd->n", do[0, h, rr], O[0, 0])
+    tasks = [(h, np.arange(r0, min(w.N, r0 + 2048))) for r0 in range(w.N - 2048, -1, -2048) for h in range(w.Hq)]
+    t0 = time.perf_counter()
+    _run_tasks(tasks, fwd_task, workers)
+
+    def grad_task(h):
+        return oracle.attention_backward_sampled(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], do[:, h:h + 1],
+                                                 w.scale, rows, rows, True, lse=L[:, h:h + 1], dv=Dv[:, h:h + 1])
+    _run_tasks(list(range(w.Hq)), grad_task, workers)
+    dt = time.perf_counter() - t0
+    f_fwd = fwd_flops(1, w.Hq, w.N, w.D)
+    # gradients: dQ rows need S, dP, dQ (6 D flops per visible pair), dK/dV
+    # rows S, dP, dK, dV (8 D per pair)
+    f_grad = w.Hq * w.D * (6.0 * float((rows + 1).sum()) + 8.0 * float((w.N - rows).sum()))
+    fs = f_fwd + f_grad
+    per[w.name] = {"work": f"fp64 forward of every row x {w.Hq} heads (LSE, Dv) + dQ, dK, dV at {len(rows)} "
+                           "sampled rows", "threads": workers, "seconds": round(dt, 3),
+                   "GFLOP/s": round(fs / dt / 1e9, 2), "algorithmic_flops": fs,
+                   "extrapolated_full_fwd_bwd_s": round(3.5 * f_fwd / (fs / dt), 1)}
+    del q, k, v, do
+    head = per["train_64k"]
+    return {"value": round(head["GFLOP/s"] / 1e3, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"train_64k: {head['work']}; {head['seconds']} s (the headline workload; "
+                      f"{head['extrapolated_full_fwd_bwd_s']} s extrapolated for its full forward + backward)",
+            "cpu_model": _cpu_model(), "blas": _blas_config(), "per_workload": per,
+            "seconds_total": round(sum(p["seconds"] for p in per.values()), 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share only: this build runs no collectives, so --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_fwd_amd as lc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    device_info = {"name": props.name, "compute_units": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", None), "hip": torch.version.hip}
+
+    if args.only and args.calibration_copy:
+        # a plain streaming kernel of known bytes, not one of the library's:
+        # its FETCH_SIZE / WRITE_SIZE calibrate the counters of the same run
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.mul(a, 2.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+    if args.only and args.only != "train_64k":
+        legs = {"listing_4k": lambda: leg_listing_4k(lc, torch, dev),
+                "ulysses_shard_32k": lambda: leg_ulysses_shard_32k(lc, torch, dev, args.steps, args.warmup, False),
+                "ring_blocks_32k": lambda: leg_ring_blocks_32k(lc, torch, dev, args.steps, args.warmup),
+                "ulysses_512k": lambda: leg_ulysses_512k(lc, torch, dev, args.steps, args.warmup)}
+        res, rls = legs[args.only]()
+        print(json.dumps({"only": args.only, "result": res, "rooflines": rls, "device_info": device_info}),
+              flush=True)
+        return
+
+    head = train_64k(lc, torch, dev, args.steps, args.warmup)
+    out = {
+        "metric": "causal attention TFLOP/s fwd/bwd at 1 GPU + % bf16 MFMA peak; relayout GB/s",
+        "value": head["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 (numpy PCG64), no dataset or weights",
+        "config": head["config"],
+        "phases": head["phases"],
+        "gpu_kernels": head["gpu_kernels"],
+        "roofline": head["roofline"],
+        "rooflines": dict(head["rooflines"]),
+        "device_info": device_info,
+    }
+    if args.only is None:
+        legs = {}
+        for name, fn in (("listing_4k", lambda: leg_listing_4k(lc, torch, dev)),
+                         ("ulysses_shard_32k", lambda: leg_ulysses_shard_32k(lc, torch, dev, 10, 2,
+                                                                             not args.no_extras)),
+                         ("ring_blocks_32k", lambda: leg_ring_blocks_32k(lc, torch, dev)),
+                         ("ulysses_512k", lambda: leg_ulysses_512k(lc, torch, dev))):
+            res, rls = fn()
+            legs[name] = res
+            out["rooflines"].update(rls)
+            torch.cuda.synchronize()
+        out["legs"] = legs
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
