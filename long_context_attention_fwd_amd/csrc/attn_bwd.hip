@@ -348,6 +348,316 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV with the work of a key group split over two waves of one SIMD:
+// workgroup = 128 keys of one key/value head x one query head, 8 waves.
+// Wave w < 4 ("A") holds K of keys 32 w .. +31 and accumulates dV: per 32-row
+// query block it computes S = Q K^T, P = exp(S - LSE) (masked), hands the
+// bf16 P to its partner through LDS and adds dV^T += dO^T P.  Wave w + 4
+// ("B"), on the same SIMD, holds V of the same keys and accumulates dK: it
+// computes dP = dO V^T, takes P from LDS, forms dS = P (dP - Dv) and adds
+// dK^T += Q^T dS, one query tile behind A.  Each wave runs half of the
+// block's products, so two waves share every SIMD: one's exponentials and
+// LDS waits overlap the other's matrix-core work.
+// Query tiles of 64 rows arrive by direct loads (rows-swizzled LDS, three
+// buffers); LSE and Dv of a tile through registers; one barrier per tile.
+// LDS is one object (Q tiles | dO tiles | LSE, Dv | P slots) and every
+// fragment address is a lane-constant base plus an offset: in the loop over
+// the unmasked tiles, unrolled over the three buffers, the offsets are
+// immediates (no address arithmetic per read).
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 8;
+
+// b * MUL + ADD, as a compile-time constant when b is one
+template <int MUL, int ADD, class Bf>
+__device__ __forceinline__ auto lin_off(Bf b) {
+  if constexpr (std::is_integral_v<Bf>) return b * MUL + ADD;
+  else return std::integral_constant<int, Bf::value * MUL + ADD>{};
+}
+
+template <int D, bool PARTIAL, bool DENSE>
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
+                                                                             float* __restrict__ dv_part) {
+  using T = SwzTile<D>;
+  constexpr int KT = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NW = kSplitWaves;
+  constexpr int BK = 128;                  // keys per workgroup
+  constexpr int TB = T::BYTES;             // one 64-row tile
+  constexpr int RB = T::ROW_BYTES;
+  constexpr int QR = 0, OR = 3 * TB;       // Q tiles, dO tiles
+  constexpr int XR = 6 * TB;               // per buffer: LSE*log2(e) (64 floats), Dv (64 floats)
+  constexpr int PR = XR + 3 * 512;         // P slots
+  constexpr int PSLOT = 4 * 2 * 2 * 64 * 16;  // 4 key groups x 2 blocks x 2 halves x 64 lanes x 16 bytes
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[PR + 3 * PSLOT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, grp = lane >> 5;
+  const bool role_a = wave < 4;            // wave-uniform
+  const int kg = wave & 3;                 // key group of 32 keys
+  const long long Nq = a.Nq, Nk = a.Nk;
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const long long bz = lin / (nx * ny);
+  const int h = (int)(lin / nx % ny);
+  const int kvh = h / a.G;
+  const long long kt0 = (lin % nx) * BK;
+  const long long kw0 = kt0 + 32 * kg;
+  const int key = (int)(kw0 + c);
+  const float sl = a.scale * kLog2e;
+
+  const long long hb = (bz * a.Hq + h) * Nq;
+  const long long kst = DENSE ? D : a.ks[2];
+  const uint16_t* kbase = DENSE ? a.k + (bz * a.Hkv + kvh) * Nk * D : a.k + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* vbase = DENSE ? a.v + (bz * a.Hkv + kvh) * Nk * D : a.v + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* qbase = DENSE ? a.q + hb * D : a.q + bz * a.qs[0] + h * a.qs[1];
+  const uint16_t* obase = DENSE ? a.d_o + hb * D : a.d_o + bz * a.qs[0] + h * a.qs[1];
+  const float* lbase = a.lse + hb;
+  const float* dbase = a.delta + hb;
+
+  const long long q_first = a.causal ? max(0LL, kt0 - a.dpos) : 0;
+  const long long first_tile = q_first / kBQ;
+  const int n_tiles = q_first >= Nq ? 0 : (int)((Nq + kBQ - 1) / kBQ - first_tile);
+  // tiles masked for wave A: those holding the diagonal of some key group
+  // (the first `head`), and the tail
+  const int head = a.causal ? (int)max(0LL, min((long long)n_tiles,
+                                                (kt0 + BK - a.dpos - first_tile * kBQ + kBQ - 1) / kBQ))
+                            : 0;
+  const bool tail = (Nq % kBQ) != 0;
+  const int body_end = max(head, n_tiles - (tail ? 1 : 0));
+  // tile i lives in buffer (i + shift) % 3: the first unmasked tile in buffer 0
+  const int shift = (3 - head % 3) % 3;
+
+  typename T::template AsyncLoader<NW> ld;
+  ld.init(wave, lane, false, DENSE ? D : a.qs[2]);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  float lv = 0.f;
+  // tile i into its buffer: Q and dO by direct loads, LSE and Dv into a
+  // register of threads 0..127 (stored by `deposit`)
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int bf = (i + shift) % 3;
+    const long long r0 = (first_tile + i) * kBQ;
+    if (r0 + kBQ <= Nq) {
+      ld.load_full(smem + QR + bf * TB, qbase, r0, wave_s);
+      ld.load_full(smem + OR + bf * TB, obase, r0, wave_s);
+    } else {
+      ld.load(smem + QR + bf * TB, qbase, r0, Nq, wave_s);
+      ld.load(smem + OR + bf * TB, obase, r0, Nq, wave_s);
+    }
+    if (tid < 2 * kBQ) {
+      long long row = r0 + (tid & (kBQ - 1));
+      row = row < Nq ? row : Nq - 1;
+      lv = (tid < kBQ ? lbase : dbase)[row];
+    }
+  };
+  auto deposit = [&](int i) __attribute__((always_inline)) {
+    if (tid < 2 * kBQ)
+      reinterpret_cast<float*>(smem + XR + ((i + shift) % 3) * 512)[tid] = tid < kBQ ? lv * kLog2e : lv;
+  };
+  if (n_tiles > 0) issue(0);
+
+  // this wave's operand rows: K (wave A) or V (wave B) of its lane's key
+  bf16x8 kv[KT];
+  {
+    const uint16_t* src = role_a ? kbase : vbase;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < Nk) x = ld_global16(src + (long long)key * kst + 16 * t + 8 * grp);
+      kv[t] = as_bf16x8(x);
+    }
+  }
+  f32x16 acc[DB];  // dV^T (wave A) or dK^T (wave B) of this wave's 32 keys
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+  // lane-constant LDS bases: row fragments of Q (A) / dO (B), transposed
+  // fragments of dO (A) / Q (B), LSE (A) / Dv (B) of the lane group's rows,
+  // this lane's P slot entry
+  const unsigned lds0 = (unsigned)reinterpret_cast<uintptr_t>(smem);
+  unsigned rbase[KT], tbase[DB][2];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) rbase[t] = lds0 + (role_a ? QR : OR) + T::row_off(c, grp, t);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) tbase[db][u] = lds0 + (role_a ? OR : QR) + T::tr_off_rows(lane, db, u);
+  const unsigned xbase = lds0 + XR + (role_a ? 0u : 4u * kBQ) + 32u * grp;
+  const unsigned pbase = lds0 + PR + (unsigned)((kg * 4 * 64 + lane) * 16);
+
+  if (n_tiles > 0) {
+    wait_vmem();
+    deposit(0);
+  }
+  __syncthreads();
+
+  auto rd16 = [&](unsigned base, auto off) __attribute__((always_inline)) {
+    if constexpr (std::is_integral_v<decltype(off)>) return lds_read16_rt(base + (unsigned)off);
+    else return lds_read16_imm<decltype(off)::value>(base);
+  };
+  auto rdtr = [&](unsigned base, auto off) __attribute__((always_inline)) {
+    if constexpr (std::is_integral_v<decltype(off)>) return tr_frag_asm_at<RB>(base, off);
+    else return tr_frag_asm_imm<decltype(off)::value, RB>(base);
+  };
+  auto wr16 = [&](unsigned base, auto off, u32x4 v) __attribute__((always_inline)) {
+    if constexpr (std::is_integral_v<decltype(off)>) lds_write16_rt(base + (unsigned)off, v);
+    else lds_write16_imm<decltype(off)::value>(base, v);
+  };
+
+  // S = Q K^T (A) or dP = dO V^T (B) of 32-row block QB of the tile in
+  // buffer bf, with the block's LSE (A) or Dv (B) rows and, for B, the
+  // partner's P (read with the fragments, waited for with them)
+  auto row_products = [&](auto qb_tag, auto bf, u32x4 (&x)[6]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(qb_tag)::value;
+    u32x4 f[KT];
+    const auto ro = lin_off<TB, QB * 32 * RB>(bf);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) f[t] = rd16(rbase[t], ro);
+    x[0] = rd16(xbase, lin_off<512, QB * 128>(bf));
+    x[1] = rd16(xbase, lin_off<512, QB * 128 + 16>(bf));
+    x[2] = rd16(xbase, lin_off<512, QB * 128 + 64>(bf));
+    x[3] = rd16(xbase, lin_off<512, QB * 128 + 80>(bf));
+    if (!role_a) {
+      x[4] = rd16(pbase, lin_off<PSLOT, (QB * 2 + 0) * 1024>(bf));
+      x[5] = rd16(pbase, lin_off<PSLOT, (QB * 2 + 1) * 1024>(bf));
+    }
+#pragma unroll
+    for (int t = 0; t < KT; t += 4) lds_wait_frags(f[t], f[t + 1], f[t + 2], f[t + 3]);
+    lds_wait_frags(x[0], x[1], x[2], x[3]);
+    if (!role_a) lds_wait_frags2(x[4], x[5]);
+    f32x16 r;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) r[v] = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) r = mfma32x32x16(as_bf16x8(f[t]), kv[t], r);
+    return r;
+  };
+  // acc += X^T W for block QB: X = dO (A) or Q (B) through transposing
+  // reads, W = P (A) or dS (B) in registers
+  auto tr_products = [&](auto qb_tag, auto bf, const bf16x8 (&w)[2]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(qb_tag)::value;
+    const auto to = lin_off<TB, QB * 32 * RB>(bf);
+    u32x4 f[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) f[db][u] = rdtr(tbase[db][u], to);
+    if constexpr (DB == 4) {
+      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+      lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
+    } else {
+      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), w[0], acc[db]);
+      acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), w[1], acc[db]);
+    }
+  };
+  // wave A, block QB of tile i (buffer bf): S, P (written for the partner), dV
+  auto block_a = [&](auto masked_tag, auto qb_tag, auto bf, int i) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int QB = decltype(qb_tag)::value;
+    u32x4 x[6];
+    const f32x16 s = row_products(qb_tag, bf, x);
+    const long long qt0 = (first_tile + i) * kBQ;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float lse2 = __uint_as_float(x[2 * u + (e >> 2)][e & 3]);
+        float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lse2));
+        if (MASKED) {
+          const int qrow = (int)qt0 + QB * 32 + 16 * u + 8 * grp + e;
+          pe = (qrow >= (int)Nq || (a.causal && qrow < key - a.dpos)) ? 0.f : pe;
+        }
+        p[e] = pe;
+      }
+      pb[u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    }
+    wr16(pbase, lin_off<PSLOT, (QB * 2 + 0) * 1024>(bf), as_u32x4(pb[0]));
+    wr16(pbase, lin_off<PSLOT, (QB * 2 + 1) * 1024>(bf), as_u32x4(pb[1]));
+    tr_products(qb_tag, bf, pb);
+  };
+  // wave B, block QB of the tile in buffer bf: dP, dS from the partner's P, dK
+  auto block_b = [&](auto qb_tag, auto bf) __attribute__((always_inline)) {
+    u32x4 x[6];
+    const f32x16 dp = row_products(qb_tag, bf, x);
+    bf16x8 sb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pw = as_bf16x8(x[4 + u]);
+      float ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        ds[e] = (float)pw[e] * (dp[8 * u + e] - __uint_as_float(x[2 * u + (e >> 2)][e & 3]));
+      sb[u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    }
+    tr_products(qb_tag, bf, sb);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // one iteration of the tile loop: A on tile i (buffer bfa), B on tile
+  // i - 1 (buffer bfb), the prefetch of tile i + 1, one barrier
+  auto iter = [&](auto masked_tag, int i, auto bfa, auto bfb) __attribute__((always_inline)) {
+    if (i + 1 < n_tiles) issue(i + 1);
+    if (role_a) {
+      if (i < n_tiles) {
+        block_a(masked_tag, I0{}, bfa, i);
+        block_a(masked_tag, I1{}, bfa, i);
+      }
+    } else if (i > 0) {
+      block_b(I0{}, bfb);
+      block_b(I1{}, bfb);
+    }
+    wait_vmem();
+    if (i + 1 < n_tiles) deposit(i + 1);
+    __syncthreads();
+  };
+  auto bfr = [&](int i) __attribute__((always_inline)) { return (i + shift + 3) % 3; };
+
+  int i = 0;
+  for (; i < head; ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
+  // unmasked tiles: tile i sits in buffer i - head (mod 3)
+  for (; i + 3 <= body_end; i += 3) {
+    iter(std::false_type{}, i, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
+    iter(std::false_type{}, i + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    iter(std::false_type{}, i + 2, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+  }
+  for (; i < body_end; ++i) iter(std::false_type{}, i, bfr(i), bfr(i - 1));
+  for (; i <= n_tiles; ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
+
+  if (key < Nk) {
+    float* part = role_a ? dv_part : dk_part;
+    float* accp = role_a ? a.dv_acc : a.dk_acc;
+    uint16_t* outp = role_a ? a.dv : a.dk;
+    const float mul = role_a ? 1.f : a.scale;
+#pragma unroll
+    for (int dbk = 0; dbk < DB; ++dbk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = dbk * 32 + 8 * j + 4 * grp;
+        f32x4 w = {acc[dbk][4 * j] * mul, acc[dbk][4 * j + 1] * mul, acc[dbk][4 * j + 2] * mul,
+                   acc[dbk][4 * j + 3] * mul};
+        if (PARTIAL) {
+          *reinterpret_cast<f32x4*>(part + ((bz * a.Hq + h) * Nk + key) * D + d) = w;
+        } else {
+          const long long base = ((bz * a.Hkv + kvh) * Nk + key) * D + d;  // fp32 accumulators
+          const long long obf = DENSE ? base : bz * a.ks[0] + kvh * a.ks[1] + key * a.ks[2] + d;  // bf16 dk, dv
+          if (a.dkv_mode != 0) {
+            f32x4* pa = reinterpret_cast<f32x4*>(accp + base);
+            if (a.dkv_mode == 2) w += *pa;  // this call's part added to the running dK, dV
+            *pa = w;
+          }
+          if (outp) *reinterpret_cast<u32x2*>(outp + obf) = pack_bf16x4_bits(w[0], w[1], w[2], w[3]);
+        }
+      }
+  }
+}
+
 // dK[b, kvh] = sum over the G query heads of the group of the fp32 partials,
 // written (or added) as the dK, dV modes of the arguments say.  One thread per
 // 4 elements.
@@ -672,7 +982,34 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const dim3 kgrid((unsigned)((a.Nk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
-  if (a.G == 1) {
+#ifndef LCATTN_DKDV_SPLIT
+#define LCATTN_DKDV_SPLIT 1
+#endif
+  if (LCATTN_DKDV_SPLIT) {
+    float* dk_part = a.G == 1 ? nullptr : a.part;
+    float* dv_part = a.G == 1 ? nullptr : dk_part + (long long)B * a.Hq * a.Nk * D;
+    const dim3 blk(64 * kSplitWaves);
+    if (a.G == 1) {
+      if (dense)
+        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, false, true>), kgrid, blk, 0, stream, a, dk_part,
+                      dv_part);
+      else
+        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, false, false>), kgrid, blk, 0, stream, a, dk_part,
+                      dv_part);
+    } else {
+      if (dense)
+        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, true, true>), kgrid, blk, 0, stream, a, dk_part,
+                      dv_part);
+      else
+        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, true, false>), kgrid, blk, 0, stream, a, dk_part,
+                      dv_part);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long slots = (long long)B * a.Hkv * a.Nk * D / 4;
+      LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
+                    dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv, dense);
+    }
+  } else if (a.G == 1) {
     if (dense)
       LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
                     nullptr, nullptr);

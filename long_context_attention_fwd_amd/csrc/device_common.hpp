@@ -347,6 +347,18 @@ __device__ __forceinline__ u32x4 lds_read16_rt(unsigned addr) {
   return r;
 }
 
+// 16-byte LDS write through inline assembly (see lds_read16_imm: the
+// compiler would otherwise wait for direct loads in flight before it).
+// Ordering against other waves' reads comes from the barrier that follows.
+__device__ __forceinline__ void lds_write16_rt(unsigned addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v));
+}
+
+template <int IMM>
+__device__ __forceinline__ void lds_write16_imm(unsigned addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(IMM));
+}
+
 // Transposed fragment (two transposing reads, the second 4 rows further) at a
 // lane-constant address plus an immediate offset (IMM + 4 ROW_BYTES < 64 KiB).
 template <int IMM, int ROW_BYTES>
@@ -362,6 +374,13 @@ __device__ __forceinline__ u32x4 tr_frag_asm_imm(unsigned addr) {
 // statement so that their uses are ordered after the wait.
 __device__ __forceinline__ void lds_wait_frags(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
   asm("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// The same for two fragments.  Every operand must be a distinct variable: an
+// operand passed twice makes the compiler copy the register, possibly before
+// the wait, i.e. while the load into it is still in flight.
+__device__ __forceinline__ void lds_wait_frags2(u32x4& a, u32x4& b) {
+  asm("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
 
 // Wait until this wave's outstanding global loads (including direct-to-LDS
