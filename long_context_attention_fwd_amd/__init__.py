@@ -48,7 +48,9 @@ __all__ = [
     "STATUS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# the library built next to this file; LCATTN_LIBRARY names another build of
+# the same sources (e.g. the host-sanitizer build of the validation layer)
+LIB_PATH = os.environ.get("LCATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_BF16, ATTN_FP32 = 0, 1
 STATUS = {

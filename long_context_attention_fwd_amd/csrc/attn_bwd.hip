@@ -11,17 +11,16 @@
 //
 // Kernels (no atomics anywhere: results are deterministic):
 //  * bwd_delta: Dv per query row, HBM bound.
-//  * bwd_dkdv: a workgroup owns 128 keys (4 waves x 32 keys, K and V of those
-//    keys resident in registers as MFMA operands) and one query head, and
-//    walks every 64-row query tile that can see them.  Q and dO tiles travel
-//    global -> registers -> LDS (row-major, swizzled; three buffers): S = Q K^T
-//    and dP = dO V^T read them by rows, dV^T += dO^T P and dK^T += Q^T dS
-//    through the transposing LDS read.  Query rows are fed to the MFMA in the
-//    pi order, so P and dS leave the accumulators already in the operand
-//    layout of the next product.  Each 32-row query block is one straight-line
-//    block: its S/dP products, then the dV/dK products of the previous block
-//    interleaved with its own elementwise step (independent MFMA and VALU
-//    work).
+//  * bwd_dkdv: a workgroup owns 128 keys and one query head; the work of each
+//    group of 32 keys is split over two waves of one SIMD.  Wave A holds K
+//    (MFMA operand in registers) and accumulates dV: S = Q K^T, P, dV^T +=
+//    dO^T P; it hands P (bf16) through LDS to wave B, which holds V and
+//    accumulates dK: dP = dO V^T, dS = P (dP - Dv), dK^T += Q^T dS, one query
+//    tile behind.  Query rows are fed to the MFMA in the pi order, so P and dS
+//    leave the accumulators already in the operand layout of the next
+//    product.  64-row Q and dO tiles arrive by direct loads (three buffers);
+//    the unmasked tiles run a loop unrolled over the buffers with immediate
+//    LDS offsets.
 //  * bwd_dkdv_reduce (grouped-query attention only): the per-query-head fp32
 //    partials of dK, dV are summed over the group and rounded to bf16.  One
 //    workgroup per (key tile, query head) gives G times more workgroups than
@@ -31,7 +30,8 @@
 //    dP^T = V dO^T and accumulating dQ^T += K^T dS^T (K through the
 //    transposing read), pipelined the same way.
 // dQ by a separate pass costs two recomputed products (7 contractions instead
-// of 5) but avoids fp32 atomic traffic proportional to N^2 / tile.
+// of 5) but avoids fp32 atomic traffic proportional to N^2 / tile (measured:
+// adding dQ blocks with fp32 atomics runs at 1.35 TB/s, too slow to pay).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "trace.hpp"
@@ -75,278 +75,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   if (n < N && u == 0) delta[(b * gridDim.y + h) * N + n] = s;
 }
 
-// ---------------------------------------------------------------------------
-// dK, dV: workgroup = 128 keys of one key/value head x one query head
-// ---------------------------------------------------------------------------
-constexpr int kDkdvWaves = 4;
 constexpr int kBQ = 64;   // query rows per tile
-
-// DENSE: contiguous [B, H, N, D] tensors (row strides D known at compile
-// time); else the strides of a.
-template <int D, bool PARTIAL, bool DENSE>
-__global__ __launch_bounds__(64 * kDkdvWaves, 1) void bwd_dkdv_kernel(BwdArgs a, float* __restrict__ dk_part,
-                                                                       float* __restrict__ dv_part) {
-  using T = LdsTile<D>;
-  constexpr int KT = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int NW = kDkdvWaves;
-  constexpr int NT = 64 * NW;
-  constexpr int BK = 32 * NW;  // keys per workgroup
-  // per buffer: Q tile, dO tile, LSE*log2(e) (64 floats), Dv (64 floats)
-  constexpr int BUF = 2 * T::BYTES + 2 * kBQ * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * BUF];
-  auto buf = [&](int i) __attribute__((always_inline)) { return smem + (i % 3) * BUF; };
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 31, grp = lane >> 5;
-  const long long Nq = a.Nq, Nk = a.Nk;
-  // XCD-aware order (neighbouring key tiles of one head share an XCD and its
-  // L2 while they stream the same query tiles: 14x less HBM traffic on the
-  // 32K shard)
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  const long long bz = lin / (nx * ny);
-  const int h = (int)(lin / nx % ny);     // query head
-  const int kvh = h / a.G;
-  const long long kt0 = (lin % nx) * BK;
-  const long long kw0 = kt0 + 32 * wave;  // this wave's first key
-  const int key = (int)(kw0 + c);         // this lane's key
-  const float sl = a.scale * kLog2e;
-
-  const long long hb = (bz * a.Hq + h) * Nq;
-  const long long kst = DENSE ? D : a.ks[2], qst_rows = DENSE ? D : a.qs[2];  // row strides
-  const uint16_t* kbase = DENSE ? a.k + (bz * a.Hkv + kvh) * Nk * D : a.k + bz * a.ks[0] + kvh * a.ks[1];
-  const uint16_t* vbase = DENSE ? a.v + (bz * a.Hkv + kvh) * Nk * D : a.v + bz * a.ks[0] + kvh * a.ks[1];
-  const uint16_t* qbase = DENSE ? a.q + hb * D : a.q + bz * a.qs[0] + h * a.qs[1];
-  const uint16_t* obase = DENSE ? a.d_o + hb * D : a.d_o + bz * a.qs[0] + h * a.qs[1];
-  const float* lbase = a.lse + hb;
-  const float* dbase = a.delta + hb;
-
-  // the first query that sees this workgroup's first key (kt0 <= i + dpos)
-  const long long q_first = a.causal ? max(0LL, kt0 - a.dpos) : 0;
-  const long long first_tile = q_first / kBQ;
-  const int n_tiles = q_first >= Nq ? 0 : (int)((Nq + kBQ - 1) / kBQ - first_tile);
-
-  // global -> registers -> LDS staging of one query tile
-  typename T::template Stage<NT> qst, ost;
-  float lv = 0.f;
-  auto fetch = [&](int i) __attribute__((always_inline)) {
-    const long long r0 = (first_tile + i) * kBQ;
-    if constexpr (DENSE) {
-      qst.load(qbase, r0, Nq, tid);
-      ost.load(obase, r0, Nq, tid);
-    } else {
-      qst.load(qbase, r0, Nq, tid, qst_rows);
-      ost.load(obase, r0, Nq, tid, qst_rows);
-    }
-    if (tid < 2 * kBQ) {
-      long long row = r0 + (tid & (kBQ - 1));
-      row = row < Nq ? row : Nq - 1;
-      // no arithmetic on the loaded value here: using it would wait for
-      // every load in flight, the tile prefetch included
-      lv = (tid < kBQ ? lbase : dbase)[row];
-    }
-  };
-  auto deposit = [&](int i) __attribute__((always_inline)) {
-    unsigned char* b = buf(i);
-    qst.store(b, tid);
-    ost.store(b + T::BYTES, tid);
-    if (tid < 2 * kBQ) reinterpret_cast<float*>(b + 2 * T::BYTES)[tid] = tid < kBQ ? lv * kLog2e : lv;
-  };
-  if (n_tiles > 0) fetch(0);
-
-  // K and V rows of this lane's key as B operands (reduction over D)
-  bf16x8 kf[KT], vf[KT];
-#pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < Nk) {
-      x = ld_global16(kbase + (long long)key * kst + 16 * t + 8 * grp);
-      y = ld_global16(vbase + (long long)key * kst + 16 * t + 8 * grp);
-    }
-    kf[t] = as_bf16x8(x);
-    vf[t] = as_bf16x8(y);
-  }
-
-  f32x16 dk_acc[DB], dv_acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      dk_acc[db][v] = 0.f;
-      dv_acc[db][v] = 0.f;
-    }
-  // P and dS of the previous 32-row query block (zero before the first)
-  bf16x8 pb[2], sb[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    pb[u] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    sb[u] = pb[u];
-  }
-  const typename T::RowAddr ra = T::row_addr(swap_bits23(c), grp);
-  const typename T::TrAddr ta = T::tr_addr(lane);
-
-  if (n_tiles > 0) deposit(0);
-  // K and V of this lane in registers before the loop: otherwise the first
-  // product of every tile waits for that tile's prefetch as well
-  wait_vmem();
-  __syncthreads();
-
-  // One 32-row query block of the tile in cur (rows qb*32 ..): S, dP (MFMA),
-  // then the dV, dK products of the previous block (whose tile sits in pbuf at
-  // rows pqb*32 ..) next to this block's elementwise step (VALU).  Straight-
-  // line code; a block with nothing visible runs masked and adds zero.
-  auto block = [&](auto masked_tag, const unsigned char* cur, int qb, long long qt0, const unsigned char* pbuf,
-                   int pqb) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    bf16x8 qrf[KT], orf[KT];
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      qrf[t] = T::row_frag_at(cur, ra, t, qb * 32);
-      orf[t] = T::row_frag_at(cur + T::BYTES, ra, t, qb * 32);
-    }
-    f32x16 s, dp;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s[v] = 0.f;
-      dp[v] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      s = mfma32x32x16(qrf[t], kf[t], s);
-      dp = mfma32x32x16(orf[t], vf[t], dp);
-    }
-    // previous block's products
-    bf16x8 tq[DB][2], to[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int o = T::tr_off(ta, pqb * 32 + 16 * u, db);
-        tq[db][u] = T::tr_frag_at(pbuf, o);
-        to[db][u] = T::tr_frag_at(pbuf + T::BYTES, o);
-      }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        dv_acc[db] = mfma32x32x16(to[db][u], pb[u], dv_acc[db]);
-        dk_acc[db] = mfma32x32x16(tq[db][u], sb[u], dk_acc[db]);
-      }
-    // this block's elementwise step
-    const float* lse_t = reinterpret_cast<const float*>(cur + 2 * T::BYTES);
-    const float* dv_t = lse_t + kBQ;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r0 = qb * 32 + 16 * u + 8 * grp;  // tile rows of registers 8u..8u+7
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_t + r0);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_t + r0 + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dv_t + r0);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dv_t + r0 + 4);
-      float p[8], ds[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float lv2 = e < 4 ? l0[e] : l1[e - 4];
-        const float dvv = e < 4 ? d0[e] : d1[e - 4];
-        float pe = fast_exp2(__builtin_fmaf(s[8 * u + e], sl, -lv2));
-        if (MASKED) {
-          const int qrow = (int)qt0 + r0 + e;
-          pe = (qrow >= (int)Nq || (a.causal && qrow < key - a.dpos)) ? 0.f : pe;
-        }
-        p[e] = pe;
-        ds[e] = pe * (dp[8 * u + e] - dvv);
-      }
-      pb[u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      sb[u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-    }
-    // Instruction order for the scheduler (groups: 0x100 LDS reads, 0x008
-    // MFMA, 0x002 VALU): the 16 row fragments, the 16 S/dP products, the
-    // transposed fragments and LSE/Dv reads, then each dV/dK product followed
-    // by a slice of the elementwise step, so the matrix cores and the vector
-    // ALU work side by side.
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 36, 0);
-#pragma unroll
-    for (int i_ = 0; i_ < 16; ++i_) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    }
-  };
-  // one query tile: prefetch the next into registers, two blocks, deposit
-  auto step = [&](auto masked_tag, int i) __attribute__((always_inline)) {
-    const bool more = i + 1 < n_tiles;
-    if (more) fetch(i + 1);
-    const long long qt0 = (first_tile + i) * kBQ;
-    // before the first block the pending P, dS are zero; point the products at
-    // this tile (finite data) rather than an unwritten buffer
-    block(masked_tag, buf(i), 0, qt0, i == 0 ? buf(i) : buf(i + 2), 1);
-    block(masked_tag, buf(i), 1, qt0, buf(i), 0);
-    if (more) deposit(i + 1);
-    __syncthreads();
-  };
-  // masked tiles: those that hold the diagonal of some wave's keys, and the tail
-  // (tiles holding a query below the workgroup's last key + 1 - dpos)
-  const int head = a.causal ? (int)max(0LL, min((long long)n_tiles,
-                                                (kt0 + BK - a.dpos - first_tile * kBQ + kBQ - 1) / kBQ))
-                            : 0;
-  const bool tail = (Nq % kBQ) != 0;
-  const int body_end = max(head, n_tiles - (tail ? 1 : 0));
-  int i = 0;
-  for (; i < head; ++i) step(std::true_type{}, i);
-  for (; i < body_end; ++i) step(std::false_type{}, i);
-  for (; i < n_tiles; ++i) step(std::true_type{}, i);
-  // products of the last block
-  if (n_tiles > 0) {
-    const unsigned char* pbuf = buf(n_tiles - 1);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int o = T::tr_off(ta, 32 + 16 * u, db);
-        dv_acc[db] = mfma32x32x16(T::tr_frag_at(pbuf + T::BYTES, o), pb[u], dv_acc[db]);
-        dk_acc[db] = mfma32x32x16(T::tr_frag_at(pbuf, o), sb[u], dk_acc[db]);
-      }
-  }
-
-  if (key < Nk) {
-#pragma unroll
-    for (int dbk = 0; dbk < DB; ++dbk)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = dbk * 32 + 8 * j + 4 * grp;
-        const float k0 = dk_acc[dbk][4 * j] * a.scale, k1 = dk_acc[dbk][4 * j + 1] * a.scale;
-        const float k2 = dk_acc[dbk][4 * j + 2] * a.scale, k3 = dk_acc[dbk][4 * j + 3] * a.scale;
-        if (PARTIAL) {
-          const long long base = ((bz * a.Hq + h) * Nk + key) * D + d;
-          const f32x4 wk = {k0, k1, k2, k3};
-          const f32x4 wv = {dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2],
-                            dv_acc[dbk][4 * j + 3]};
-          *reinterpret_cast<f32x4*>(dk_part + base) = wk;
-          *reinterpret_cast<f32x4*>(dv_part + base) = wv;
-        } else {
-          const long long base = ((bz * a.Hkv + kvh) * Nk + key) * D + d;  // fp32 accumulators
-          const long long obf = DENSE ? base : bz * a.ks[0] + kvh * a.ks[1] + key * a.ks[2] + d;  // bf16 dk, dv
-          f32x4 wk = {k0, k1, k2, k3};
-          f32x4 wv = {dv_acc[dbk][4 * j], dv_acc[dbk][4 * j + 1], dv_acc[dbk][4 * j + 2], dv_acc[dbk][4 * j + 3]};
-          if (a.dkv_mode != 0) {
-            f32x4* pk = reinterpret_cast<f32x4*>(a.dk_acc + base);
-            f32x4* pv = reinterpret_cast<f32x4*>(a.dv_acc + base);
-            if (a.dkv_mode == 2) {  // this call's part added to the running dK, dV
-              wk += *pk;
-              wv += *pv;
-            }
-            *pk = wk;
-            *pv = wv;
-          }
-          if (a.dk) {
-            *reinterpret_cast<u32x2*>(a.dk + obf) = pack_bf16x4_bits(wk[0], wk[1], wk[2], wk[3]);
-            *reinterpret_cast<u32x2*>(a.dv + obf) = pack_bf16x4_bits(wv[0], wv[1], wv[2], wv[3]);
-          }
-        }
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK, dV with the work of a key group split over two waves of one SIMD:
@@ -505,15 +234,35 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
     else lds_write16_imm<decltype(off)::value>(base, v);
   };
 
-  // S = Q K^T (A) or dP = dO V^T (B) of 32-row block QB of the tile in
-  // buffer bf, with the block's LSE (A) or Dv (B) rows and, for B, the
-  // partner's P (read with the fragments, waited for with them)
-  auto row_products = [&](auto qb_tag, auto bf, u32x4 (&x)[6]) __attribute__((always_inline)) {
+  // Fragment reads (inline assembly, waited for explicitly) of 32-row block
+  // QB of the tile in buffer bf: rows of Q (A) / dO (B) against this wave's
+  // K / V, and transposed fragments of dO (A) / Q (B)
+  auto read_rows = [&](auto qb_tag, auto bf, u32x4 (&f)[KT]) __attribute__((always_inline)) {
     constexpr int QB = decltype(qb_tag)::value;
-    u32x4 f[KT];
     const auto ro = lin_off<TB, QB * 32 * RB>(bf);
 #pragma unroll
     for (int t = 0; t < KT; ++t) f[t] = rd16(rbase[t], ro);
+  };
+  auto wait_rows = [&](u32x4 (&f)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < KT; t += 4) lds_wait_frags(f[t], f[t + 1], f[t + 2], f[t + 3]);
+  };
+  auto read_tr = [&](auto qb_tag, auto bf, u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(qb_tag)::value;
+    const auto to = lin_off<TB, QB * 32 * RB>(bf);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) f[db][u] = rdtr(tbase[db][u], to);
+  };
+  auto wait_tr = [&](u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; db += 2) lds_wait_frags(f[db][0], f[db][1], f[db + 1][0], f[db + 1][1]);
+  };
+  // the block's LSE (A) or Dv (B) of the lane group's rows, and for B the
+  // partner's P
+  auto read_x = [&](auto qb_tag, auto bf, u32x4 (&x)[6]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(qb_tag)::value;
     x[0] = rd16(xbase, lin_off<512, QB * 128>(bf));
     x[1] = rd16(xbase, lin_off<512, QB * 128 + 16>(bf));
     x[2] = rd16(xbase, lin_off<512, QB * 128 + 64>(bf));
@@ -522,10 +271,12 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
       x[4] = rd16(pbase, lin_off<PSLOT, (QB * 2 + 0) * 1024>(bf));
       x[5] = rd16(pbase, lin_off<PSLOT, (QB * 2 + 1) * 1024>(bf));
     }
-#pragma unroll
-    for (int t = 0; t < KT; t += 4) lds_wait_frags(f[t], f[t + 1], f[t + 2], f[t + 3]);
+  };
+  auto wait_x = [&](u32x4 (&x)[6]) __attribute__((always_inline)) {
     lds_wait_frags(x[0], x[1], x[2], x[3]);
     if (!role_a) lds_wait_frags2(x[4], x[5]);
+  };
+  auto mfma_rows = [&](u32x4 (&f)[KT]) __attribute__((always_inline)) {
     f32x16 r;
 #pragma unroll
     for (int v = 0; v < 16; ++v) r[v] = 0.f;
@@ -533,36 +284,18 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
     for (int t = 0; t < KT; ++t) r = mfma32x32x16(as_bf16x8(f[t]), kv[t], r);
     return r;
   };
-  // acc += X^T W for block QB: X = dO (A) or Q (B) through transposing
-  // reads, W = P (A) or dS (B) in registers
-  auto tr_products = [&](auto qb_tag, auto bf, const bf16x8 (&w)[2]) __attribute__((always_inline)) {
-    constexpr int QB = decltype(qb_tag)::value;
-    const auto to = lin_off<TB, QB * 32 * RB>(bf);
-    u32x4 f[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) f[db][u] = rdtr(tbase[db][u], to);
-    if constexpr (DB == 4) {
-      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
-      lds_wait_frags(f[2][0], f[2][1], f[3][0], f[3][1]);
-    } else {
-      lds_wait_frags(f[0][0], f[0][1], f[1][0], f[1][1]);
-    }
+  auto mfma_tr = [&](u32x4 (&f)[DB][2], const bf16x8 (&w)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       acc[db] = mfma32x32x16(as_bf16x8(f[db][0]), w[0], acc[db]);
       acc[db] = mfma32x32x16(as_bf16x8(f[db][1]), w[1], acc[db]);
     }
   };
-  // wave A, block QB of tile i (buffer bf): S, P (written for the partner), dV
-  auto block_a = [&](auto masked_tag, auto qb_tag, auto bf, int i) __attribute__((always_inline)) {
+  // P of block QB from its S (masked on diagonal and tail tiles)
+  auto probs = [&](auto masked_tag, auto qb_tag, const f32x16& s, const u32x4 (&x)[6], long long qt0,
+                   bf16x8 (&pb)[2]) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int QB = decltype(qb_tag)::value;
-    u32x4 x[6];
-    const f32x16 s = row_products(qb_tag, bf, x);
-    const long long qt0 = (first_tile + i) * kBQ;
-    bf16x8 pb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float p[8];
@@ -578,15 +311,9 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
       }
       pb[u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
     }
-    wr16(pbase, lin_off<PSLOT, (QB * 2 + 0) * 1024>(bf), as_u32x4(pb[0]));
-    wr16(pbase, lin_off<PSLOT, (QB * 2 + 1) * 1024>(bf), as_u32x4(pb[1]));
-    tr_products(qb_tag, bf, pb);
   };
-  // wave B, block QB of the tile in buffer bf: dP, dS from the partner's P, dK
-  auto block_b = [&](auto qb_tag, auto bf) __attribute__((always_inline)) {
-    u32x4 x[6];
-    const f32x16 dp = row_products(qb_tag, bf, x);
-    bf16x8 sb[2];
+  // dS of a block from its dP, Dv and the partner's P
+  auto grads = [&](const f32x16& dp, const u32x4 (&x)[6], bf16x8 (&sb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const bf16x8 pw = as_bf16x8(x[4 + u]);
@@ -596,22 +323,71 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
         ds[e] = (float)pw[e] * (dp[8 * u + e] - __uint_as_float(x[2 * u + (e >> 2)][e & 3]));
       sb[u] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
     }
-    tr_products(qb_tag, bf, sb);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  // wave A, tile i (buffer bf): S of both 32-row blocks; P of block 0
+  // (written for the partner) next to block 1's S products; dV of block 0
+  // next to P of block 1; dV of block 1.  Block 1's LSE is read with block
+  // 0's transposed fragments, so it is not held from the start of the tile.
+  auto tile_a = [&](auto masked_tag, auto bf, int i) __attribute__((always_inline)) {
+    const long long qt0 = (first_tile + i) * kBQ;
+    u32x4 f[KT], g[DB][2], x0[6], x1[6];
+    bf16x8 p0[2], p1[2];
+    read_rows(I0{}, bf, f);
+    read_x(I0{}, bf, x0);
+    wait_rows(f);
+    wait_x(x0);
+    const f32x16 s0 = mfma_rows(f);
+    read_rows(I1{}, bf, f);
+    wait_rows(f);
+    const f32x16 s1 = mfma_rows(f);
+    probs(masked_tag, I0{}, s0, x0, qt0, p0);
+    wr16(pbase, lin_off<PSLOT, 0 * 1024>(bf), as_u32x4(p0[0]));
+    wr16(pbase, lin_off<PSLOT, 1 * 1024>(bf), as_u32x4(p0[1]));
+    read_tr(I0{}, bf, g);
+    read_x(I1{}, bf, x1);
+    wait_tr(g);
+    wait_x(x1);
+    mfma_tr(g, p0);
+    probs(masked_tag, I1{}, s1, x1, qt0, p1);
+    wr16(pbase, lin_off<PSLOT, 2 * 1024>(bf), as_u32x4(p1[0]));
+    wr16(pbase, lin_off<PSLOT, 3 * 1024>(bf), as_u32x4(p1[1]));
+    read_tr(I1{}, bf, g);
+    wait_tr(g);
+    mfma_tr(g, p1);
+  };
+  // wave B, the tile in buffer bf: the same order with dP, dS, dK
+  auto tile_b = [&](auto bf) __attribute__((always_inline)) {
+    u32x4 f[KT], g[DB][2], x0[6], x1[6];
+    bf16x8 d0[2], d1[2];
+    read_rows(I0{}, bf, f);
+    read_x(I0{}, bf, x0);
+    wait_rows(f);
+    wait_x(x0);
+    const f32x16 dp0 = mfma_rows(f);
+    read_rows(I1{}, bf, f);
+    wait_rows(f);
+    const f32x16 dp1 = mfma_rows(f);
+    grads(dp0, x0, d0);
+    read_tr(I0{}, bf, g);
+    read_x(I1{}, bf, x1);
+    wait_tr(g);
+    wait_x(x1);
+    mfma_tr(g, d0);
+    grads(dp1, x1, d1);
+    read_tr(I1{}, bf, g);
+    wait_tr(g);
+    mfma_tr(g, d1);
+  };
   // one iteration of the tile loop: A on tile i (buffer bfa), B on tile
   // i - 1 (buffer bfb), the prefetch of tile i + 1, one barrier
   auto iter = [&](auto masked_tag, int i, auto bfa, auto bfb) __attribute__((always_inline)) {
     if (i + 1 < n_tiles) issue(i + 1);
     if (role_a) {
-      if (i < n_tiles) {
-        block_a(masked_tag, I0{}, bfa, i);
-        block_a(masked_tag, I1{}, bfa, i);
-      }
+      if (i < n_tiles) tile_a(masked_tag, bfa, i);
     } else if (i > 0) {
-      block_b(I0{}, bfb);
-      block_b(I1{}, bfb);
+      tile_b(bfb);
     }
     wait_vmem();
     if (i + 1 < n_tiles) deposit(i + 1);
@@ -981,11 +757,8 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
     e = launch_delta<D>(a.o, a.d_o, a.delta, B, a.Hq, a.Nq, a.qs, stream);
     if (e != hipSuccess) return e;
   }
-  const dim3 kgrid((unsigned)((a.Nk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves)), (unsigned)a.Hq, (unsigned)B);
-#ifndef LCATTN_DKDV_SPLIT
-#define LCATTN_DKDV_SPLIT 1
-#endif
-  if (LCATTN_DKDV_SPLIT) {
+  const dim3 kgrid((unsigned)((a.Nk + 127) / 128), (unsigned)a.Hq, (unsigned)B);  // 128 keys per workgroup
+  {
     float* dk_part = a.G == 1 ? nullptr : a.part;
     float* dv_part = a.G == 1 ? nullptr : dk_part + (long long)B * a.Hq * a.Nk * D;
     const dim3 blk(64 * kSplitWaves);
@@ -1009,27 +782,6 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
       LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
                     dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv, dense);
     }
-  } else if (a.G == 1) {
-    if (dense)
-      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
-                    nullptr, nullptr);
-    else
-      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, false, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
-                    nullptr, nullptr);
-  } else {
-    float* dk_part = a.part;
-    float* dv_part = dk_part + (long long)B * a.Hq * a.Nk * D;
-    if (dense)
-      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true, true>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
-                    dk_part, dv_part);
-    else
-      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_kernel<D, true, false>), kgrid, dim3(64 * kDkdvWaves), 0, stream, a,
-                    dk_part, dv_part);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long slots = (long long)B * a.Hkv * a.Nk * D / 4;
-    LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
-                  dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv, dense);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -78,7 +78,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, lo
   constexpr int QW = 32 * QB;      // query rows per wave
   constexpr int SPAN = (kWaves / HP) * QW;  // query rows per workgroup (per head)
   static_assert(QB == 1, "one block of 32 query rows per wave");
-  static_assert(kBN == 64, "LdsTile holds 64 rows");
+  static_assert(kBN == 64, "SwzTile holds 64 rows");
 
   // LDS: the K tiles of the three pipeline buffers, then their V tiles
   // (row-major, swizzled), in one object so that every fragment read is a

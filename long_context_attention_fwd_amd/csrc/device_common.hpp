@@ -94,97 +94,6 @@ __device__ __forceinline__ int acc_row_pi(int v, int grp) { return 16 * (v >> 3)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
 
-template <int D>
-struct LdsTile {
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int UNITS = D / 8;          // 16-byte units per row
-  static constexpr int BYTES = 64 * ROW_BYTES;  // one 64-row tile
-
-  // Byte offset of 16-byte unit u of row r.
-  __device__ static int off(int r, int u) { return r * ROW_BYTES + ((u ^ tile_swz(r)) << 4); }
-
-  // Per-lane base offsets for the row fragments of rows r + 32k (k any) and
-  // steps t: unit (2t + grp) ^ f(r) = 8 (t >> 2) + ((2 (t & 3)) ^ (grp ^ f(r)))
-  // because 2t and grp occupy different bits and f(r) < 8; so four bases and
-  // immediate offsets cover every t.
-  struct RowAddr {
-    int b[4];
-  };
-  __device__ static RowAddr row_addr(int r, int grp) {
-    RowAddr ra;
-    const int g = grp ^ tile_swz(r);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra.b[i] = r * ROW_BYTES + (((2 * i) ^ g) << 4);
-    return ra;
-  }
-  __device__ static bf16x8 row_frag_at(const unsigned char* lds, const RowAddr& ra, int t, int row_off) {
-    return as_bf16x8(ld_lds16(lds, ra.b[t & 3] + (t >> 2) * 128 + row_off * ROW_BYTES));
-  }
-
-  // Per-lane base offsets of the transposed fragments T[r0 + 8 grp + e][d0 + c]
-  // for r0 a multiple of 16 and d0 = 32 db: the unit is (4 db + x) ^ f(row) with
-  // x < 4, which is a0's or a1's unit plus 8 (db >> 1); rows add 16-row steps.
-  struct TrAddr {
-    int a0, a1;
-  };
-  __device__ static TrAddr tr_addr(int lane) {
-    const int gi = lane >> 4, s = lane & 15;
-    const int row = 8 * (gi >> 1) + (s >> 2);
-    const int x = 2 * (gi & 1) + ((s & 3) >> 1);
-    const int y = x ^ tile_swz(row);
-    TrAddr ta;
-    ta.a0 = row * ROW_BYTES + (y << 4) + ((s & 1) << 3);
-    ta.a1 = row * ROW_BYTES + ((y ^ 4) << 4) + ((s & 1) << 3);
-    return ta;
-  }
-  __device__ static int tr_off(const TrAddr& ta, int r0, int db) {
-    return ((db & 1) ? ta.a1 : ta.a0) + (db >> 1) * 128 + r0 * ROW_BYTES;
-  }
-
-  // Register-staged tile load: NT threads fetch rows [r0, r0 + 64) of a
-  // row-major [rows_total, D] matrix (rows rs elements apart) into CH 16-byte
-  // registers each, then store them into the swizzled LDS tile.  Rows past
-  // rows_total read row rows_total - 1 (finite data that the callers mask).
-  template <int NT>
-  struct Stage {
-    static constexpr int CH = 64 * UNITS / NT;
-    static_assert(CH >= 1 && 64 * UNITS % NT == 0, "threads must divide the tile");
-    u32x4 r[CH];
-    // rows rs elements apart (rs = D: a contiguous matrix)
-    __device__ void load(const uint16_t* g, long long r0, long long rows_total, int tid, long long rs = D) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int id = tid + i * NT;
-        const int row = id / UNITS, u = id % UNITS;
-        long long gr = r0 + row;
-        gr = gr < rows_total ? gr : rows_total - 1;
-        r[i] = ld_global16(g + gr * rs + 8 * u);
-      }
-    }
-    __device__ void store(unsigned char* lds, int tid) const {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int id = tid + i * NT;
-        const int row = id / UNITS, u = id % UNITS;
-        st_lds16(lds, off(row, u), r[i]);
-      }
-    }
-  };
-
-  // Transposed fragment at a precomputed offset (see tr_addr / tr_off).
-  __device__ static bf16x8 tr_frag_at(const unsigned char* lds, int o) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<__attribute__((address_space(3))) s16x4*>(reinterpret_cast<uintptr_t>(lds) + o +
-                                                                   4 * ROW_BYTES));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  }
-};
-
 // Swizzles measured for the two read patterns on gfx950 (64-row x 256-byte
 // tiles, eight waves reading).  tile_swz above reaches about 115 B/clk/CU for
 // either pattern; these reach about 170:
