@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "trace.cpp", "relayout.hip", "merge.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "trace.cpp", "sizes.cpp", "relayout.hip", "merge.hip", "attn_fwd.hip", "attn_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

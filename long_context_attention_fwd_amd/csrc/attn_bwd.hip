@@ -849,19 +849,6 @@ hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
   return hipSuccess;
 }
 
-long long bwd_delta_floats(int B, int Hq, long long Nq) {
-  // Dv rows, padded to a multiple of 64 floats (256 bytes)
-  return ((long long)B * Hq * Nq + 63) / 64 * 64;
-}
-
-long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D) {
-  return Hq != Hkv ? 2LL * B * Hq * Nk * D : 0;  // per-query-head dK, dV partials
-}
-
-long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D) {
-  return (bwd_delta_floats(B, Hq, Nq) + bwd_part_floats(B, Hq, Hkv, Nk, D)) * 4;
-}
-
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream) {
   return D == 64 ? launch_d<64>(a, B, stream) : launch_d<128>(a, B, stream);
 }

@@ -63,9 +63,9 @@ namespace lcattn {
 
 namespace {
 
-constexpr int kWaves = 8;      // two waves per SIMD: one's softmax overlaps the other's MFMAs
+constexpr int kWaves = kFwdWaves;  // two waves per SIMD: one's softmax overlaps the other's MFMAs
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;         // keys per tile
+constexpr int kBN = kFwdKeyTile;   // keys per tile
 
 // The kernel body: workgroup number lin (already in XCD-aware order) of a
 // grid of nx query tiles x ny head groups x (splits x batch).
@@ -582,22 +582,6 @@ hipError_t launch_attn_fwd(const FwdArgs& a0, int B, int D, bool out_f32, hipStr
   contiguous(a.os, a.Hq, a.Nq);
   if (D == 64) return out_f32 ? launch_hp<64, 1, true>(a, B, stream) : launch_hp<64, 1, false>(a, B, stream);
   return out_f32 ? launch_hp<128, 1, true>(a, B, stream) : launch_hp<128, 1, false>(a, B, stream);
-}
-
-int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits) {
-  if (n_splits > 0) return n_splits;
-  const int G = Hq / Hkv;
-  const int HP = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-  const long long span = (kWaves / HP) * 32;
-  const long long wgs = (Nq + span - 1) / span * (Hq / HP) * B;
-  const long long tiles = (Nk + kBN - 1) / kBN;
-  // about one and a half workgroups per compute unit, ranges of at least 16
-  // key tiles (measured: 4K tokens x 4 heads run fastest with 4 ranges, 16K x
-  // 4 query heads on one KV head with 2, 32K x 4 heads unsplit)
-  long long n = (384 + wgs - 1) / wgs;
-  n = std::min<long long>(n, std::max<long long>(1, tiles / 16));
-  (void)causal;
-  return (int)std::max<long long>(1, std::min<long long>(n, 64));
 }
 
 hipError_t launch_attn_fwd_splitkv(const FwdArgs& a0, int B, int D, int n_splits, float* o_parts, float* lse_parts,

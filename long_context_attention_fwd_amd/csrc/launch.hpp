@@ -26,6 +26,10 @@ hipError_t launch_transpose_rows_batch(const TransposeJob* jobs, int n, unsigned
 hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long long A, long long Bn, int D, int rep,
                                hipStream_t stream);
 
+// forward kernel geometry (shared by the launcher and the split-count heuristic)
+constexpr int kFwdWaves = 8;     // waves per workgroup
+constexpr int kFwdKeyTile = 64;  // keys per tile
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
