@@ -326,6 +326,43 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
                    void* hip_stream);
 
 /*
+ * attn_bwd_block_group -- up to ATTN_MAX_BWD_GROUP independent attn_bwd_block
+ * calls in one dK/dV launch and one dQ launch (plus, for grouped-query
+ * attention, one small reduction per call).  On a ring whose ranks hold two
+ * query chunks and receive two key/value chunks per step (zigzag sharding of
+ * "So funktioniert Kontextparallelität"), the step's visible (query chunk,
+ * key chunk) pairs that share neither chunk -- (q1, k1) with (q2, k2), and
+ * (q1, k2) with (q2, k1) -- are independent: their dQ and their dK, dV go to
+ * different accumulators.  Each call's fields mean what the arguments of
+ * attn_bwd_block mean; B, Hq, Hkv, D, scale and causal are shared.  Every call
+ * is validated as attn_bwd_block (errors name the call); in addition no call
+ * may write what another call reads or writes (ATTN_ERR_ALIAS).  Results are
+ * bit-identical to the same calls made one at a time.  Requires 1 <= n <=
+ * ATTN_MAX_BWD_GROUP and B * n <= 65535.
+ */
+#define ATTN_MAX_BWD_GROUP 4
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* lse;
+  const float* delta;
+  float* dq_acc;
+  float* dk_acc;
+  float* dv_acc;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;
+  size_t workspace_bytes;
+  int64_t Nq, Nk, q_pos0, k_pos0;
+  int dq_accumulate, dkv_accumulate;
+} attn_bwd_block_call;
+int attn_bwd_block_group(const attn_bwd_block_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
+                         int causal, void* hip_stream);
+
+/*
  * seq_to_head_relayout -- the Ulysses all-to-all's data movement on one GPU.
  *
  * in  [P, N/P, H, D]: shard p holds tokens p*N/P .. (p+1)*N/P - 1, all heads.

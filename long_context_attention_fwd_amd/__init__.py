@@ -32,6 +32,7 @@ __all__ = [
     "attn_bwd_strided",
     "attn_bwd_delta",
     "attn_bwd_block",
+    "attn_bwd_block_group",
     "attn_bwd_block_workspace_size",
     "seq_to_head_relayout",
     "head_to_seq_relayout",
@@ -79,6 +80,17 @@ class AccumulateCall(ctypes.Structure):
                 ("k_pos0", ctypes.c_int64), ("first", ctypes.c_int)]
 
 
+class BwdBlockCall(ctypes.Structure):
+    """One entry of attn_bwd_block_group (mirrors attn_bwd_block_call)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("d_o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("delta", ctypes.c_void_p),
+                ("dq_acc", ctypes.c_void_p), ("dk_acc", ctypes.c_void_p), ("dv_acc", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64), ("q_pos0", ctypes.c_int64),
+                ("k_pos0", ctypes.c_int64), ("dq_accumulate", ctypes.c_int), ("dkv_accumulate", ctypes.c_int)]
+
+
 _SIGS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P]),
     "attn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P, _P, _P, _P]),
@@ -97,6 +109,7 @@ _SIGS = {
                               _P, _P, _P]),
     "head_to_seq_reduce": (_I, [_P, _I, _P, _I, _L, _I, _I, _P]),
     "attn_bwd_block_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
+    "attn_bwd_block_group": (_I, [_P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_block": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                             _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _I, _P]),
     "seq_to_head_relayout": (_I, [_P, _P, _I, _L, _I, _I, _I, _P]),
@@ -487,15 +500,12 @@ def attn_bwd_block_workspace_size(B: int, Hq: int, Hkv: int, Nk: int, D: int) ->
     return int(lib().attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D))
 
 
-def attn_bwd_block(q, k, v, do, lse, delta, *, causal: bool = True, scale: float | None = None,
-                   q_pos0: int = 0, k_pos0: int = 0, dq_acc=None, dq_accumulate: bool = False,
-                   dk_acc=None, dv_acc=None, dkv_accumulate: bool = False, dq=None, dk=None, dv=None,
-                   workspace=None):
-    """Gradients through one KV block (k, v at global position k_pos0) of the
-    attention of q, given the global lse and Dv (attn_bwd_delta).  fp32
-    accumulators are overwritten, or added to with the *_accumulate flags;
-    bf16 dq / dk / dv, when given, receive rounded copies.  Returns
-    (dq_acc or dq, dk_acc or dk, dv_acc or dv)."""
+def _bwd_block_prepare(q, k, v, do, lse, delta, q_pos0, k_pos0, dq_acc, dq_accumulate, dk_acc, dv_acc,
+                       dkv_accumulate, dq, dk, dv, workspace):
+    """Checks of one block-backward call; allocates the default outputs and
+    workspace.  Returns (BwdBlockCall, (B, Hq, Hkv, D), outputs, workspace):
+    the caller holds the workspace until the launch is enqueued, or its memory
+    could go to the next allocation (another call of the same group)."""
     torch = _torch()
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
         _need(t, name, torch.bfloat16, 4)
@@ -524,19 +534,65 @@ def attn_bwd_block(q, k, v, do, lse, delta, *, causal: bool = True, scale: float
     need = attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
 
     def ptr(t):
-        return t.data_ptr() if t is not None else 0
+        return t.data_ptr() if t is not None else None
 
-    _check(lib().attn_bwd_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                                delta.data_ptr(), ptr(dq_acc), ptr(dk_acc), ptr(dv_acc), ptr(dq), ptr(dk), ptr(dv),
-                                ws_ptr, ws_bytes, B, Hq, Hkv, Nq, Nk, D, scale, 1 if causal else 0, int(q_pos0),
-                                int(k_pos0), 1 if dq_accumulate else 0, 1 if dkv_accumulate else 0, _stream(q)))
-    return (dq_acc if dq_acc is not None else dq, dk_acc if dk_acc is not None else dk,
+    call = BwdBlockCall(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), delta.data_ptr(),
+                        ptr(dq_acc), ptr(dk_acc), ptr(dv_acc), ptr(dq), ptr(dk), ptr(dv), ptr(workspace),
+                        workspace.numel() * workspace.element_size() if workspace is not None else 0, Nq, Nk,
+                        int(q_pos0), int(k_pos0), 1 if dq_accumulate else 0, 1 if dkv_accumulate else 0)
+    outs = (dq_acc if dq_acc is not None else dq, dk_acc if dk_acc is not None else dk,
             dv_acc if dv_acc is not None else dv)
+    return call, (B, Hq, Hkv, D), outs, workspace
+
+
+def attn_bwd_block(q, k, v, do, lse, delta, *, causal: bool = True, scale: float | None = None,
+                   q_pos0: int = 0, k_pos0: int = 0, dq_acc=None, dq_accumulate: bool = False,
+                   dk_acc=None, dv_acc=None, dkv_accumulate: bool = False, dq=None, dk=None, dv=None,
+                   workspace=None):
+    """Gradients through one KV block (k, v at global position k_pos0) of the
+    attention of q, given the global lse and Dv (attn_bwd_delta).  fp32
+    accumulators are overwritten, or added to with the *_accumulate flags;
+    bf16 dq / dk / dv, when given, receive rounded copies.  Returns
+    (dq_acc or dq, dk_acc or dk, dv_acc or dv)."""
+    c, (B, Hq, Hkv, D), outs, ws = _bwd_block_prepare(q, k, v, do, lse, delta, q_pos0, k_pos0, dq_acc, dq_accumulate,
+                                                  dk_acc, dv_acc, dkv_accumulate, dq, dk, dv, workspace)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_bwd_block(c.q, c.k, c.v, c.d_o, c.lse, c.delta, c.dq_acc, c.dk_acc, c.dv_acc, c.dq, c.dk, c.dv,
+                                c.workspace, c.workspace_bytes, B, Hq, Hkv, c.Nq, c.Nk, D, scale, 1 if causal else 0,
+                                c.q_pos0, c.k_pos0, c.dq_accumulate, c.dkv_accumulate, _stream(q)))
+    return outs
+
+
+def attn_bwd_block_group(calls, *, causal: bool = True, scale: float | None = None):
+    """Independent attn_bwd_block calls (1 to 4) in one dK/dV and one dQ
+    launch.  calls: dicts with q, k, v, do, lse, delta and optionally q_pos0,
+    k_pos0, dq_acc, dq_accumulate, dk_acc, dv_acc, dkv_accumulate, dq, dk, dv,
+    workspace (meanings as in attn_bwd_block); B, Hq, Hkv, D are shared.  No
+    call may write what another call reads or writes.  Returns, per call,
+    (dq_acc or dq, dk_acc or dk, dv_acc or dv)."""
+    calls = list(calls)
+    if not 1 <= len(calls) <= 4:
+        raise ValueError("a group holds 1 to 4 calls")
+    arr = (BwdBlockCall * len(calls))()
+    outs, dims, keep = [], None, []
+    for i, c in enumerate(calls):
+        arr[i], d, o, ws = _bwd_block_prepare(c["q"], c["k"], c["v"], c["do"], c["lse"], c["delta"], c.get("q_pos0", 0),
+                                          c.get("k_pos0", 0), c.get("dq_acc"), c.get("dq_accumulate", False),
+                                          c.get("dk_acc"), c.get("dv_acc"), c.get("dkv_accumulate", False),
+                                          c.get("dq"), c.get("dk"), c.get("dv"), c.get("workspace"))
+        if dims is not None and d != dims:
+            raise ValueError("the calls of a group share B, Hq, Hkv and D")
+        dims = d
+        outs.append(o)
+        keep.append(ws)
+    B, Hq, Hkv, D = dims
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_bwd_block_group(arr, len(calls), B, Hq, Hkv, D, scale, 1 if causal else 0,
+                                      _stream(calls[0]["q"])))
+    del keep  # the launches are enqueued: the stream orders any reuse after them
+    return outs
 
 
 def _relayout_shape(x, P, out, to_head):

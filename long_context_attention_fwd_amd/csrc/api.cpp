@@ -265,6 +265,7 @@ int attn_fwd_accumulate(const void* q, const void* k, const void* v, float* o_ac
 }
 
 static_assert(ATTN_MAX_FWD_GROUP == lcattn::kMaxFwdGroup, "group limit of the header and the kernel");
+static_assert(ATTN_MAX_BWD_GROUP == lcattn::kMaxBwdGroup, "group limit of the header and the kernels");
 
 int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
                               int causal, void* hip_stream) {
@@ -536,12 +537,14 @@ size_t attn_bwd_block_workspace_size(int B, int Hq, int Hkv, int64_t Nk, int D) 
   return (size_t)lcattn::bwd_part_floats(B, Hq, Hkv, Nk, D) * 4;
 }
 
-int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
-                   const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
-                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D,
-                   float scale, int causal, int64_t q_pos0, int64_t k_pos0, int dq_accumulate, int dkv_accumulate,
-                   void* hip_stream) {
-  const char* name = "attn_bwd_block";
+// Validation of one block-backward call; fills the kernel arguments and the
+// byte ranges of its inputs (6) and outputs (7, null when absent).
+static int bwd_block_check(const char* name, const void* q, const void* k, const void* v, const void* d_o,
+                           const float* lse, const float* delta, float* dq_acc, float* dk_acc, float* dv_acc,
+                           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq,
+                           int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0,
+                           int64_t k_pos0, int dq_accumulate, int dkv_accumulate, lcattn::BwdArgs* args,
+                           const void* (&ins)[6], size_t (&inb)[6], const void* (&outs)[7], size_t (&outb)[7]) {
   if (!q || !k || !v || !d_o || !lse || !delta)
     return fail(ATTN_ERR_NULL, "%s: q, k, v, d_o, lse and delta must be non-null", name);
   if (!dq_acc && !dq) return fail(ATTN_ERR_NULL, "%s: dq_acc or dq must be set", name);
@@ -569,10 +572,18 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
   for (int i = 0; i < 13; ++i)
     if (all[i] && !aligned16(all[i])) return fail(ATTN_ERR_ALIGN, "%s: pointers must be 16-byte aligned", name);
   const size_t qb = (size_t)nq_el * 2, kb = (size_t)nk_el * 2, lb = (size_t)nl * 4;
-  const void* ins[6] = {q, k, v, d_o, lse, delta};
-  const size_t inb[6] = {qb, kb, kb, qb, lb, lb};
-  const void* outs[7] = {dq_acc, dk_acc, dv_acc, dq, dk, dv, need ? workspace : nullptr};
-  const size_t outb[7] = {qb * 2, kb * 2, kb * 2, qb, kb, kb, need};
+  const void* in_[6] = {q, k, v, d_o, lse, delta};
+  const size_t inb_[6] = {qb, kb, kb, qb, lb, lb};
+  const void* out_[7] = {dq_acc, dk_acc, dv_acc, dq, dk, dv, need ? workspace : nullptr};
+  const size_t outb_[7] = {qb * 2, kb * 2, kb * 2, qb, kb, kb, need};
+  for (int i = 0; i < 7; ++i) {
+    outs[i] = out_[i];
+    outb[i] = out_[i] ? outb_[i] : 0;
+    if (i < 6) {
+      ins[i] = in_[i];
+      inb[i] = inb_[i];
+    }
+  }
   for (int i = 0; i < 7; ++i) {
     if (!outs[i]) continue;
     for (int j = 0; j < 6; ++j)
@@ -581,7 +592,8 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
       if (outs[j] && overlap(outs[i], outb[i], outs[j], outb[j]))
         return fail(ATTN_ERR_ALIAS, "%s: outputs overlap", name);
   }
-  lcattn::BwdArgs a;
+  lcattn::BwdArgs& a = *args;
+  a = lcattn::BwdArgs{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -606,7 +618,66 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
   a.dkv_mode = dk_acc ? (dkv_accumulate ? 2 : 1) : 0;
   a.dk_acc = dk_acc;
   a.dv_acc = dv_acc;
+  return ok();
+}
+
+int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                   const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D,
+                   float scale, int causal, int64_t q_pos0, int64_t k_pos0, int dq_accumulate, int dkv_accumulate,
+                   void* hip_stream) {
+  lcattn::BwdArgs a;
+  const void* ins[6];
+  size_t inb[6];
+  const void* outs[7];
+  size_t outb[7];
+  const int st = bwd_block_check("attn_bwd_block", q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, dq, dk, dv,
+                                 workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0, k_pos0,
+                                 dq_accumulate, dkv_accumulate, &a, ins, inb, outs, outb);
+  if (st != ATTN_OK) return st;
   return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd_block launch");
+}
+
+int attn_bwd_block_group(const attn_bwd_block_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
+                         int causal, void* hip_stream) {
+  const char* name = "attn_bwd_block_group";
+  if (!calls) return fail(ATTN_ERR_NULL, "%s: null call array", name);
+  if (n < 1 || n > ATTN_MAX_BWD_GROUP)
+    return fail(ATTN_ERR_SHAPE, "%s: n=%d calls (1 .. %d)", name, n, ATTN_MAX_BWD_GROUP);
+  if ((int64_t)B * n > 65535) return fail(ATTN_ERR_UNSUPPORTED, "%s: B * n must be <= 65535", name);
+  lcattn::BwdArgs args[ATTN_MAX_BWD_GROUP];
+  const void* ins[ATTN_MAX_BWD_GROUP][6];
+  size_t inb[ATTN_MAX_BWD_GROUP][6];
+  const void* outs[ATTN_MAX_BWD_GROUP][7];
+  size_t outb[ATTN_MAX_BWD_GROUP][7];
+  for (int c = 0; c < n; ++c) {
+    const attn_bwd_block_call& x = calls[c];
+    const int st = bwd_block_check(name, x.q, x.k, x.v, x.d_o, x.lse, x.delta, x.dq_acc, x.dk_acc, x.dv_acc, x.dq,
+                                   x.dk, x.dv, x.workspace, x.workspace_bytes, B, Hq, Hkv, x.Nq, x.Nk, D, scale,
+                                   causal, x.q_pos0, x.k_pos0, x.dq_accumulate, x.dkv_accumulate, &args[c], ins[c],
+                                   inb[c], outs[c], outb[c]);
+    if (st != ATTN_OK) {
+      char detail[sizeof(g_last_error)];
+      snprintf(detail, sizeof(detail), "%s", g_last_error);
+      return fail(st, "%s (call %d)", detail, c);
+    }
+  }
+  // the calls run side by side: no call may write what another reads or writes
+  for (int c = 0; c < n; ++c)
+    for (int d = 0; d < n; ++d) {
+      if (c == d) continue;
+      for (int i = 0; i < 7; ++i) {
+        if (!outs[c][i]) continue;
+        for (int j = 0; j < 6; ++j)
+          if (overlap(outs[c][i], outb[c][i], ins[d][j], inb[d][j]))
+            return fail(ATTN_ERR_ALIAS, "%s: outputs of call %d overlap inputs of call %d", name, c, d);
+        for (int j = 0; j < 7; ++j)
+          if (outs[d][j] && overlap(outs[c][i], outb[c][i], outs[d][j], outb[d][j]))
+            return fail(ATTN_ERR_ALIAS, "%s: outputs of calls %d and %d overlap", name, c, d);
+      }
+    }
+  return hip_status(lcattn::launch_attn_bwd_group(args, n, B, D, static_cast<hipStream_t>(hip_stream)),
+                    "attn_bwd_block_group launch");
 }
 
 // Validates one tensor of a relayout and fills its job; returns a status.

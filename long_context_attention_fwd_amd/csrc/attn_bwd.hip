@@ -36,6 +36,7 @@
 #include "launch.hpp"
 #include "trace.hpp"
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -104,9 +105,12 @@ __device__ __forceinline__ auto lin_off(Bf b) {
   else return std::integral_constant<int, Bf::value * MUL + ADD>{};
 }
 
+// The kernel body: workgroup number lin (already in XCD-aware order) of a
+// grid of nx key tiles x ny query heads x B.
 template <int D, bool PARTIAL, bool DENSE>
-__global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
-                                                                             float* __restrict__ dv_part) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restrict__ dk_part,
+                                              float* __restrict__ dv_part, long long lin, long long nx,
+                                              long long ny) {
   using T = SwzTile<D>;
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
@@ -125,12 +129,11 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
   const bool role_a = wave < 4;            // wave-uniform
   const int kg = wave & 3;                 // key group of 32 keys
   const long long Nq = a.Nq, Nk = a.Nk;
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
   const long long bz = lin / (nx * ny);
   const int h = (int)(lin / nx % ny);
   const int kvh = h / a.G;
   const long long kt0 = (lin % nx) * BK;
+  if (kt0 >= Nk) return;  // a grouped launch's grid covers its longest call
   const long long kw0 = kt0 + 32 * kg;
   const int key = (int)(kw0 + c);
   const float sl = a.scale * kLog2e;
@@ -434,6 +437,33 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(Bwd
   }
 }
 
+template <int D, bool PARTIAL, bool DENSE>
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
+                                                                             float* __restrict__ dv_part) {
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  bwd_dkdv_body<D, PARTIAL, DENSE>(a, dk_part, dv_part, lin, nx, ny);
+}
+
+// Independent block-backward calls in one launch (a ring step's calls that
+// share neither a query chunk nor a key/value chunk): grid z = call * B +
+// batch; call c covers the first ceil(Nk_c / 128) key tiles of the grid.
+struct BwdGroup {
+  BwdArgs a[kMaxBwdGroup];
+  float* dk_part[kMaxBwdGroup];
+  float* dv_part[kMaxBwdGroup];
+  int n_qtiles[kMaxBwdGroup];
+};
+
+template <int D, bool PARTIAL>
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_group_kernel(BwdGroup g, int B) {
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const long long per_call = nx * ny * B;
+  const int c = (int)(lin / per_call);
+  bwd_dkdv_body<D, PARTIAL, true>(g.a[c], g.dk_part[c], g.dv_part[c], lin - c * per_call, nx, ny);
+}
+
 // dK[b, kvh] = sum over the G query heads of the group of the fp32 partials,
 // written (or added) as the dK, dV modes of the arguments say.  One thread per
 // 4 elements.
@@ -482,8 +512,11 @@ constexpr int kBN = 64;
 
 // DENSE: contiguous [B, H, N, D] tensors (row strides D known at compile
 // time, which keeps the kernel within its registers); else the strides of a.
+// The kernel body: workgroup number lin (already in XCD-aware order) of a
+// grid of nx query tiles x ny head groups x B; the call has n_qtiles <= nx.
 template <int D, int HP, bool DENSE>
-__global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, long long lin, long long nx,
+                                            long long ny) {
   using T = SwzTile<D>;  // K tiles are read both ways, V tiles by rows: rows swizzle
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
@@ -498,11 +531,10 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   const long long Nq = a.Nq, Nk = a.Nk;
   // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
   // they stream the same key/value tiles; longest causal rows first
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
   const int by = (int)(lin / nx % ny);
   const long long bz = lin / (nx * ny);
   const int qt = n_qtiles - 1 - (int)(lin % nx);
+  if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;
   const long long q_start = (long long)qt * SPAN;
@@ -728,6 +760,24 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   }
 }
 
+template <int D, int HP, bool DENSE>
+__global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+  // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
+  // they stream the same key/value tiles; longest causal rows first
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  bwd_dq_body<D, HP, DENSE>(a, n_qtiles, lin, nx, ny);
+}
+
+template <int D, int HP>
+__global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_group_kernel(BwdGroup g, int B) {
+  const long long nx = gridDim.x, ny = gridDim.y;
+  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
+  const long long per_call = nx * ny * B;
+  const int c = (int)(lin / per_call);
+  bwd_dq_body<D, HP, true>(g.a[c], g.n_qtiles[c], lin - c * per_call, nx, ny);
+}
+
 template <int D>
 hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, int B, int H, long long N,
                         const long long (&st)[3], hipStream_t stream) {
@@ -807,6 +857,54 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// One launch per kernel for up to kMaxBwdGroup block calls (dense tensors,
+// Dv given, shared B, Hq, Hkv, D, scale and mask kind).
+template <int D>
+hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream) {
+  hipError_t e;
+  BwdGroup g{};
+  long long nk_tiles = 0;
+  const int G = calls[0].G;
+  const int HP = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+  const long long span = (kDqWaves / HP) * 32;
+  int nq_tiles = 0;
+  for (int c = 0; c < n; ++c) {
+    BwdArgs a = calls[c];
+    a.qs[2] = D; a.qs[1] = a.Nq * D; a.qs[0] = a.Hq * a.Nq * D;
+    a.ks[2] = D; a.ks[1] = a.Nk * D; a.ks[0] = a.Hkv * a.Nk * D;
+    g.a[c] = a;
+    g.dk_part[c] = G == 1 ? nullptr : a.part;
+    g.dv_part[c] = G == 1 ? nullptr : a.part + (long long)B * a.Hq * a.Nk * D;
+    g.n_qtiles[c] = (int)((a.Nq + span - 1) / span);
+    nk_tiles = std::max<long long>(nk_tiles, (a.Nk + 127) / 128);
+    nq_tiles = std::max(nq_tiles, g.n_qtiles[c]);
+  }
+  const dim3 kgrid((unsigned)nk_tiles, (unsigned)calls[0].Hq, (unsigned)(B * n));
+  if (G == 1)
+    LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_group_kernel<D, false>), kgrid, dim3(64 * kSplitWaves), 0, stream, g,
+                  B);
+  else
+    LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_group_kernel<D, true>), kgrid, dim3(64 * kSplitWaves), 0, stream, g, B);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (G != 1)
+    for (int c = 0; c < n; ++c) {
+      const long long slots = (long long)B * g.a[c].Hkv * g.a[c].Nk * D / 4;
+      LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
+                    dim3(256), 0, stream, g.a[c], g.dk_part[c], g.dv_part[c], (long long)B * g.a[c].Hkv, true);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  const dim3 qgrid((unsigned)nq_tiles, (unsigned)(calls[0].Hq / HP), (unsigned)(B * n));
+  if (HP == 4)
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 4>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
+  else if (HP == 2)
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 2>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
+  else
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 1>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -847,6 +945,10 @@ hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
   }
   *ptr = g_scratch_ptr[dev];
   return hipSuccess;
+}
+
+hipError_t launch_attn_bwd_group(const BwdArgs* calls, int n, int B, int D, hipStream_t stream) {
+  return D == 64 ? launch_d_group<64>(calls, n, B, stream) : launch_d_group<128>(calls, n, B, stream);
 }
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream) {

@@ -125,6 +125,11 @@ long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D);
 long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream);
+// Up to kMaxBwdGroup independent block-backward calls (contiguous tensors, Dv
+// given, the same B, Hq, Hkv, D, scale and mask kind): one dK/dV launch and
+// one dQ launch for all of them.
+constexpr int kMaxBwdGroup = 4;
+hipError_t launch_attn_bwd_group(const BwdArgs* calls, int n, int B, int D, hipStream_t stream);
 
 // The allocation-free backward's scratch: kNoAllocScratchBytes of device
 // memory per GPU, held by the library until the process ends.  *ptr receives

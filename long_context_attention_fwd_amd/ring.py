@@ -129,3 +129,76 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
             join = torch.cuda.Event()
             join.record(st)
             caller.wait_event(join)
+
+
+def ring_backward_groups(rank: int, P: int, scheme: str = "zigzag", causal: bool = True):
+    """The launches of one rank's ring backward when a step's calls go out
+    together: a call adds into the dQ of its query chunk and into the dK, dV of
+    its key/value chunk, so calls that share neither chunk are independent.
+    Each step's calls are packed greedily in schedule order into groups of
+    such calls; returns the groups in launch order, each a list of (index into
+    ring_schedule's calls, call).  With two chunks on each side a step needs
+    at most two launches: (q1, k1) with (q2, k2), and (q1, k2) with (q2, k1)."""
+    calls = ring_schedule(rank, P, scheme, causal)
+    groups = []
+    for step in range(P):
+        pending = [(i, c) for i, c in enumerate(calls) if c[0] == step]
+        while pending:
+            g, rest, used_q, used_k = [], [], set(), set()
+            for i, c in pending:
+                if c[2] in used_q or c[3] in used_k:
+                    rest.append((i, c))
+                    continue
+                g.append((i, c))
+                used_q.add(c[2])
+                used_k.add(c[3])
+            groups.append(g)
+            pending = rest
+    return groups
+
+
+def ring_backward(q_chunks, do_chunks, lse_chunks, delta_chunks, kv_chunks, rank: int, P: int, C: int, *,
+                  dq_acc, dkv_acc, scheme: str = "zigzag", causal: bool = True, scale: float | None = None,
+                  steps=None, grouped: bool = False, workspaces=None):
+    """Run rank ``rank``'s ring backward on this GPU: every visible (query
+    chunk, key/value chunk) pair of ``ring_schedule`` as one attn_bwd_block
+    call with the chunks' global positions, adding into fp32 accumulators.
+
+    q_chunks, do_chunks: the rank's two query chunks and their output
+    gradients, [B, Hq, C, D] bf16; lse_chunks, delta_chunks: their global LSE
+    and Dv, [B, Hq, C] float.  kv_chunks(src): ((k, v), (k, v)) of rank src's
+    chunks.  dq_acc: per query chunk, an fp32 dQ accumulator; dkv_acc(src, ki):
+    the fp32 (dK, dV) accumulators of rank src's key/value chunk ki (on a ring
+    they travel with the chunk).  All accumulators are added to, so the caller
+    zeroes them first.  steps: restrict to these ring steps (for timing one
+    step).  grouped: each group of ``ring_backward_groups`` goes out as one
+    ``attn_bwd_block_group``.  workspaces: up to four workspace tensors (one
+    per call of a group; needed for grouped-query attention)."""
+    from . import attn_bwd_block, attn_bwd_block_group
+
+    calls = ring_schedule(rank, P, scheme, causal)
+    mine = rank_chunks(rank, P, scheme)
+
+    def fields(step, src, qi, ki, slot):
+        k, v = kv_chunks(src)[ki]
+        dk_acc, dv_acc = dkv_acc(src, ki)
+        kc = rank_chunks(src, P, scheme)[ki]
+        d = dict(q=q_chunks[qi], k=k, v=v, do=do_chunks[qi], lse=lse_chunks[qi], delta=delta_chunks[qi],
+                 q_pos0=mine[qi] * C, k_pos0=kc * C, dq_acc=dq_acc[qi], dq_accumulate=True, dk_acc=dk_acc,
+                 dv_acc=dv_acc, dkv_accumulate=True)
+        if workspaces is not None:
+            d["workspace"] = workspaces[slot]
+        return d
+
+    if grouped:
+        for g in ring_backward_groups(rank, P, scheme, causal):
+            if steps is not None and g[0][1][0] not in steps:
+                continue
+            attn_bwd_block_group([fields(*c, slot) for slot, (_, c) in enumerate(g)], causal=causal, scale=scale)
+        return
+    for step, src, qi, ki in calls:
+        if steps is not None and step not in steps:
+            continue
+        d = fields(step, src, qi, ki, 0)
+        q, k, v, do, lse, delta = (d.pop(n) for n in ("q", "k", "v", "do", "lse", "delta"))
+        attn_bwd_block(q, k, v, do, lse, delta, causal=causal, scale=scale, **d)

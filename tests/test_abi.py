@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
-              "attn_bwd_strided", "attn_bwd_noalloc", "attn_bwd_noalloc_max_scratch", "attn_fwd_accumulate_group", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
+              "attn_bwd_strided", "attn_bwd_noalloc", "attn_bwd_block_group", "attn_bwd_noalloc_max_scratch", "attn_fwd_accumulate_group", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
               "head_to_seq_relayout_batch", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -300,6 +300,45 @@ def bwd_block(L, **kw):
 def test_bwd_block_rejects(L, kw, status):
     assert bwd_block(L, **kw) == status
     assert L.attn_last_error()
+
+
+def bwd_group_call(base, **kw):
+    """One attn_bwd_block_call with its own 13 fake buffers (16 MiB apart) from base."""
+    n = 1 << 24
+    f = dict(q=base, k=base + n, v=base + 2 * n, d_o=base + 3 * n, lse=base + 4 * n, delta=base + 5 * n,
+             dq_acc=base + 6 * n, dk_acc=base + 7 * n, dv_acc=base + 8 * n, dq=base + 9 * n, dk=base + 10 * n,
+             dv=base + 11 * n, workspace=base + 12 * n, workspace_bytes=1 << 24, Nq=1024, Nk=512, q_pos0=512,
+             k_pos0=0, dq_accumulate=1, dkv_accumulate=1)
+    f.update(kw)
+    return lc.BwdBlockCall(**f)
+
+
+def bwd_group(L, calls, n=None, **kw):
+    arr = (lc.BwdBlockCall * max(1, len(calls)))(*calls)
+    args = dict(calls=arr, n=len(calls) if n is None else n, B=1, Hq=8, Hkv=2, D=128, scale=0.088, causal=1,
+                stream=None)
+    args.update(kw)
+    return L.attn_bwd_block_group(*args.values())
+
+
+def test_bwd_block_group_rejects(L):
+    """The group validates every call as attn_bwd_block (the error names the
+    call) and rejects calls that write what another call reads or writes."""
+    c0 = bwd_group_call(A)
+    c1 = bwd_group_call(A + (16 << 24))
+    assert bwd_group(L, [c0], n=0) == 2 and bwd_group(L, [c0] * 5, n=5) == 2
+    assert L.attn_bwd_block_group(None, 1, 1, 8, 2, 128, 0.088, 1, None) == 1
+    bad = bwd_group_call(A + (16 << 24), delta=None)
+    assert bwd_group(L, [c0, bad]) == 1 and b"call 1" in L.attn_last_error()
+    assert bwd_group(L, [c0, bwd_group_call(A + (16 << 24), Nk=0)]) == 2
+    assert bwd_group(L, [c0, bwd_group_call(A + (16 << 24), workspace=None)]) == 6
+    # the second call adds into the first call's dQ accumulator
+    shared_dq = bwd_group_call(A + (16 << 24), dq_acc=A + 6 * (1 << 24))
+    assert bwd_group(L, [c0, shared_dq]) == 5 and b"overlap" in L.attn_last_error()
+    # the second call writes its dK into the first call's q
+    writes_input = bwd_group_call(A + (16 << 24), dk=A)
+    assert bwd_group(L, [c0, writes_input]) == 5
+    assert bwd_group(L, [c0, c1], B=65535) == 3
 
 
 @pytest.mark.parametrize("fn", ["seq_to_head_relayout", "head_to_seq_relayout"])

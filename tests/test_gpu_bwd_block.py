@@ -247,3 +247,100 @@ def test_ring_backward_32k_sampled(gpu, Hq, Hkv):
     do_np[:, :, ~mask] = 0.0
     rq, rk, rv = oracle.attention_backward_row_support(d["q"], d["k"], d["v"], do_np, w.scale, rows)
     check((dq[:, :, idx], dk, dv), (rq, rk, rv), f"32K ring Hq={Hq} Hkv={Hkv}")
+
+
+def _block_call_inputs(Hq, Hkv, D, Nq, Nk, q_pos0, k_pos0, seed):
+    """q, k, v, dO of one block call and finite LSE, Dv for it (from the
+    forward of q against this block)."""
+    import torch
+    d = make_qkv(1, Hq, Hkv, max(Nq, Nk), D, seed=seed, with_do=True)
+    q, do = (to_dev(d[n][:, :, :Nq].copy()) for n in ("q", "do"))
+    k, v = (to_dev(d[n][:, :, :Nk].copy()) for n in ("k", "v"))
+    o, lse = lc.attn_fwd(q, k, v, causal=False, scale=sdpa_scale(D))
+    delta = lc.attn_bwd_delta(o, do)
+    torch.cuda.synchronize()
+    return dict(q=q, k=k, v=v, do=do, lse=lse, delta=delta, q_pos0=q_pos0, k_pos0=k_pos0)
+
+
+@pytest.mark.parametrize("D,G", [(128, 1), (128, 4), (64, 2)])
+def test_bwd_block_group_matches_calls(gpu, D, G):
+    """Up to four independent block calls in one group launch give exactly the
+    results of the same calls made one at a time: uneven lengths and global
+    positions (a diagonal block, a block partly visible, one fully visible,
+    one no query sees), fp32 accumulators overwritten or added to, bf16
+    copies."""
+    import torch
+    Hkv = 2
+    Hq = Hkv * G
+    specs = [(300, 200, 200, 0), (256, 512, 1024, 512), (100, 64, 0, 0), (192, 128, 0, 4096)]
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    calls = []
+    for i, (Nq, Nk, qp, kp) in enumerate(specs):
+        c = _block_call_inputs(Hq, Hkv, D, Nq, Nk, qp, kp, seed=300 + i)
+        acc = i % 2 == 1  # odd calls add into accumulators that already hold values
+        c["dq_acc"] = torch.randn((1, Hq, Nq, D), generator=gen, device="cuda")
+        c["dk_acc"] = torch.randn((1, Hkv, Nk, D), generator=gen, device="cuda")
+        c["dv_acc"] = torch.randn((1, Hkv, Nk, D), generator=gen, device="cuda")
+        c["dq_accumulate"] = acc
+        c["dkv_accumulate"] = acc
+        c["dq"] = poisoned((1, Hq, Nq, D), torch.bfloat16)
+        c["dk"] = poisoned((1, Hkv, Nk, D), torch.bfloat16)
+        c["dv"] = poisoned((1, Hkv, Nk, D), torch.bfloat16)
+        calls.append(c)
+    outs = ("dq_acc", "dk_acc", "dv_acc", "dq", "dk", "dv")
+    for n in (2, 4):
+        grp = [dict(c, **{o: c[o].clone() for o in outs}) for c in calls[:n]]
+        one = [dict(c, **{o: c[o].clone() for o in outs}) for c in calls[:n]]
+        lc.attn_bwd_block_group(grp, causal=True, scale=sdpa_scale(D))
+        for c in one:
+            kw = {x: c[x] for x in c if x not in ("q", "k", "v", "do", "lse", "delta")}
+            lc.attn_bwd_block(c["q"], c["k"], c["v"], c["do"], c["lse"], c["delta"], causal=True,
+                              scale=sdpa_scale(D), **kw)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(grp, one)):
+            for o in outs:
+                x, y = a[o], b[o]
+                if x.dtype == torch.bfloat16:
+                    x, y = x.view(torch.int16), y.view(torch.int16)
+                assert torch.equal(x, y), f"group of {n}: call {i} {o} differs"
+
+
+@pytest.mark.parametrize("scheme", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("P,C,G,D", [(2, 128, 1, 128), (4, 64, 4, 128), (4, 96, 2, 64)])
+def test_ring_backward_schemes(gpu, scheme, P, C, G, D):
+    """Every rank's ring backward on one GPU, grouped and one call at a time:
+    the dQ of each rank's query chunks and the dK, dV accumulated in each
+    key/value chunk (as they would travel around the ring) equal the oracle's
+    full backward.  LSE and Dv come from the GPU's full forward."""
+    import torch
+    from long_context_attention_fwd_amd.ring import rank_chunks, ring_backward
+    Hkv = 2
+    Hq = Hkv * G
+    N = 2 * P * C
+    s = sdpa_scale(D)
+    d = make_qkv(1, Hq, Hkv, N, D, seed=900 + P + C + G, with_do=True)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
+    delta = lc.attn_bwd_delta(o, do)
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, True)
+
+    def ch(x, c):
+        return x[:, :, c * C:(c + 1) * C].contiguous()
+    ws = [torch.empty(max(16, lc.attn_bwd_block_workspace_size(1, Hq, Hkv, C, D)), dtype=torch.uint8,
+                      device="cuda") for _ in range(4)]
+    for grouped in (False, True):
+        dq_acc = [torch.zeros((1, Hq, C, D), device="cuda") for _ in range(2 * P)]
+        dk_acc = [torch.zeros((1, Hkv, C, D), device="cuda") for _ in range(2 * P)]
+        dv_acc = [torch.zeros((1, Hkv, C, D), device="cuda") for _ in range(2 * P)]
+        for r in range(P):
+            mine = rank_chunks(r, P, scheme)
+            ring_backward([ch(q, c) for c in mine], [ch(do, c) for c in mine], [ch(lse, c) for c in mine],
+                          [ch(delta, c) for c in mine],
+                          lambda src: tuple((ch(k, c), ch(v, c)) for c in rank_chunks(src, P, scheme)),
+                          r, P, C, dq_acc=[dq_acc[c] for c in mine],
+                          dkv_acc=lambda src, ki: (dk_acc[rank_chunks(src, P, scheme)[ki]],
+                                                   dv_acc[rank_chunks(src, P, scheme)[ki]]),
+                          scheme=scheme, scale=s, grouped=grouped, workspaces=ws)
+        torch.cuda.synchronize()
+        got = [torch.cat(x, dim=2) for x in (dq_acc, dk_acc, dv_acc)]
+        check(got, (dQ, dK, dV), f"{scheme} P={P} C={C} G={G} D={D} grouped={grouped}")

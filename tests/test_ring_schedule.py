@@ -4,7 +4,7 @@ gives every rank the same work at every step."""
 
 import pytest
 
-from long_context_attention_fwd_amd.ring import rank_chunks, ring_schedule
+from long_context_attention_fwd_amd.ring import SCHEMES, rank_chunks, ring_backward_groups, ring_schedule
 
 
 @pytest.mark.parametrize("scheme", ["contiguous", "zigzag"])
@@ -94,3 +94,27 @@ def test_zigzag_groups_per_step():
         assert sizes[0] == [2, 1]
         for step in range(1, 4):
             assert sizes[step] == ([2] if step <= r else [1, 1]), (r, step, sizes)
+
+
+@pytest.mark.parametrize("scheme", SCHEMES)
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_groups(scheme, P, causal):
+    """Every call of the schedule once; a group never shares a query chunk
+    (its dQ) or a key/value chunk (its dK, dV); groups stay within a step and
+    steps keep their order; at most two groups per step."""
+    for r in range(P):
+        calls = ring_schedule(r, P, scheme, causal)
+        groups = ring_backward_groups(r, P, scheme, causal)
+        seen = [i for g in groups for i, _ in g]
+        assert sorted(seen) == list(range(len(calls)))
+        steps = [g[0][1][0] for g in groups]
+        assert steps == sorted(steps)
+        for g in groups:
+            assert len({c[0] for _, c in g}) == 1
+            assert len({c[2] for _, c in g}) == len(g)
+            assert len({c[3] for _, c in g}) == len(g)
+            for i, c in g:
+                assert calls[i] == c
+        for s in range(P):
+            assert sum(1 for g in groups if g[0][1][0] == s) <= 2
