@@ -191,7 +191,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    p.add_argument("--only", choices=WORKLOAD_NAMES, help="run one workload alone (for a profiler)")
+    p.add_argument("--only", choices=list(WORKLOAD_NAMES) + ["ulysses_shard_32k_extras"],
+                   help="run one workload alone (for a profiler); ulysses_shard_32k_extras: the shard leg with "
+                        "its extra variants")
     p.add_argument("--calibration-copy", action="store_true",
                    help="with --only: first one elementwise kernel of known traffic (1 GiB fp32 read, 1 GiB "
                         "written), the reference for scaling the profiler's byte counters")
@@ -555,17 +557,19 @@ def shard_extras(lc, torch, dev, w, xs, heads, o, dq, dk, dv, lse, o_parts, lse_
                               workspace=ws_blk)
     out["ring_backward"] = {"call": "attn_bwd_delta + 4 x attn_bwd_block (fp32 dQ accumulated)",
                             **r(time_calls(torch, ring_backward), 2.5 * f_ring)}
-    out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd)
+    out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, o, lse)
     return out
 
 
-def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, Pr=4):
+def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, o_full, lse_full, Pr=4):
     """Shard 0's causal attention as a Pr-rank ring over 2*Pr chunks, every
     rank's every step timed on this GPU: the ring waits for the slowest rank
     at each step, so its critical path is the sum over steps of the maximum
     over ranks.  Contiguous sharding against zigzag (rank r holds chunks r
-    and 2*Pr-1-r)."""
-    from long_context_attention_fwd_amd.ring import SCHEMES, rank_chunks, ring_forward
+    and 2*Pr-1-r); forward, then backward (from the full forward's O and
+    LSE), each one call at a time and with a step's independent calls in one
+    launch."""
+    from long_context_attention_fwd_amd.ring import SCHEMES, rank_chunks, ring_backward, ring_forward
     C = N // (2 * Pr)
     q0, k0, v0 = (heads[n][0:1] for n in ("q", "k", "v"))
     cq = [q0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
@@ -591,6 +595,42 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, Pr=4):
         res[scheme + ("_grouped" if grouped else "")] = {
             "critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
             "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
+            "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
+            "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
+    # backward: Dv of the full forward, chunked like Q; fp32 dQ per query
+    # chunk and dK, dV per key/value chunk (they travel with the chunk)
+    do0 = heads["do"][0:1]
+    delta = lc.attn_bwd_delta(o_full, do0)
+    cdo = [do0[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    clse = [lse_full[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    cdl = [delta[:, :, c * C:(c + 1) * C].contiguous() for c in range(2 * Pr)]
+    dq_acc = [torch.zeros((1, hq, C, D), dtype=torch.float32, device=dev) for _ in range(2 * Pr)]
+    dkv_acc = [tuple(torch.zeros((1, ck[0].shape[1], C, D), dtype=torch.float32, device=dev) for _ in range(2))
+               for _ in range(2 * Pr)]
+    wsz = max(16, lc.attn_bwd_block_workspace_size(1, hq, ck[0].shape[1], C, D))
+    wss = [torch.empty(wsz, dtype=torch.uint8, device=dev) for _ in range(4)]
+    f_bwd = 2.5 * f_fwd
+    res["backward_call"] = ("attn_bwd_block per visible (query chunk, key chunk) pair, or "
+                            "attn_bwd_block_group per set of a step's pairs that share no chunk")
+    for scheme, grouped in [(sc, g) for g in (False, True) for sc in SCHEMES]:
+        t = [[0.0] * Pr for _ in range(Pr)]
+        for r in range(Pr):
+            mine = rank_chunks(r, Pr, scheme)
+
+            def kv(src, scheme=scheme):
+                return tuple((ck[c], cv[c]) for c in rank_chunks(src, Pr, scheme))
+
+            def acc(src, ki, scheme=scheme):
+                return dkv_acc[rank_chunks(src, Pr, scheme)[ki]]
+            for st in range(Pr):
+                t[r][st] = time_calls(torch, lambda: ring_backward(
+                    [cq[c] for c in mine], [cdo[c] for c in mine], [clse[c] for c in mine],
+                    [cdl[c] for c in mine], kv, r, Pr, C, dq_acc=[dq_acc[c] for c in mine], dkv_acc=acc,
+                    scheme=scheme, scale=scale, steps={st}, grouped=grouped, workspaces=wss))
+        crit = sum(max(t[r][s] for r in range(Pr)) for s in range(Pr))
+        res["backward_" + scheme + ("_grouped" if grouped else "")] = {
+            "critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_bwd, crit), 2),
+            "per_rank_TFLOP/s": round(tflops(f_bwd, crit) / Pr, 2),
             "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],
             "per_step_max_ms": [round(max(t[r][s] for r in range(Pr)), 4) for s in range(Pr)]}
     return res
@@ -807,6 +847,8 @@ def main():
     if args.only and args.only != "train_64k":
         legs = {"listing_4k": lambda: leg_listing_4k(lc, torch, dev),
                 "ulysses_shard_32k": lambda: leg_ulysses_shard_32k(lc, torch, dev, args.steps, args.warmup, False),
+                "ulysses_shard_32k_extras": lambda: leg_ulysses_shard_32k(lc, torch, dev, args.steps, args.warmup,
+                                                                          True),
                 "ring_blocks_32k": lambda: leg_ring_blocks_32k(lc, torch, dev, args.steps, args.warmup),
                 "ulysses_512k": lambda: leg_ulysses_512k(lc, torch, dev, args.steps, args.warmup)}
         res, rls = legs[args.only]()
