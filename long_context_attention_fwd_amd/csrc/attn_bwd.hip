@@ -109,8 +109,8 @@ __device__ __forceinline__ auto lin_off(Bf b) {
 // grid of nx key tiles x ny query heads x B.
 template <int D, bool PARTIAL, bool DENSE>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restrict__ dk_part,
-                                              float* __restrict__ dv_part, long long lin, long long nx,
-                                              long long ny) {
+                                              float* __restrict__ dv_part, unsigned lin, unsigned nx,
+                                              unsigned ny) {
   using T = SwzTile<D>;
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
@@ -129,10 +129,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   const bool role_a = wave < 4;            // wave-uniform
   const int kg = wave & 3;                 // key group of 32 keys
   const long long Nq = a.Nq, Nk = a.Nk;
-  const long long bz = lin / (nx * ny);
-  const int h = (int)(lin / nx % ny);
+  const unsigned lxy = lin / nx;
+  const long long bz = lxy / ny;
+  const int h = (int)(lxy % ny);
   const int kvh = h / a.G;
-  const long long kt0 = (lin % nx) * BK;
+  const long long kt0 = (long long)(lin - lxy * nx) * BK;
   if (kt0 >= Nk) return;  // a grouped launch's grid covers its longest call
   const long long kw0 = kt0 + 32 * kg;
   const int key = (int)(kw0 + c);
@@ -440,9 +441,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
 template <int D, bool PARTIAL, bool DENSE>
 __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
                                                                              float* __restrict__ dv_part) {
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  bwd_dkdv_body<D, PARTIAL, DENSE>(a, dk_part, dv_part, lin, nx, ny);
+  bwd_dkdv_body<D, PARTIAL, DENSE>(a, dk_part, dv_part, wg_number(), gridDim.x, gridDim.y);
 }
 
 // Independent block-backward calls in one launch (a ring step's calls that
@@ -457,11 +456,10 @@ struct BwdGroup {
 
 template <int D, bool PARTIAL>
 __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_group_kernel(BwdGroup g, int B) {
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  const long long per_call = nx * ny * B;
-  const int c = (int)(lin / per_call);
-  bwd_dkdv_body<D, PARTIAL, true>(g.a[c], g.dk_part[c], g.dv_part[c], lin - c * per_call, nx, ny);
+  const unsigned lin = wg_number();
+  const unsigned per_call = gridDim.x * gridDim.y * (unsigned)B;
+  const unsigned c = lin / per_call;
+  bwd_dkdv_body<D, PARTIAL, true>(g.a[c], g.dk_part[c], g.dv_part[c], lin - c * per_call, gridDim.x, gridDim.y);
 }
 
 // dK[b, kvh] = sum over the G query heads of the group of the fp32 partials,
@@ -515,8 +513,8 @@ constexpr int kBN = 64;
 // The kernel body: workgroup number lin (already in XCD-aware order) of a
 // grid of nx query tiles x ny head groups x B; the call has n_qtiles <= nx.
 template <int D, int HP, bool DENSE>
-__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, long long lin, long long nx,
-                                            long long ny) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsigned lin, unsigned nx,
+                                            unsigned ny) {
   using T = SwzTile<D>;  // K tiles are read both ways, V tiles by rows: rows swizzle
   constexpr int KT = D / 16;
   constexpr int DB = D / 32;
@@ -531,9 +529,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, long
   const long long Nq = a.Nq, Nk = a.Nk;
   // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
   // they stream the same key/value tiles; longest causal rows first
-  const int by = (int)(lin / nx % ny);
-  const long long bz = lin / (nx * ny);
-  const int qt = n_qtiles - 1 - (int)(lin % nx);
+  const unsigned lxy = lin / nx;
+  const int by = (int)(lxy % ny);
+  const long long bz = lxy / ny;
+  const int qt = n_qtiles - 1 - (int)(lin - lxy * nx);
   if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;
@@ -764,18 +763,15 @@ template <int D, int HP, bool DENSE>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
   // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
   // they stream the same key/value tiles; longest causal rows first
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  bwd_dq_body<D, HP, DENSE>(a, n_qtiles, lin, nx, ny);
+  bwd_dq_body<D, HP, DENSE>(a, n_qtiles, wg_number(), gridDim.x, gridDim.y);
 }
 
 template <int D, int HP>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_group_kernel(BwdGroup g, int B) {
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  const long long per_call = nx * ny * B;
-  const int c = (int)(lin / per_call);
-  bwd_dq_body<D, HP, true>(g.a[c], g.n_qtiles[c], lin - c * per_call, nx, ny);
+  const unsigned lin = wg_number();
+  const unsigned per_call = gridDim.x * gridDim.y * (unsigned)B;
+  const unsigned c = lin / per_call;
+  bwd_dq_body<D, HP, true>(g.a[c], g.n_qtiles[c], lin - c * per_call, gridDim.x, gridDim.y);
 }
 
 template <int D>
@@ -803,11 +799,16 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
     a.ks[1] = a.Nk * D;
     a.ks[0] = a.Hkv * a.Nk * D;
   }
+  const dim3 kgrid((unsigned)((a.Nk + 127) / 128), (unsigned)a.Hq, (unsigned)B);  // 128 keys per workgroup
+  const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
+  const long long span = (kDqWaves / HP) * 32;
+  const int n_qt = (int)((a.Nq + span - 1) / span);
+  dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
+  if (!grid_fits(kgrid) || !grid_fits(grid)) return hipErrorInvalidConfiguration;
   if (a.o) {
     e = launch_delta<D>(a.o, a.d_o, a.delta, B, a.Hq, a.Nq, a.qs, stream);
     if (e != hipSuccess) return e;
   }
-  const dim3 kgrid((unsigned)((a.Nk + 127) / 128), (unsigned)a.Hq, (unsigned)B);  // 128 keys per workgroup
   {
     float* dk_part = a.G == 1 ? nullptr : a.part;
     float* dv_part = a.G == 1 ? nullptr : dk_part + (long long)B * a.Hq * a.Nk * D;
@@ -835,10 +836,6 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
-  const long long span = (kDqWaves / HP) * 32;
-  const int n_qt = (int)((a.Nq + span - 1) / span);
-  dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
   if (dense) {
     if (HP == 4)
       LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
@@ -880,6 +877,8 @@ hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream
     nq_tiles = std::max(nq_tiles, g.n_qtiles[c]);
   }
   const dim3 kgrid((unsigned)nk_tiles, (unsigned)calls[0].Hq, (unsigned)(B * n));
+  const dim3 qgrid((unsigned)nq_tiles, (unsigned)(calls[0].Hq / HP), (unsigned)(B * n));
+  if (!grid_fits(kgrid) || !grid_fits(qgrid)) return hipErrorInvalidConfiguration;
   if (G == 1)
     LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_group_kernel<D, false>), kgrid, dim3(64 * kSplitWaves), 0, stream, g,
                   B);
@@ -895,7 +894,6 @@ hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-  const dim3 qgrid((unsigned)nq_tiles, (unsigned)(calls[0].Hq / HP), (unsigned)(B * n));
   if (HP == 4)
     LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 4>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
   else if (HP == 2)

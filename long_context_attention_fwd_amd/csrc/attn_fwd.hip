@@ -70,8 +70,8 @@ constexpr int kBN = kFwdKeyTile;   // keys per tile
 // The kernel body: workgroup number lin (already in XCD-aware order) of a
 // grid of nx query tiles x ny head groups x (splits x batch).
 template <int D, int QB, int HP, bool OUT_F32>
-__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, long long lin, long long nx,
-                                              long long ny) {
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, unsigned lin, unsigned nx,
+                                              unsigned ny) {
   using T = SwzTile<D>;
   constexpr int KT = D / 16;       // reduction steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
@@ -94,14 +94,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, lo
   // the first ranges of every query tile before the later, shorter ones
   // XCD-aware order: neighbouring query tiles of one head group share an XCD
   // and its L2 while they stream the same key/value tiles
-  const int by = (int)(lin / nx % ny);
-  const long long bzs = lin / (nx * ny);
-  const int qt = n_qtiles - 1 - (int)(lin % nx);
+  const unsigned lxy = lin / nx;
+  const int by = (int)(lxy % ny);
+  const unsigned bzs = lxy / ny;
+  const int qt = n_qtiles - 1 - (int)(lin - lxy * nx);
   if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;
-  const long long bz = bzs % a.B;
-  const int split = (int)(bzs / a.B);
+  const unsigned split_u = bzs / (unsigned)a.B;
+  const long long bz = bzs - split_u * (unsigned)a.B;
+  const int split = (int)split_u;
   const long long q_start = (long long)qt * SPAN;
   const long long wq0 = q_start + (long long)(wave / HP) * QW;
 
@@ -118,6 +120,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, lo
   // this workgroup's key tiles: [j0, j0 + n_tiles) of its split
   const int j0 = split * a.split_tiles;
   const int n_tiles = max(0, min((int)((kv_end + kBN - 1) / kBN), j0 + a.split_tiles) - j0);
+  // a key range of the split forward that no query of the tile sees writes
+  // no partial: the merge reads only the ranges below the tile's last visible
+  // key tile
+  if (a.n_splits > 1 && n_tiles == 0) return;
   const int n_sub = 2 * n_tiles;  // 32-key sub-tiles
   // q_pos0 - k_pos0, clamped to the int range (rows and keys are < 2^31)
   const int dpos = (int)max(min(a.q_pos0 - a.k_pos0, (long long)INT32_MAX), (long long)INT32_MIN + 1);
@@ -491,9 +497,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, lo
 
 template <int D, int QB, int HP, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_qtiles) {
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  attn_fwd_body<D, QB, HP, OUT_F32>(a, n_qtiles, lin, nx, ny);
+  attn_fwd_body<D, QB, HP, OUT_F32>(a, n_qtiles, wg_number(), gridDim.x, gridDim.y);
 }
 
 // Independent calls in one launch (a ring step's query chunks against one
@@ -506,11 +510,10 @@ struct FwdGroup {
 
 template <int D, int QB, int HP, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_group_kernel(FwdGroup g, int B) {
-  const long long nx = gridDim.x, ny = gridDim.y;
-  const long long lin = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * (long long)blockIdx.z), nx * ny * gridDim.z);
-  const long long per_call = nx * ny * B;
-  const int c = (int)(lin / per_call);
-  attn_fwd_body<D, QB, HP, OUT_F32>(g.a[c], g.n_qtiles[c], lin - c * per_call, nx, ny);
+  const unsigned lin = wg_number();
+  const unsigned per_call = gridDim.x * gridDim.y * (unsigned)B;
+  const unsigned c = lin / per_call;
+  attn_fwd_body<D, QB, HP, OUT_F32>(g.a[c], g.n_qtiles[c], lin - c * per_call, gridDim.x, gridDim.y);
 }
 
 template <int D, int QB, int HP, bool F32>
@@ -518,6 +521,7 @@ hipError_t launch_cfg(const FwdArgs& a, int B, hipStream_t stream) {
   constexpr int SPAN = (kWaves / HP) * 32 * QB;
   const long long n_qtiles = (a.Nq + SPAN - 1) / SPAN;
   dim3 grid((unsigned)n_qtiles, (unsigned)(a.Hq / HP), (unsigned)(B * a.n_splits));
+  if (!grid_fits(grid)) return hipErrorInvalidConfiguration;
   LCATTN_LAUNCH(F32 ? "attn_fwd_kernel_fp32out" : "attn_fwd_kernel", (attn_fwd_kernel<D, QB, HP, F32>), grid,
                 dim3(kThreads), 0, stream, a, (int)n_qtiles);
   return hipGetLastError();
@@ -539,6 +543,7 @@ hipError_t launch_group_hp(FwdGroup& g, int n, int B, hipStream_t stream) {
     nx = std::max<long long>(nx, g.n_qtiles[c]);
   }
   dim3 grid((unsigned)nx, (unsigned)(g.a[0].Hq / HP), (unsigned)(B * n));
+  if (!grid_fits(grid)) return hipErrorInvalidConfiguration;
   LCATTN_LAUNCH("attn_fwd_kernel_fp32out", (attn_fwd_group_kernel<D, 1, HP, true>), grid, dim3(kThreads), 0, stream,
                 g, B);
   return hipGetLastError();
@@ -598,7 +603,16 @@ hipError_t launch_attn_fwd_splitkv(const FwdArgs& a0, int B, int D, int n_splits
   a.part_stride = (long long)B * a.Hq * a.Nq * D;
   hipError_t e = launch_attn_fwd(a, B, D, true, stream);
   if (e != hipSuccess) return e;
-  return launch_partial_merge(o_parts, true, lse_parts, n_splits, o, lse, (long long)B * a.Hq * a.Nq, D, stream);
+  const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
+  MergeSplits ms;
+  ms.span = (kWaves / HP) * 32;
+  ms.split_tiles = a.split_tiles;
+  ms.key_tile = kBN;
+  ms.Nq = a.Nq;
+  ms.Nk = a.Nk;
+  ms.dpos = a.q_pos0 - a.k_pos0;
+  ms.causal = a.causal;
+  return launch_partial_merge(o_parts, true, lse_parts, n_splits, o, lse, (long long)B * a.Hq * a.Nq, D, stream, &ms);
 }
 
 }  // namespace lcattn

@@ -305,11 +305,20 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // takes chunk x of even rounds and chunk 7 - x of odd ones, so that the long
 // and short workgroups of a longest-first order alternate on every XCD.
 // A bijection on [0, total); a last partial round keeps the identity.
-__device__ __forceinline__ long long xcd_order(long long lin, long long total) {
+__device__ __forceinline__ unsigned xcd_order(unsigned lin, unsigned total) {
   if (lin >= total / 256 * 256) return lin;
-  const long long round = lin / 256, x = lin % 8;
-  const long long chunk = (round & 1) ? 7 - x : x;
+  const unsigned round = lin / 256, x = lin % 8;
+  const unsigned chunk = (round & 1) ? 7 - x : x;
   return round * 256 + chunk * 32 + (lin % 256) / 8;
+}
+
+// This workgroup's number in its grid (x fastest), remapped by xcd_order.
+// 32-bit: every launch keeps its grid under 2^31 workgroups (checked on the
+// host), and 64-bit division by a run-time value costs hundreds of scalar
+// instructions in each workgroup's prologue.
+__device__ __forceinline__ unsigned wg_number() {
+  return xcd_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                   gridDim.x * gridDim.y * gridDim.z);
 }
 
 

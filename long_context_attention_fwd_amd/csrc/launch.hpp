@@ -30,6 +30,10 @@ hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long 
 constexpr int kFwdWaves = 8;     // waves per workgroup
 constexpr int kFwdKeyTile = 64;  // keys per tile
 
+// The attention kernels number their workgroups in 32 bits: a launch whose
+// grid has 2^31 or more workgroups is refused (hipErrorInvalidConfiguration).
+inline bool grid_fits(const dim3& g) { return (unsigned long long)g.x * g.y * g.z < (1ull << 31); }
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -75,8 +79,25 @@ hipError_t launch_attn_fwd_splitkv(const FwdArgs& a, int B, int D, int n_splits,
 // enough for two non-empty workgroups per compute unit.
 int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits);
 
+// Geometry of the split forward's partials: a query tile of `span` rows
+// (row i of the Nq rows of a head lies in tile i / span) has a partial for
+// every key range that starts before its last visible key, ranges being
+// split_tiles tiles of key_tile keys; the ranges after it wrote nothing.
+struct MergeSplits {
+  int span = 0;
+  int split_tiles = 0;
+  int key_tile = 0;
+  long long Nq = 0, Nk = 0;
+  long long dpos = 0;  // q_pos0 - k_pos0
+  int causal = 0;
+};
+
+// o[row] = LSE merge of the n_parts partials of each row; with `splits`, a
+// row reads only the partials its query tile has (fewer than n_parts when
+// its keys end early)
 hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
-                                uint16_t* o, float* lse, long long rows, int D, hipStream_t stream);
+                                uint16_t* o, float* lse, long long rows, int D, hipStream_t stream,
+                                const MergeSplits* splits = nullptr);
 
 struct BwdArgs {
   const uint16_t* q;

@@ -26,14 +26,25 @@ constexpr int kMergeThreads = 256;
 template <int D, bool PART_F32>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const void* __restrict__ o_parts,
                                                               const float* __restrict__ lse_parts,
-                                                              int n_parts, long long rows,
+                                                              int n_parts_max, long long rows,
                                                               uint16_t* __restrict__ o,
-                                                              float* __restrict__ lse) {
+                                                              float* __restrict__ lse, MergeSplits sp) {
   constexpr int U = D / 8;  // 8-element slices per row
   const long long idx = (long long)blockIdx.x * kMergeThreads + threadIdx.x;
   const long long row = idx / U;
   const int u = (int)(idx % U);
   if (row >= rows) return;
+  int n_parts = n_parts_max;
+  if (sp.span > 0) {
+    // the split forward: ranges past the query tile's last visible key wrote
+    // no partial (the bound uses the tile's last row, as the forward does)
+    const long long qt = (row % sp.Nq) / sp.span;
+    const long long q_last = min((qt + 1) * sp.span, sp.Nq) - 1;
+    long long kv_end = sp.Nk;
+    if (sp.causal) kv_end = max(0LL, min(sp.Nk, sp.dpos + q_last + 1));
+    const long long tiles = (kv_end + sp.key_tile - 1) / sp.key_tile;
+    n_parts = (int)min((long long)n_parts_max, (tiles + sp.split_tiles - 1) / sp.split_tiles);
+  }
 
   float m = -INFINITY;
   bool nan = false;
@@ -83,12 +94,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const void* __rest
 }
 
 hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
-                                uint16_t* o, float* lse, long long rows, int D, hipStream_t stream) {
+                                uint16_t* o, float* lse, long long rows, int D, hipStream_t stream,
+                                const MergeSplits* splits) {
   const long long threads = rows * (D / 8);
   const unsigned blocks = (unsigned)((threads + kMergeThreads - 1) / kMergeThreads);
+  const MergeSplits sp = splits ? *splits : MergeSplits{};
 #define LCATTN_MERGE(DD, F32)                                                                      \
   LCATTN_LAUNCH("merge_kernel", (merge_kernel<DD, F32>), dim3(blocks), dim3(kMergeThreads), 0, stream, o_parts, \
-                     lse_parts, n_parts, rows, o, lse)
+                     lse_parts, n_parts, rows, o, lse, sp)
   if (D == 64) {
     if (parts_f32) LCATTN_MERGE(64, true); else LCATTN_MERGE(64, false);
   } else {

@@ -19,7 +19,7 @@ hipError_t launch_attn_fwd_splitkv(const FwdArgs&, int, int, int, float*, float*
   return hipErrorNoDevice;
 }
 hipError_t launch_partial_merge(const void*, bool, const float*, int, uint16_t*, float*, long long, int,
-                                hipStream_t) {
+                                hipStream_t, const MergeSplits*) {
   return hipErrorNoDevice;
 }
 hipError_t launch_attn_bwd(const BwdArgs&, int, int, hipStream_t) { return hipErrorNoDevice; }
