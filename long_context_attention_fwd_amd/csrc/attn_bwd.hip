@@ -129,11 +129,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   const bool role_a = wave < 4;            // wave-uniform
   const int kg = wave & 3;                 // key group of 32 keys
   const long long Nq = a.Nq, Nk = a.Nk;
-  const unsigned lxy = lin / nx;
-  const long long bz = lxy / ny;
-  const int h = (int)(lxy % ny);
+  // 64-bit decode here: with the 32-bit one the register allocator spills
+  // lane offsets of the epilogue (measured: 48 MiB more writes per launch at
+  // 64K); the few hundred prologue instructions do not show in a launch
+  const long long llin = lin, lnx = nx, lny = ny;
+  const long long bz = llin / (lnx * lny);
+  const int h = (int)(llin / lnx % lny);
   const int kvh = h / a.G;
-  const long long kt0 = (long long)(lin - lxy * nx) * BK;
+  const long long kt0 = (llin % lnx) * BK;
   if (kt0 >= Nk) return;  // a grouped launch's grid covers its longest call
   const long long kw0 = kt0 + 32 * kg;
   const int key = (int)(kw0 + c);
@@ -529,10 +532,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
   const long long Nq = a.Nq, Nk = a.Nk;
   // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
   // they stream the same key/value tiles; longest causal rows first
-  const unsigned lxy = lin / nx;
-  const int by = (int)(lxy % ny);
-  const long long bz = lxy / ny;
-  const int qt = n_qtiles - 1 - (int)(lin - lxy * nx);
+  // workgroup-uniform: kept in scalar registers
+  const unsigned lxy = __builtin_amdgcn_readfirstlane(lin / nx);
+  const int by = __builtin_amdgcn_readfirstlane(lxy % ny);
+  const long long bz = (unsigned)__builtin_amdgcn_readfirstlane(lxy / ny);
+  const int qt = n_qtiles - 1 - __builtin_amdgcn_readfirstlane(lin - lxy * nx);
   if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;

@@ -94,14 +94,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
   // the first ranges of every query tile before the later, shorter ones
   // XCD-aware order: neighbouring query tiles of one head group share an XCD
   // and its L2 while they stream the same key/value tiles
-  const unsigned lxy = lin / nx;
-  const int by = (int)(lxy % ny);
-  const unsigned bzs = lxy / ny;
-  const int qt = n_qtiles - 1 - (int)(lin - lxy * nx);
+  // workgroup-uniform: kept in scalar registers
+  const unsigned lxy = __builtin_amdgcn_readfirstlane(lin / nx);
+  const int by = __builtin_amdgcn_readfirstlane(lxy % ny);
+  const unsigned bzs = __builtin_amdgcn_readfirstlane(lxy / ny);
+  const int qt = n_qtiles - 1 - __builtin_amdgcn_readfirstlane(lin - lxy * nx);
   if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;
-  const unsigned split_u = bzs / (unsigned)a.B;
+  const unsigned split_u = __builtin_amdgcn_readfirstlane(bzs / (unsigned)a.B);
   const long long bz = bzs - split_u * (unsigned)a.B;
   const int split = (int)split_u;
   const long long q_start = (long long)qt * SPAN;
