@@ -249,11 +249,11 @@ def test_ring_backward_32k_sampled(gpu, Hq, Hkv):
     check((dq[:, :, idx], dk, dv), (rq, rk, rv), f"32K ring Hq={Hq} Hkv={Hkv}")
 
 
-def _block_call_inputs(Hq, Hkv, D, Nq, Nk, q_pos0, k_pos0, seed):
+def _block_call_inputs(Hq, Hkv, D, Nq, Nk, q_pos0, k_pos0, seed, B=1):
     """q, k, v, dO of one block call and finite LSE, Dv for it (from the
     forward of q against this block)."""
     import torch
-    d = make_qkv(1, Hq, Hkv, max(Nq, Nk), D, seed=seed, with_do=True)
+    d = make_qkv(B, Hq, Hkv, max(Nq, Nk), D, seed=seed, with_do=True)
     q, do = (to_dev(d[n][:, :, :Nq].copy()) for n in ("q", "do"))
     k, v = (to_dev(d[n][:, :, :Nk].copy()) for n in ("k", "v"))
     o, lse = lc.attn_fwd(q, k, v, causal=False, scale=sdpa_scale(D))
@@ -262,13 +262,13 @@ def _block_call_inputs(Hq, Hkv, D, Nq, Nk, q_pos0, k_pos0, seed):
     return dict(q=q, k=k, v=v, do=do, lse=lse, delta=delta, q_pos0=q_pos0, k_pos0=k_pos0)
 
 
-@pytest.mark.parametrize("D,G", [(128, 1), (128, 4), (64, 2)])
-def test_bwd_block_group_matches_calls(gpu, D, G):
+@pytest.mark.parametrize("D,G,B", [(128, 1, 1), (128, 4, 1), (64, 2, 1), (128, 2, 2)])
+def test_bwd_block_group_matches_calls(gpu, D, G, B):
     """Up to four independent block calls in one group launch give exactly the
     results of the same calls made one at a time: uneven lengths and global
     positions (a diagonal block, a block partly visible, one fully visible,
     one no query sees), fp32 accumulators overwritten or added to, bf16
-    copies."""
+    copies; B = 2 checks the grid's (call, batch) numbering."""
     import torch
     Hkv = 2
     Hq = Hkv * G
@@ -276,16 +276,16 @@ def test_bwd_block_group_matches_calls(gpu, D, G):
     gen = torch.Generator(device="cuda").manual_seed(7)
     calls = []
     for i, (Nq, Nk, qp, kp) in enumerate(specs):
-        c = _block_call_inputs(Hq, Hkv, D, Nq, Nk, qp, kp, seed=300 + i)
+        c = _block_call_inputs(Hq, Hkv, D, Nq, Nk, qp, kp, seed=300 + i, B=B)
         acc = i % 2 == 1  # odd calls add into accumulators that already hold values
-        c["dq_acc"] = torch.randn((1, Hq, Nq, D), generator=gen, device="cuda")
-        c["dk_acc"] = torch.randn((1, Hkv, Nk, D), generator=gen, device="cuda")
-        c["dv_acc"] = torch.randn((1, Hkv, Nk, D), generator=gen, device="cuda")
+        c["dq_acc"] = torch.randn((B, Hq, Nq, D), generator=gen, device="cuda")
+        c["dk_acc"] = torch.randn((B, Hkv, Nk, D), generator=gen, device="cuda")
+        c["dv_acc"] = torch.randn((B, Hkv, Nk, D), generator=gen, device="cuda")
         c["dq_accumulate"] = acc
         c["dkv_accumulate"] = acc
-        c["dq"] = poisoned((1, Hq, Nq, D), torch.bfloat16)
-        c["dk"] = poisoned((1, Hkv, Nk, D), torch.bfloat16)
-        c["dv"] = poisoned((1, Hkv, Nk, D), torch.bfloat16)
+        c["dq"] = poisoned((B, Hq, Nq, D), torch.bfloat16)
+        c["dk"] = poisoned((B, Hkv, Nk, D), torch.bfloat16)
+        c["dv"] = poisoned((B, Hkv, Nk, D), torch.bfloat16)
         calls.append(c)
     outs = ("dq_acc", "dk_acc", "dv_acc", "dq", "dk", "dv")
     for n in (2, 4):
