@@ -21,15 +21,20 @@
  *    aligned, all tensors contiguous row-major in the layouts stated below.
  *  - bf16 tensors hold raw bfloat16 words; LSE and fp32 tensors hold float.
  *  - Ownership: the caller owns every buffer, including the backward
- *    workspace.  The library allocates and frees no device memory and keeps no
- *    global state apart from a thread-local error text (and the records of
- *    the optional measurement hook below).
+ *    workspace.  The library allocates and frees no device memory.  Its global
+ *    state: a thread-local error text, the records of the optional
+ *    measurement hook below, the per-GPU address of attn_bwd_noalloc's scratch
+ *    array, and the backward's side streams (one with two events per caller
+ *    stream, for up to 64 caller streams; see attn_bwd), all created at first
+ *    use and kept until the process ends.
  *  - Asynchrony: each call validates its arguments on the host, then enqueues
  *    its kernels on `hip_stream` (a hipStream_t; NULL = the default stream)
- *    and returns.  A validation failure returns a nonzero status before
- *    anything is launched and leaves the outputs untouched.  A launch failure
- *    returns ATTN_ERR_HIP.  Faults inside kernels surface at the caller's next
- *    synchronisation.
+ *    and returns.  Work a call puts on the side stream is forked from and
+ *    joined back into `hip_stream` with events, so everything a call does is
+ *    ordered on `hip_stream`.  A validation failure returns a nonzero status
+ *    before anything is launched and leaves the outputs untouched.  A launch
+ *    failure returns ATTN_ERR_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronisation.
  *  - Every element of every output is written, including masked rows.
  *  - Inputs and outputs must not overlap.
  */
@@ -217,6 +222,14 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
  * workspace (caller-owned, >= attn_bwd_workspace_size bytes, 16-byte aligned)
  * is scratch; its contents on return are unspecified.  The glossary example
  * backpropagates the mean of O^2, i.e. d_o = 2 O / numel.
+ * When the dK/dV pass has fewer than two workgroups per compute unit (short
+ * sequences, ring steps), the dQ pass runs beside it on a side stream of the
+ * library's own, forked from hip_stream after Dv and joined back before the
+ * call returns; results are the same bits either way.  Each caller stream
+ * has its own side stream (default priority, created on its first such call;
+ * up to 64 caller streams, further ones run single-stream), so no ordering
+ * between different caller streams is added.  Calls from several host
+ * threads are serialised around the fork and join.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
              const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -239,6 +252,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * threads) race and must be serialised by the caller.  Nothing in it needs
  * to start at zero.  The first call on a GPU looks up the array's device
  * address (not a device allocation); an error there returns ATTN_ERR_HIP.
+ * Every launch stays on hip_stream (no side stream is created or used).
  */
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                      const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int64_t N, int D,
@@ -432,8 +446,7 @@ int head_to_seq_reduce(const void* in, int in_dtype, void* out, int P, int64_t N
  * total_ms[i] and the launch count into calls[i] for i < max_kernels --
  * releases the records and returns the number of distinct kernels, or
  * -ATTN_ERR_HIP if an event could not be read.  The events are created once
- * and reused; this is the library's only state besides the thread-local
- * error text.  Thread-safe.
+ * and reused.  Thread-safe.
  */
 int attn_trace_enable(int on);
 int attn_trace_collect(char* names, int name_len, double* total_ms, int* calls, int max_kernels);

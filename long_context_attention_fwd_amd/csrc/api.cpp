@@ -2,9 +2,11 @@
 //
 // Every entry point validates on the host first and returns a status without
 // touching the GPU when validation fails, so the error paths are testable on a
-// machine without a GPU.  Kernels are enqueued on the caller's stream; the
-// library allocates nothing and keeps no state except a thread-local error
-// text.
+// machine without a GPU.  Kernels are enqueued on the caller's stream (the
+// backward of a small problem forks its dQ pass onto a side stream of the
+// library and joins it back); the library allocates no device memory, and its
+// only state is a thread-local error text, the measurement hook's records and
+// per-GPU handles created at first use (scratch address, side stream).
 #include "attn.h"
 
 #include <hip/hip_runtime.h>
@@ -484,7 +486,7 @@ static int bwd_entry(const char* name, const void* q, const void* k, const void*
     }
   char what[64];
   snprintf(what, sizeof(what), "%s launch", name);
-  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), what);
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), !use_scratch), what);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -635,7 +637,8 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
                                  workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0, k_pos0,
                                  dq_accumulate, dkv_accumulate, &a, ins, inb, outs, outb);
   if (st != ATTN_OK) return st;
-  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream)), "attn_bwd_block launch");
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), true),
+                    "attn_bwd_block launch");
 }
 
 int attn_bwd_block_group(const attn_bwd_block_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,

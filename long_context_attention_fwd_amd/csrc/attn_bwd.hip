@@ -778,6 +778,107 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_group_kernel(BwdGroup
   bwd_dq_body<D, HP, true>(g.a[c], g.n_qtiles[c], lin - c * per_call, gridDim.x, gridDim.y);
 }
 
+// ---------------------------------------------------------------------------
+// Small problems: the dQ pass beside the dK/dV pass.  Both read only the
+// inputs and Dv and write disjoint outputs, so when the dK/dV grid would not
+// fill the GPU twice over, the dQ pass runs on a side stream of the library's
+// own, forked from the caller's stream after Dv and joined back into it after
+// the dK/dV launches (events): every launch of a call stays ordered on the
+// caller's stream.  Each caller stream gets its own side stream and pair of
+// events (default priority; created at its first such call with the stream's
+// device current, kept until the process ends), so a side stream only ever
+// carries work forked from one caller stream, in that stream's order, and adds
+// no dependency between different caller streams.  At most kSideSlots caller
+// streams get one; calls on further streams run on their stream alone.  A
+// mutex keeps concurrent calls from interleaving their fork/join pairs.
+// ---------------------------------------------------------------------------
+constexpr int kSideSlots = 64;
+struct SideStream {
+  bool used = false;
+  int dev = -1;
+  hipStream_t caller = nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int cus = 0;
+};
+std::mutex g_side_mu;
+SideStream g_side[kSideSlots];
+
+// The side stream of `caller` (nullptr with hipSuccess when every slot is
+// taken); g_side_mu must be held.
+hipError_t side_stream(hipStream_t caller, SideStream** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(caller, &dev);
+  if (e != hipSuccess) return e;
+  SideStream* slot = nullptr;
+  for (SideStream& ss : g_side) {
+    if (ss.used && ss.dev == dev && ss.caller == caller) {
+      *out = &ss;
+      return hipSuccess;
+    }
+    if (!ss.used && !slot) slot = &ss;
+  }
+  if (!slot) return hipSuccess;
+  int cur = 0;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+  SideStream n;
+  n.used = true;
+  n.dev = dev;
+  n.caller = caller;
+  e = hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+  const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+  if (e != hipSuccess || e2 != hipSuccess) {
+    if (n.join) (void)hipEventDestroy(n.join);
+    if (n.fork) (void)hipEventDestroy(n.fork);
+    if (n.s) (void)hipStreamDestroy(n.s);
+    return e != hipSuccess ? e : e2;
+  }
+  *slot = n;
+  *out = slot;
+  return hipSuccess;
+}
+
+// Where a call's dQ pass goes.  begin() decides (the dK/dV pass has fewer
+// than two workgroups per compute unit and the caller allows a second
+// stream) and forks; end() joins, after the dK/dV launches were enqueued.
+class DqStream {
+ public:
+  hipError_t begin(hipStream_t caller, bool allow, long long dkdv_workgroups) {
+    caller_ = caller;
+    if (!allow) return hipSuccess;
+    lock_ = std::unique_lock<std::mutex>(g_side_mu);
+    SideStream* ss = nullptr;
+    hipError_t e = side_stream(caller, &ss);
+    if (e != hipSuccess) return e;
+    if (!ss || dkdv_workgroups >= 2LL * ss->cus) {
+      lock_.unlock();
+      return hipSuccess;
+    }
+    if ((e = hipEventRecord(ss->fork, caller)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+    side_ = ss;
+    return hipSuccess;
+  }
+  hipStream_t stream() const { return side_ ? side_->s : caller_; }
+  hipError_t end() {
+    if (!side_) return hipSuccess;
+    hipError_t e = hipEventRecord(side_->join, side_->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(caller_, side_->join, 0);
+    side_ = nullptr;
+    return e;
+  }
+
+ private:
+  hipStream_t caller_ = nullptr;
+  SideStream* side_ = nullptr;
+  std::unique_lock<std::mutex> lock_;
+};
+
 template <int D>
 hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, int B, int H, long long N,
                         const long long (&st)[3], hipStream_t stream) {
@@ -789,7 +890,7 @@ hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, in
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
+hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_side) {
   hipError_t e;
   BwdArgs a = a0;
   const bool dense = a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0 && a.ks[0] == 0 && a.ks[1] == 0 && a.ks[2] == 0;
@@ -813,6 +914,27 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
     e = launch_delta<D>(a.o, a.d_o, a.delta, B, a.Hq, a.Nq, a.qs, stream);
     if (e != hipSuccess) return e;
   }
+  DqStream dqs;
+  if ((e = dqs.begin(stream, allow_side, (long long)kgrid.x * kgrid.y * kgrid.z)) != hipSuccess) return e;
+  const hipStream_t qstream = dqs.stream();
+  // the dQ pass first: on the side stream it then runs beside the dK/dV pass
+  if (dense) {
+    if (HP == 4)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, true>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
+    else if (HP == 2)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2, true>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
+    else
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1, true>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
+  } else {
+    if (HP == 4)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, false>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
+    else if (HP == 2)
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2, false>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
+    else
+      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1, false>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     float* dk_part = a.G == 1 ? nullptr : a.part;
     float* dv_part = a.G == 1 ? nullptr : dk_part + (long long)B * a.Hq * a.Nk * D;
@@ -840,28 +962,13 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dense) {
-    if (HP == 4)
-      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-    else if (HP == 2)
-      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-    else
-      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1, true>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-  } else {
-    if (HP == 4)
-      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, false>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-    else if (HP == 2)
-      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 2, false>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-    else
-      LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 1, false>), grid, dim3(64 * kDqWaves), 0, stream, a, n_qt);
-  }
-  return hipGetLastError();
+  return dqs.end();
 }
 
 // One launch per kernel for up to kMaxBwdGroup block calls (dense tensors,
 // Dv given, shared B, Hq, Hkv, D, scale and mask kind).
 template <int D>
-hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream) {
+hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream, bool allow_side) {
   hipError_t e;
   BwdGroup g{};
   long long nk_tiles = 0;
@@ -883,6 +990,17 @@ hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream
   const dim3 kgrid((unsigned)nk_tiles, (unsigned)calls[0].Hq, (unsigned)(B * n));
   const dim3 qgrid((unsigned)nq_tiles, (unsigned)(calls[0].Hq / HP), (unsigned)(B * n));
   if (!grid_fits(kgrid) || !grid_fits(qgrid)) return hipErrorInvalidConfiguration;
+  DqStream dqs;
+  if ((e = dqs.begin(stream, allow_side, (long long)kgrid.x * kgrid.y * kgrid.z)) != hipSuccess) return e;
+  const hipStream_t qstream = dqs.stream();
+  if (HP == 4)
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 4>), qgrid, dim3(64 * kDqWaves), 0, qstream, g, B);
+  else if (HP == 2)
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 2>), qgrid, dim3(64 * kDqWaves), 0, qstream, g, B);
+  else
+    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 1>), qgrid, dim3(64 * kDqWaves), 0, qstream, g, B);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (G == 1)
     LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_group_kernel<D, false>), kgrid, dim3(64 * kSplitWaves), 0, stream, g,
                   B);
@@ -898,13 +1016,7 @@ hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-  if (HP == 4)
-    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 4>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
-  else if (HP == 2)
-    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 2>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
-  else
-    LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_group_kernel<D, 1>), qgrid, dim3(64 * kDqWaves), 0, stream, g, B);
-  return hipGetLastError();
+  return dqs.end();
 }
 
 }  // namespace
@@ -950,11 +1062,11 @@ hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
 }
 
 hipError_t launch_attn_bwd_group(const BwdArgs* calls, int n, int B, int D, hipStream_t stream) {
-  return D == 64 ? launch_d_group<64>(calls, n, B, stream) : launch_d_group<128>(calls, n, B, stream);
+  return D == 64 ? launch_d_group<64>(calls, n, B, stream, true) : launch_d_group<128>(calls, n, B, stream, true);
 }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream) {
-  return D == 64 ? launch_d<64>(a, B, stream) : launch_d<128>(a, B, stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream, bool allow_side) {
+  return D == 64 ? launch_d<64>(a, B, stream, allow_side) : launch_d<128>(a, B, stream, allow_side);
 }
 
 hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, int D,

@@ -145,7 +145,11 @@ long long bwd_delta_floats(int B, int Hq, long long Nq);
 long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D);
 long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream);
+// allow_side: a problem whose dK/dV grid has fewer than two workgroups per
+// compute unit runs its dQ pass on the library's side stream of the device
+// (forked from and joined back into `stream`); false keeps every launch on
+// `stream` and creates nothing (the allocation-free entry point)
+hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream, bool allow_side);
 // Up to kMaxBwdGroup independent block-backward calls (contiguous tensors, Dv
 // given, the same B, Hq, Hkv, D, scale and mask kind): one dK/dV launch and
 // one dQ launch for all of them.

@@ -22,7 +22,7 @@ hipError_t launch_partial_merge(const void*, bool, const float*, int, uint16_t*,
                                 hipStream_t, const MergeSplits*) {
   return hipErrorNoDevice;
 }
-hipError_t launch_attn_bwd(const BwdArgs&, int, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_attn_bwd(const BwdArgs&, int, int, hipStream_t, bool) { return hipErrorNoDevice; }
 hipError_t launch_attn_bwd_group(const BwdArgs*, int, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_bwd_delta(const uint16_t*, const uint16_t*, float*, long long, int, hipStream_t) {
   return hipErrorNoDevice;

@@ -217,3 +217,58 @@ def test_bwd_ulysses_shard_32k_full_do(gpu):
     errs = [grad_rel_err(g, r) for g, r in zip(got, (rq, rk, rv))]
     assert all(np.isfinite(g).all() for g in got)
     assert max(errs) <= GRAD_REL_TOL, errs
+
+
+def test_bwd_side_stream_concurrent_callers(gpu):
+    """Small backwards run their dQ pass on a side stream of the library's own,
+    one per caller stream.  Calls issued concurrently from two caller streams,
+    and a chain of accumulating block calls on a third, give the same bits as
+    the same work done alone, one call at a time, on the default stream; the
+    allocation-free entry point (single stream) agrees with both."""
+    import torch
+    D, N = 64, 4096
+    ins = []
+    for seed in (31, 32):
+        d = make_qkv(1, 4, 4, N, D, seed=seed, with_do=True)
+        q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+        o, lse = lc.attn_fwd(q, k, v, scale=sdpa_scale(D))
+        ins.append((q, k, v, o, do, lse))
+    torch.cuda.synchronize()
+
+    def bwd(x):
+        q, k, v, o, do, lse = x
+        return lc.attn_bwd(q, k, v, o, do, lse, scale=sdpa_scale(D))
+    ref = [bwd(x) for x in ins]
+    torch.cuda.synchronize()
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    out = [None, None]
+    for _ in range(3):
+        ev = torch.cuda.Event()
+        ev.record()
+        for st in (s1, s2, s3):
+            st.wait_event(ev)
+        with torch.cuda.stream(s1):
+            out[0] = bwd(ins[0])
+        with torch.cuda.stream(s2):
+            out[1] = bwd(ins[1])
+        with torch.cuda.stream(s3):
+            # four KV blocks of ins[0] accumulated into one fp32 dQ, in order
+            q, k, v, o, do, lse = ins[0]
+            delta = lc.attn_bwd_delta(o, do)
+            dq_acc = torch.empty(tuple(q.shape), dtype=torch.float32, device="cuda")
+            for i, a in enumerate(range(0, N, 1024)):
+                lc.attn_bwd_block(q, k[:, :, a:a + 1024].contiguous(), v[:, :, a:a + 1024].contiguous(), do, lse, delta,
+                                  scale=sdpa_scale(D), k_pos0=a, dq_acc=dq_acc, dq_accumulate=i > 0)
+            dq_blocks = dq_acc.to(torch.bfloat16)
+        torch.cuda.synchronize()
+        for r, g in zip(ref, out):
+            for x, y in zip(r, g):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+        # the block chain sums the same fp32 terms in another grouping: gate, not bits
+        assert grad_rel_err(f64_of(dq_blocks), f64_of(ref[0][0])) <= GRAD_REL_TOL
+    q, k, v, o, do, lse = ins[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lc.attn_bwd_noalloc(q, k, v, o, do, lse, scale=sdpa_scale(D), dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for x, y in zip(ref[1], (dq, dk, dv)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
