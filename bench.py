@@ -287,10 +287,12 @@ def train_64k(lc, torch, dev, steps, warmup):
 # legs
 # ---------------------------------------------------------------------------
 def leg_listing_4k(lc, torch, dev, iters=50, warmup=10):
-    """The glossary example's forward shape ([1, 4, 4096, 64], causal):
-    attn_fwd, and attn_fwd_splitkv with the library's choice of key ranges
-    (one workgroup per 256 query rows gives only 64 workgroups here, so the
-    longest row sets attn_fwd's time)."""
+    """The glossary example's shape ([1, 4, 4096, 64], causal): attn_fwd, and
+    attn_fwd_splitkv with the library's choice of key ranges (one workgroup
+    per 256 query rows gives only 64 workgroups here, so the longest row sets
+    attn_fwd's time); then the example's backward, attn_bwd of its loss
+    mean(O^2) (dO = 2 O / numel), whose dQ pass runs beside the dK/dV pass at
+    this size."""
     from long_context_attention_fwd_amd.inputs import WORKLOADS
     w = WORKLOADS["listing_4k"]
     d = host_inputs(w.name)
@@ -313,6 +315,22 @@ def leg_listing_4k(lc, torch, dev, iters=50, warmup=10):
                      "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in tr.items()}}
         kern = "attn_fwd_kernel" if name == "attn_fwd" else "attn_fwd_kernel_fp32out"
         rls[f"{w.name}.{name}"] = roofline_entry(kern, tr, f, "TFLOP/s", w.name)
+    lc.attn_fwd(q, k, v, scale=w.scale, o=o, lse=lse)
+    do = (o.float() * (2.0 / o.numel())).to(torch.bfloat16)
+    wsb = torch.empty(max(16, lc.attn_bwd_workspace_size(B, Hq, w.Hkv, N, D)), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    f_bwd = 2.5 * f
+
+    def bwd():
+        lc.attn_bwd(q, k, v, o, do, lse, scale=w.scale, workspace=wsb, dq=dq, dk=dk, dv=dv)
+    ms, tr = traced_calls(lc, torch, bwd, iters, warmup)
+    ms_plain = time_calls(torch, bwd, iters, warmup)
+    res["attn_bwd"] = {"us": round(1e3 * ms_plain, 2), "TFLOP/s": round(tflops(f_bwd, ms_plain), 2),
+                       "frac_peak": round(tflops(f_bwd, ms_plain) / PEAK_BF16_TFLOPS, 4),
+                       "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in tr.items()},
+                       "loss": "mean(O^2): dO = 2 O / numel"}
+    rls[f"{w.name}.bwd_dkdv_kernel"] = roofline_entry("bwd_dkdv_kernel", tr, 0.8 * f_bwd, "TFLOP/s", w.name)
+    rls[f"{w.name}.bwd_dq_kernel"] = roofline_entry("bwd_dq_kernel", tr, 0.2 * f_bwd, "TFLOP/s", w.name)
     return res, rls
 
 
