@@ -272,3 +272,44 @@ def test_bwd_side_stream_concurrent_callers(gpu):
     torch.cuda.synchronize()
     for x, y in zip(ref[1], (dq, dk, dv)):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_bwd_graph_capture_replays(gpu):
+    """Forward and backward of the glossary shape captured into one HIP graph
+    (the backward forks its dQ pass onto its side stream and joins it back
+    inside the capture) and replayed three times, with eager library calls on
+    other inputs in between: every replay equals the eager result bit for bit."""
+    import torch
+    D, N = 64, 4096
+    d = make_qkv(1, 4, 4, N, D, seed=41, with_do=True)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    s = sdpa_scale(D)
+    o, lse = torch.empty_like(q), torch.empty((1, 4, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, lc.attn_bwd_workspace_size(1, 4, 4, N, D)), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        lc.attn_fwd(q, k, v, scale=s, o=o, lse=lse)
+        lc.attn_bwd(q, k, v, o, do, lse, scale=s, workspace=ws, dq=dq, dk=dk, dv=dv)
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        step()  # the capture stream's side stream exists before the capture
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (o, lse, dq, dk, dv)]
+    other = make_qkv(1, 4, 4, N, D, seed=42, with_do=True)
+    oq, ok_, ov, odo = (to_dev(other[n]) for n in ("q", "k", "v", "do"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    for _ in range(3):
+        for x in (o, lse, dq, dk, dv):
+            x.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for r, x in zip(ref, (o, lse, dq, dk, dv)):
+            assert torch.equal(r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32),
+                               x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32))
+        # eager work of the library between replays
+        oo, ol = lc.attn_fwd(oq, ok_, ov, scale=s)
+        lc.attn_bwd(oq, ok_, ov, oo, odo, ol, scale=s)
+        torch.cuda.synchronize()
