@@ -596,9 +596,16 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, o_full, lse_ful
     o_acc = [torch.empty((1, hq, C, D), dtype=torch.float32, device=dev) for _ in range(2)]
     lse = [torch.empty((1, hq, C), dtype=torch.float32, device=dev) for _ in range(2)]
     o_fin = [torch.empty((1, hq, C, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    hkv = ck[0].shape[1]
+    n_split = lc.attn_fwd_split_suggest(1, hq, hkv, C, C, True, 2)
+    fws = [torch.empty(max(16, lc.attn_fwd_accumulate_workspace_size(1, hq, C, D, n_split)), dtype=torch.uint8,
+                       device=dev) for _ in range(4)]
     res = {"ranks": Pr, "chunk_tokens": C,
-           "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair, in sequence"}
-    for scheme, grouped in [(sc, g) for g in (False, True) for sc in SCHEMES]:
+           "call": "attn_fwd_accumulate per visible (query chunk, key chunk) pair, in sequence; _grouped: a step's "
+                   "independent calls in one launch; _grouped_split: that launch with each call's keys in "
+                   f"{n_split} ranges (attn_fwd_accumulate_group_split) and a merge per call"}
+    for scheme, grouped, split in [(sc, g, sp) for g, sp in ((False, 1), (True, 1), (True, n_split))
+                                   for sc in SCHEMES]:
         t = [[0.0] * Pr for _ in range(Pr)]
         for r in range(Pr):
             qs = [cq[c] for c in rank_chunks(r, Pr, scheme)]
@@ -608,9 +615,10 @@ def ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, o_full, lse_ful
             for st in range(Pr):
                 t[r][st] = time_calls(torch, lambda: ring_forward(qs, kv, r, Pr, C, o_acc=o_acc, lse_acc=lse,
                                                                   o_final=o_fin, scheme=scheme, scale=scale,
-                                                                  steps={st}, grouped=grouped))
+                                                                  steps={st}, grouped=grouped, n_splits=split,
+                                                                  workspaces=fws))
         crit = sum(max(t[r][s] for r in range(Pr)) for s in range(Pr))
-        res[scheme + ("_grouped" if grouped else "")] = {
+        res[scheme + ("_grouped" if grouped else "") + ("_split" if split > 1 else "")] = {
             "critical_path_ms": round(crit, 4), "ring_TFLOP/s": round(tflops(f_fwd, crit), 2),
             "per_rank_TFLOP/s": round(tflops(f_fwd, crit) / Pr, 2),
             "per_rank_ms": [round(sum(t[r]), 4) for r in range(Pr)],

@@ -153,6 +153,38 @@ int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, i
                               int causal, void* hip_stream);
 
 /*
+ * attn_fwd_accumulate_group_split -- attn_fwd_accumulate_group with each
+ * call's key/value block cut into n_splits ranges of key tiles that run side
+ * by side, for calls too small to fill the GPU (a ring step of a short chunk:
+ * the query rows alone give a few workgroups per compute unit at most).  Each
+ * range's attention goes, in fp32, into the call's workspace; then one merge
+ * pass per call combines the ranges that hold visible keys with the running
+ * result (o_acc, lse_acc; not read when first) by the attn_partial_merge rule
+ * ("So funktioniert Kontextparallelität") and writes o_acc, lse_acc and
+ * o_final.  The sums are grouped differently from attn_fwd_accumulate, so
+ * results agree with it up to rounding, not bit for bit; n_splits = 1 still
+ * takes this path (one range, then the merge).
+ *
+ * Each entry: an attn_accumulate_call with the meaning of
+ * attn_fwd_accumulate_group's entries, and its workspace (device memory of
+ * at least attn_fwd_accumulate_workspace_size(B, Hq, call.Nq, D, n_splits)
+ * bytes, 16-byte aligned, apart from every argument and every other
+ * workspace; contents unspecified on return).  1 <= n_splits <= 64 and
+ * B * n * n_splits <= 65535.  attn_fwd_split_suggest gives the library's
+ * choice of n_splits for n_calls such calls side by side (1: no split).
+ * Validation as attn_fwd_accumulate_group, workspaces included.
+ */
+typedef struct {
+  attn_accumulate_call call;
+  void* workspace;          /* fp32 partials of the call's key ranges */
+  size_t workspace_bytes;
+} attn_accumulate_split_call;
+int attn_fwd_split_suggest(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int causal, int n_calls);
+size_t attn_fwd_accumulate_workspace_size(int B, int Hq, int64_t Nq, int D, int n_splits);
+int attn_fwd_accumulate_group_split(const attn_accumulate_split_call* calls, int n, int B, int Hq, int Hkv, int D,
+                                    float scale, int causal, int n_splits, void* hip_stream);
+
+/*
  * attn_fwd_splitkv_workspace_size -- bytes of device workspace attn_fwd_splitkv
  * needs for the same arguments: fp32 partial outputs and log-sum-exps of every
  * key range, n * B*Hq*Nq*(D + 1) floats for n ranges (n_splits > 0: that many;

@@ -24,6 +24,9 @@ __all__ = [
     "attn_fwd_strided",
     "attn_fwd_accumulate",
     "attn_fwd_accumulate_group",
+    "attn_fwd_split_suggest",
+    "attn_fwd_accumulate_workspace_size",
+    "attn_fwd_accumulate_group_split",
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_size",
     "attn_partial_merge",
@@ -80,6 +83,11 @@ class AccumulateCall(ctypes.Structure):
                 ("k_pos0", ctypes.c_int64), ("first", ctypes.c_int)]
 
 
+class AccumulateSplitCall(ctypes.Structure):
+    """One entry of attn_fwd_accumulate_group_split (mirrors attn_accumulate_split_call)."""
+    _fields_ = [("call", AccumulateCall), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class BwdBlockCall(ctypes.Structure):
     """One entry of attn_bwd_block_group (mirrors attn_bwd_block_call)."""
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
@@ -96,6 +104,9 @@ _SIGS = {
     "attn_fwd_strided": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _P, _P, _P, _P]),
     "attn_fwd_accumulate": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P]),
     "attn_fwd_accumulate_group": (_I, [_P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_split_suggest": (_I, [_I, _I, _I, _L, _L, _I, _I]),
+    "attn_fwd_accumulate_workspace_size": (ctypes.c_size_t, [_I, _I, _L, _I, _I]),
+    "attn_fwd_accumulate_group_split": (_I, [_P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_fwd_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _L, _I, _I, _I]),
     "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _P, ctypes.c_size_t,
                               _P]),
@@ -278,13 +289,10 @@ def attn_fwd_accumulate(q, k, v, o_acc, lse_acc, *, first: bool, causal: bool = 
     return o_acc, lse_acc
 
 
-def attn_fwd_accumulate_group(calls, *, causal: bool = True, scale: float | None = None):
-    """Independent attn_fwd_accumulate calls (1 to 4) in one launch.  calls:
-    dicts with q, k, v, o_acc, lse_acc, first and optionally o_final,
-    q_pos0, k_pos0 (meanings as in attn_fwd_accumulate); B, Hq, Hkv, D are
-    shared.  The calls must not write what another call reads or writes."""
+def _accumulate_calls(calls):
+    """Checks of a group of accumulate calls; returns (AccumulateCall array,
+    B, Hq, Hkv, D)."""
     torch = _torch()
-    calls = list(calls)
     if not 1 <= len(calls) <= 4:
         raise ValueError("a group holds 1 to 4 calls")
     B, Hq, _, D = calls[0]["q"].shape
@@ -311,9 +319,52 @@ def attn_fwd_accumulate_group(calls, *, causal: bool = True, scale: float | None
         arr[i] = AccumulateCall(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_acc.data_ptr(), lse_acc.data_ptr(),
                                 None if of is None else of.data_ptr(), Nq, Nk, int(c.get("q_pos0", 0)),
                                 int(c.get("k_pos0", 0)), 1 if c["first"] else 0)
+    return arr, B, Hq, Hkv, D
+
+
+def attn_fwd_accumulate_group(calls, *, causal: bool = True, scale: float | None = None):
+    """Independent attn_fwd_accumulate calls (1 to 4) in one launch.  calls:
+    dicts with q, k, v, o_acc, lse_acc, first and optionally o_final,
+    q_pos0, k_pos0 (meanings as in attn_fwd_accumulate); B, Hq, Hkv, D are
+    shared.  The calls must not write what another call reads or writes."""
+    calls = list(calls)
+    arr, B, Hq, Hkv, D = _accumulate_calls(calls)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib().attn_fwd_accumulate_group(arr, len(calls), B, Hq, Hkv, D, scale, 1 if causal else 0,
                                            _stream(calls[0]["q"])))
+
+
+def attn_fwd_split_suggest(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, causal: bool = True, n_calls: int = 1) -> int:
+    """The library's choice of key ranges for n_calls accumulate calls of this
+    size run side by side (1: no split)."""
+    return int(lib().attn_fwd_split_suggest(B, Hq, Hkv, Nq, Nk, 1 if causal else 0, n_calls))
+
+
+def attn_fwd_accumulate_workspace_size(B: int, Hq: int, Nq: int, D: int, n_splits: int) -> int:
+    return int(lib().attn_fwd_accumulate_workspace_size(B, Hq, Nq, D, n_splits))
+
+
+def attn_fwd_accumulate_group_split(calls, *, n_splits: int, causal: bool = True, scale: float | None = None):
+    """attn_fwd_accumulate_group with each call's keys in n_splits ranges side
+    by side, then one merge per call into its running result.  calls: as
+    attn_fwd_accumulate_group's, each with a "workspace" (uint8 device tensor
+    of >= attn_fwd_accumulate_workspace_size bytes; allocated when absent)."""
+    torch = _torch()
+    calls = list(calls)
+    arr, B, Hq, Hkv, D = _accumulate_calls(calls)
+    sarr = (AccumulateSplitCall * len(calls))()
+    keep = []
+    for i, c in enumerate(calls):
+        need = attn_fwd_accumulate_workspace_size(B, Hq, c["q"].shape[2], D, n_splits)
+        ws = c.get("workspace")
+        if ws is None:
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=c["q"].device)
+        keep.append(ws)
+        sarr[i] = AccumulateSplitCall(arr[i], ws.data_ptr(), ws.numel() * ws.element_size())
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().attn_fwd_accumulate_group_split(sarr, len(calls), B, Hq, Hkv, D, scale, 1 if causal else 0,
+                                                 int(n_splits), _stream(calls[0]["q"])))
+    del keep  # the launches are enqueued: the stream orders any reuse after them
 
 
 def attn_fwd_splitkv_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, causal: bool = True,

@@ -269,23 +269,26 @@ int attn_fwd_accumulate(const void* q, const void* k, const void* v, float* o_ac
 static_assert(ATTN_MAX_FWD_GROUP == lcattn::kMaxFwdGroup, "group limit of the header and the kernel");
 static_assert(ATTN_MAX_BWD_GROUP == lcattn::kMaxBwdGroup, "group limit of the header and the kernels");
 
-int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
-                              int causal, void* hip_stream) {
-  const char* name = "attn_fwd_accumulate_group";
-  if (!calls) return fail(ATTN_ERR_NULL, "%s: null call array", name);
+}  // extern "C"
+
+namespace {
+
+// Validation of a group of accumulate calls (each as attn_fwd_accumulate; no
+// call's outputs may overlap another call's inputs or outputs); fills the
+// kernel arguments and each call's byte ranges (inputs q, k, v; outputs
+// o_acc, lse_acc, o_final).
+int accumulate_group_check(const char* name, const attn_accumulate_call* const* calls, int n, int B, int Hq,
+                           int Hkv, int D, float scale, int causal, lcattn::FwdArgs* args,
+                           const void* (*in_p)[3], size_t (*in_b)[3], const void* (*out_p)[3],
+                           size_t (*out_b)[3]) {
   if (n < 1 || n > ATTN_MAX_FWD_GROUP) return fail(ATTN_ERR_SHAPE, "%s: n=%d calls (1 .. %d)", name, n, ATTN_MAX_FWD_GROUP);
-  if ((int64_t)B * n > 65535) return fail(ATTN_ERR_UNSUPPORTED, "%s: B * n must be <= 65535", name);
-  lcattn::FwdArgs args[ATTN_MAX_FWD_GROUP];
-  // byte ranges of every call's inputs (q, k, v) and outputs (o_acc, lse_acc, o_final)
-  const void* in_p[ATTN_MAX_FWD_GROUP][3];
-  size_t in_b[ATTN_MAX_FWD_GROUP][3];
-  const void* out_p[ATTN_MAX_FWD_GROUP][3];
-  size_t out_b[ATTN_MAX_FWD_GROUP][3];
+  for (int c = 0; c < n; ++c)
+    if (!calls[c]) return fail(ATTN_ERR_NULL, "%s: null call array", name);
   for (int c = 0; c < n; ++c) {
-    const attn_accumulate_call& x = calls[c];
+    const attn_accumulate_call& x = *calls[c];
     int st = fwd_check(name, x.q, x.k, x.v, x.o_acc, ATTN_FP32, x.lse_acc, B, Hq, Hkv, x.Nq, x.Nk, D, scale, causal,
                        x.q_pos0, x.k_pos0, &args[c]);
-    int64_t nq_el, nk_el, nl;
+    int64_t nq_el = 0, nk_el = 0, nl = 0;
     elems(&nq_el, {B, Hq, x.Nq, D});
     elems(&nk_el, {B, Hkv, x.Nk, D});
     elems(&nl, {B, Hq, x.Nq});
@@ -325,8 +328,86 @@ int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, i
         }
       }
     }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_accumulate_group(const attn_accumulate_call* calls, int n, int B, int Hq, int Hkv, int D, float scale,
+                              int causal, void* hip_stream) {
+  const char* name = "attn_fwd_accumulate_group";
+  if (!calls) return fail(ATTN_ERR_NULL, "%s: null call array", name);
+  if (n < 1 || n > ATTN_MAX_FWD_GROUP) return fail(ATTN_ERR_SHAPE, "%s: n=%d calls (1 .. %d)", name, n, ATTN_MAX_FWD_GROUP);
+  if ((int64_t)B * n > 65535) return fail(ATTN_ERR_UNSUPPORTED, "%s: B * n must be <= 65535", name);
+  const attn_accumulate_call* ptrs[ATTN_MAX_FWD_GROUP];
+  for (int c = 0; c < n; ++c) ptrs[c] = &calls[c];
+  lcattn::FwdArgs args[ATTN_MAX_FWD_GROUP];
+  const void* in_p[ATTN_MAX_FWD_GROUP][3];
+  size_t in_b[ATTN_MAX_FWD_GROUP][3];
+  const void* out_p[ATTN_MAX_FWD_GROUP][3];
+  size_t out_b[ATTN_MAX_FWD_GROUP][3];
+  const int st = accumulate_group_check(name, ptrs, n, B, Hq, Hkv, D, scale, causal, args, in_p, in_b, out_p, out_b);
+  if (st != ATTN_OK) return st;
   return hip_status(lcattn::launch_attn_fwd_group(args, n, B, D, static_cast<hipStream_t>(hip_stream)),
                     "attn_fwd_accumulate_group launch");
+}
+
+int attn_fwd_split_suggest(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int causal, int n_calls) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || n_calls < 1) return 1;
+  // the choice for one call of n_calls times the rows: the calls run side by side
+  return lcattn::fwd_split_count(B, Hq, Hkv, Nq * n_calls, Nk, causal, 0);
+}
+
+size_t attn_fwd_accumulate_workspace_size(int B, int Hq, int64_t Nq, int D, int n_splits) {
+  if (B < 1 || Hq < 1 || Nq < 1 || D < 1 || n_splits < 1 || n_splits > kMaxSplits) return 0;
+  return splitkv_bytes(B, Hq, Nq, D, n_splits);
+}
+
+int attn_fwd_accumulate_group_split(const attn_accumulate_split_call* calls, int n, int B, int Hq, int Hkv, int D,
+                                    float scale, int causal, int n_splits, void* hip_stream) {
+  const char* name = "attn_fwd_accumulate_group_split";
+  if (!calls) return fail(ATTN_ERR_NULL, "%s: null call array", name);
+  if (n < 1 || n > ATTN_MAX_FWD_GROUP) return fail(ATTN_ERR_SHAPE, "%s: n=%d calls (1 .. %d)", name, n, ATTN_MAX_FWD_GROUP);
+  if (n_splits < 1 || n_splits > kMaxSplits)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: n_splits=%d (1 .. %d)", name, n_splits, kMaxSplits);
+  if ((int64_t)B * n * n_splits > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: B * n * n_splits must be <= 65535", name);
+  const attn_accumulate_call* ptrs[ATTN_MAX_FWD_GROUP];
+  for (int c = 0; c < n; ++c) ptrs[c] = &calls[c].call;
+  lcattn::FwdArgs args[ATTN_MAX_FWD_GROUP];
+  const void* in_p[ATTN_MAX_FWD_GROUP][3];
+  size_t in_b[ATTN_MAX_FWD_GROUP][3];
+  const void* out_p[ATTN_MAX_FWD_GROUP][3];
+  size_t out_b[ATTN_MAX_FWD_GROUP][3];
+  const int st = accumulate_group_check(name, ptrs, n, B, Hq, Hkv, D, scale, causal, args, in_p, in_b, out_p, out_b);
+  if (st != ATTN_OK) return st;
+  // workspaces: large enough, aligned, apart from every argument and one another
+  float* parts[ATTN_MAX_FWD_GROUP];
+  size_t need[ATTN_MAX_FWD_GROUP];
+  for (int c = 0; c < n; ++c) {
+    const attn_accumulate_split_call& x = calls[c];
+    need[c] = splitkv_bytes(B, Hq, x.call.Nq, D, n_splits);
+    if (need[c] == 0) return fail(ATTN_ERR_SHAPE, "%s: workspace size overflows (call %d)", name, c);
+    if (!x.workspace || x.workspace_bytes < need[c])
+      return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (call %d)", name, need[c], c);
+    if (!aligned16(x.workspace)) return fail(ATTN_ERR_ALIGN, "%s: workspace must be 16-byte aligned (call %d)", name, c);
+    parts[c] = static_cast<float*>(x.workspace);
+  }
+  for (int c = 0; c < n; ++c)
+    for (int d = 0; d < n; ++d) {
+      for (int j = 0; j < 3; ++j) {
+        if (overlap(calls[c].workspace, need[c], in_p[d][j], in_b[d][j]) ||
+            (out_p[d][j] && overlap(calls[c].workspace, need[c], out_p[d][j], out_b[d][j])))
+          return fail(ATTN_ERR_ALIAS, "%s: workspace of call %d overlaps an argument of call %d", name, c, d);
+      }
+      if (d != c && overlap(calls[c].workspace, need[c], calls[d].workspace, need[d]))
+        return fail(ATTN_ERR_ALIAS, "%s: workspaces of calls %d and %d overlap", name, c, d);
+    }
+  return hip_status(lcattn::launch_attn_fwd_group_split(args, parts, n, B, D, n_splits,
+                                                        static_cast<hipStream_t>(hip_stream)),
+                    "attn_fwd_accumulate_group_split launch");
 }
 
 size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,

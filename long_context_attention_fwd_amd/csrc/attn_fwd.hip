@@ -502,17 +502,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a, int n_
 }
 
 // Independent calls in one launch (a ring step's query chunks against one
-// key/value chunk): grid z = call * B + batch; call c covers
-// n_qtiles[c] <= gridDim.x query tiles.
+// key/value chunk): grid z = (call * splits + split) * B + batch, zc = splits
+// * B workgroup layers per call; call c covers n_qtiles[c] <= gridDim.x query
+// tiles.
 struct FwdGroup {
   FwdArgs a[kMaxFwdGroup];
   int n_qtiles[kMaxFwdGroup];
 };
 
 template <int D, int QB, int HP, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_group_kernel(FwdGroup g, int B) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_group_kernel(FwdGroup g, int zc) {
   const unsigned lin = wg_number();
-  const unsigned per_call = gridDim.x * gridDim.y * (unsigned)B;
+  const unsigned per_call = gridDim.x * gridDim.y * (unsigned)zc;
   const unsigned c = lin / per_call;
   attn_fwd_body<D, QB, HP, OUT_F32>(g.a[c], g.n_qtiles[c], lin - c * per_call, gridDim.x, gridDim.y);
 }
@@ -536,18 +537,26 @@ hipError_t launch_hp(const FwdArgs& a, int B, hipStream_t stream) {
 }
 
 template <int D, int HP>
-hipError_t launch_group_hp(FwdGroup& g, int n, int B, hipStream_t stream) {
+hipError_t launch_group_hp(FwdGroup& g, int n, int B, int splits, hipStream_t stream) {
   constexpr int SPAN = (kWaves / HP) * 32;
   long long nx = 0;
   for (int c = 0; c < n; ++c) {
     g.n_qtiles[c] = (int)((g.a[c].Nq + SPAN - 1) / SPAN);
     nx = std::max<long long>(nx, g.n_qtiles[c]);
   }
-  dim3 grid((unsigned)nx, (unsigned)(g.a[0].Hq / HP), (unsigned)(B * n));
+  dim3 grid((unsigned)nx, (unsigned)(g.a[0].Hq / HP), (unsigned)(B * splits * n));
   if (!grid_fits(grid)) return hipErrorInvalidConfiguration;
   LCATTN_LAUNCH("attn_fwd_kernel_fp32out", (attn_fwd_group_kernel<D, 1, HP, true>), grid, dim3(kThreads), 0, stream,
-                g, B);
+                g, B * splits);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_group_d(FwdGroup& g, int n, int B, int splits, hipStream_t stream) {
+  const int G = g.a[0].G;
+  if (G % 4 == 0) return launch_group_hp<D, 4>(g, n, B, splits, stream);
+  if (G % 2 == 0) return launch_group_hp<D, 2>(g, n, B, splits, stream);
+  return launch_group_hp<D, 1>(g, n, B, splits, stream);
 }
 
 }  // namespace
@@ -562,15 +571,48 @@ hipError_t launch_attn_fwd_group(const FwdArgs* calls, int n, int B, int D, hipS
     a.os[2] = D; a.os[1] = a.Nq * D; a.os[0] = a.Hq * a.Nq * D;
     g.a[c] = a;
   }
-  const int G = calls[0].G;
-  if (D == 64) {
-    if (G % 4 == 0) return launch_group_hp<64, 4>(g, n, B, stream);
-    if (G % 2 == 0) return launch_group_hp<64, 2>(g, n, B, stream);
-    return launch_group_hp<64, 1>(g, n, B, stream);
+  return D == 64 ? launch_group_d<64>(g, n, B, 1, stream) : launch_group_d<128>(g, n, B, 1, stream);
+}
+
+hipError_t launch_attn_fwd_group_split(const FwdArgs* calls, float* const* parts, int n, int B, int D, int splits,
+                                       hipStream_t stream) {
+  FwdGroup g{};
+  MergeSplits ms[kMaxFwdGroup];
+  const int HP = calls[0].G % 4 == 0 ? 4 : (calls[0].G % 2 == 0 ? 2 : 1);
+  for (int c = 0; c < n; ++c) {
+    FwdArgs a = calls[c];
+    a.B = B;
+    a.qs[2] = D; a.qs[1] = a.Nq * D; a.qs[0] = a.Hq * a.Nq * D;
+    a.ks[2] = D; a.ks[1] = a.Nk * D; a.ks[0] = a.Hkv * a.Nk * D;
+    a.os[2] = D; a.os[1] = a.Nq * D; a.os[0] = a.Hq * a.Nq * D;  // partials: contiguous [B, Hq, Nq, D]
+    const long long tiles = (a.Nk + kBN - 1) / kBN;
+    const long long stride = (long long)B * a.Hq * a.Nq * D;
+    a.o = parts[c];
+    a.lse = parts[c] + (long long)splits * stride;
+    a.n_splits = splits;
+    a.split_tiles = (int)((tiles + splits - 1) / splits);
+    a.part_stride = stride;
+    a.accum = 0;
+    a.o_final = nullptr;
+    g.a[c] = a;
+    ms[c].span = (kWaves / HP) * 32;
+    ms[c].split_tiles = a.split_tiles;
+    ms[c].key_tile = kBN;
+    ms[c].Nq = a.Nq;
+    ms[c].Nk = a.Nk;
+    ms[c].dpos = a.q_pos0 - a.k_pos0;
+    ms[c].causal = a.causal;
   }
-  if (G % 4 == 0) return launch_group_hp<128, 4>(g, n, B, stream);
-  if (G % 2 == 0) return launch_group_hp<128, 2>(g, n, B, stream);
-  return launch_group_hp<128, 1>(g, n, B, stream);
+  hipError_t e = D == 64 ? launch_group_d<64>(g, n, B, splits, stream) : launch_group_d<128>(g, n, B, splits, stream);
+  if (e != hipSuccess) return e;
+  for (int c = 0; c < n; ++c) {
+    const FwdArgs& a = calls[c];
+    e = launch_merge_into(parts[c], g.a[c].lse, splits, ms[c],
+                          static_cast<float*>(a.o), a.lse, a.accum == 0, a.o_final, (long long)B * a.Hq * a.Nq, D,
+                          stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a0, int B, int D, bool out_f32, hipStream_t stream) {

@@ -69,6 +69,13 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int B, int D, bool out_f32, hipStre
 // same B, Hq, Hkv, D, scale and mask kind) in one launch.
 constexpr int kMaxFwdGroup = 4;
 hipError_t launch_attn_fwd_group(const FwdArgs* calls, int n, int B, int D, hipStream_t stream);
+// The same calls with each call's keys cut into `splits` ranges computed side
+// by side: fp32 partials of call c in parts[c] ([splits, B, Hq, Nq, D] O,
+// then [splits, B, Hq, Nq] LSE), then one merge per call of its partials and
+// its running result (o, lse of calls[c], merged unless accum == 0) into that
+// running result, and o_final.
+hipError_t launch_attn_fwd_group_split(const FwdArgs* calls, float* const* parts, int n, int B, int D, int splits,
+                                       hipStream_t stream);
 
 // Forward over n_splits key ranges side by side (fp32 partials in o_parts /
 // lse_parts, [n_splits, B, Hq, Nq(, D)]), then their LSE merge into o (bf16)
@@ -98,6 +105,12 @@ struct MergeSplits {
 hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
                                 uint16_t* o, float* lse, long long rows, int D, hipStream_t stream,
                                 const MergeSplits* splits = nullptr);
+// fp32 partials of the split forward (geometry sp) merged into a running
+// fp32 result o_run, lse_run (which counts as one more part unless first);
+// o_final (optional) receives the merged O in bf16
+hipError_t launch_merge_into(const float* o_parts, const float* lse_parts, int n_parts, const MergeSplits& sp,
+                             float* o_run, float* lse_run, bool first, uint16_t* o_final, long long rows, int D,
+                             hipStream_t stream);
 
 struct BwdArgs {
   const uint16_t* q;

@@ -93,6 +93,97 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const void* __rest
   if (u == 0) lse[row] = out_lse;
 }
 
+// The same merge with the running result of a streaming ring as one more
+// part: o_run, lse_run (fp32, the attention over the earlier KV blocks) are
+// read unless `first`, and overwritten with the merged result; o_final, if
+// set, receives it rounded to bf16.  A row's threads are consecutive lanes
+// of one wave (D / 8 of 64), so every lane reads lse_run[row] before the
+// lane of slice 0 writes it.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_into_kernel(const float* __restrict__ o_parts,
+                                                                   const float* __restrict__ lse_parts,
+                                                                   int n_parts_max, long long rows,
+                                                                   float* __restrict__ o_run,
+                                                                   float* __restrict__ lse_run, int first,
+                                                                   uint16_t* __restrict__ o_final, MergeSplits sp) {
+  constexpr int U = D / 8;
+  static_assert(64 % U == 0, "a row's threads lie in one wave");
+  const long long idx = (long long)blockIdx.x * kMergeThreads + threadIdx.x;
+  const long long row = idx / U;
+  const int u = (int)(idx % U);
+  if (row >= rows) return;
+  const long long qt = (row % sp.Nq) / sp.span;
+  const long long q_last = min((qt + 1) * sp.span, sp.Nq) - 1;
+  long long kv_end = sp.Nk;
+  if (sp.causal) kv_end = max(0LL, min(sp.Nk, sp.dpos + q_last + 1));
+  const long long tiles = (kv_end + sp.key_tile - 1) / sp.key_tile;
+  const int n_parts = (int)min((long long)n_parts_max, (tiles + sp.split_tiles - 1) / sp.split_tiles);
+
+  const float lr = first ? -INFINITY : lse_run[row];
+  float m = lr;
+  bool nan = lr != lr;
+  for (int b = 0; b < n_parts; ++b) {
+    const float lb = lse_parts[(long long)b * rows + row];
+    nan |= lb != lb;
+    m = fmaxf(m, lb);  // ignores NaN operands
+  }
+  if (nan && m == -INFINITY) m = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float out_lse = -INFINITY;
+  const long long off = row * D + 8 * u;
+  if (m != -INFINITY) {
+    float tot = first ? 0.f : fast_exp2((lr - m) * kLog2e);
+    for (int b = 0; b < n_parts; ++b) tot += fast_exp2((lse_parts[(long long)b * rows + row] - m) * kLog2e);
+    const float inv = 1.0f / tot;
+    out_lse = m + fast_log2(tot) * kLn2;
+    if (!first) {
+      const float w = fast_exp2((lr - m) * kLog2e) * inv;
+      if (w != 0.f) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(o_run + off);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_run + off + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += w * x0[e];
+          acc[4 + e] += w * x1[e];
+        }
+      }
+    }
+    for (int b = 0; b < n_parts; ++b) {
+      const float w = fast_exp2((lse_parts[(long long)b * rows + row] - m) * kLog2e) * inv;
+      if (w == 0.f) continue;
+      const float* p = o_parts + (long long)b * rows * D + off;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * x0[e];
+        acc[4 + e] += w * x1[e];
+      }
+    }
+  }
+  *reinterpret_cast<f32x4*>(o_run + off) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(o_run + off + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  if (o_final) {
+    const bf16x8 r = pack_bf16x8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7]);
+    st_global16(o_final + off, as_u32x4(r));
+  }
+  if (u == 0) lse_run[row] = out_lse;
+}
+
+hipError_t launch_merge_into(const float* o_parts, const float* lse_parts, int n_parts, const MergeSplits& sp,
+                             float* o_run, float* lse_run, bool first, uint16_t* o_final, long long rows, int D,
+                             hipStream_t stream) {
+  const long long threads = rows * (D / 8);
+  const unsigned blocks = (unsigned)((threads + kMergeThreads - 1) / kMergeThreads);
+  if (D == 64)
+    LCATTN_LAUNCH("merge_into_kernel", (merge_into_kernel<64>), dim3(blocks), dim3(kMergeThreads), 0, stream, o_parts,
+                  lse_parts, n_parts, rows, o_run, lse_run, first ? 1 : 0, o_final, sp);
+  else
+    LCATTN_LAUNCH("merge_into_kernel", (merge_into_kernel<128>), dim3(blocks), dim3(kMergeThreads), 0, stream, o_parts,
+                  lse_parts, n_parts, rows, o_run, lse_run, first ? 1 : 0, o_final, sp);
+  return hipGetLastError();
+}
+
 hipError_t launch_partial_merge(const void* o_parts, bool parts_f32, const float* lse_parts, int n_parts,
                                 uint16_t* o, float* lse, long long rows, int D, hipStream_t stream,
                                 const MergeSplits* splits) {

@@ -71,7 +71,7 @@ def ring_groups(rank: int, P: int, scheme: str = "zigzag", causal: bool = True):
 
 def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_acc, o_final=None,
                  scheme: str = "zigzag", causal: bool = True, scale: float | None = None, steps=None,
-                 streams=None, grouped: bool = False):
+                 streams=None, grouped: bool = False, n_splits: int = 1, workspaces=None):
     """Run rank ``rank``'s ring on this GPU.
 
     q_chunks: the rank's two query chunks, [B, Hq, C, D] bf16 each.
@@ -86,6 +86,12 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
     grouped: the calls of a step that read the same key/value chunk (one per
     query chunk: independent running results) go out as one
     ``attn_fwd_accumulate_group`` launch instead (streams is then unused).
+    n_splits > 1 (grouped only): each call's keys in that many ranges side by
+    side, merged into the running result (``attn_fwd_accumulate_group_split``;
+    ``attn_fwd_split_suggest`` gives the library's choice); workspaces: one
+    uint8 tensor per call of a group, each of at least
+    ``attn_fwd_accumulate_workspace_size(B, Hq, C, D, n_splits)`` bytes
+    (allocated per call when None).
     """
     import torch
 
@@ -107,8 +113,17 @@ def ring_forward(q_chunks, kv_chunks, rank: int, P: int, C: int, *, o_acc, lse_a
                 group.append(dict(q=q_chunks[qi], k=k, v=v, o_acc=o_acc[qi], lse_acc=lse_acc[qi],
                                   first=(i == first_call[qi]), q_pos0=mine[qi] * C, k_pos0=kc * C,
                                   o_final=(o_final[qi] if o_final is not None and i == last[qi] else None)))
-            attn_fwd_accumulate_group(group, causal=causal, scale=scale)
+            if n_splits > 1:
+                from . import attn_fwd_accumulate_group_split
+                if workspaces is not None:
+                    for slot, c in enumerate(group):
+                        c["workspace"] = workspaces[slot]
+                attn_fwd_accumulate_group_split(group, n_splits=n_splits, causal=causal, scale=scale)
+            else:
+                attn_fwd_accumulate_group(group, causal=causal, scale=scale)
         return
+    if n_splits > 1:
+        raise ValueError("n_splits > 1 needs grouped=True")
     caller = torch.cuda.current_stream(q_chunks[0].device)
     if streams is not None:
         fork = torch.cuda.Event()

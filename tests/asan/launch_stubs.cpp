@@ -15,11 +15,18 @@ hipError_t launch_sum_replicas(const void*, bool, uint16_t*, long long, long lon
 }
 hipError_t launch_attn_fwd(const FwdArgs&, int, int, bool, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn_fwd_group(const FwdArgs*, int, int, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_attn_fwd_group_split(const FwdArgs*, float* const*, int, int, int, int, hipStream_t) {
+  return hipErrorNoDevice;
+}
 hipError_t launch_attn_fwd_splitkv(const FwdArgs&, int, int, int, float*, float*, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_partial_merge(const void*, bool, const float*, int, uint16_t*, float*, long long, int,
                                 hipStream_t, const MergeSplits*) {
+  return hipErrorNoDevice;
+}
+hipError_t launch_merge_into(const float*, const float*, int, const MergeSplits&, float*, float*, bool, uint16_t*,
+                             long long, int, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_attn_bwd(const BwdArgs&, int, int, hipStream_t, bool) { return hipErrorNoDevice; }

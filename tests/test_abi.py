@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
               "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
-              "attn_bwd_strided", "attn_bwd_noalloc", "attn_bwd_block_group", "attn_bwd_noalloc_max_scratch", "attn_fwd_accumulate_group", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
+              "attn_bwd_strided", "attn_bwd_noalloc", "attn_bwd_block_group", "attn_bwd_noalloc_max_scratch", "attn_fwd_accumulate_group", "attn_fwd_accumulate_group_split",
+              "attn_fwd_accumulate_workspace_size", "attn_fwd_split_suggest", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
               "head_to_seq_relayout_batch", "attn_status_string", "attn_last_error"):
         assert n in names, names
 
@@ -141,6 +142,48 @@ def test_accumulate_group_rejects(L):
     assert group_call(L, [c0, c1[:5] + (F_ + 8,) + c1[6:]]) == 4           # misaligned o_final
     assert group_call(L, [c0], D=96) == 3
     assert group_call(L, [c0] * 4, B=20000) == 3                           # grid z = B * n too large
+
+
+W_ = 0x60000000  # fake workspace address
+
+
+def split_group_call(L, calls, n=None, n_splits=2, B=1, Hq=4, Hkv=1, D=128, scale=0.125, causal=1):
+    arr = (lc.AccumulateSplitCall * max(1, len(calls)))(
+        *[lc.AccumulateSplitCall(lc.AccumulateCall(*c), ws, wb) for c, ws, wb in calls])
+    return L.attn_fwd_accumulate_group_split(arr if calls else None, len(calls) if n is None else n, B, Hq, Hkv, D,
+                                             scale, causal, n_splits, None)
+
+
+def test_accumulate_workspace_size_and_suggestion(L):
+    assert L.attn_fwd_accumulate_workspace_size(1, 4, 128, 128, 2) == 2 * 4 * 128 * (128 + 1) * 4
+    assert L.attn_fwd_accumulate_workspace_size(1, 4, 128, 128, 0) == 0
+    assert L.attn_fwd_accumulate_workspace_size(1, 4, 128, 128, 65) == 0
+    assert L.attn_fwd_split_suggest(1, 4, 1, 4096, 4096, 1, 2) >= 1
+    assert L.attn_fwd_split_suggest(1, 4, 3, 4096, 4096, 1, 2) == 1  # Hkv does not divide Hq: no split
+    # long rows fill the GPU without a split
+    assert L.attn_fwd_split_suggest(1, 8, 8, 1 << 16, 1 << 16, 1, 1) == 1
+
+
+def test_accumulate_group_split_rejects(L):
+    """Every case fails validation (nothing is launched)."""
+    need = L.attn_fwd_accumulate_workspace_size(1, 4, 128, 128, 2)
+    c0 = ((A, B_, C_, D_, E_, None, 128, 128, 0, 0, 1), W_, need)
+    c1 = ((A + (1 << 20), B_, C_, D_ + (1 << 20), E_ + (1 << 20), None, 128, 128, 128, 0, 0), W_ + (1 << 24), need)
+    assert split_group_call(L, []) == 1
+    assert split_group_call(L, [c0], n=0) == 2
+    assert split_group_call(L, [c0] * 5) == 2
+    assert split_group_call(L, [c0], n_splits=0) == 3
+    assert split_group_call(L, [c0], n_splits=65) == 3
+    assert split_group_call(L, [c0, c1], B=20000, n_splits=4) == 3        # grid z = B * n * splits too large
+    assert split_group_call(L, [c0, ((None,) + c1[0][1:], c1[1], c1[2])]) == 1
+    assert b"call 1" in L.attn_last_error()
+    assert split_group_call(L, [(c0[0], None, need)]) == 6                 # no workspace
+    assert split_group_call(L, [(c0[0], W_, need - 16)]) == 6              # workspace too small
+    assert split_group_call(L, [(c0[0], W_ + 8, need)]) == 4               # misaligned workspace
+    assert split_group_call(L, [(c0[0], A + 256, need)]) == 5              # workspace overlaps q
+    assert split_group_call(L, [c0, (c1[0], W_ + 1024, need)]) == 5        # workspaces of two calls overlap
+    assert split_group_call(L, [c0, (c1[0], D_ + (1 << 20) + 64, need)]) == 5  # workspace overlaps call 1's o_acc
+    assert split_group_call(L, [c0, (c1[0][:3] + (D_ + 64,) + c1[0][4:], c1[1], c1[2])]) == 5  # outputs overlap
 
 
 def bwd_strided(L, qs=(0, 128, 1024), ks=(0, 128, 256), **kw):

@@ -176,3 +176,130 @@ def test_accumulate_group_uneven_calls(gpu, B):
     for (o1, l1), g in zip(ref, grp):
         assert torch.equal(o1.view(torch.int32), g["o_acc"].view(torch.int32))
         assert torch.equal(l1.view(torch.int32), g["lse_acc"].view(torch.int32))
+
+
+def stream_ring_split(q, k, v, blk, causal, scale, n_splits, order=None):
+    """The ring of stream_ring, each block's call split into n_splits key
+    ranges (attn_fwd_accumulate_group_split with one call)."""
+    import torch
+    B, Hq, Nq, D = q.shape
+    Nk = k.shape[2]
+    starts = list(range(0, Nk, blk))
+    if order is not None:
+        starts = [starts[i] for i in order]
+    o_acc = poisoned((B, Hq, Nq, D), torch.float32)
+    lse_acc = poisoned((B, Hq, Nq), torch.float32)
+    o = poisoned((B, Hq, Nq, D), torch.bfloat16)
+    ws = torch.empty(lc.attn_fwd_accumulate_workspace_size(B, Hq, Nq, D, n_splits), dtype=torch.uint8, device="cuda")
+    for i, a in enumerate(starts):
+        e = min(a + blk, Nk)
+        lc.attn_fwd_accumulate_group_split(
+            [dict(q=q, k=k[:, :, a:e].contiguous(), v=v[:, :, a:e].contiguous(), o_acc=o_acc, lse_acc=lse_acc,
+                  first=(i == 0), k_pos0=a, o_final=o if i == len(starts) - 1 else None, workspace=ws)],
+            n_splits=n_splits, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse_acc, o_acc
+
+
+@pytest.mark.parametrize("N,blk,n_splits", [(200, 64, 2), (1000, 256, 3), (1000, 1000, 5), (777, 100, 1),
+                                            (1000, 1000, 64)])
+@pytest.mark.parametrize("G,causal,D", [(1, True, 128), (4, True, 64), (2, False, 128)])
+def test_ring_stream_split_matches_oracle(gpu, N, blk, n_splits, G, causal, D):
+    """Each block's keys in n_splits ranges side by side, merged with the
+    running result: the oracle's attention over every block (also with more
+    ranges than key tiles, where most ranges see nothing)."""
+    d = make_qkv(1, 2 * G, 2, N, D, seed=700 + N + blk + G + n_splits)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    o, lse, o_acc = stream_ring_split(q, k, v, blk, causal, sdpa_scale(D), n_splits)
+    O, L = oracle.attention_forward(d["q"], d["k"], d["v"], sdpa_scale(D), causal)
+    check_forward(f64_of(o), f64_of(lse), O, L, f"split stream N={N} blk={blk} S={n_splits} G={G} causal={causal}")
+    check_forward(f64_of(o_acc), f64_of(lse), O, L, f"split stream fp32 N={N} blk={blk} S={n_splits}")
+
+
+def test_ring_stream_split_any_order_and_empty_blocks(gpu):
+    """Blocks in shuffled order, the first one seen by no early query; a block
+    past every query leaves the running result bit for bit as it was."""
+    import torch
+    d = make_qkv(1, 4, 1, 900, 64, seed=78)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    O, L = oracle.attention_forward(d["q"], d["k"], d["v"], sdpa_scale(64), True)
+    o, lse, o_acc = stream_ring_split(q, k, v, 225, True, sdpa_scale(64), 3, order=[3, 0, 2, 1])
+    check_forward(f64_of(o), f64_of(lse), O, L, "split stream shuffled")
+    before_o, before_l = o_acc.clone(), lse.clone()
+    kb = to_dev(make_qkv(1, 4, 1, 300, 64, seed=79)["k"])
+    vb = to_dev(make_qkv(1, 4, 1, 300, 64, seed=80)["v"])
+    ws = torch.empty(lc.attn_fwd_accumulate_workspace_size(1, 4, 900, 64, 4), dtype=torch.uint8, device="cuda")
+    lc.attn_fwd_accumulate_group_split([dict(q=q, k=kb, v=vb, o_acc=o_acc, lse_acc=lse, first=False, k_pos0=900,
+                                             workspace=ws)], n_splits=4, scale=sdpa_scale(64))
+    torch.cuda.synchronize()
+    assert torch.equal(o_acc.view(torch.int32), before_o.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), before_l.view(torch.int32))
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_accumulate_group_split_uneven_calls(gpu, B):
+    """Calls of different lengths and positions, split and merged in one
+    launch each way: each within the gate of the oracle over its block, and
+    close to its own unsplit attn_fwd_accumulate."""
+    import torch
+    D, G = 128, 4
+    d = make_qkv(B, G, 1, 1500, D, seed=87 + B)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    s = sdpa_scale(D)
+    spec = [(0, 700, 0, 900), (700, 1500, 300, 1200), (1400, 1500, 0, 1500)]  # (q0, q1, k0, k1)
+    grp, ref = [], []
+    for q0, q1, k0, k1 in spec:
+        args = dict(q=q[:, :, q0:q1].contiguous(), k=k[:, :, k0:k1].contiguous(), v=v[:, :, k0:k1].contiguous(),
+                    q_pos0=q0, k_pos0=k0)
+        o1 = poisoned((B, G, q1 - q0, D), torch.float32)
+        l1 = poisoned((B, G, q1 - q0), torch.float32)
+        lc.attn_fwd_accumulate(args["q"], args["k"], args["v"], o1, l1, first=True, scale=s, q_pos0=q0, k_pos0=k0)
+        ref.append((o1, l1))
+        grp.append(dict(args, o_acc=poisoned((B, G, q1 - q0, D), torch.float32),
+                        lse_acc=poisoned((B, G, q1 - q0), torch.float32), first=True,
+                        o_final=poisoned((B, G, q1 - q0, D), torch.bfloat16)))
+    lc.attn_fwd_accumulate_group_split(grp, n_splits=3, scale=s)
+    torch.cuda.synchronize()
+    for (q0, q1, k0, k1), (o1, l1), g in zip(spec, ref, grp):
+        qs = d["q"][:, :, q0:q1].copy()
+        O, L = oracle.attention_forward(qs, d["k"][:, :, k0:k1].copy(), d["v"][:, :, k0:k1].copy(), s, True, q0, k0)
+        check_forward(f64_of(g["o_final"]), f64_of(g["lse_acc"]), O, L, f"split group call q0={q0} k0={k0}")
+        vis = torch.isfinite(l1)
+        assert torch.equal(vis, torch.isfinite(g["lse_acc"]))
+        assert torch.allclose(g["lse_acc"][vis], l1[vis], rtol=0, atol=1e-4)
+        assert torch.allclose(g["o_acc"], o1, rtol=0, atol=2e-3)
+        assert torch.equal(g["o_final"].view(torch.int16), g["o_acc"].to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("scheme", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("P,C,G,causal,D,S", [(4, 256, 4, True, 128, 4), (2, 300, 1, True, 64, 3),
+                                              (4, 100, 2, False, 128, 2)])
+def test_ring_grouped_split_matches_oracle(gpu, scheme, P, C, G, causal, D, S):
+    """Every rank's ring with each step's grouped calls split into S key
+    ranges (ring_forward(..., grouped=True, n_splits=S)): the oracle's rows of
+    the rank's chunks."""
+    import torch
+    from long_context_attention_fwd_amd.ring import rank_chunks, ring_forward
+    N, Hkv = 2 * P * C, 1
+    d = make_qkv(1, Hkv * G, Hkv, N, D, seed=950 + P + C + G + D)
+    q, k, v = (to_dev(d[n]) for n in "qkv")
+    s = sdpa_scale(D)
+
+    def chunk(t, c):
+        return t[:, :, c * C:(c + 1) * C].contiguous()
+
+    kv = {r: tuple((chunk(k, c), chunk(v, c)) for c in rank_chunks(r, P, scheme)) for r in range(P)}
+    wss = [torch.empty(lc.attn_fwd_accumulate_workspace_size(1, Hkv * G, C, D, S), dtype=torch.uint8, device="cuda")
+           for _ in range(4)]
+    for r in range(P):
+        mine = rank_chunks(r, P, scheme)
+        o_acc = [poisoned((1, Hkv * G, C, D), torch.float32) for _ in mine]
+        lse = [poisoned((1, Hkv * G, C), torch.float32) for _ in mine]
+        o = [poisoned((1, Hkv * G, C, D), torch.bfloat16) for _ in mine]
+        ring_forward([chunk(q, c) for c in mine], lambda src: kv[src], r, P, C, o_acc=o_acc, lse_acc=lse, o_final=o,
+                     scheme=scheme, scale=s, causal=causal, grouped=True, n_splits=S, workspaces=wss)
+        torch.cuda.synchronize()
+        for i, c in enumerate(mine):
+            rows = np.arange(c * C, (c + 1) * C)
+            O, L = oracle.attention_forward(d["q"], d["k"], d["v"], s, causal, rows=rows)
+            check_forward(f64_of(o[i]), f64_of(lse[i]), O, L, f"split grouped {scheme} rank {r} chunk {c}")
