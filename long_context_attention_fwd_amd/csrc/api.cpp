@@ -413,7 +413,7 @@ int attn_fwd_accumulate_group_split(const attn_accumulate_split_call* calls, int
 size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D, int causal,
                                        int n_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1 || n_splits > kMaxSplits) return 0;
-  return splitkv_bytes(B, Hq, Nq, D, lcattn::fwd_split_count(B, Hq, Hkv, Nq, Nk, causal, n_splits));
+  return splitkv_bytes(B, Hq, Nq, D, lcattn::splitkv_split_count(B, Hq, Hkv, Nq, Nk, causal, n_splits));
 }
 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -425,7 +425,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (st != ATTN_OK) return st;
   if (n_splits > kMaxSplits)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv: n_splits=%d (at most %d)", n_splits, kMaxSplits);
-  const int n = lcattn::fwd_split_count(B, Hq, Hkv, Nq, Nk, causal, n_splits);
+  const int n = lcattn::splitkv_split_count(B, Hq, Hkv, Nq, Nk, causal, n_splits);
   if ((int64_t)B * n > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv: B * n_splits must be <= 65535");
   const size_t need = splitkv_bytes(B, Hq, Nq, D, n);

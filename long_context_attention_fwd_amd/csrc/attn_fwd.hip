@@ -98,13 +98,44 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
   const unsigned lxy = __builtin_amdgcn_readfirstlane(lin / nx);
   const int by = __builtin_amdgcn_readfirstlane(lxy % ny);
   const unsigned bzs = __builtin_amdgcn_readfirstlane(lxy / ny);
-  const int qt = n_qtiles - 1 - __builtin_amdgcn_readfirstlane(lin - lxy * nx);
+  const unsigned xi = __builtin_amdgcn_readfirstlane(lin - lxy * nx);
+  int qt, split;
+  long long bz;
+  if (a.compact) {
+    // x enumerates the (key range, query tile) pairs with work: range r holds
+    // the query tiles that see one of its keys, longest first (the host
+    // sizes the grid by the same count)
+    const long long tiles = (a.Nk + kBN - 1) / kBN;
+    const int st = a.split_tiles;
+    const long long dp = a.q_pos0 - a.k_pos0;
+    unsigned i = xi;
+    int r = 0;
+    for (; r < a.n_splits; ++r) {
+      long long c = 0;
+      const long long x0 = (long long)r * st * kBN;
+      if (r < (tiles + st - 1) / st && x0 < a.Nk) {
+        const long long y = x0 - dp;  // a tile has work iff its last row >= y
+        if (!a.causal || y <= 0)
+          c = n_qtiles;
+        else if (y + 1 <= a.Nq)
+          c = n_qtiles - ((y + SPAN) / SPAN - 1);
+      }
+      if (i < c) break;
+      i -= (unsigned)c;
+    }
+    if (r >= a.n_splits) return;  // past the pairs with work
+    qt = n_qtiles - 1 - (int)i;
+    split = r;
+    bz = bzs;
+  } else {
+    qt = n_qtiles - 1 - (int)xi;
+    const unsigned split_u = __builtin_amdgcn_readfirstlane(bzs / (unsigned)a.B);
+    bz = bzs - split_u * (unsigned)a.B;
+    split = (int)split_u;
+  }
   if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
   const int kvh = (by * HP) / a.G;
-  const unsigned split_u = __builtin_amdgcn_readfirstlane(bzs / (unsigned)a.B);
-  const long long bz = bzs - split_u * (unsigned)a.B;
-  const int split = (int)split_u;
   const long long q_start = (long long)qt * SPAN;
   const long long wq0 = q_start + (long long)(wave / HP) * QW;
 
@@ -523,6 +554,12 @@ hipError_t launch_cfg(const FwdArgs& a, int B, hipStream_t stream) {
   constexpr int SPAN = (kWaves / HP) * 32 * QB;
   const long long n_qtiles = (a.Nq + SPAN - 1) / SPAN;
   dim3 grid((unsigned)n_qtiles, (unsigned)(a.Hq / HP), (unsigned)(B * a.n_splits));
+  if (a.compact) {
+    const long long pairs = splitkv_pairs(a.Nq, a.Nk, a.q_pos0 - a.k_pos0, a.causal, SPAN, a.n_splits);
+    if (pairs == 0) return hipSuccess;  // no query sees a key: the merge writes the empty rows
+    if (pairs >= (1LL << 31)) return hipErrorInvalidConfiguration;
+    grid = dim3((unsigned)pairs, (unsigned)(a.Hq / HP), (unsigned)B);
+  }
   if (!grid_fits(grid)) return hipErrorInvalidConfiguration;
   LCATTN_LAUNCH(F32 ? "attn_fwd_kernel_fp32out" : "attn_fwd_kernel", (attn_fwd_kernel<D, QB, HP, F32>), grid,
                 dim3(kThreads), 0, stream, a, (int)n_qtiles);
@@ -644,6 +681,7 @@ hipError_t launch_attn_fwd_splitkv(const FwdArgs& a0, int B, int D, int n_splits
   a.n_splits = n_splits;
   a.split_tiles = (int)((tiles + n_splits - 1) / n_splits);
   a.part_stride = (long long)B * a.Hq * a.Nq * D;
+  a.compact = n_splits > 1 ? 1 : 0;
   hipError_t e = launch_attn_fwd(a, B, D, true, stream);
   if (e != hipSuccess) return e;
   const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);

@@ -61,6 +61,9 @@ struct FwdArgs {
   // contiguous [B, Hq, Nq, D]
   int accum = 0;
   uint16_t* o_final = nullptr;
+  // split forward: grid x enumerates only the (key range, query tile) pairs
+  // with work (range-major, longest query tiles first within a range)
+  int compact = 0;
 };
 
 // (strides left at zero are filled in for contiguous [B, H, N, D] tensors)
@@ -85,6 +88,13 @@ hipError_t launch_attn_fwd_splitkv(const FwdArgs& a, int B, int D, int n_splits,
 // Number of key ranges for attn_fwd_splitkv: n_splits if > 0, else about
 // enough for two non-empty workgroups per compute unit.
 int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits);
+// attn_fwd_splitkv's ranges: n_splits if > 0; else 1 when the unsplit grid
+// fills the GPU, otherwise the most ranges whose (range, query tile) pairs
+// with work fit one workgroup per compute unit
+int splitkv_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits);
+// (range, query tile) pairs with work of the split forward (n_splits ranges
+// of whole key tiles; query tiles of `span` rows; dpos = q_pos0 - k_pos0)
+long long splitkv_pairs(long long Nq, long long Nk, long long dpos, int causal, int span, int n_splits);
 
 // Geometry of the split forward's partials: a query tile of `span` rows
 // (row i of the Nq rows of a head lies in tile i / span) has a partial for
