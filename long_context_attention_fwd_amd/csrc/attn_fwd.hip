@@ -112,9 +112,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
     int r = 0;
     for (; r < a.n_splits; ++r) {
       long long c = 0;
-      const long long x0 = (long long)r * st * kBN;
-      if (r < (tiles + st - 1) / st && x0 < a.Nk) {
-        const long long y = x0 - dp;  // a tile has work iff its last row >= y
+      if ((long long)r * st < tiles) {  // the range's first key exists
+        const long long y = (long long)r * st * kBN - dp;  // a tile has work iff its last row >= y
         if (!a.causal || y <= 0)
           c = n_qtiles;
         else if (y + 1 <= a.Nq)
