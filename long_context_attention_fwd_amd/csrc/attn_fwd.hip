@@ -33,7 +33,8 @@
 //    instruction crosses: [1] transposing reads of the V^T fragments of
 //    sub-tile t-1, row max of S(t); [2] the 8 MFMAs of O^T += V^T P(t-1)^T,
 //    one at a time between the exponentials of S(t); [3] the 8 K fragment
-//    reads of sub-tile t+1 (all in flight at once), row sum and bf16 P(t);
+//    reads of sub-tile t+1 (all in flight at once; at D = 64 they go out in
+//    [1] with the V^T reads), row sum and bf16 P(t);
 //    [4] the 8 MFMAs of S(t+1) = K Q^T.  Fragment reads are inline assembly
 //    with explicit lgkmcnt waits (the compiler would otherwise wait for the
 //    direct loads in flight, or read and wait for one K fragment at a time).
@@ -79,6 +80,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
   constexpr int SPAN = (kWaves / HP) * QW;  // query rows per workgroup (per head)
   static_assert(QB == 1, "one block of 32 query rows per wave");
   static_assert(kBN == 64, "SwzTile holds 64 rows");
+  // D = 64: the K fragments of the next sub-tile are read at the start of a
+  // step, next to the V^T reads, so their latency hides behind the row max,
+  // the PV products and the exponentials (measured 10% faster there).  At
+  // D = 128 the extra 32 live registers cost more than that latency (the
+  // other wave of the SIMD already covers it): they are read after the
+  // exponentials.
+  constexpr bool kEarlyK = D <= 64;
 
   // LDS: the K tiles of the three pipeline buffers, then their V tiles
   // (row-major, swizzled), in one object so that every fragment read is a
@@ -247,6 +255,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
 #pragma unroll
     for (int db = 0; db < DB; db += 2) lds_wait_frags(f[db][0], f[db][1], f[db + 1][0], f[db + 1][1]);
   };
+  // the V^T fragments while the KT reads of the next K fragments, issued
+  // after them, may still be in flight
+  auto wait_v_before_k = [&](u32x4 (&f)[DB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; db += 2) lds_wait_frags_n<KT>(f[db][0], f[db][1], f[db + 1][0], f[db + 1][1]);
+  };
   // S^T of one sub-tile from its K fragments (rows in pi order)
   auto s_mfma = [&](u32x4 (&kf)[KT]) __attribute__((always_inline)) {
     f32x16 s;
@@ -337,18 +351,23 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
   //   [2] O^T += V^T P(t-1)^T (8 MFMAs), one at a time between the
   //       exponentials of S(t) (independent VALU work)
   //   [3] reads of the K fragments of sub-tile t+1 (all eight in flight at
-  //       once); row sum and bf16 P(t)
+  //       once; in [1] when kEarlyK); row sum and bf16 P(t)
   //   [4] S(t+1) = K Q^T (8 MFMAs); rescale when some row's maximum moved
   // koff_t / voff_t: byte offsets of sub-tiles t+1 (K) and t-1 (V) from
   // buffer 0 (compile-time in the unrolled loop).  Returns S(t+1).
   auto step = [&](auto masked_tag, int t, f32x16 s_cur, auto koff_t, auto voff_t) __attribute__((always_inline)) {
     u32x4 f[DB][2];
     read_v(voff_t, f);
+    u32x4 kf[KT];
+    if constexpr (kEarlyK) read_k(koff_t, kf);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out before the row max
     float m_old;
     const float m_use = row_max(masked_tag, s_cur, t, m_old);
     __builtin_amdgcn_sched_barrier(0);
-    wait_v(f);
+    if constexpr (kEarlyK)
+      wait_v_before_k(f);
+    else
+      wait_v(f);
     pv_mfma(f);
     weights(s_cur, m_use);
     constexpr int NPV = 2 * DB;
@@ -361,8 +380,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a, int n_qtiles, un
     // are sunk past the rescale branch below, out of reach of the MFMAs)
     pin16(s_cur);
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 kf[KT];
-    read_k(koff_t, kf);
+    if constexpr (!kEarlyK) read_k(koff_t, kf);
     float psum = pack(s_cur);
     {
       u32x4 p0 = as_u32x4(pf[0]), p1 = as_u32x4(pf[1]);

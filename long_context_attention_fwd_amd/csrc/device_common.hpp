@@ -285,6 +285,15 @@ __device__ __forceinline__ void lds_wait_frags(u32x4& a, u32x4& b, u32x4& c, u32
   asm("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
+// Wait until at most N of this wave's LDS operations are outstanding.  LDS
+// operations complete in issue order, so every read issued before the last N
+// has landed (scalar memory operations only add to the count).
+template <int N>
+__device__ __forceinline__ void lds_wait_frags_n(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt holds 4 bits");
+  asm("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+
 // The same for two fragments.  Every operand must be a distinct variable: an
 // operand passed twice makes the compiler copy the register, possibly before
 // the wait, i.e. while the load into it is still in flight.
