@@ -238,7 +238,12 @@ int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_par
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs: the
  * per-row <dO, O> in fp32 and, for grouped-query attention (Hq != Hkv),
  * per-query-head fp32 partials of dK and dV (2 * B*Hq*N*D floats) that are
- * summed over each group.  Returns 0 for invalid sizes.
+ * summed over each group.  A small problem (fewer than 256 dK/dV workgroups,
+ * i.e. B * Hq * ceil(N / 128) < 256) also splits its passes into ranges:
+ * rkv query ranges of dK, dV partials (2 * rkv * B*Hq*N*D floats, replacing
+ * the grouped-query ones) and rq key ranges of dQ partials (rq * B*Hq*N*D
+ * floats), at most 8 ranges a pass and 64 MiB for the two.  Returns 0 for
+ * invalid sizes.
  */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
 
@@ -254,6 +259,15 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
  * workspace (caller-owned, >= attn_bwd_workspace_size bytes, 16-byte aligned)
  * is scratch; its contents on return are unspecified.  The glossary example
  * backpropagates the mean of O^2, i.e. d_o = 2 O / numel.
+ * Small problems (fewer than 256 dK/dV workgroups: the glossary example's
+ * [1, 4, 4096, 64]) are limited by their longest workgroups, the first key
+ * tile against every query and the last query tile against every key: the
+ * dK/dV pass then runs over ranges of about 1024 * 64 / D query rows and the
+ * dQ pass over ranges of about 512 * 64 / D keys, each range writing fp32
+ * partials into the workspace that a reduce kernel sums in a fixed order
+ * (deterministic; the grouping of the sums differs from the unsplit passes,
+ * so results agree with attn_bwd_block over the whole sequence to rounding,
+ * not bit for bit).
  * When the dK/dV pass has fewer than two workgroups per compute unit (short
  * sequences, ring steps), the dQ pass runs beside it on a side stream of the
  * library's own, forked from hip_stream after Dv and joined back before the
@@ -274,8 +288,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  *
  * Same arguments, layout and results as attn_bwd (the same kernels; outputs
  * bit-identical), minus workspace / workspace_bytes.  The scratch those
- * kernels need (attn_bwd_workspace_size bytes: Dv per query row, and for
- * grouped-query attention per-query-head fp32 dK/dV partials) lives in a
+ * kernels need (attn_bwd_workspace_size bytes: Dv per query row, the
+ * grouped-query dK/dV partials and a small problem's range partials) lives in a
  * device array inside the library, attn_bwd_noalloc_max_scratch() bytes
  * (160 MiB) per GPU, held from the first call on that GPU until the process
  * ends.  A call that needs more returns ATTN_ERR_WORKSPACE before any GPU

@@ -567,7 +567,7 @@ static int bwd_entry(const char* name, const void* q, const void* k, const void*
     }
   char what[64];
   snprintf(what, sizeof(what), "%s launch", name);
-  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), !use_scratch), what);
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), !use_scratch, true), what);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -718,7 +718,7 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
                                  workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0, k_pos0,
                                  dq_accumulate, dkv_accumulate, &a, ins, inb, outs, outb);
   if (st != ATTN_OK) return st;
-  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), true),
+  return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), true, false),
                     "attn_bwd_block launch");
 }
 

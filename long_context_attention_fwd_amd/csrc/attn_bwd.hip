@@ -32,6 +32,9 @@
 // dQ by a separate pass costs two recomputed products (7 contractions instead
 // of 5) but avoids fp32 atomic traffic proportional to N^2 / tile (measured:
 // adding dQ blocks with fp32 atomics runs at 1.35 TB/s, too slow to pay).
+// Small problems split both passes into ranges (query ranges for dK/dV, key
+// ranges for dQ; grid z = range * B + batch), each range writing fp32
+// partials that bwd_dkdv_reduce / bwd_dq_reduce sum in range order.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "trace.hpp"
@@ -133,7 +136,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   // lane offsets of the epilogue (measured: 48 MiB more writes per launch at
   // 64K); the few hundred prologue instructions do not show in a launch
   const long long llin = lin, lnx = nx, lny = ny;
-  const long long bz = llin / (lnx * lny);
+  const long long zz = llin / (lnx * lny);  // query range * B + batch
+  const int rr = (int)(zz / a.B);
+  const long long bz = zz - (long long)rr * a.B;
   const int h = (int)(llin / lnx % lny);
   const int kvh = h / a.G;
   const long long kt0 = (llin % lnx) * BK;
@@ -163,6 +168,12 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   const int body_end = max(head, n_tiles - (tail ? 1 : 0));
   // tile i lives in buffer (i + shift) % 3: the first unmasked tile in buffer 0
   const int shift = (3 - head % 3) % 3;
+  // this workgroup's tiles [i_lo, i_hi): query range rr of the split pass
+  // (absolute tiles [rr * qst, (rr + 1) * qst)), else all of them; a range
+  // that none of the key tile's queries reach writes no partial
+  const int i_lo = (int)max(0LL, (long long)rr * a.qst - first_tile);
+  const int i_hi = (int)min((long long)n_tiles, ((long long)rr + 1) * a.qst - first_tile);
+  if (a.rkv > 1 && i_lo >= i_hi) return;
 
   typename T::template AsyncLoader<NW> ld;
   ld.init(wave, lane, false, DENSE ? D : a.qs[2]);
@@ -190,7 +201,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
     if (tid < 2 * kBQ)
       reinterpret_cast<float*>(smem + XR + ((i + shift) % 3) * 512)[tid] = tid < kBQ ? lv * kLog2e : lv;
   };
-  if (n_tiles > 0) issue(0);
+  if (i_lo < i_hi) issue(i_lo);
 
   // this wave's operand rows: K (wave A) or V (wave B) of its lane's key
   bf16x8 kv[KT];
@@ -222,9 +233,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   const unsigned xbase = lds0 + XR + (role_a ? 0u : 4u * kBQ) + 32u * grp;
   const unsigned pbase = lds0 + PR + (unsigned)((kg * 4 * 64 + lane) * 16);
 
-  if (n_tiles > 0) {
+  if (i_lo < i_hi) {
     wait_vmem();
-    deposit(0);
+    deposit(i_lo);
   }
   __syncthreads();
 
@@ -390,28 +401,31 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   // one iteration of the tile loop: A on tile i (buffer bfa), B on tile
   // i - 1 (buffer bfb), the prefetch of tile i + 1, one barrier
   auto iter = [&](auto masked_tag, int i, auto bfa, auto bfb) __attribute__((always_inline)) {
-    if (i + 1 < n_tiles) issue(i + 1);
+    if (i + 1 < i_hi) issue(i + 1);
     if (role_a) {
-      if (i < n_tiles) tile_a(masked_tag, bfa, i);
-    } else if (i > 0) {
+      if (i < i_hi) tile_a(masked_tag, bfa, i);
+    } else if (i > i_lo) {
       tile_b(bfb);
     }
     wait_vmem();
-    if (i + 1 < n_tiles) deposit(i + 1);
+    if (i + 1 < i_hi) deposit(i + 1);
     __syncthreads();
   };
   auto bfr = [&](int i) __attribute__((always_inline)) { return (i + shift + 3) % 3; };
 
-  int i = 0;
-  for (; i < head; ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
-  // unmasked tiles: tile i sits in buffer i - head (mod 3)
-  for (; i + 3 <= body_end; i += 3) {
+  int i = i_lo;
+  for (; i < min(head, i_hi); ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
+  // unmasked tiles: tile i sits in buffer i - head (mod 3); a range that
+  // starts inside them first steps to that pattern
+  const int b_end = min(body_end, i_hi);
+  for (; i < b_end && (i - head) % 3 != 0; ++i) iter(std::false_type{}, i, bfr(i), bfr(i - 1));
+  for (; i + 3 <= b_end; i += 3) {
     iter(std::false_type{}, i, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
     iter(std::false_type{}, i + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
     iter(std::false_type{}, i + 2, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
   }
-  for (; i < body_end; ++i) iter(std::false_type{}, i, bfr(i), bfr(i - 1));
-  for (; i <= n_tiles; ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
+  for (; i < b_end; ++i) iter(std::false_type{}, i, bfr(i), bfr(i - 1));
+  for (; i <= i_hi; ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
 
   if (key < Nk) {
     float* part = role_a ? dv_part : dk_part;
@@ -426,7 +440,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
         f32x4 w = {acc[dbk][4 * j] * mul, acc[dbk][4 * j + 1] * mul, acc[dbk][4 * j + 2] * mul,
                    acc[dbk][4 * j + 3] * mul};
         if (PARTIAL) {
-          *reinterpret_cast<f32x4*>(part + ((bz * a.Hq + h) * Nk + key) * D + d) = w;
+          *reinterpret_cast<f32x4*>(part + (((rr * a.B + bz) * a.Hq + h) * Nk + key) * D + d) = w;
         } else {
           const long long base = ((bz * a.Hkv + kvh) * Nk + key) * D + d;  // fp32 accumulators
           const long long obf = DENSE ? base : bz * a.ks[0] + kvh * a.ks[1] + key * a.ks[2] + d;  // bf16 dk, dv
@@ -465,9 +479,10 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_group_kernel(Bwd
   bwd_dkdv_body<D, PARTIAL, true>(g.a[c], g.dk_part[c], g.dv_part[c], lin - c * per_call, gridDim.x, gridDim.y);
 }
 
-// dK[b, kvh] = sum over the G query heads of the group of the fp32 partials,
-// written (or added) as the dK, dV modes of the arguments say.  One thread per
-// 4 elements.
+// dK[b, kvh] = sum over the query ranges that wrote a partial for the key's
+// tile (all of them, unsplit: one) and over the G query heads of the group of
+// the fp32 partials, written (or added) as the dK, dV modes of the arguments
+// say.  One thread per 4 elements.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const float* __restrict__ dk_part,
                                                               const float* __restrict__ dv_part,
@@ -478,12 +493,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const f
   if (idx >= kv_heads_total * per_head) return;
   const long long hk = idx / per_head;        // flattened (b, kvh)
   const long long rem = idx - hk * per_head;  // 4-element slot within the head
-  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-  for (int g = 0; g < G; ++g) {
-    const long long src = ((hk * G + g) * per_head + rem) * 4;
-    sk += *reinterpret_cast<const f32x4*>(dk_part + src);
-    sv += *reinterpret_cast<const f32x4*>(dv_part + src);
+  // the query ranges of the split pass that reach the key's 128-key tile (the
+  // dK/dV kernel's first query tile and tile count for it)
+  int r0 = 0, r1 = 1;
+  if (a.rkv > 1) {
+    const long long kt0 = rem / (D / 4) / 128 * 128;
+    const long long q_first = a.causal ? max(0LL, kt0 - a.dpos) : 0;
+    const long long nqt = (a.Nq + kBQ - 1) / kBQ;
+    r0 = (int)(q_first / kBQ / a.qst);
+    r1 = q_first >= a.Nq ? r0 : (int)((nqt - 1) / a.qst + 1);
   }
+  const long long rstride = kv_heads_total * G * per_head * 4;  // one range's partials
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < r1; ++r)
+    for (int g = 0; g < G; ++g) {
+      const long long src = r * rstride + ((hk * G + g) * per_head + rem) * 4;
+      sk += *reinterpret_cast<const f32x4*>(dk_part + src);
+      sv += *reinterpret_cast<const f32x4*>(dv_part + src);
+    }
   if (a.dkv_mode != 0) {
     f32x4* pk = reinterpret_cast<f32x4*>(a.dk_acc + idx * 4);
     f32x4* pv = reinterpret_cast<f32x4*>(a.dv_acc + idx * 4);
@@ -508,7 +535,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs a, const f
 // ---------------------------------------------------------------------------
 // dQ: workgroup = query rows of HP heads sharing a key/value head
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 8;
+constexpr int kDqWaves = kBwdDqWaves;
 constexpr int kBN = 64;
 
 // DENSE: contiguous [B, H, N, D] tensors (row strides D known at compile
@@ -535,7 +562,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
   // workgroup-uniform: kept in scalar registers
   const unsigned lxy = __builtin_amdgcn_readfirstlane(lin / nx);
   const int by = __builtin_amdgcn_readfirstlane(lxy % ny);
-  const long long bz = (unsigned)__builtin_amdgcn_readfirstlane(lxy / ny);
+  const unsigned zz = __builtin_amdgcn_readfirstlane(lxy / ny);  // key range * B + batch
+  const int rr = (int)__builtin_amdgcn_readfirstlane(zz / (unsigned)a.B);
+  const long long bz = zz - (unsigned)rr * (unsigned)a.B;
   const int qt = n_qtiles - 1 - __builtin_amdgcn_readfirstlane(lin - lxy * nx);
   if (qt < 0) return;  // a grouped launch's grid covers its longest call
   const int h = by * HP + (wave % HP);
@@ -553,7 +582,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
   // keys the workgroup can see
   long long kv_end = Nk;
   if (a.causal) kv_end = max(0LL, min(Nk, min(q_start + SPAN, Nq) + a.dpos));
-  const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
+  // its key tiles [j0, j0 + n_tiles): key range rr of the split pass, else
+  // all; a range that no query of the tile sees writes no partial
+  const int j0 = rr * a.kst;
+  const int n_tiles = (int)max(0LL, min((kv_end + kBN - 1) / kBN, (long long)j0 + a.kst) - j0);
+  if (a.rq > 1 && n_tiles == 0) return;
   const int n_sub = 2 * n_tiles;  // 32-key sub-tiles
 
   typename T::template AsyncLoader<NW> ld;
@@ -562,7 +595,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
   // then scalar arithmetic; full tiles skip the row clamping
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    const long long r0 = (long long)j * kBN;
+    const long long r0 = ((long long)j0 + j) * kBN;
     if (r0 + kBN <= Nk) {
       ld.load_full(buf, kbase, r0, wave_s);
       ld.load_full(buf + T::BYTES, vbase, r0, wave_s);
@@ -659,7 +692,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
     for (int v = 0; v < 16; ++v) {
       float p = fast_exp2(__builtin_fmaf(s[v], sl, -lse2));
       if (MASKED) {
-        const int key = 32 * t + acc_row_pi(v, grp);
+        const int key = kBN * j0 + 32 * t + acc_row_pi(v, grp);
         if (key >= klim || (a.causal && key > qrow_i + a.dpos)) p = 0.f;
       }
       ds[v] = p * (dp[v] - dvv);
@@ -697,7 +730,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
   // Tiles [0, n_full) need no element mask for any wave of the workgroup.
   long long full_keys = Nk;
   if (a.causal) full_keys = max(0LL, min(full_keys, q_start + 1 + a.dpos));
-  const int n_full = (int)min((long long)n_tiles, full_keys / kBN);
+  const int n_full = (int)min((long long)n_tiles, max(0LL, full_keys / kBN - j0));
 
   // Schedule: tile j lives in buffer j % 3 and is read in steps 2j .. 2j+2.
   // Odd steps t issue the direct loads of tile (t+3)/2 (its buffer was last
@@ -753,6 +786,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int n_qtiles, unsi
         const int d = db * 32 + 8 * jj + 4 * grp;
         f32x4 g = {acc[db][4 * jj] * a.scale, acc[db][4 * jj + 1] * a.scale, acc[db][4 * jj + 2] * a.scale,
                    acc[db][4 * jj + 3] * a.scale};
+        if (a.rq > 1) {  // this key range's part, summed by bwd_dq_reduce
+          *reinterpret_cast<f32x4*>(a.dq_part + (long long)rr * a.B * a.Hq * Nq * D + base + d) = g;
+          continue;
+        }
         if (a.dq_mode != 0) {
           f32x4* p = reinterpret_cast<f32x4*>(a.dq_acc + base + d);
           if (a.dq_mode == 2) g += *p;  // this KV block's part added to the running dQ
@@ -768,6 +805,40 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(BwdArgs a, int
   // XCD-aware order: neighbouring query tiles share an XCD and its L2 while
   // they stream the same key/value tiles; longest causal rows first
   bwd_dq_body<D, HP, DENSE>(a, n_qtiles, wg_number(), gridDim.x, gridDim.y);
+}
+
+// dQ = the sum over the key ranges that wrote a partial for the row's query
+// tile (tiles of `span` rows, as the dQ kernel's) of the scaled fp32
+// partials, written (or added) as the dQ mode of the arguments says.  One
+// thread per 4 elements.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(BwdArgs a, int span, bool dense) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;  // over B * Hq * Nq * D / 4
+  constexpr long long per_row = D / 4;
+  if (idx >= (long long)a.B * a.Hq * a.Nq * per_row) return;
+  const long long row_all = idx / per_row;  // flattened (b, h, row)
+  const long long row = row_all % a.Nq;
+  const long long q_start = row / span * span;
+  long long kv_end = a.Nk;
+  if (a.causal) kv_end = max(0LL, min(a.Nk, min(q_start + span, a.Nq) + a.dpos));
+  const long long tiles = (kv_end + kBN - 1) / kBN;
+  const int r1 = (int)min((long long)a.rq, (tiles + a.kst - 1) / a.kst);
+  const long long rstride = (long long)a.B * a.Hq * a.Nq * D;  // one range's partials
+  f32x4 g = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < r1; ++r) g += *reinterpret_cast<const f32x4*>(a.dq_part + r * rstride + idx * 4);
+  if (a.dq_mode != 0) {
+    f32x4* p = reinterpret_cast<f32x4*>(a.dq_acc + idx * 4);
+    if (a.dq_mode == 2) g += *p;
+    *p = g;
+  }
+  if (a.dq) {
+    long long obf = idx * 4;  // contiguous
+    if (!dense) {
+      const long long bh = row_all / a.Nq;
+      obf = bh / a.Hq * a.qs[0] + bh % a.Hq * a.qs[1] + row * a.qs[2] + 4 * (idx % per_row);
+    }
+    *reinterpret_cast<u32x2*>(a.dq + obf) = pack_bf16x4_bits(g[0], g[1], g[2], g[3]);
+  }
 }
 
 template <int D, int HP>
@@ -890,9 +961,16 @@ hipError_t launch_delta(const uint16_t* o, const uint16_t* d_o, float* delta, in
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_side) {
+hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_side, bool split) {
   hipError_t e;
   BwdArgs a = a0;
+  a.B = B;
+  const BwdSplit sp = split ? bwd_split_plan(B, a.Hq, a.Hkv, a.Nq, a.Nk, D) : BwdSplit{};
+  a.rkv = sp.rkv;
+  a.qst = sp.qst;
+  a.rq = sp.rq;
+  a.kst = sp.kst;
+  a.dq_part = a.part + bwd_split_part_floats(B, a.Hq, a.Hkv, a.Nk, D, sp);
   const bool dense = a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0 && a.ks[0] == 0 && a.ks[1] == 0 && a.ks[2] == 0;
   if (a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0) {
     a.qs[2] = D;
@@ -904,18 +982,19 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
     a.ks[1] = a.Nk * D;
     a.ks[0] = a.Hkv * a.Nk * D;
   }
-  const dim3 kgrid((unsigned)((a.Nk + 127) / 128), (unsigned)a.Hq, (unsigned)B);  // 128 keys per workgroup
+  // 128 keys per workgroup; grid z = query range * B + batch
+  const dim3 kgrid((unsigned)((a.Nk + 127) / 128), (unsigned)a.Hq, (unsigned)(B * a.rkv));
   const int HP = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
   const long long span = (kDqWaves / HP) * 32;
   const int n_qt = (int)((a.Nq + span - 1) / span);
-  dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)B);
+  dim3 grid((unsigned)n_qt, (unsigned)(a.Hq / HP), (unsigned)(B * a.rq));  // z = key range * B + batch
   if (!grid_fits(kgrid) || !grid_fits(grid)) return hipErrorInvalidConfiguration;
   if (a.o) {
     e = launch_delta<D>(a.o, a.d_o, a.delta, B, a.Hq, a.Nq, a.qs, stream);
     if (e != hipSuccess) return e;
   }
   DqStream dqs;
-  if ((e = dqs.begin(stream, allow_side, (long long)kgrid.x * kgrid.y * kgrid.z)) != hipSuccess) return e;
+  if ((e = dqs.begin(stream, allow_side, (long long)kgrid.x * kgrid.y * B)) != hipSuccess) return e;
   const hipStream_t qstream = dqs.stream();
   // the dQ pass first: on the side stream it then runs beside the dK/dV pass
   if (dense) {
@@ -935,11 +1014,19 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.rq > 1) {
+    const long long slots = (long long)B * a.Hq * a.Nq * D / 4;
+    LCATTN_LAUNCH("bwd_dq_reduce_kernel", (bwd_dq_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)), dim3(256),
+                  0, qstream, a, (int)span, dense);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
-    float* dk_part = a.G == 1 ? nullptr : a.part;
-    float* dv_part = a.G == 1 ? nullptr : dk_part + (long long)B * a.Hq * a.Nk * D;
+    const bool partial = a.G != 1 || a.rkv > 1;
+    float* dk_part = partial ? a.part : nullptr;
+    float* dv_part = partial ? dk_part + (long long)a.rkv * B * a.Hq * a.Nk * D : nullptr;
     const dim3 blk(64 * kSplitWaves);
-    if (a.G == 1) {
+    if (!partial) {
       if (dense)
         LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, false, true>), kgrid, blk, 0, stream, a, dk_part,
                       dv_part);
@@ -978,6 +1065,9 @@ hipError_t launch_d_group(const BwdArgs* calls, int n, int B, hipStream_t stream
   int nq_tiles = 0;
   for (int c = 0; c < n; ++c) {
     BwdArgs a = calls[c];
+    a.B = B;  // grid z = call * B + batch: the bodies see z = batch (one range)
+    a.rkv = a.rq = 1;
+    a.qst = a.kst = 1 << 30;
     a.qs[2] = D; a.qs[1] = a.Nq * D; a.qs[0] = a.Hq * a.Nq * D;
     a.ks[2] = D; a.ks[1] = a.Nk * D; a.ks[0] = a.Hkv * a.Nk * D;
     g.a[c] = a;
@@ -1065,8 +1155,8 @@ hipError_t launch_attn_bwd_group(const BwdArgs* calls, int n, int B, int D, hipS
   return D == 64 ? launch_d_group<64>(calls, n, B, stream, true) : launch_d_group<128>(calls, n, B, stream, true);
 }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream, bool allow_side) {
-  return D == 64 ? launch_d<64>(a, B, stream, allow_side) : launch_d<128>(a, B, stream, allow_side);
+hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream, bool allow_side, bool split) {
+  return D == 64 ? launch_d<64>(a, B, stream, allow_side, split) : launch_d<128>(a, B, stream, allow_side, split);
 }
 
 hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta, long long rows, int D,

@@ -29,6 +29,7 @@ hipError_t launch_sum_replicas(const void* in, bool in_f32, uint16_t* out, long 
 // forward kernel geometry (shared by the launcher and the split-count heuristic)
 constexpr int kFwdWaves = 8;     // waves per workgroup
 constexpr int kFwdKeyTile = 64;  // keys per tile
+constexpr int kBwdDqWaves = 8;   // waves per workgroup of the backward's dQ pass (32 query rows each)
 
 // The attention kernels number their workgroups in 32 bits: a launch whose
 // grid has 2^31 or more workgroups is refused (hipErrorInvalidConfiguration).
@@ -159,20 +160,46 @@ struct BwdArgs {
   // [B, H, N, D].  lse, the delta, the fp32 accumulators and the workspace
   // are always contiguous.
   long long qs[3] = {0, 0, 0}, ks[3] = {0, 0, 0};
+  // Split passes (filled in by the launcher from a BwdSplit): the dK/dV pass
+  // over rkv ranges of qst 64-row query tiles, its fp32 partials at part
+  // ([rkv, B, Hq, Nk, D] for dK, then the same for dV) when rkv > 1 or the
+  // heads are grouped; the dQ pass over rq ranges of kst 64-key tiles, its
+  // fp32 partials (scaled) at dq_part ([rq, B, Hq, Nq, D]) when rq > 1.  A
+  // range that no query (key) of a workgroup's tile sees writes nothing.
+  int B = 1;
+  int rkv = 1, qst = 1 << 30;
+  int rq = 1, kst = 1 << 30;
+  float* dq_part = nullptr;
 };
+
+// How a small backward problem splits its passes (one per call shape): the
+// dK/dV pass over rkv query ranges of qst 64-row tiles, the dQ pass over rq
+// key ranges of kst 64-key tiles; 1: not split.
+struct BwdSplit {
+  int rkv = 1, qst = 1 << 30;
+  int rq = 1, kst = 1 << 30;
+};
+BwdSplit bwd_split_plan(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
 // Backward workspace: Dv per query row (fp32, padded to 64 floats), then, for
 // grouped-query attention (Hq != Hkv), per-query-head fp32 partials of dK and
-// dV ([B, Hq, Nk, D] each).
+// dV ([B, Hq, Nk, D] each).  bwd_workspace_bytes is that of attn_bwd, whose
+// split plan (bwd_split_plan) also holds rkv partials of dK and dV and rq of
+// dQ: Dv | dK, dV partials (bwd_split_part_floats) | dQ partials.
 long long bwd_delta_floats(int B, int Hq, long long Nq);
 long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D);
+long long bwd_split_part_floats(int B, int Hq, int Hkv, long long Nk, int D, const BwdSplit& s);
+long long bwd_split_dq_floats(int B, int Hq, long long Nq, int D, const BwdSplit& s);
 long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
 // allow_side: a problem whose dK/dV grid has fewer than two workgroups per
 // compute unit runs its dQ pass on the library's side stream of the device
 // (forked from and joined back into `stream`); false keeps every launch on
 // `stream` and creates nothing (the allocation-free entry point)
-hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream, bool allow_side);
+// split: run the passes as bwd_split_plan says (a.part, a.dq_part then point
+// at its partials; attn_bwd and its strided and allocation-free forms); else
+// unsplit (block calls, whose workspace holds the grouped-query partials only)
+hipError_t launch_attn_bwd(const BwdArgs& a, int B, int D, hipStream_t stream, bool allow_side, bool split);
 // Up to kMaxBwdGroup independent block-backward calls (contiguous tensors, Dv
 // given, the same B, Hq, Hkv, D, scale and mask kind): one dK/dV launch and
 // one dQ launch for all of them.

@@ -17,8 +17,49 @@ long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D) {
   return Hq != Hkv ? 2LL * B * Hq * Nk * D : 0;  // per-query-head dK, dV partials
 }
 
+long long bwd_split_part_floats(int B, int Hq, int Hkv, long long Nk, int D, const BwdSplit& s) {
+  return s.rkv > 1 ? 2LL * s.rkv * B * Hq * Nk * D : bwd_part_floats(B, Hq, Hkv, Nk, D);
+}
+
+long long bwd_split_dq_floats(int B, int Hq, long long Nq, int D, const BwdSplit& s) {
+  return s.rq > 1 ? (long long)s.rq * B * Hq * Nq * D : 0;
+}
+
+// A backward whose dK/dV grid (one workgroup per 128 keys and query head)
+// leaves compute units idle is limited by its longest workgroups: the first
+// key tile walks every query tile, the last query tile every key tile.  Cut
+// into ranges, every workgroup of either pass does at most about the work of
+// 1024 query rows x 128 keys at D = 64: the dK/dV pass takes query ranges of
+// 1024 * 64 / D rows, the dQ pass key ranges of 512 * 64 / D keys (its
+// workgroups hold 256 query rows).  At most 8 ranges a pass, and their fp32
+// partials within 64 MiB.  (Measured on the glossary example's backward
+// [1, 4, 4096, 64]: 4 and 8 ranges 95 us against 121 us unsplit, fewer ranges
+// 97-128 us; [1, 8, 1024, 128]: 2 and 4 ranges 58 us against 77 us.)
+BwdSplit bwd_split_plan(int B, int Hq, int Hkv, long long Nq, long long Nk, int D) {
+  const long long wkv = (long long)B * Hq * ((Nk + 127) / 128);
+  if (wkv >= 256 || Hq % Hkv) return BwdSplit{};
+  const long long nqt = (Nq + 63) / 64, nkt = (Nk + 63) / 64;
+  long long rkv = std::min<long long>(8, (nqt + 16 * 64 / D - 1) / (16 * 64 / D));
+  long long rq = std::min<long long>(8, (nkt + 8 * 64 / D - 1) / (8 * 64 / D));
+  for (;;) {
+    BwdSplit t;
+    t.qst = (int)((nqt + rkv - 1) / rkv);
+    t.rkv = (int)((nqt + t.qst - 1) / t.qst);
+    t.kst = (int)((nkt + rq - 1) / rq);
+    t.rq = (int)((nkt + t.kst - 1) / t.kst);
+    if (t.rkv == 1) t.qst = 1 << 30;
+    if (t.rq == 1) t.kst = 1 << 30;
+    const long long extra = (t.rkv > 1 ? 2LL * t.rkv * B * Hq * Nk * D : 0) + bwd_split_dq_floats(B, Hq, Nq, D, t);
+    if (extra * 4 <= (64LL << 20)) return t;
+    if (rkv == 1 && rq == 1) return BwdSplit{};
+    if (rkv >= rq) --rkv; else --rq;
+  }
+}
+
 long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D) {
-  return (bwd_delta_floats(B, Hq, Nq) + bwd_part_floats(B, Hq, Hkv, Nk, D)) * 4;
+  const BwdSplit s = bwd_split_plan(B, Hq, Hkv, Nq, Nk, D);
+  return (bwd_delta_floats(B, Hq, Nq) + bwd_split_part_floats(B, Hq, Hkv, Nk, D, s) +
+          bwd_split_dq_floats(B, Hq, Nq, D, s)) * 4;
 }
 
 int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits) {

@@ -29,7 +29,7 @@ hipError_t launch_merge_into(const float*, const float*, int, const MergeSplits&
                              long long, int, hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t launch_attn_bwd(const BwdArgs&, int, int, hipStream_t, bool) { return hipErrorNoDevice; }
+hipError_t launch_attn_bwd(const BwdArgs&, int, int, hipStream_t, bool, bool) { return hipErrorNoDevice; }
 hipError_t launch_attn_bwd_group(const BwdArgs*, int, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_bwd_delta(const uint16_t*, const uint16_t*, float*, long long, int, hipStream_t) {
   return hipErrorNoDevice;

@@ -193,8 +193,9 @@ def bwd_strided(L, qs=(0, 128, 1024), ks=(0, 128, 256), **kw):
     arr = ctypes.c_int64 * 3
     n = 1 << 22
     args = dict(q=A, k=A + n, v=A + 2 * n, o=A + 3 * n, do=A + 4 * n, lse=A + 5 * n, dq=A + 6 * n, dk=A + 7 * n,
-                dv=A + 8 * n, ws=A + 9 * n, ws_bytes=1 << 24, B=1, Hq=8, Hkv=2, N=1024, D=128, scale=0.088,
-                causal=1, qs=arr(*qs) if qs else None, ks=arr(*ks) if ks else None, stream=None)
+                dv=A + 8 * n, ws=A + 9 * n, ws_bytes=L.attn_bwd_workspace_size(1, 8, 2, 1024, 128), B=1, Hq=8,
+                Hkv=2, N=1024, D=128, scale=0.088, causal=1, qs=arr(*qs) if qs else None,
+                ks=arr(*ks) if ks else None, stream=None)
     args.update(kw)
     return L.attn_bwd_strided(*args.values())
 
@@ -248,6 +249,9 @@ def test_merge_rejects(L, kw, status):
 
 def test_bwd_workspace_size(L):
     assert L.attn_bwd_workspace_size(1, 8, 8, 65536, 128) >= 8 * 65536 * 4
+    # the glossary example's backward splits its passes: 4 query ranges of dK,
+    # dV partials and 8 key ranges of dQ partials (fp32), then Dv
+    assert L.attn_bwd_workspace_size(1, 4, 4, 4096, 64) == (2 * 4 + 8) * 4 * 4096 * 64 * 4 + 4 * 4096 * 4
     assert L.attn_bwd_workspace_size(1, 8, 3, 1024, 128) == 0
     assert L.attn_bwd_workspace_size(0, 8, 8, 1024, 128) == 0
 
@@ -255,8 +259,8 @@ def test_bwd_workspace_size(L):
 def bwd(L, **kw):
     n = 1 << 22
     args = dict(q=A, k=A + n, v=A + 2 * n, o=A + 3 * n, do=A + 4 * n, lse=A + 5 * n, dq=A + 6 * n, dk=A + 7 * n,
-                dv=A + 8 * n, ws=A + 9 * n, ws_bytes=1 << 20, B=1, Hq=8, Hkv=8, N=1024, D=128, scale=0.088,
-                causal=1, stream=None)
+                dv=A + 8 * n, ws=A + 9 * n, ws_bytes=L.attn_bwd_workspace_size(1, 8, 8, 1024, 128), B=1, Hq=8,
+                Hkv=8, N=1024, D=128, scale=0.088, causal=1, stream=None)
     args.update(kw)
     return L.attn_bwd(*args.values())
 

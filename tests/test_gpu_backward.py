@@ -56,6 +56,22 @@ def test_bwd_small_sweep(gpu, N, D, G, causal):
     check_grads((dq, dk, dv), (dQ, dK, dV), f"N={N} D={D} G={G} causal={causal}")
 
 
+@pytest.mark.parametrize("N,D", [(1500, 64), (2049, 128)])
+@pytest.mark.parametrize("G,causal", [(1, True), (4, True), (2, False)])
+def test_bwd_split_ranges(gpu, N, D, G, causal):
+    """Small problems run the dK/dV pass over query ranges and the dQ pass over
+    key ranges (fp32 partials summed by the reduce kernels): batch 2 and a
+    ragged N put range edges inside the diagonal and tail tiles."""
+    B, Hkv = 2, 1 if G != 2 else 2
+    d = make_qkv(B, Hkv * G, Hkv, N, D, seed=900 + N + G, with_do=True)
+    s = sdpa_scale(D)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s, causal)
+    O, L, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, causal)
+    check_forward(f64_of(o), f64_of(lse), O, L, f"fwd N={N}")
+    check_grads((dq, dk, dv), (dQ, dK, dV), f"split B={B} N={N} D={D} G={G} causal={causal}")
+
+
 def test_bwd_full_1024(gpu):
     """B=1, H=8, D=128, N=1024: every row of O, LSE, dQ, dK and dV."""
     d = make_qkv(1, 8, 8, 1024, 128, seed=5, with_do=True)

@@ -112,9 +112,11 @@ def test_ring_backward_batch(gpu, causal):
 @pytest.mark.parametrize("G", [1, 4])
 def test_single_block_is_attn_bwd_bit_for_bit(gpu, G):
     """One block over the whole sequence with bf16 outputs runs attn_bwd's
-    kernels on the same values."""
+    kernels on the same values.  The shape gives the dK/dV pass 256 or more
+    workgroups, so attn_bwd does not split its passes into ranges (a split
+    sums the same terms in another grouping: see the next test)."""
     import torch
-    d = make_qkv(1, 2 * G, 2, 777, 128, seed=41 + G, with_do=True)
+    d = make_qkv(2, 2 * G, 2, 8192 - 57, 128, seed=41 + G, with_do=True)
     s = sdpa_scale(128)
     q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
     o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
@@ -124,6 +126,23 @@ def test_single_block_is_attn_bwd_bit_for_bit(gpu, G):
     torch.cuda.synchronize()
     for a, b in ((dq0, dq1), (dk0, dk1), (dv0, dv1)):
         assert np.array_equal(bits_of(a), bits_of(b))
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_single_block_matches_split_attn_bwd(gpu, G):
+    """On a small problem attn_bwd splits its passes into query and key ranges
+    (fp32 partials, summed by the reduce kernels); the unsplit block call
+    agrees with it to rounding, and both with the oracle."""
+    d = make_qkv(1, 2 * G, 2, 777, 128, seed=41 + G, with_do=True)
+    s = sdpa_scale(128)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
+    got0 = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s)
+    delta = lc.attn_bwd_delta(o, do)
+    got1 = lc.attn_bwd_block(q, k, v, do, lse, delta, causal=True, scale=s)
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, True)
+    check(got0, (dQ, dK, dV), f"split attn_bwd G={G}")
+    check(got1, (dQ, dK, dV), f"block call G={G}")
 
 
 def test_query_shards_and_kv_blocks(gpu):
