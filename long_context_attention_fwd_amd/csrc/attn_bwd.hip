@@ -970,7 +970,7 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
   a.qst = sp.qst;
   a.rq = sp.rq;
   a.kst = sp.kst;
-  a.dq_part = a.part + bwd_split_part_floats(B, a.Hq, a.Hkv, a.Nk, D, sp);
+  a.dq_part = sp.rq > 1 ? a.part + bwd_split_part_floats(B, a.Hq, a.Hkv, a.Nk, D, sp) : nullptr;
   const bool dense = a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0 && a.ks[0] == 0 && a.ks[1] == 0 && a.ks[2] == 0;
   if (a.qs[0] == 0 && a.qs[1] == 0 && a.qs[2] == 0) {
     a.qs[2] = D;

@@ -86,8 +86,10 @@ hipError_t launch_attn_fwd_group_split(const FwdArgs* calls, float* const* parts
 // and lse.
 hipError_t launch_attn_fwd_splitkv(const FwdArgs& a, int B, int D, int n_splits, float* o_parts, float* lse_parts,
                                    hipStream_t stream);
-// Number of key ranges for attn_fwd_splitkv: n_splits if > 0, else about
-// enough for two non-empty workgroups per compute unit.
+// Number of key ranges for a ring step's grouped accumulate calls
+// (attn_fwd_split_suggest, whose grid is not compacted): n_splits if > 0,
+// else about one and a half workgroups per compute unit with ranges of at
+// least 16 key tiles.
 int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits);
 // attn_fwd_splitkv's ranges: n_splits if > 0; else 1 when the unsplit grid
 // fills the GPU, otherwise the most ranges whose (range, query tile) pairs

@@ -70,8 +70,10 @@ int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int caus
   const long long wgs = (Nq + span - 1) / span * (Hq / HP) * B;
   const long long tiles = (Nk + kFwdKeyTile - 1) / kFwdKeyTile;
   // about one and a half workgroups per compute unit, ranges of at least 16
-  // key tiles (measured: 4K tokens x 4 heads run fastest with 4 ranges, 16K x
-  // 4 query heads on one KV head with 2, 32K x 4 heads unsplit)
+  // key tiles (measured on the split forward before its grid held only the
+  // pairs with work: 4K tokens x 4 heads fastest with 4 ranges, 16K x 4 query
+  // heads on one KV head with 2, 32K x 4 heads unsplit; a zigzag ring step of
+  // two 4096-token chunk calls fastest with the 3 it gives)
   long long n = (384 + wgs - 1) / wgs;
   n = std::min<long long>(n, std::max<long long>(1, tiles / 16));
   (void)causal;
