@@ -331,6 +331,27 @@ def leg_listing_4k(lc, torch, dev, iters=50, warmup=10):
                        "loss": "mean(O^2): dO = 2 O / numel"}
     rls[f"{w.name}.bwd_dkdv_kernel"] = roofline_entry("bwd_dkdv_kernel", tr, 0.8 * f_bwd, "TFLOP/s", w.name)
     rls[f"{w.name}.bwd_dq_kernel"] = roofline_entry("bwd_dq_kernel", tr, 0.2 * f_bwd, "TFLOP/s", w.name)
+
+    # the example's whole training step at this size is launch-bound (two
+    # forward launches, the loss gradient, five backward launches and the side
+    # stream's fork and join): eager, and captured once into a HIP graph
+    def train_step():
+        lc.attn_fwd_splitkv(q, k, v, scale=w.scale, workspace=ws, o=o, lse=lse)
+        torch.mul(o, 2.0 / o.numel(), out=do)
+        lc.attn_bwd(q, k, v, o, do, lse, scale=w.scale, workspace=wsb, dq=dq, dk=dk, dv=dv)
+    step = {"call": "attn_fwd_splitkv, dO of mean(O^2), attn_bwd"}
+    ms = time_calls(torch, train_step, iters, warmup)
+    step["eager"] = {"us": round(1e3 * ms, 2), "TFLOP/s": round(tflops(f + f_bwd, ms), 2)}
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        train_step()  # the capture stream's side stream exists before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        train_step()
+    ms = time_calls(torch, graph.replay, iters, warmup)
+    step["graph"] = {"us": round(1e3 * ms, 2), "TFLOP/s": round(tflops(f + f_bwd, ms), 2)}
+    res["train_step"] = step
     return res, rls
 
 
