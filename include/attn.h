@@ -204,8 +204,11 @@ size_t attn_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64
  * whole 64-key tiles; each range's attention (fp32 O and LSE) is the partial
  * attention of "So funktioniert Kontextparallelität" for one KV block, and the
  * ranges are combined by the attn_partial_merge rule.  n_splits in [1, 64]
- * fixes n; n_splits <= 0 lets the library choose (about two non-empty
- * workgroups per compute unit).  The workspace (caller-owned, >=
+ * fixes n; n_splits <= 0 lets the library choose: unsplit when the plain
+ * grid already has 384 or more workgroups, else the most ranges whose
+ * (range, query tile) pairs with work fit one workgroup per compute unit.
+ * Only those pairs are launched; a range no query of a tile sees writes no
+ * partial and the merge skips it.  The workspace (caller-owned, >=
  * attn_fwd_splitkv_workspace_size bytes, 16-byte aligned, not overlapping
  * any argument) is scratch; its contents on return are unspecified.
  * Deterministic.  Errors as attn_fwd, plus ATTN_ERR_WORKSPACE and
