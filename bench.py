@@ -55,7 +55,7 @@ def pair_flops_block(Hq, D, N, a, b):
     return 4.0 * Hq * D * pairs
 
 
-KERNEL_SOURCES = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip",
+KERNEL_SOURCES = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip", "bwd_dq_ds_kernel": "attn_bwd.hip",
                   "bwd_delta_kernel": "attn_bwd.hip", "bwd_dkdv_reduce_kernel": "attn_bwd.hip",
                   "attn_fwd_kernel": "attn_fwd.hip", "attn_fwd_kernel_fp32out": "attn_fwd.hip",
                   "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}
@@ -97,6 +97,27 @@ def measured_traffic(name, workload):
                 "source": os.path.relpath(path, ROOT)}
     except (KeyError, ValueError):
         return None
+
+
+def bwd_workspace(lc, torch, dev, B, Hq, Hkv, N, D):
+    """attn_bwd's workspace as the binding allocates it by default: room for
+    the stored dS (dq as its product) when the shape has that path and it
+    fits lc.STORED_DS_AUTO_BYTES, else the minimal one (dq recomputed).
+    Returns (workspace, stored)."""
+    need = lc.attn_bwd_ds_workspace_size(B, Hq, Hkv, N, D, True)
+    stored = 0 < need <= lc.STORED_DS_AUTO_BYTES
+    if not stored:
+        need = lc.attn_bwd_workspace_size(B, Hq, Hkv, N, D)
+    return torch.empty(max(16, need), dtype=torch.uint8, device=dev), stored
+
+
+def ds_pass_bytes(B, Hq, Hkv, N, D):
+    """Algorithmic HBM bytes of the product pass dq = scale dS K (causal,
+    Nq = Nk = N): every stored 64 x 64 dS block a query tile's rows see, read
+    once (bf16), K read once per key/value head, dq written (bf16)."""
+    nqt = (N + 63) // 64
+    blocks = sum(min(nqt, 2 * (qt // 2) + 2) for qt in range(nqt))
+    return B * Hq * blocks * 64 * 64 * 2 + 2 * B * Hkv * N * D + 2 * B * Hq * N * D
 
 
 def tflops(f, ms):
@@ -214,7 +235,7 @@ def train_64k(lc, torch, dev, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(lc.attn_bwd_workspace_size(B, Hq, w.Hkv, N, D), dtype=torch.uint8, device=dev)
+    ws, stored = bwd_workspace(lc, torch, dev, B, Hq, w.Hkv, N, D)
     stream = torch.cuda.current_stream(dev)
     f_fwd = fwd_flops(B, Hq, N, D)
     f_bwd = 2.5 * f_fwd
@@ -253,7 +274,7 @@ def train_64k(lc, torch, dev, steps, warmup):
     ms_step = t0.elapsed_time(t1) / steps
     ph = [sum(m[i].elapsed_time(m[i + 1]) for m in all_marks) / steps for i in range(2)]
     work = {"attn_fwd_kernel": ("TFLOP/s", f_fwd), "bwd_dkdv_kernel": ("TFLOP/s", 0.8 * f_bwd),
-            "bwd_dq_kernel": ("TFLOP/s", 0.2 * f_bwd),
+            "bwd_dq_kernel": ("TFLOP/s", 0.2 * f_bwd), "bwd_dq_ds_kernel": ("GB/s", ds_pass_bytes(B, Hq, w.Hkv, N, D)),
             "bwd_delta_kernel": ("GB/s", 2 * 2 * B * Hq * N * D + 4 * B * Hq * N)}
     gpu_kernels = {}
     for name, (tot, calls) in tr.items():
@@ -271,7 +292,8 @@ def train_64k(lc, torch, dev, steps, warmup):
         "value": round(tflops(f_fwd + f_bwd, ms_step), 3), "ms_per_step": round(ms_step, 4),
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": w.Hkv, "N": N, "D": D, "causal": True,
                    "seed": w.seed, "step": "attn_fwd -> attn_bwd (dQ, dK, dV from the forward's O and LSE)",
-                   "algorithmic_flops_per_step": f_fwd + f_bwd},
+                   "dq_path": "product of the stored dS" if stored else "recomputing dQ pass",
+                   "bwd_workspace_bytes": ws.numel(), "algorithmic_flops_per_step": f_fwd + f_bwd},
         "phases": {"fwd": {"ms": round(ph[0], 4), "TFLOP/s": round(tflops(f_fwd, ph[0]), 2),
                            "frac_peak": round(tflops(f_fwd, ph[0]) / PEAK_BF16_TFLOPS, 4)},
                    "bwd": {"ms": round(ph[1], 4), "TFLOP/s": round(tflops(f_bwd, ph[1]), 2),
@@ -465,7 +487,7 @@ def leg_ulysses_shard_32k(lc, torch, dev, steps, warmup, extras):
     lse_parts = torch.empty((n_blk, 1, hq, N), dtype=torch.float32, device=dev)
     o_ring = torch.empty((1, hq, N, D), dtype=torch.bfloat16, device=dev)
     lse_ring = torch.empty_like(lse)
-    ws = torch.empty(lc.attn_bwd_workspace_size(1, hq, hkv, N, D), dtype=torch.uint8, device=dev)
+    ws, stored = bwd_workspace(lc, torch, dev, 1, hq, hkv, N, D)
     scale = w.scale
     stream = torch.cuda.current_stream(dev)
     ring_blocks = [(a, heads["k"][0:1, :, a:a + blk], heads["v"][0:1, :, a:a + blk]) for a in range(0, N, blk)]
@@ -530,6 +552,7 @@ def leg_ulysses_shard_32k(lc, torch, dev, steps, warmup, extras):
         return {"ms": round(ms, 4), "GB/s": round(gbps(b, ms), 1), "frac_peak": round(gbps(b, ms) / PEAK_HBM_GBPS, 4)}
     res = {"workload": w.name, "P": P, "N": N, "shard_heads_q": hq, "shard_heads_kv": hkv, "D": D,
            "step": "relayout q,k,v,dO -> fwd -> 4 partial fwd + merge -> bwd -> relayout o,dq,dk,dv",
+           "dq_path": "product of the stored dS" if stored else "recomputing dQ pass",
            "ms_per_step": round(ms_step, 4),
            "attention_TFLOP/s": round(tflops(f_fwd + f_ring + f_bwd, ms_step), 2),
            "phases": {"relayout_seq_to_head_qkvdo": ph(per["relayout_in"], b=rel_in),
@@ -540,8 +563,12 @@ def leg_ulysses_shard_32k(lc, torch, dev, steps, warmup, extras):
            f"{w.name}.attn_fwd": roofline_entry("attn_fwd_kernel", tr, f_fwd, "TFLOP/s", w.name),
            f"{w.name}.ring_partials": roofline_entry("attn_fwd_kernel_fp32out", tr, f_ring, "TFLOP/s", w.name),
            f"{w.name}.merge": roofline_entry("merge_kernel", tr, merge_bytes, "GB/s", w.name),
-           f"{w.name}.bwd_dkdv_kernel": roofline_entry("bwd_dkdv_kernel", tr, 0.8 * f_bwd, "TFLOP/s", w.name),
-           f"{w.name}.bwd_dq_kernel": roofline_entry("bwd_dq_kernel", tr, 0.2 * f_bwd, "TFLOP/s", w.name)}
+           f"{w.name}.bwd_dkdv_kernel": roofline_entry("bwd_dkdv_kernel", tr, 0.8 * f_bwd, "TFLOP/s", w.name)}
+    if stored:
+        rls[f"{w.name}.bwd_dq_ds_kernel"] = roofline_entry("bwd_dq_ds_kernel", tr, ds_pass_bytes(1, hq, hkv, N, D),
+                                                           "GB/s", w.name)
+    else:
+        rls[f"{w.name}.bwd_dq_kernel"] = roofline_entry("bwd_dq_kernel", tr, 0.2 * f_bwd, "TFLOP/s", w.name)
     if extras:
         res.update(shard_extras(lc, torch, dev, w, xs, heads, o, dq, dk, dv, lse, o_parts, lse_parts, o_ring, ws,
                                 f_fwd, f_ring, f_bwd))

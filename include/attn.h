@@ -251,6 +251,23 @@ int attn_partial_merge(const void* o_parts, int part_dtype, const float* lse_par
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
 
 /*
+ * attn_bwd_ds_workspace_size -- bytes of workspace with which attn_bwd (and
+ * attn_bwd_strided) forms dq from stored dS instead of recomputing it.
+ * dq = scale dS K needs, per query row, dS against every key it sees; the
+ * recomputing dQ pass forms S = Q K^T and dO V^T a second time for that
+ * (seven products per visible pair instead of five).  With this workspace
+ * the dK/dV pass also writes the dS it forms (bf16, the same rounding the
+ * products use) in 64 x 64 blocks -- every block at or left of the diagonal
+ * when causal, all of them otherwise: about B * Hq * N^2 bytes causal, twice
+ * that otherwise -- and a product pass reads them back: dq = scale dS K.
+ * Layout: attn_bwd_workspace_size bytes rounded up to 256, then the blocks.
+ * Returns 0 (path not available) for invalid sizes and for small problems
+ * (fewer than 256 dK/dV workgroups: B * Hq * ceil(N / 128) < 256), whose
+ * passes run as attn_bwd describes.
+ */
+size_t attn_bwd_ds_workspace_size(int B, int Hq, int Hkv, int64_t N, int D, int causal);
+
+/*
  * attn_bwd -- gradients of sum(O * dO) with respect to q, k and v.
  *
  * q, o, d_o, dq [B, Hq, N, D] bf16;  k, v, dk, dv [B, Hkv, N, D] bf16;
@@ -271,6 +288,11 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D);
  * (deterministic; the grouping of the sums differs from the unsplit passes,
  * so results agree with attn_bwd_block over the whole sequence to rounding,
  * not bit for bit).
+ * With workspace_bytes >= attn_bwd_ds_workspace_size (nonzero), dq comes
+ * from the stored dS (that function describes it): dk and dv are the same
+ * bits as with the minimal workspace; dq sums the same terms over keys in
+ * the same order, but its dS is formed from P after P's rounding to bf16 (as
+ * dk's is), so it agrees with the recomputing pass to rounding.
  * When the dK/dV pass has fewer than two workgroups per compute unit (short
  * sequences, ring steps), the dQ pass runs beside it on a side stream of the
  * library's own, forked from hip_stream after Dv and joined back before the
@@ -289,8 +311,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * device allocation, for callers that cannot allocate: code under HIP graph
  * capture, tight training loops, harnesses that forbid hipMalloc.
  *
- * Same arguments, layout and results as attn_bwd (the same kernels; outputs
- * bit-identical), minus workspace / workspace_bytes.  The scratch those
+ * Same arguments, layout and results as attn_bwd given attn_bwd_workspace_size
+ * bytes of workspace (the same kernels, with dq from the recomputing pass;
+ * outputs bit-identical), minus workspace / workspace_bytes.  The scratch those
  * kernels need (attn_bwd_workspace_size bytes: Dv per query row, the
  * grouped-query dK/dV partials and a small problem's range partials) lives in a
  * device array inside the library, attn_bwd_noalloc_max_scratch() bytes

@@ -32,6 +32,7 @@ __all__ = [
     "attn_partial_merge",
     "attn_bwd",
     "attn_bwd_workspace_size",
+    "attn_bwd_ds_workspace_size",
     "attn_bwd_strided",
     "attn_bwd_delta",
     "attn_bwd_block",
@@ -112,6 +113,7 @@ _SIGS = {
                               _P]),
     "attn_partial_merge": (_I, [_P, _I, _P, _I, _P, _P, _I, _I, _L, _I, _P]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
+    "attn_bwd_ds_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _L, _I, _F, _I, _P]),
     "attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _I, _F, _I, _P]),
     "attn_bwd_noalloc_max_scratch": (ctypes.c_size_t, []),
@@ -428,9 +430,37 @@ def attn_bwd_workspace_size(B: int, Hq: int, Hkv: int, N: int, D: int) -> int:
     return int(lib().attn_bwd_workspace_size(B, Hq, Hkv, N, D))
 
 
+def attn_bwd_ds_workspace_size(B: int, Hq: int, Hkv: int, N: int, D: int, causal: bool = True) -> int:
+    """Workspace bytes with which attn_bwd forms dq from stored dS (0: not
+    available for this shape)."""
+    return int(lib().attn_bwd_ds_workspace_size(B, Hq, Hkv, N, D, 1 if causal else 0))
+
+
+# the largest stored-dS workspace the backward allocates by itself
+# (stored_ds=None): the 64K-token training shape at 8 heads needs 32 GiB
+STORED_DS_AUTO_BYTES = 64 << 30
+
+
+def _bwd_workspace(B, Hq, Hkv, N, D, causal, stored_ds, device):
+    torch = _torch()
+    need = 0
+    if stored_ds is not False:
+        need = attn_bwd_ds_workspace_size(B, Hq, Hkv, N, D, causal)
+        if stored_ds is None and need > STORED_DS_AUTO_BYTES:
+            need = 0
+    if need == 0:
+        need = attn_bwd_workspace_size(B, Hq, Hkv, N, D)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def attn_bwd(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = None, workspace=None,
-             dq=None, dk=None, dv=None):
-    """Gradients of sum(o * do): returns (dq, dk, dv) as bf16, shaped like q, k, v."""
+             dq=None, dk=None, dv=None, stored_ds: bool | None = None):
+    """Gradients of sum(o * do): returns (dq, dk, dv) as bf16, shaped like q, k, v.
+    The library picks the dq path by the workspace's size.  Without a
+    workspace one is allocated: with room for the stored dS (dq as a product
+    of it, attn_bwd_ds_workspace_size) when the shape has that path and
+    stored_ds is True, or None and the room is at most STORED_DS_AUTO_BYTES;
+    else the minimal one (dq recomputed)."""
     torch = _torch()
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _need(t, name, torch.bfloat16, 4)
@@ -444,9 +474,8 @@ def attn_bwd(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = 
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = attn_bwd_workspace_size(B, Hq, Hkv, N, D)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _bwd_workspace(B, Hq, Hkv, N, D, causal, stored_ds, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
@@ -491,7 +520,7 @@ def attn_bwd_noalloc(q, k, v, o, do, lse, *, causal: bool = True, scale: float |
 
 
 def attn_bwd_strided(q, k, v, o, do, lse, *, causal: bool = True, scale: float | None = None, workspace=None,
-                     dq=None, dk=None, dv=None):
+                     dq=None, dk=None, dv=None, stored_ds: bool | None = None):
     """attn_bwd on [B, H, N, D] views with any batch / head / token strides
     (the last dimension contiguous), e.g. heads of token-major [N, H, D]
     shards: q, o, do (and dq) share one stride set, k, v (and dk, dv)
@@ -518,9 +547,8 @@ def attn_bwd_strided(q, k, v, o, do, lse, *, causal: bool = True, scale: float |
         _need(t, name, torch.bfloat16, 4, strided=True)
         if tuple(t.shape) != tuple(ref.shape) or tuple(t.stride()) != tuple(ref.stride()):
             raise ValueError(f"{name} must have the shape and strides of {'q' if ref is q else 'k'}")
-    need = attn_bwd_workspace_size(B, Hq, Hkv, N, D)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _bwd_workspace(B, Hq, Hkv, N, D, causal, stored_ds, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     arr = ctypes.c_int64 * 3
     qs, ks = arr(*q.stride()[:3]), arr(*k.stride()[:3])

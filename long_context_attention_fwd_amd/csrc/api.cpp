@@ -482,6 +482,15 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int64_t N, int D) {
   return (size_t)lcattn::bwd_workspace_bytes(B, Hq, Hkv, N, N, D);
 }
 
+size_t attn_bwd_ds_workspace_size(int B, int Hq, int Hkv, int64_t N, int D, int causal) {
+  if (attn_bwd_workspace_size(B, Hq, Hkv, N, D) == 0 || (D != 64 && D != 128)) return 0;
+  // the stored blocks: at most B * Hq * N^2 elements (checked against
+  // overflow before multiplying out)
+  const double approx = (double)B * Hq * ((double)N + 128) * ((double)N + 128) * 2.0;
+  if (approx > 9.0e18) return 0;
+  return (size_t)lcattn::bwd_ds_workspace_bytes(B, Hq, Hkv, N, D, causal ? 1 : 0);
+}
+
 // attn_bwd and attn_bwd_strided: validation and launch.  Null strides:
 // contiguous [B, H, N, D] tensors.
 static int bwd_entry(const char* name, const void* q, const void* k, const void* v, const void* o, const void* d_o,
@@ -500,7 +509,11 @@ static int bwd_entry(const char* name, const void* q, const void* k, const void*
     return fail(ATTN_ERR_SHAPE, "%s: tensor sizes overflow", name);
   if (N >= INT32_MAX || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: N must be < 2^31, B and Hq <= 65535", name);
-  const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, N, D);
+  const size_t need_min = attn_bwd_workspace_size(B, Hq, Hkv, N, D);
+  // a workspace with room for the stored dS takes the product pass for dQ
+  const size_t need_ds = use_scratch ? 0 : attn_bwd_ds_workspace_size(B, Hq, Hkv, N, D, causal);
+  const bool use_ds = need_ds != 0 && workspace && workspace_bytes >= need_ds;
+  const size_t need = use_ds ? need_ds : need_min;
   if (use_scratch) {
     if (need > lcattn::kNoAllocScratchBytes)
       return fail(ATTN_ERR_WORKSPACE, "%s: needs %zu bytes of scratch; the library holds %zu per GPU", name, need,
@@ -553,6 +566,11 @@ static int bwd_entry(const char* name, const void* q, const void* k, const void*
   a.dv = static_cast<uint16_t*>(dv);
   a.delta = static_cast<float*>(workspace);
   a.part = a.delta + lcattn::bwd_delta_floats(B, Hq, N);
+  if (use_ds) {
+    a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                       lcattn::bwd_ds_offset_bytes(B, Hq, Hkv, N, D));
+    a.ds_head = lcattn::bwd_ds_head_elems(N, causal ? 1 : 0);
+  }
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = Hq / Hkv;

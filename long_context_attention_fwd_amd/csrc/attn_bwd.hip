@@ -109,8 +109,9 @@ __device__ __forceinline__ auto lin_off(Bf b) {
 }
 
 // The kernel body: workgroup number lin (already in XCD-aware order) of a
-// grid of nx key tiles x ny query heads x B.
-template <int D, bool PARTIAL, bool DENSE>
+// grid of nx key tiles x ny query heads x B.  DS: wave B also stores its dS
+// blocks (a.ds) for the dQ product pass.
+template <int D, bool PARTIAL, bool DENSE, bool DS>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restrict__ dk_part,
                                               float* __restrict__ dv_part, unsigned lin, unsigned nx,
                                               unsigned ny) {
@@ -196,6 +197,45 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
       row = row < Nq ? row : Nq - 1;
       lv = (tid < kBQ ? lbase : dbase)[row];
     }
+  };
+  // stored dS (wave B): block (query tile, key tile kt0 / 64 + kg / 2), in
+  // the order the stores produce it: the half of the block's keys of this
+  // key group (kg % 2), then the (32-row block, 16-row half) of the query
+  // tile, then the lane, 16 bytes each -- every store writes 1 KiB in one
+  // piece (the product pass's loads put the units back in rows).  Keys past
+  // Nk store what their unmasked scores give (without the causal mask); the
+  // product pass masks them.
+  long long ds_wave = 0;  // elements from a.ds to the wave's block of query tile 0's row
+  unsigned ds_lane = 0;
+  long long ds_nkt2 = 0;
+  if constexpr (DS) {
+    const int kg_s = __builtin_amdgcn_readfirstlane(kg);
+    ds_wave = (bz * a.Hq + h) * a.ds_head + (kt0 / 64 + (kg_s >> 1)) * kDsBlockElems;
+    ds_lane = (unsigned)((kg & 1) * 4096 + lane * 16);
+    ds_nkt2 = (Nk + 127) / 128 * 2;
+  }
+  // A tile's dS is stored during wave B's next tile, after that tile's dP
+  // products went out (measured: 1-3% faster than at its start or end, or
+  // before the loads of the next tile; stores count in the same counter as
+  // the tile loads, and stored at once they held every barrier until they
+  // reached memory).  The address is a.ds
+  // plus a wave-uniform element offset (scalar registers; kept as pointer
+  // arithmetic on a.ds, so that the compiler knows it is global memory and
+  // emits global stores -- flat stores would also count against the LDS
+  // counter that every fragment wait uses) plus the lane's byte offset.
+  u32x4 ds_pend[4];
+  auto store_ds = [&](int i) __attribute__((always_inline)) {
+    const long long qt = first_tile + i;
+    const unsigned long long off =
+        (unsigned long long)(ds_wave + bwd_ds_row_start(qt, a.causal, ds_nkt2) * kDsBlockElems);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(off >> 32));
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)off);
+    unsigned char* p = reinterpret_cast<unsigned char*>(a.ds + (long long)(((unsigned long long)hi << 32) | lo)) +
+                       ds_lane;
+    __builtin_nontemporal_store(ds_pend[0], reinterpret_cast<u32x4*>(p));
+    __builtin_nontemporal_store(ds_pend[1], reinterpret_cast<u32x4*>(p + 1024));
+    __builtin_nontemporal_store(ds_pend[2], reinterpret_cast<u32x4*>(p + 2048));
+    __builtin_nontemporal_store(ds_pend[3], reinterpret_cast<u32x4*>(p + 3072));
   };
   auto deposit = [&](int i) __attribute__((always_inline)) {
     if (tid < 2 * kBQ)
@@ -375,8 +415,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
     wait_tr(g);
     mfma_tr(g, p1);
   };
-  // wave B, the tile in buffer bf: the same order with dP, dS, dK
-  auto tile_b = [&](auto bf) __attribute__((always_inline)) {
+  // wave B, the tile in buffer bf: the same order with dP, dS, dK (with
+  // stored dS, the tile's dS is kept for store_ds, and the previous tile's,
+  // ps >= 0, is stored after the dP products)
+  auto tile_b = [&](auto bf, int ps) __attribute__((always_inline)) {
     u32x4 f[KT], g[DB][2], x0[6], x1[6];
     bf16x8 d0[2], d1[2];
     read_rows(I0{}, bf, f);
@@ -387,13 +429,24 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
     read_rows(I1{}, bf, f);
     wait_rows(f);
     const f32x16 dp1 = mfma_rows(f);
+    if constexpr (DS) {
+      if (ps >= 0) store_ds(ps);
+    }
     grads(dp0, x0, d0);
+    if constexpr (DS) {
+      ds_pend[0] = as_u32x4(d0[0]);
+      ds_pend[1] = as_u32x4(d0[1]);
+    }
     read_tr(I0{}, bf, g);
     read_x(I1{}, bf, x1);
     wait_tr(g);
     wait_x(x1);
     mfma_tr(g, d0);
     grads(dp1, x1, d1);
+    if constexpr (DS) {
+      ds_pend[2] = as_u32x4(d1[0]);
+      ds_pend[3] = as_u32x4(d1[1]);
+    }
     read_tr(I1{}, bf, g);
     wait_tr(g);
     mfma_tr(g, d1);
@@ -405,7 +458,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
     if (role_a) {
       if (i < i_hi) tile_a(masked_tag, bfa, i);
     } else if (i > i_lo) {
-      tile_b(bfb);
+      tile_b(bfb, i - 1 > i_lo ? i - 2 : -1);
     }
     wait_vmem();
     if (i + 1 < i_hi) deposit(i + 1);
@@ -426,6 +479,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   }
   for (; i < b_end; ++i) iter(std::false_type{}, i, bfr(i), bfr(i - 1));
   for (; i <= i_hi; ++i) iter(std::true_type{}, i, bfr(i), bfr(i - 1));
+  if constexpr (DS) {
+    if (!role_a && i_hi > i_lo) store_ds(i_hi - 1);  // the last tile's dS
+  }
 
   if (key < Nk) {
     float* part = role_a ? dv_part : dk_part;
@@ -455,10 +511,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   }
 }
 
-template <int D, bool PARTIAL, bool DENSE>
+template <int D, bool PARTIAL, bool DENSE, bool DS>
 __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
                                                                              float* __restrict__ dv_part) {
-  bwd_dkdv_body<D, PARTIAL, DENSE>(a, dk_part, dv_part, wg_number(), gridDim.x, gridDim.y);
+  bwd_dkdv_body<D, PARTIAL, DENSE, DS>(a, dk_part, dv_part, wg_number(), gridDim.x, gridDim.y);
 }
 
 // Independent block-backward calls in one launch (a ring step's calls that
@@ -476,7 +532,8 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_group_kernel(Bwd
   const unsigned lin = wg_number();
   const unsigned per_call = gridDim.x * gridDim.y * (unsigned)B;
   const unsigned c = lin / per_call;
-  bwd_dkdv_body<D, PARTIAL, true>(g.a[c], g.dk_part[c], g.dv_part[c], lin - c * per_call, gridDim.x, gridDim.y);
+  bwd_dkdv_body<D, PARTIAL, true, false>(g.a[c], g.dk_part[c], g.dv_part[c], lin - c * per_call, gridDim.x,
+                                         gridDim.y);
 }
 
 // dK[b, kvh] = sum over the query ranges that wrote a partial for the key's
@@ -850,6 +907,156 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_group_kernel(BwdGroup
 }
 
 // ---------------------------------------------------------------------------
+// dQ = scale dS K from the dS^T blocks the dK/dV pass stored (the dQ pass
+// without its two recomputed products).  A workgroup owns 256 query rows (4
+// query tiles) of one query head, 8 waves of 32 rows each, and walks the key
+// tiles its rows see: per key tile, the K tile and the 4 dS^T blocks of its
+// query tiles arrive by direct loads (three LDS buffers, two tiles ahead,
+// one barrier per tile), and each wave adds dQ^T += K^T dS^T for its rows,
+// both operands through the transposing LDS read (A: K^T, 32 head dims x 16
+// keys; B: dS^T, 16 keys x 32 query rows).  Bound by reading dS from HBM.
+// ---------------------------------------------------------------------------
+constexpr int kDsWaves = 8;
+
+template <int D, bool DENSE>
+__global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, int n_groups) {
+  using T = SwzTile<D>;   // K tiles, read transposed only
+  using S = SwzTile<64>;  // dS^T blocks: 64 key rows x 64 query columns
+  constexpr int DB = D / 32;
+  constexpr int STAGE = T::BYTES + 4 * S::BYTES;
+  constexpr int NL = T::LOADS / kDsWaves + 4;  // direct loads per wave and stage
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, grp = lane >> 5;
+  const unsigned lin = wg_number();
+  const unsigned lxy = __builtin_amdgcn_readfirstlane(lin / gridDim.x);
+  const int h = (int)__builtin_amdgcn_readfirstlane(lxy % gridDim.y);
+  const long long bz = __builtin_amdgcn_readfirstlane(lxy / gridDim.y);
+  // query group g: tiles 4 g .. 4 g + 3, longest rows first
+  const int g = n_groups - 1 - (int)__builtin_amdgcn_readfirstlane(lin - lxy * gridDim.x);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const long long Nq = a.Nq, Nk = a.Nk;
+  const long long nqt = (Nq + 63) / 64, nkt = (Nk + 63) / 64, nkt2 = (Nk + 127) / 128 * 2;
+  const int kvh = h / a.G;
+  // key tiles a query tile's rows see (and its stored row holds)
+  auto kt_end = [&](long long qt) __attribute__((always_inline)) {
+    return min(nkt, a.causal ? 2 * (qt >> 1) + 2 : nkt2);
+  };
+  const long long qt0 = 4LL * g;
+  const int n_kt = (int)kt_end(min(qt0 + 3, nqt - 1));
+  const long long qt_w = qt0 + (wave_s >> 1);  // this wave's query tile; rows 32 (wave % 2) ..
+  const int n_kt_w = qt_w < nqt ? (int)kt_end(qt_w) : 0;
+  const uint16_t* kbase = DENSE ? a.k + (bz * a.Hkv + kvh) * Nk * D : a.k + bz * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* dsh = a.ds + (bz * a.Hq + h) * a.ds_head;
+
+  typename T::template AsyncLoader<kDsWaves> kld;
+  kld.init(wave, lane, true, DENSE ? D : a.ks[2]);
+  // a dS^T block into LDS as a row-major tile (64 key rows of 8 units of 8
+  // query columns, units XOR-swizzled per row as S::off_rows): wave w fills
+  // LDS bytes [w KiB, w KiB + 1 KiB), lane i its 16 bytes at 16 i, i.e. row
+  // r = 8 w + i / 8, LDS unit i % 8, which holds query unit uq = (i % 8) ^
+  // swz(r); in the stored order that unit of key r = 32 kh + c is unit
+  // (kh * 4 + uq / 2) * 64 + (uq % 2) * 32 + c
+  unsigned s_goff;
+  {
+    const int slot = wave * 64 + lane, r = slot >> 3;
+    const int uq = (slot & 7) ^ S::swz_rows(r);
+    s_goff = (unsigned)((((r >> 5) * 4 + (uq >> 1)) * 64 + (uq & 1) * 32 + (r & 31)) * 16);
+  }
+  // stage kt into buffer st: the K tile and the four dS^T blocks (a query
+  // tile past the last, or whose row ends before kt, loads a block of its
+  // row that it then ignores: every wave issues NL loads per stage)
+  auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+    unsigned char* buf = smem + st * STAGE;
+    kld.load(buf, kbase, (long long)kt * 64, Nk, wave_s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long long qt = min(qt0 + j, nqt - 1);
+      const long long kb = min((long long)kt, kt_end(qt) - 1);
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(
+          dsh + (bwd_ds_row_start(qt, a.causal, nkt2) + kb) * kDsBlockElems);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + s_goff),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(buf + T::BYTES + j * S::BYTES) + wave_s * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+  const unsigned lds0 = (unsigned)reinterpret_cast<uintptr_t>(smem);
+  unsigned koff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) koff[db] = lds0 + T::tr_off(lane, db);
+  const unsigned soff = lds0 + T::BYTES + (wave >> 1) * S::BYTES + S::tr_off(lane, wave & 1);
+
+  issue(0, 0);
+  if (n_kt > 1) issue(1, 1);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int st = kt % 3;
+    if (kt + 1 < n_kt) wait_vmem_n<NL>();  // stage kt has landed (kt + 1 may be in flight)
+    else wait_vmem();
+    // every wave's part of stage kt is in LDS, and every wave's reads of the
+    // buffer the next issue overwrites (stage kt - 1, waited for before its
+    // products) are done: a plain barrier, no fence that would also wait for
+    // stage kt + 1
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < n_kt) issue(kt + 2, (kt + 2) % 3);
+    if (kt < n_kt_w) {
+      const unsigned sh = (unsigned)(st * STAGE);
+      u32x4 fb[4], fa[4][DB];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) fb[ks] = tr_frag_asm_at<S::ROW_BYTES>(soff + sh, ks * 16 * S::ROW_BYTES);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) fa[ks][db] = tr_frag_asm_at<T::ROW_BYTES>(koff[db] + sh, ks * 16 * T::ROW_BYTES);
+      lds_wait_frags(fb[0], fb[1], fb[2], fb[3]);
+      if (!a.causal && kt == nkt - 1) {
+        // keys past Nk in the last tile: their stored dS is not masked, and
+        // their K rows repeat row Nk - 1
+        const int lim = (int)(Nk - (long long)kt * 64);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int k0 = 16 * ks + 8 * grp + 2 * w;  // keys k0 (low half), k0 + 1 (high half)
+            fb[ks][w] &= (k0 < lim ? 0x0000FFFFu : 0u) | (k0 + 1 < lim ? 0xFFFF0000u : 0u);
+          }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (DB == 4) {
+          lds_wait_frags(fa[ks][0], fa[ks][1], fa[ks][2], fa[ks][3]);
+        } else {
+          lds_wait_frags2(fa[ks][0], fa[ks][1]);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16(as_bf16x8(fa[ks][db]), as_bf16x8(fb[ks]), acc[db]);
+      }
+    }
+  }
+
+  const long long qrow = qt_w * 64 + 32 * (wave & 1) + c;
+  if (qt_w < nqt && qrow < Nq) {
+    const long long obf = DENSE ? ((bz * a.Hq + h) * Nq + qrow) * D : bz * a.qs[0] + h * a.qs[1] + qrow * a.qs[2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = db * 32 + 8 * jj + 4 * grp;
+        *reinterpret_cast<u32x2*>(a.dq + obf + d) =
+            pack_bf16x4_bits(acc[db][4 * jj] * a.scale, acc[db][4 * jj + 1] * a.scale, acc[db][4 * jj + 2] * a.scale,
+                             acc[db][4 * jj + 3] * a.scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Small problems: the dQ pass beside the dK/dV pass.  Both read only the
 // inputs and Dv and write disjoint outputs, so when the dK/dV grid would not
 // fill the GPU twice over, the dQ pass runs on a side stream of the library's
@@ -965,7 +1172,9 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
   hipError_t e;
   BwdArgs a = a0;
   a.B = B;
-  const BwdSplit sp = split ? bwd_split_plan(B, a.Hq, a.Hkv, a.Nq, a.Nk, D) : BwdSplit{};
+  // stored dS: the dQ pass becomes the product pass after dK/dV (unsplit)
+  const bool ds = a.ds != nullptr;
+  const BwdSplit sp = split && !ds ? bwd_split_plan(B, a.Hq, a.Hkv, a.Nq, a.Nk, D) : BwdSplit{};
   a.rkv = sp.rkv;
   a.qst = sp.qst;
   a.rq = sp.rq;
@@ -993,11 +1202,16 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
     e = launch_delta<D>(a.o, a.d_o, a.delta, B, a.Hq, a.Nq, a.qs, stream);
     if (e != hipSuccess) return e;
   }
+  const int n_groups = (int)((a.Nq + 255) / 256);
+  const dim3 sgrid((unsigned)n_groups, (unsigned)a.Hq, (unsigned)B);
+  if (ds && !grid_fits(sgrid)) return hipErrorInvalidConfiguration;
   DqStream dqs;
-  if ((e = dqs.begin(stream, allow_side, (long long)kgrid.x * kgrid.y * B)) != hipSuccess) return e;
+  if ((e = dqs.begin(stream, allow_side && !ds, (long long)kgrid.x * kgrid.y * B)) != hipSuccess) return e;
   const hipStream_t qstream = dqs.stream();
   // the dQ pass first: on the side stream it then runs beside the dK/dV pass
-  if (dense) {
+  if (ds) {
+    // after the dK/dV pass, below
+  } else if (dense) {
     if (HP == 4)
       LCATTN_LAUNCH("bwd_dq_kernel", (bwd_dq_kernel<D, 4, true>), grid, dim3(64 * kDqWaves), 0, qstream, a, n_qt);
     else if (HP == 2)
@@ -1014,7 +1228,7 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.rq > 1) {
+  if (!ds && a.rq > 1) {
     const long long slots = (long long)B * a.Hq * a.Nq * D / 4;
     LCATTN_LAUNCH("bwd_dq_reduce_kernel", (bwd_dq_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)), dim3(256),
                   0, qstream, a, (int)span, dense);
@@ -1026,29 +1240,41 @@ hipError_t launch_d(const BwdArgs& a0, int B, hipStream_t stream, bool allow_sid
     float* dk_part = partial ? a.part : nullptr;
     float* dv_part = partial ? dk_part + (long long)a.rkv * B * a.Hq * a.Nk * D : nullptr;
     const dim3 blk(64 * kSplitWaves);
+#define LCATTN_DKDV(P, DN)                                                                                        \
+  do {                                                                                                            \
+    if (ds)                                                                                                       \
+      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, P, DN, true>), kgrid, blk, 0, stream, a, dk_part, \
+                    dv_part);                                                                                     \
+    else                                                                                                          \
+      LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, P, DN, false>), kgrid, blk, 0, stream, a,         \
+                    dk_part, dv_part);                                                                            \
+  } while (0)
     if (!partial) {
-      if (dense)
-        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, false, true>), kgrid, blk, 0, stream, a, dk_part,
-                      dv_part);
-      else
-        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, false, false>), kgrid, blk, 0, stream, a, dk_part,
-                      dv_part);
+      if (dense) LCATTN_DKDV(false, true);
+      else LCATTN_DKDV(false, false);
     } else {
-      if (dense)
-        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, true, true>), kgrid, blk, 0, stream, a, dk_part,
-                      dv_part);
-      else
-        LCATTN_LAUNCH("bwd_dkdv_kernel", (bwd_dkdv_split_kernel<D, true, false>), kgrid, blk, 0, stream, a, dk_part,
-                      dv_part);
+      if (dense) LCATTN_DKDV(true, true);
+      else LCATTN_DKDV(true, false);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       const long long slots = (long long)B * a.Hkv * a.Nk * D / 4;
       LCATTN_LAUNCH("bwd_dkdv_reduce_kernel", (bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((slots + 255) / 256)),
                     dim3(256), 0, stream, a, dk_part, dv_part, (long long)B * a.Hkv, dense);
     }
+#undef LCATTN_DKDV
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ds) {
+    if (dense)
+      LCATTN_LAUNCH("bwd_dq_ds_kernel", (bwd_dq_ds_kernel<D, true>), sgrid, dim3(64 * kDsWaves), 0, stream, a,
+                    n_groups);
+    else
+      LCATTN_LAUNCH("bwd_dq_ds_kernel", (bwd_dq_ds_kernel<D, false>), sgrid, dim3(64 * kDsWaves), 0, stream, a,
+                    n_groups);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return dqs.end();
 }
 

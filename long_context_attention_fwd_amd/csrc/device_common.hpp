@@ -307,6 +307,14 @@ __device__ __forceinline__ void lds_wait_frags2(u32x4& a, u32x4& b) {
 // [6:4], lgkmcnt in [11:8]; 0x0F70 = vmcnt(0) with the other counters free.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's global loads are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt values above 15 need the high field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // XCD-aware workgroup order.  The 8 XCDs of the chip take workgroups
 // round-robin by linear id, and each has its own L2.  Within every round of
 // 8 x 32 ids, XCD x is given 32 consecutive logical workgroups (neighbours

@@ -172,7 +172,24 @@ struct BwdArgs {
   int rkv = 1, qst = 1 << 30;
   int rq = 1, kst = 1 << 30;
   float* dq_part = nullptr;
+  // dQ as a product of stored dS (attn_bwd given the larger workspace): the
+  // dK/dV pass also writes dS^T in blocks (layout at bwd_ds_row_start) at ds,
+  // ds_head elements per (batch, query head), and a product pass forms
+  // dQ = scale dS K from them; null: the dQ pass recomputes S and dP
+  uint16_t* ds = nullptr;
+  long long ds_head = 0;
 };
+
+// Stored dS: per (batch, query head), dS^T in blocks of 64 keys x 64 query
+// rows (bf16, row-major [key][query], kDsBlockElems elements).  Query tile qt
+// (rows 64 qt ..) has a row of blocks for key tiles [0, len(qt)): causal
+// (Nq = Nk, no offset), len = 2 (qt / 2) + 2, the key-tile pairs of the dK/dV
+// workgroups that see the tile; otherwise every key tile, rounded up to pairs
+// (nkt2).  Rows follow one another: row qt starts at block bwd_ds_row_start.
+constexpr long long kDsBlockElems = 64 * 64;
+constexpr long long bwd_ds_row_start(long long qt, int causal, long long nkt2) {
+  return causal ? 2 * (qt >> 1) * ((qt >> 1) + 1) + (qt & 1) * (2 * (qt >> 1) + 2) : qt * nkt2;
+}
 
 // How a small backward problem splits its passes (one per call shape): the
 // dK/dV pass over rkv query ranges of qst 64-row tiles, the dQ pass over rq
@@ -193,6 +210,14 @@ long long bwd_part_floats(int B, int Hq, int Hkv, long long Nk, int D);
 long long bwd_split_part_floats(int B, int Hq, int Hkv, long long Nk, int D, const BwdSplit& s);
 long long bwd_split_dq_floats(int B, int Hq, long long Nq, int D, const BwdSplit& s);
 long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
+// attn_bwd's workspace with room for stored dS: the workspace above, padded
+// to 256 bytes (bwd_ds_offset_bytes, where the blocks start), then the blocks
+// (bwd_ds_head_elems per batch and query head).  0 for small problems (a
+// dK/dV grid below 256 workgroups), which keep the recomputing dQ pass
+// beside the dK/dV pass.
+long long bwd_ds_head_elems(long long N, int causal);
+long long bwd_ds_offset_bytes(int B, int Hq, int Hkv, long long N, int D);
+long long bwd_ds_workspace_bytes(int B, int Hq, int Hkv, long long N, int D, int causal);
 
 // allow_side: a problem whose dK/dV grid has fewer than two workgroups per
 // compute unit runs its dQ pass on the library's side stream of the device

@@ -62,6 +62,22 @@ long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk
           bwd_split_dq_floats(B, Hq, Nq, D, s)) * 4;
 }
 
+long long bwd_ds_head_elems(long long N, int causal) {
+  const long long nqt = (N + 63) / 64, nkt2 = (N + 127) / 128 * 2;
+  return bwd_ds_row_start(nqt, causal, nkt2) * kDsBlockElems;
+}
+
+long long bwd_ds_offset_bytes(int B, int Hq, int Hkv, long long N, int D) {
+  return (bwd_workspace_bytes(B, Hq, Hkv, N, N, D) + 255) / 256 * 256;
+}
+
+long long bwd_ds_workspace_bytes(int B, int Hq, int Hkv, long long N, int D, int causal) {
+  // a dK/dV grid below one workgroup per compute unit (the small problems
+  // whose passes are split and run side by side) keeps the dQ pass
+  if ((long long)B * Hq * ((N + 127) / 128) < 256) return 0;
+  return bwd_ds_offset_bytes(B, Hq, Hkv, N, D) + 2LL * B * Hq * bwd_ds_head_elems(N, causal);
+}
+
 int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits) {
   if (n_splits > 0) return n_splits;
   const int G = Hq / Hkv;

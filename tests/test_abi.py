@@ -36,7 +36,7 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fwd_strided", "attn_fwd_accumulate", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size", "attn_bwd",
-              "attn_bwd_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
+              "attn_bwd_workspace_size", "attn_bwd_ds_workspace_size", "attn_bwd_delta", "attn_bwd_block", "attn_bwd_block_workspace_size",
               "attn_partial_merge", "head_to_seq_reduce",
               "attn_bwd_strided", "attn_bwd_noalloc", "attn_bwd_block_group", "attn_bwd_noalloc_max_scratch", "attn_fwd_accumulate_group", "attn_fwd_accumulate_group_split",
               "attn_fwd_accumulate_workspace_size", "attn_fwd_split_suggest", "seq_to_head_relayout", "head_to_seq_relayout", "seq_to_head_relayout_batch",
@@ -254,6 +254,48 @@ def test_bwd_workspace_size(L):
     assert L.attn_bwd_workspace_size(1, 4, 4, 4096, 64) == (2 * 4 + 8) * 4 * 4096 * 64 * 4 + 4 * 4096 * 4
     assert L.attn_bwd_workspace_size(1, 8, 3, 1024, 128) == 0
     assert L.attn_bwd_workspace_size(0, 8, 8, 1024, 128) == 0
+
+
+def test_bwd_ds_workspace_size(L):
+    # the 64K training shape: Dv (8 heads x 65536 rows, fp32) then, for each
+    # head, the dS blocks at or left of the diagonal in pairs of key tiles:
+    # query tile qt (of 1024) has 2 (qt // 2) + 2 blocks of 64 x 64 bf16
+    blocks = sum(2 * (qt // 2) + 2 for qt in range(1024))
+    assert blocks == 2 * 512 * 513
+    assert L.attn_bwd_ds_workspace_size(1, 8, 8, 65536, 128, 1) == 8 * 65536 * 4 + 8 * blocks * 8192
+    # without the mask every block of the 1024 x 1024 grid
+    assert L.attn_bwd_ds_workspace_size(1, 8, 8, 65536, 128, 0) == 8 * 65536 * 4 + 8 * 1024 * 1024 * 8192
+    # grouped heads: the per-query-head dK, dV partials sit before the blocks
+    # (Dv 4 x 32768 floats, partials 2 x 4 x 32768 x 128 floats)
+    blocks = sum(2 * (qt // 2) + 2 for qt in range(512))
+    assert L.attn_bwd_ds_workspace_size(1, 4, 1, 32768, 128, 1) == (4 * 32768 + 2 * 4 * 32768 * 128) * 4 + \
+        4 * blocks * 8192
+    # ragged N: an odd number of query tiles (33), rows of key-tile pairs;
+    # the first part padded to 256 bytes (Dv of 2 x 8 x 2100 rows, 64-float padded)
+    first = (2 * 8 * 2100 + 63) // 64 * 64 * 4
+    first = (first + 255) // 256 * 256
+    assert L.attn_bwd_ds_workspace_size(2, 8, 8, 2100, 64, 1) == first + 2 * 8 * sum(2 * (qt // 2) + 2 for qt in
+                                                                                    range(33)) * 8192
+    # small problems (fewer than 256 dK/dV workgroups) have no such path
+    assert L.attn_bwd_ds_workspace_size(1, 4, 4, 4096, 64, 1) == 0
+    assert L.attn_bwd_ds_workspace_size(1, 8, 8, 4096, 128, 1) > 0  # 8 x 32 workgroups
+    assert L.attn_bwd_ds_workspace_size(1, 8, 8, 3968, 128, 1) == 0  # 8 x 31
+    assert L.attn_bwd_ds_workspace_size(1, 8, 3, 65536, 128, 1) == 0
+    assert L.attn_bwd_ds_workspace_size(1, 8, 8, 65536, 96, 1) == 0
+
+
+def test_bwd_ds_workspace_selects_path(L):
+    """A workspace between the two sizes is accepted (recomputing path); one
+    below the minimum is refused."""
+    need = L.attn_bwd_workspace_size(1, 8, 8, 4096, 128)
+    big = L.attn_bwd_ds_workspace_size(1, 8, 8, 4096, 128, 1)
+    assert big > need > 0
+    n = 1 << 24
+    common = (A, A + n, A + 2 * n, A + 3 * n, A + 4 * n, A + 5 * n, A + 6 * n, A + 7 * n, A + 8 * n, A + 9 * n)
+    # null stream pointer on a machine without a GPU: validation runs first,
+    # so a too-small workspace is reported before any launch
+    rc = L.attn_bwd(*common, need - 16, 1, 8, 8, 4096, 128, 0.088, 1, None)
+    assert rc == 6  # ATTN_ERR_WORKSPACE
 
 
 def bwd(L, **kw):

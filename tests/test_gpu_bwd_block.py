@@ -114,13 +114,16 @@ def test_single_block_is_attn_bwd_bit_for_bit(gpu, G):
     """One block over the whole sequence with bf16 outputs runs attn_bwd's
     kernels on the same values.  The shape gives the dK/dV pass 256 or more
     workgroups, so attn_bwd does not split its passes into ranges (a split
-    sums the same terms in another grouping: see the next test)."""
+    sums the same terms in another grouping: see the next test); its minimal
+    workspace keeps the recomputing dQ pass (with room for the stored dS,
+    dK and dV are the same bits and dq agrees to rounding: the stored-dS
+    tests)."""
     import torch
     d = make_qkv(2, 2 * G, 2, 8192 - 57, 128, seed=41 + G, with_do=True)
     s = sdpa_scale(128)
     q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
     o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
-    dq0, dk0, dv0 = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s)
+    dq0, dk0, dv0 = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s, stored_ds=False)
     delta = lc.attn_bwd_delta(o, do)
     dq1, dk1, dv1 = lc.attn_bwd_block(q, k, v, do, lse, delta, causal=True, scale=s)
     torch.cuda.synchronize()

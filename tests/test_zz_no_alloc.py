@@ -30,7 +30,9 @@ def test_bwd_noalloc_matches_attn_bwd(gpu):
         q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
         s = float(np.float32(1.0 / math.sqrt(D)))
         o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
-        ref = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s)
+        # attn_bwd with its minimal workspace (the recomputing dQ pass, the
+        # kernels the allocation-free form runs)
+        ref = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s, stored_ds=False)
         got = tuple(poisoned(tuple(t.shape), torch.bfloat16) for t in (q, k, v))
         lc.attn_bwd_noalloc(q, k, v, o, do, lse, causal=True, scale=s, dq=got[0], dk=got[1], dv=got[2])
         torch.cuda.synchronize()
