@@ -183,7 +183,8 @@ def test_bwd_train_64k_full_do(gpu):
     rows and dK, dV at the key rows with the same 128 indices, against the
     oracle with its own fp64 LSE and Dv for every query row (each sampled key
     row is reached by its own query row and every later one, up to 65536
-    terms per element of dK and dV)."""
+    terms per element of dK and dV).  Both dQ paths: the product of the
+    stored dS and the recomputing pass."""
     import time
     import torch
     from gpu_util import oracle_full_lse_delta
@@ -193,9 +194,15 @@ def test_bwd_train_64k_full_do(gpu):
     rows = sample_rows(w.N, w.seed, w.sampled_rows)
     idx = torch.from_numpy(rows).cuda()
     q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
-    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s)
+    o, lse, dq, dk, dv = gpu_fwd_bwd(q, k, v, do, s)  # dq from the stored dS (the binding's default here)
     got = (f64_of(dq[:, :, idx]), f64_of(dk[:, :, idx]), f64_of(dv[:, :, idx]))
-    del q, k, v, do, o, lse, dq, dk, dv
+    # the recomputing dQ pass on the same values: dK, dV the same bits
+    dq_r, dk_r, dv_r = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s, stored_ds=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dk.view(torch.int16), dk_r.view(torch.int16))
+    assert torch.equal(dv.view(torch.int16), dv_r.view(torch.int16))
+    got_dq_r = f64_of(dq_r[:, :, idx])
+    del q, k, v, do, o, lse, dq, dk, dv, dq_r, dk_r, dv_r
     f = {n: oracle.bf16_bits_to_f64(d[n]) for n in ("q", "k", "v", "do")}
     t0 = time.perf_counter()
     L, Dv = oracle_full_lse_delta(f["q"], f["k"], f["v"], f["do"], s)
@@ -203,8 +210,8 @@ def test_bwd_train_64k_full_do(gpu):
     rq, rk, rv = oracle.attention_backward_sampled(f["q"], f["k"], f["v"], f["do"], s, rows, rows, True,
                                                    lse=L, dv=Dv)
     print(f"oracle: full fp64 LSE/Dv {t1 - t0:.1f} s, sampled gradients {time.perf_counter() - t1:.1f} s")
-    errs = [grad_rel_err(g, r) for g, r in zip(got, (rq, rk, rv))]
-    assert all(np.isfinite(g).all() for g in got)
+    errs = [grad_rel_err(g, r) for g, r in zip(got + (got_dq_r,), (rq, rk, rv, rq))]
+    assert all(np.isfinite(g).all() for g in got + (got_dq_r,))
     assert max(errs) <= GRAD_REL_TOL, errs
 
 
@@ -224,13 +231,18 @@ def test_bwd_ulysses_shard_32k_full_do(gpu):
     idx = torch.from_numpy(rows).cuda()
     o, lse = lc.attn_fwd(heads["q"], heads["k"], heads["v"], causal=True, scale=w.scale)
     dq, dk, dv = lc.attn_bwd(heads["q"], heads["k"], heads["v"], o, heads["do"], lse, causal=True, scale=w.scale)
+    # the recomputing dQ pass on the same values (the call above took the stored dS)
+    dq_r, dk_r, dv_r = lc.attn_bwd(heads["q"], heads["k"], heads["v"], o, heads["do"], lse, causal=True,
+                                   scale=w.scale, stored_ds=False)
     torch.cuda.synchronize()
-    got = (f64_of(dq[:, :, idx]), f64_of(dk[:, :, idx]), f64_of(dv[:, :, idx]))
+    assert torch.equal(dk.view(torch.int16), dk_r.view(torch.int16))
+    assert torch.equal(dv.view(torch.int16), dv_r.view(torch.int16))
+    got = (f64_of(dq[:, :, idx]), f64_of(dk[:, :, idx]), f64_of(dv[:, :, idx]), f64_of(dq_r[:, :, idx]))
     f = {n: oracle.bf16_bits_to_f64(oracle.seq_to_head(d[n], w.P)[0:1]) for n in ("q", "k", "v", "do")}
     L, Dv = oracle_full_lse_delta(f["q"], f["k"], f["v"], f["do"], w.scale)
     rq, rk, rv = oracle.attention_backward_sampled(f["q"], f["k"], f["v"], f["do"], w.scale, rows, rows, True,
                                                    lse=L, dv=Dv)
-    errs = [grad_rel_err(g, r) for g, r in zip(got, (rq, rk, rv))]
+    errs = [grad_rel_err(g, r) for g, r in zip(got, (rq, rk, rv, rq))]
     assert all(np.isfinite(g).all() for g in got)
     assert max(errs) <= GRAD_REL_TOL, errs
 
