@@ -622,10 +622,12 @@ def shard_extras(lc, torch, dev, w, xs, heads, o, dq, dk, dv, lse, o_parts, lse_
     lc.attn_fwd(q0, k0, v0, causal=True, scale=scale, o=o, lse=lse)
     dq_acc = o_parts[1]
     delta = torch.empty_like(lse)
-    ws_blk = torch.empty(max(16, lc.attn_bwd_block_workspace_size(1, hq, hkv, blk, D)), dtype=torch.uint8,
+    ws_min = torch.empty(max(16, lc.attn_bwd_block_workspace_size(1, hq, hkv, blk, D)), dtype=torch.uint8,
                          device=dev)
+    big = lc.attn_bwd_block_ds_workspace_size(1, hq, hkv, N, blk, D)
+    ws_ds = torch.empty(big, dtype=torch.uint8, device=dev) if 0 < big <= lc.STORED_DS_AUTO_BYTES else None
 
-    def ring_backward():
+    def ring_backward(ws_blk):
         lc.attn_bwd_delta(o, do0, delta=delta)
         for i, a in enumerate(range(0, N, blk)):
             lc.attn_bwd_block(q0, k0[:, :, a:a + blk], v0[:, :, a:a + blk], do0, lse, delta, causal=True,
@@ -633,7 +635,13 @@ def shard_extras(lc, torch, dev, w, xs, heads, o, dq, dk, dv, lse, o_parts, lse_
                               dq=dq if a + blk >= N else None, dk=dk[:, :, a:a + blk], dv=dv[:, :, a:a + blk],
                               workspace=ws_blk)
     out["ring_backward"] = {"call": "attn_bwd_delta + 4 x attn_bwd_block (fp32 dQ accumulated)",
-                            **r(time_calls(torch, ring_backward), 2.5 * f_ring)}
+                            "dq_path": "product of the stored dS" if ws_ds is not None else "recomputing dQ pass",
+                            **r(time_calls(torch, lambda: ring_backward(ws_ds if ws_ds is not None else ws_min)),
+                                2.5 * f_ring)}
+    if ws_ds is not None:
+        out["ring_backward_recomputing_dq"] = {"call": "the same with the minimal workspace",
+                                               **r(time_calls(torch, lambda: ring_backward(ws_min)), 2.5 * f_ring)}
+        del ws_ds
     out["ring_sharding"] = ring_sharding(lc, torch, dev, heads, hq, N, D, scale, f_fwd, o, lse)
     return out
 

@@ -373,6 +373,21 @@ int attn_bwd_delta(const void* o, const void* d_o, float* delta, int B, int Hq, 
 size_t attn_bwd_block_workspace_size(int B, int Hq, int Hkv, int64_t Nk, int D);
 
 /*
+ * attn_bwd_block_ds_workspace_size -- bytes of workspace with which
+ * attn_bwd_block forms dq from stored dS, as attn_bwd does with
+ * attn_bwd_ds_workspace_size: the dK/dV pass also writes the dS it forms, in
+ * 64 x 64 bf16 blocks, and a product pass adds scale dS K to dq (or dq_acc).
+ * Layout: attn_bwd_block_workspace_size bytes rounded up to 256, then, per
+ * batch and query head, ceil(Nq / 64) rows of 2 ceil(Nk / 128) blocks (the
+ * position offsets make the causal rows irregular, so every row has room for
+ * every block; only the blocks a row sees are written and read).  Returns 0
+ * (path not available) for invalid sizes and for fewer than 256 dK/dV
+ * workgroups (B * Hq * ceil(Nk / 128) < 256).  attn_bwd_block_group keeps the
+ * recomputing pass.
+ */
+size_t attn_bwd_block_ds_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D);
+
+/*
  * attn_bwd_block -- the backward of one ring step: the gradients that flow
  * through one KV block's part of the attention of q ("So funktioniert
  * Kontextparallelität" on the "Context Parallelism" glossary page: each
@@ -401,9 +416,11 @@ size_t attn_bwd_block_workspace_size(int B, int Hq, int Hkv, int64_t Nk, int D);
  *     shards); dk, dv [B, Hkv, Nk, D] bf16: rounded copies.
  * Keys that no query sees get zero gradients.  Requires Nq, Nk < 2^30;
  * workspace >= attn_bwd_block_workspace_size bytes (may be null when that
- * is 0; contents unspecified on return); outputs must not overlap inputs or
- * one another.  Calls accumulating into the same buffers must be ordered
- * (one stream).  Deterministic.  Otherwise as attn_bwd.
+ * is 0; contents unspecified on return); with at least
+ * attn_bwd_block_ds_workspace_size bytes (nonzero) dq comes from stored dS
+ * (dk, dv the same bits; dq agrees to rounding).  Outputs must not overlap
+ * inputs or one another.  Calls accumulating into the same buffers must be
+ * ordered (one stream).  Deterministic.  Otherwise as attn_bwd.
  */
 int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o, const float* lse,
                    const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
@@ -423,7 +440,9 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
  * attn_bwd_block mean; B, Hq, Hkv, D, scale and causal are shared.  Every call
  * is validated as attn_bwd_block (errors name the call); in addition no call
  * may write what another call reads or writes (ATTN_ERR_ALIAS).  Results are
- * bit-identical to the same calls made one at a time.  Requires 1 <= n <=
+ * bit-identical to the same calls made one at a time with the recomputing dQ
+ * pass (a workspace below attn_bwd_block_ds_workspace_size; a group call's
+ * workspace may be larger, it is not used for stored dS).  Requires 1 <= n <=
  * ATTN_MAX_BWD_GROUP and B * n <= 65535.
  */
 #define ATTN_MAX_BWD_GROUP 4

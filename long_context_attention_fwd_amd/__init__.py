@@ -38,6 +38,7 @@ __all__ = [
     "attn_bwd_block",
     "attn_bwd_block_group",
     "attn_bwd_block_workspace_size",
+    "attn_bwd_block_ds_workspace_size",
     "seq_to_head_relayout",
     "head_to_seq_relayout",
     "seq_to_head_relayout_batch",
@@ -122,6 +123,7 @@ _SIGS = {
                               _P, _P, _P]),
     "head_to_seq_reduce": (_I, [_P, _I, _P, _I, _L, _I, _I, _P]),
     "attn_bwd_block_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _I]),
+    "attn_bwd_block_ds_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _L, _L, _I]),
     "attn_bwd_block_group": (_I, [_P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_block": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                             _I, _I, _I, _L, _L, _I, _F, _I, _L, _L, _I, _I, _P]),
@@ -579,8 +581,14 @@ def attn_bwd_block_workspace_size(B: int, Hq: int, Hkv: int, Nk: int, D: int) ->
     return int(lib().attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D))
 
 
+def attn_bwd_block_ds_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int) -> int:
+    """Workspace bytes with which attn_bwd_block forms dq from stored dS (0:
+    not available for this shape)."""
+    return int(lib().attn_bwd_block_ds_workspace_size(B, Hq, Hkv, Nq, Nk, D))
+
+
 def _bwd_block_prepare(q, k, v, do, lse, delta, q_pos0, k_pos0, dq_acc, dq_accumulate, dk_acc, dv_acc,
-                       dkv_accumulate, dq, dk, dv, workspace):
+                       dkv_accumulate, dq, dk, dv, workspace, stored_ds=False):
     """Checks of one block-backward call; allocates the default outputs and
     workspace.  Returns (BwdBlockCall, (B, Hq, Hkv, D), outputs, workspace):
     the caller holds the workspace until the launch is enqueued, or its memory
@@ -611,6 +619,10 @@ def _bwd_block_prepare(q, k, v, do, lse, delta, q_pos0, k_pos0, dq_acc, dq_accum
         dk = torch.empty_like(k)
         dv = torch.empty_like(v) if dv is None else dv
     need = attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D)
+    if stored_ds is not False:
+        big = attn_bwd_block_ds_workspace_size(B, Hq, Hkv, Nq, Nk, D)
+        if big and (stored_ds is True or big <= STORED_DS_AUTO_BYTES):
+            need = big
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
 
@@ -629,14 +641,16 @@ def _bwd_block_prepare(q, k, v, do, lse, delta, q_pos0, k_pos0, dq_acc, dq_accum
 def attn_bwd_block(q, k, v, do, lse, delta, *, causal: bool = True, scale: float | None = None,
                    q_pos0: int = 0, k_pos0: int = 0, dq_acc=None, dq_accumulate: bool = False,
                    dk_acc=None, dv_acc=None, dkv_accumulate: bool = False, dq=None, dk=None, dv=None,
-                   workspace=None):
+                   workspace=None, stored_ds: bool | None = None):
     """Gradients through one KV block (k, v at global position k_pos0) of the
     attention of q, given the global lse and Dv (attn_bwd_delta).  fp32
     accumulators are overwritten, or added to with the *_accumulate flags;
-    bf16 dq / dk / dv, when given, receive rounded copies.  Returns
+    bf16 dq / dk / dv, when given, receive rounded copies.  The library picks
+    the dq path by the workspace's size; without a workspace one is
+    allocated with room for stored dS as attn_bwd does (stored_ds).  Returns
     (dq_acc or dq, dk_acc or dk, dv_acc or dv)."""
     c, (B, Hq, Hkv, D), outs, ws = _bwd_block_prepare(q, k, v, do, lse, delta, q_pos0, k_pos0, dq_acc, dq_accumulate,
-                                                  dk_acc, dv_acc, dkv_accumulate, dq, dk, dv, workspace)
+                                                  dk_acc, dv_acc, dkv_accumulate, dq, dk, dv, workspace, stored_ds)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib().attn_bwd_block(c.q, c.k, c.v, c.d_o, c.lse, c.delta, c.dq_acc, c.dk_acc, c.dv_acc, c.dq, c.dk, c.dv,
                                 c.workspace, c.workspace_bytes, B, Hq, Hkv, c.Nq, c.Nk, D, scale, 1 if causal else 0,

@@ -638,14 +638,28 @@ size_t attn_bwd_block_workspace_size(int B, int Hq, int Hkv, int64_t Nk, int D) 
   return (size_t)lcattn::bwd_part_floats(B, Hq, Hkv, Nk, D) * 4;
 }
 
+size_t attn_bwd_block_ds_workspace_size(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv || (D != 64 && D != 128)) return 0;
+  int64_t el;
+  if (!elems(&el, {B, Hq, Nk, D}) || el > INT64_MAX / 16) return 0;
+  // the uniform rows: B * Hq * ceil(Nq / 64) * ceil(Nk / 128) * 2 blocks of
+  // 8 KiB (checked against overflow before multiplying out)
+  const double approx = (double)B * Hq * ((double)Nq + 64) * ((double)Nk + 128) * 2.0;
+  if (approx > 9.0e18) return 0;
+  return (size_t)lcattn::bwd_block_ds_workspace_bytes(B, Hq, Hkv, Nq, Nk, D);
+}
+
 // Validation of one block-backward call; fills the kernel arguments and the
-// byte ranges of its inputs (6) and outputs (7, null when absent).
+// byte ranges of its inputs (6) and outputs (7, null when absent).  allow_ds:
+// a workspace of attn_bwd_block_ds_workspace_size bytes selects the stored-dS
+// dQ (single calls; the grouped launch keeps the recomputing pass).
 static int bwd_block_check(const char* name, const void* q, const void* k, const void* v, const void* d_o,
                            const float* lse, const float* delta, float* dq_acc, float* dk_acc, float* dv_acc,
                            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq,
                            int Hkv, int64_t Nq, int64_t Nk, int D, float scale, int causal, int64_t q_pos0,
                            int64_t k_pos0, int dq_accumulate, int dkv_accumulate, lcattn::BwdArgs* args,
-                           const void* (&ins)[6], size_t (&inb)[6], const void* (&outs)[7], size_t (&outb)[7]) {
+                           const void* (&ins)[6], size_t (&inb)[6], const void* (&outs)[7], size_t (&outb)[7],
+                           bool allow_ds = false) {
   if (!q || !k || !v || !d_o || !lse || !delta)
     return fail(ATTN_ERR_NULL, "%s: q, k, v, d_o, lse and delta must be non-null", name);
   if (!dq_acc && !dq) return fail(ATTN_ERR_NULL, "%s: dq_acc or dq must be set", name);
@@ -666,7 +680,10 @@ static int bwd_block_check(const char* name, const void* q, const void* k, const
     return fail(ATTN_ERR_SHAPE, "%s: tensor sizes overflow", name);
   if (Nq >= (int64_t(1) << 30) || Nk >= (int64_t(1) << 30) || B > 65535 || Hq > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: Nq and Nk must be < 2^30, B and Hq <= 65535", name);
-  const size_t need = attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D);
+  const size_t need_min = attn_bwd_block_workspace_size(B, Hq, Hkv, Nk, D);
+  const size_t need_ds = allow_ds ? attn_bwd_block_ds_workspace_size(B, Hq, Hkv, Nq, Nk, D) : 0;
+  const bool use_ds = need_ds != 0 && workspace && workspace_bytes >= need_ds;
+  const size_t need = use_ds ? need_ds : need_min;
   if (need && (!workspace || workspace_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", name, need, workspace_bytes);
   const void* all[13] = {q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, dq, dk, dv, need ? workspace : nullptr};
@@ -719,6 +736,12 @@ static int bwd_block_check(const char* name, const void* q, const void* k, const
   a.dkv_mode = dk_acc ? (dkv_accumulate ? 2 : 1) : 0;
   a.dk_acc = dk_acc;
   a.dv_acc = dv_acc;
+  if (use_ds) {
+    a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                       lcattn::bwd_block_ds_offset_bytes(B, Hq, Hkv, Nk, D));
+    a.ds_head = lcattn::bwd_block_ds_head_elems(Nq, Nk);
+    a.ds_uniform = 1;
+  }
   return ok();
 }
 
@@ -734,7 +757,7 @@ int attn_bwd_block(const void* q, const void* k, const void* v, const void* d_o,
   size_t outb[7];
   const int st = bwd_block_check("attn_bwd_block", q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, dq, dk, dv,
                                  workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, D, scale, causal, q_pos0, k_pos0,
-                                 dq_accumulate, dkv_accumulate, &a, ins, inb, outs, outb);
+                                 dq_accumulate, dkv_accumulate, &a, ins, inb, outs, outb, true);
   if (st != ATTN_OK) return st;
   return hip_status(lcattn::launch_attn_bwd(a, B, D, static_cast<hipStream_t>(hip_stream), true, false),
                     "attn_bwd_block launch");

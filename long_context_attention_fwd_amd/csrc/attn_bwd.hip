@@ -227,7 +227,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   auto store_ds = [&](int i) __attribute__((always_inline)) {
     const long long qt = first_tile + i;
     const unsigned long long off =
-        (unsigned long long)(ds_wave + bwd_ds_row_start(qt, a.causal, ds_nkt2) * kDsBlockElems);
+        (unsigned long long)(ds_wave + bwd_ds_row_start(qt, a.causal && !a.ds_uniform, ds_nkt2) * kDsBlockElems);
     const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(off >> 32));
     const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)off);
     unsigned char* p = reinterpret_cast<unsigned char*>(a.ds + (long long)(((unsigned long long)hi << 32) | lo)) +
@@ -943,12 +943,19 @@ __global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, 
   const long long Nq = a.Nq, Nk = a.Nk;
   const long long nqt = (Nq + 63) / 64, nkt = (Nk + 63) / 64, nkt2 = (Nk + 127) / 128 * 2;
   const int kvh = h / a.G;
-  // key tiles a query tile's rows see (and its stored row holds)
-  auto kt_end = [&](long long qt) __attribute__((always_inline)) {
-    return min(nkt, a.causal ? 2 * (qt >> 1) + 2 : nkt2);
+  const int row_causal = a.causal && !a.ds_uniform;  // compact rows
+  // key tiles whose stored blocks a query tile's row holds: those of the
+  // key-tile pairs whose dK/dV workgroups reach the tile (causal: a pair
+  // starts at query row 128 x - dpos), at most the tiles of Nk
+  auto kt_end = [&](long long qt) __attribute__((always_inline)) -> long long {
+    if (!a.causal) return nkt;
+    const long long L = (Nq < 64 * qt + 64 ? Nq : 64 * qt + 64) + a.dpos;  // pairs x with 128 x < L
+    long long x = L > 0 ? (L + 127) / 128 : 0;
+    x = x < nkt2 / 2 ? x : nkt2 / 2;
+    return 2 * x < nkt ? 2 * x : nkt;
   };
   const long long qt0 = 4LL * g;
-  const int n_kt = (int)kt_end(min(qt0 + 3, nqt - 1));
+  const int n_kt = (int)kt_end(min(qt0 + 3, nqt - 1));  // (nondecreasing in qt)
   const long long qt_w = qt0 + (wave_s >> 1);  // this wave's query tile (both 32-row blocks; head dims 64 (wave % 2) ..)
   const int n_kt_w = qt_w < nqt ? (int)kt_end(qt_w) : 0;
   const uint16_t* kbase = DENSE ? a.k + (bz * a.Hkv + kvh) * Nk * D : a.k + bz * a.ks[0] + kvh * a.ks[1];
@@ -977,9 +984,11 @@ __global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long long qt = min(qt0 + j, nqt - 1);
-      const long long kb = min((long long)kt, kt_end(qt) - 1);
+      // (a tile whose row ends before kt, or that sees no key at all, loads a
+      // block of its row that it then ignores)
+      const long long kb = max(0LL, min((long long)kt, kt_end(qt) - 1));
       const unsigned char* src = reinterpret_cast<const unsigned char*>(
-          dsh + (bwd_ds_row_start(qt, a.causal, nkt2) + kb) * kDsBlockElems);
+          dsh + (bwd_ds_row_start(qt, row_causal, nkt2) + kb) * kDsBlockElems);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + s_goff),
                                        reinterpret_cast<__attribute__((address_space(3))) void*>(
                                            reinterpret_cast<uintptr_t>(buf + T::BYTES + j * S::BYTES) + wave_s * 1024),
@@ -1003,7 +1012,7 @@ __global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) soff[qb] = lds0 + T::BYTES + (wave >> 1) * S::BYTES + S::tr_off(lane, qb);
 
-  issue(0, 0);
+  if (n_kt > 0) issue(0, 0);
   if (n_kt > 1) issue(1, 1);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int st = kt % 3;
@@ -1064,9 +1073,14 @@ __global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, 
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d = ((wave & 1) * HB + db) * 32 + 8 * jj + 4 * grp;
-          *reinterpret_cast<u32x2*>(a.dq + obf + d) =
-              pack_bf16x4_bits(acc[qb][db][4 * jj] * a.scale, acc[qb][db][4 * jj + 1] * a.scale,
-                               acc[qb][db][4 * jj + 2] * a.scale, acc[qb][db][4 * jj + 3] * a.scale);
+          f32x4 gq = {acc[qb][db][4 * jj] * a.scale, acc[qb][db][4 * jj + 1] * a.scale,
+                      acc[qb][db][4 * jj + 2] * a.scale, acc[qb][db][4 * jj + 3] * a.scale};
+          if (a.dq_mode != 0) {  // fp32 accumulator (contiguous): overwritten, or added to
+            f32x4* pa = reinterpret_cast<f32x4*>(a.dq_acc + ((bz * a.Hq + h) * Nq + qrow) * D + d);
+            if (a.dq_mode == 2) gq += *pa;
+            *pa = gq;
+          }
+          if (a.dq) *reinterpret_cast<u32x2*>(a.dq + obf + d) = pack_bf16x4_bits(gq[0], gq[1], gq[2], gq[3]);
         }
     }
   }

@@ -178,6 +178,9 @@ struct BwdArgs {
   // dQ = scale dS K from them; null: the dQ pass recomputes S and dP
   uint16_t* ds = nullptr;
   long long ds_head = 0;
+  // 1: every query tile's row of blocks has the same length (nkt2; block
+  // calls, whose offsets make the compact causal rows irregular)
+  int ds_uniform = 0;
 };
 
 // Stored dS: per (batch, query head), dS^T in blocks of 64 keys x 64 query
@@ -218,6 +221,12 @@ long long bwd_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk
 long long bwd_ds_head_elems(long long N, int causal);
 long long bwd_ds_offset_bytes(int B, int Hq, int Hkv, long long N, int D);
 long long bwd_ds_workspace_bytes(int B, int Hq, int Hkv, long long N, int D, int causal);
+// A block call's workspace with room for stored dS: its grouped-query
+// partials padded to 256 bytes, then uniform rows (nqt x nkt2 blocks per
+// batch and query head); 0 below 256 dK/dV workgroups.
+long long bwd_block_ds_head_elems(long long Nq, long long Nk);
+long long bwd_block_ds_offset_bytes(int B, int Hq, int Hkv, long long Nk, int D);
+long long bwd_block_ds_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D);
 
 // allow_side: a problem whose dK/dV grid has fewer than two workgroups per
 // compute unit runs its dQ pass on the library's side stream of the device

@@ -78,6 +78,19 @@ long long bwd_ds_workspace_bytes(int B, int Hq, int Hkv, long long N, int D, int
   return bwd_ds_offset_bytes(B, Hq, Hkv, N, D) + 2LL * B * Hq * bwd_ds_head_elems(N, causal);
 }
 
+long long bwd_block_ds_head_elems(long long Nq, long long Nk) {
+  return (Nq + 63) / 64 * ((Nk + 127) / 128 * 2) * kDsBlockElems;
+}
+
+long long bwd_block_ds_offset_bytes(int B, int Hq, int Hkv, long long Nk, int D) {
+  return (bwd_part_floats(B, Hq, Hkv, Nk, D) * 4 + 255) / 256 * 256;
+}
+
+long long bwd_block_ds_workspace_bytes(int B, int Hq, int Hkv, long long Nq, long long Nk, int D) {
+  if ((long long)B * Hq * ((Nk + 127) / 128) < 256) return 0;
+  return bwd_block_ds_offset_bytes(B, Hq, Hkv, Nk, D) + 2LL * B * Hq * bwd_block_ds_head_elems(Nq, Nk);
+}
+
 int fwd_split_count(int B, int Hq, int Hkv, long long Nq, long long Nk, int causal, int n_splits) {
   if (n_splits > 0) return n_splits;
   const int G = Hq / Hkv;

@@ -284,6 +284,22 @@ def test_bwd_ds_workspace_size(L):
     assert L.attn_bwd_ds_workspace_size(1, 8, 8, 65536, 96, 1) == 0
 
 
+def test_bwd_block_ds_workspace_size(L):
+    # grouped heads: the per-query-head dK, dV partials (2 B Hq Nk D floats),
+    # padded to 256 bytes, then ceil(Nq / 64) rows of 2 ceil(Nk / 128)
+    # blocks of 64 x 64 bf16 per batch and query head
+    part = 2 * 2 * 16 * 1100 * 128 * 4
+    assert part % 256 == 0
+    assert L.attn_bwd_block_ds_workspace_size(2, 16, 4, 3000, 1100, 128) == part + 2 * 16 * 47 * 18 * 8192
+    # no grouped heads: no partials
+    assert L.attn_bwd_block_ds_workspace_size(1, 32, 32, 648, 1024, 64) == 32 * 11 * 16 * 8192
+    # fewer than 256 dK/dV workgroups, bad sizes
+    assert L.attn_bwd_block_ds_workspace_size(2, 16, 4, 3000, 700, 128) == 0
+    assert L.attn_bwd_block_ds_workspace_size(2, 16, 3, 3000, 1100, 128) == 0
+    assert L.attn_bwd_block_ds_workspace_size(2, 16, 4, 0, 1100, 128) == 0
+    assert L.attn_bwd_block_ds_workspace_size(2, 16, 4, 3000, 1100, 96) == 0
+
+
 def test_bwd_ds_workspace_selects_path(L):
     """A workspace between the two sizes is accepted (recomputing path); one
     below the minimum is refused."""

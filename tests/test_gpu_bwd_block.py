@@ -125,9 +125,15 @@ def test_single_block_is_attn_bwd_bit_for_bit(gpu, G):
     o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
     dq0, dk0, dv0 = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s, stored_ds=False)
     delta = lc.attn_bwd_delta(o, do)
-    dq1, dk1, dv1 = lc.attn_bwd_block(q, k, v, do, lse, delta, causal=True, scale=s)
+    dq1, dk1, dv1 = lc.attn_bwd_block(q, k, v, do, lse, delta, causal=True, scale=s, stored_ds=False)
     torch.cuda.synchronize()
     for a, b in ((dq0, dq1), (dk0, dk1), (dv0, dv1)):
+        assert np.array_equal(bits_of(a), bits_of(b))
+    # with room for the stored dS both calls take the product pass: the same bits again
+    dq2, dk2, dv2 = lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s, stored_ds=True)
+    dq3, dk3, dv3 = lc.attn_bwd_block(q, k, v, do, lse, delta, causal=True, scale=s, stored_ds=True)
+    torch.cuda.synchronize()
+    for a, b in ((dq2, dq3), (dk2, dk3), (dv2, dv3), (dk0, dk2), (dv0, dv2)):
         assert np.array_equal(bits_of(a), bits_of(b))
 
 

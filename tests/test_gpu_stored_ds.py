@@ -115,3 +115,84 @@ def test_stored_ds_repeat_is_deterministic(gpu):
     torch.cuda.synchronize()
     for a, b, n in zip(first, second, ("dq", "dk", "dv")):
         assert np.array_equal(a, bits_of(b)), n
+
+
+def test_stored_ds_block_ring(gpu):
+    """attn_bwd_block over three uneven KV blocks (fp32 dQ accumulated, a bf16
+    copy on the last block; bf16 dK, dV per block).  The two larger blocks
+    have the stored-dS path (B * Hq * ceil(Nk / 128) >= 256), the last not.
+    Against the oracle's full backward, and dK, dV the same bits as the same
+    ring with the recomputing pass."""
+    import torch
+    B, Hq, Hkv, N, D = 2, 16, 4, 3000, 128
+    cuts = [0, 1100, 2300, 3000]
+    assert lc.attn_bwd_block_ds_workspace_size(B, Hq, Hkv, N, 1100, D) > 0
+    assert lc.attn_bwd_block_ds_workspace_size(B, Hq, Hkv, N, 700, D) == 0
+    d = make_qkv(B, Hq, Hkv, N, D, seed=9400, with_do=True)
+    s = sdpa_scale(D)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
+    delta = lc.attn_bwd_delta(o, do)
+    res = {}
+    for stored in (True, False):
+        dq_acc = poisoned((B, Hq, N, D), torch.float32)
+        dq = poisoned((B, Hq, N, D), torch.bfloat16)
+        dks, dvs = [], []
+        for i, (c, e) in enumerate(zip(cuts[:-1], cuts[1:])):
+            kb, vb = k[:, :, c:e].contiguous(), v[:, :, c:e].contiguous()
+            dk = poisoned(tuple(kb.shape), torch.bfloat16)
+            dv = poisoned(tuple(vb.shape), torch.bfloat16)
+            lc.attn_bwd_block(q, kb, vb, do, lse, delta, causal=True, scale=s, k_pos0=c, dq_acc=dq_acc,
+                              dq_accumulate=i > 0, dq=dq if i == len(cuts) - 2 else None, dk=dk, dv=dv,
+                              stored_ds=stored)
+            dks.append(dk)
+            dvs.append(dv)
+        torch.cuda.synchronize()
+        res[stored] = (dq, torch.cat(dks, dim=2), torch.cat(dvs, dim=2), dq_acc)
+    for i, n in ((1, "dk"), (2, "dv")):
+        assert np.array_equal(bits_of(res[True][i]), bits_of(res[False][i])), n
+    assert np.array_equal(bits_of(res[True][0]), bits_of(res[True][3].to(torch.bfloat16))), "bf16 copy of dq_acc"
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, True)
+    for stored in (True, False):
+        for name, g, r in (("dq", res[stored][0], dQ), ("dk", res[stored][1], dK), ("dv", res[stored][2], dV)):
+            e = grad_rel_err(f64_of(g), r)
+            assert e <= GRAD_REL_TOL, f"stored={stored} {name} relative error {e}"
+
+
+def test_stored_ds_block_query_shard(gpu):
+    """A query shard at global rows 1400..2047 against KV blocks before, across
+    and after it (q_pos0 != k_pos0: irregular causal rows, query tiles that
+    see no key of a block, a block that no query sees), with the stored-dS
+    path, fp32 dQ overwritten then added to: against
+    oracle.attention_backward_block for each block."""
+    import torch
+    B, Hq, Hkv, N, D = 1, 32, 8, 3072, 64
+    q0, q1 = 1400, 2048
+    d = make_qkv(B, Hq, Hkv, N, D, seed=9500, with_do=True)
+    s = sdpa_scale(D)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
+    delta = lc.attn_bwd_delta(o, do)
+    qs, dos = q[:, :, q0:q1].contiguous(), do[:, :, q0:q1].contiguous()
+    lses, deltas = lse[:, :, q0:q1].contiguous(), delta[:, :, q0:q1].contiguous()
+    q_np, do_np = d["q"][:, :, q0:q1], d["do"][:, :, q0:q1]
+    lse_np, delta_np = f64_of(lses), f64_of(deltas)
+    blocks = [(0, 1024), (1024, 2048), (2048, 3072)]
+    dq_acc = poisoned(tuple(qs.shape), torch.float32)
+    want_dq = 0.0
+    for i, (c, e) in enumerate(blocks):
+        assert lc.attn_bwd_block_ds_workspace_size(B, Hq, Hkv, q1 - q0, e - c, D) > 0
+        kb, vb = k[:, :, c:e].contiguous(), v[:, :, c:e].contiguous()
+        dk = poisoned(tuple(kb.shape), torch.bfloat16)
+        dv = poisoned(tuple(vb.shape), torch.bfloat16)
+        lc.attn_bwd_block(qs, kb, vb, dos, lses, deltas, causal=True, scale=s, q_pos0=q0, k_pos0=c, dq_acc=dq_acc,
+                          dq_accumulate=i > 0, dk=dk, dv=dv, stored_ds=True)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.attention_backward_block(q_np, d["k"][:, :, c:e], d["v"][:, :, c:e], do_np, lse_np,
+                                                     delta_np, s, True, q0, c)
+        want_dq = want_dq + rq
+        for name, g, r in (("dk", dk, rk), ("dv", dv, rv)):
+            e_ = grad_rel_err(f64_of(g), r)
+            assert e_ <= GRAD_REL_TOL, f"block {i} {name} relative error {e_}"
+        e_ = grad_rel_err(f64_of(dq_acc), want_dq)
+        assert e_ <= GRAD_REL_TOL, f"dq after block {i}: relative error {e_}"
