@@ -117,21 +117,22 @@ def test_stored_ds_repeat_is_deterministic(gpu):
         assert np.array_equal(a, bits_of(b)), n
 
 
-def test_stored_ds_block_ring(gpu):
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_stored_ds_block_ring(gpu, D, causal):
     """attn_bwd_block over three uneven KV blocks (fp32 dQ accumulated, a bf16
     copy on the last block; bf16 dK, dV per block).  The two larger blocks
     have the stored-dS path (B * Hq * ceil(Nk / 128) >= 256), the last not.
     Against the oracle's full backward, and dK, dV the same bits as the same
     ring with the recomputing pass."""
     import torch
-    B, Hq, Hkv, N, D = 2, 16, 4, 3000, 128
+    B, Hq, Hkv, N = 2, 16, 4, 3000
     cuts = [0, 1100, 2300, 3000]
     assert lc.attn_bwd_block_ds_workspace_size(B, Hq, Hkv, N, 1100, D) > 0
     assert lc.attn_bwd_block_ds_workspace_size(B, Hq, Hkv, N, 700, D) == 0
-    d = make_qkv(B, Hq, Hkv, N, D, seed=9400, with_do=True)
+    d = make_qkv(B, Hq, Hkv, N, D, seed=9400 + D, with_do=True)
     s = sdpa_scale(D)
     q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
-    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
+    o, lse = lc.attn_fwd(q, k, v, causal=causal, scale=s)
     delta = lc.attn_bwd_delta(o, do)
     res = {}
     for stored in (True, False):
@@ -142,7 +143,7 @@ def test_stored_ds_block_ring(gpu):
             kb, vb = k[:, :, c:e].contiguous(), v[:, :, c:e].contiguous()
             dk = poisoned(tuple(kb.shape), torch.bfloat16)
             dv = poisoned(tuple(vb.shape), torch.bfloat16)
-            lc.attn_bwd_block(q, kb, vb, do, lse, delta, causal=True, scale=s, k_pos0=c, dq_acc=dq_acc,
+            lc.attn_bwd_block(q, kb, vb, do, lse, delta, causal=causal, scale=s, k_pos0=c, dq_acc=dq_acc,
                               dq_accumulate=i > 0, dq=dq if i == len(cuts) - 2 else None, dk=dk, dv=dv,
                               stored_ds=stored)
             dks.append(dk)
@@ -152,7 +153,7 @@ def test_stored_ds_block_ring(gpu):
     for i, n in ((1, "dk"), (2, "dv")):
         assert np.array_equal(bits_of(res[True][i]), bits_of(res[False][i])), n
     assert np.array_equal(bits_of(res[True][0]), bits_of(res[True][3].to(torch.bfloat16))), "bf16 copy of dq_acc"
-    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, True)
+    _, _, dQ, dK, dV = oracle.attention_backward(d["q"], d["k"], d["v"], d["do"], s, causal)
     for stored in (True, False):
         for name, g, r in (("dq", res[stored][0], dQ), ("dk", res[stored][1], dK), ("dv", res[stored][2], dV)):
             e = grad_rel_err(f64_of(g), r)
