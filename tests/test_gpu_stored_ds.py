@@ -197,3 +197,42 @@ def test_stored_ds_block_query_shard(gpu):
             assert e_ <= GRAD_REL_TOL, f"block {i} {name} relative error {e_}"
         e_ = grad_rel_err(f64_of(dq_acc), want_dq)
         assert e_ <= GRAD_REL_TOL, f"dq after block {i}: relative error {e_}"
+
+
+def test_stored_ds_graph_replays(gpu):
+    """attn_bwd with the stored-dS workspace captured into a HIP graph and
+    replayed three times, with eager library calls on other inputs in
+    between: every replay equals the eager result bit for bit."""
+    import torch
+    B, Hq, Hkv, N, D = 1, 8, 8, 4096, 128
+    big = lc.attn_bwd_ds_workspace_size(B, Hq, Hkv, N, D, True)
+    assert big > 0
+    d = make_qkv(B, Hq, Hkv, N, D, seed=9600, with_do=True)
+    s = sdpa_scale(D)
+    q, k, v, do = (to_dev(d[n]) for n in ("q", "k", "v", "do"))
+    o, lse = lc.attn_fwd(q, k, v, causal=True, scale=s)
+    ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        lc.attn_bwd(q, k, v, o, do, lse, causal=True, scale=s, workspace=ws, dq=dq, dk=dk, dv=dv)
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dq, dk, dv)]
+    other = make_qkv(B, Hq, Hkv, N, D, seed=9601, with_do=True)
+    oq, ok_, ov, odo = (to_dev(other[n]) for n in ("q", "k", "v", "do"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    for _ in range(3):
+        for x in (dq, dk, dv):
+            x.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for r, x in zip(ref, (dq, dk, dv)):
+            assert torch.equal(r.view(torch.int16), x.view(torch.int16))
+        oo, ol = lc.attn_fwd(oq, ok_, ov, scale=s)
+        lc.attn_bwd(oq, ok_, ov, oo, odo, ol, scale=s, stored_ds=True)
+        torch.cuda.synchronize()
