@@ -203,8 +203,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   // key group (kg % 2), then the (32-row block, 16-row half) of the query
   // tile, then the lane, 16 bytes each -- every store writes 1 KiB in one
   // piece (the product pass's loads put the units back in rows).  Keys past
-  // Nk store what their unmasked scores give (without the causal mask); the
-  // product pass masks them.
+  // Nk store what their scores give (the pass does not mask them; they are
+  // visible without the causal mask, and with it to queries positioned past
+  // the keys); the product pass masks them.
   long long ds_wave = 0;  // elements from a.ds to the wave's block of query tile 0's row
   unsigned ds_lane = 0;
   long long ds_nkt2 = 0;
@@ -1037,7 +1038,12 @@ __global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, 
         for (int db = 0; db < HB; ++db) fa[ks][db] = tr_frag_asm_at<T::ROW_BYTES>(koff[db] + sh, ks * 16 * T::ROW_BYTES);
       lds_wait_frags(fb[0][0], fb[0][1], fb[1][0], fb[1][1]);
       lds_wait_frags(fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
-      if (!a.causal && kt == nkt - 1) {
+      if (kt == nkt - 1 && (Nk & 63)) {
+        // keys past Nk in the last tile: the dK/dV pass does not mask them
+        // (their scores come from zero K rows and are visible wherever the
+        // positions allow: always without the causal mask, and with it when
+        // the queries lie past the keys), and their K rows here repeat row
+        // Nk - 1
         const int lim = (int)(Nk - (long long)kt * 64);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)

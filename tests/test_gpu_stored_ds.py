@@ -236,3 +236,32 @@ def test_stored_ds_graph_replays(gpu):
         oo, ol = lc.attn_fwd(oq, ok_, ov, scale=s)
         lc.attn_bwd(oq, ok_, ov, oo, odo, ol, scale=s, stored_ds=True)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_stored_ds_block_ragged_tail_visible(gpu, causal):
+    """A 70-key block (the last 64-key tile ragged) whose queries lie past
+    it (q_pos0 - k_pos0 = 500): by position every padding key of the tile is
+    visible, so their stored dS must be masked by the product pass.  LSE
+    over this block only, so a padding key's weight would be about 1/70 of
+    a row: an unmasked one shows far above the gate.  Against
+    oracle.attention_backward_block."""
+    B, Hq, Hkv, Nq, Nk, D = 4, 64, 16, 256, 70, 64
+    q_pos0, k_pos0 = 1000, 500
+    assert lc.attn_bwd_block_ds_workspace_size(B, Hq, Hkv, Nq, Nk, D) > 0
+    dq_in = make_qkv(B, Hq, Hkv, Nq, D, seed=9700, with_do=True)
+    dk_in = make_qkv(B, Hq, Hkv, Nk, D, seed=9701)
+    s = sdpa_scale(D)
+    q, do = to_dev(dq_in["q"]), to_dev(dq_in["do"])
+    k, v = to_dev(dk_in["k"]), to_dev(dk_in["v"])
+    o, lse = lc.attn_fwd(q, k, v, causal=causal, scale=s, q_pos0=q_pos0, k_pos0=k_pos0)
+    delta = lc.attn_bwd_delta(o, do)
+    dq, dk, dv = lc.attn_bwd_block(q, k, v, do, lse, delta, causal=causal, scale=s, q_pos0=q_pos0, k_pos0=k_pos0,
+                                   stored_ds=True)
+    import torch
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward_block(dq_in["q"], dk_in["k"], dk_in["v"], dq_in["do"], f64_of(lse),
+                                                 f64_of(delta), s, causal, q_pos0, k_pos0)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        e = grad_rel_err(f64_of(g), r)
+        assert e <= GRAD_REL_TOL, f"{name} relative error {e}"
