@@ -1027,44 +1027,48 @@ __global__ __launch_bounds__(64 * kDsWaves, 1) void bwd_dq_ds_kernel(BwdArgs a, 
     if (kt + 2 < n_kt) issue(kt + 2, (kt + 2) % 3);
     if (kt < n_kt_w) {
       const unsigned sh = (unsigned)(st * STAGE);
+      // keys past Nk in the last tile: the dK/dV pass does not mask them
+      // (their scores come from zero K rows and are visible wherever the
+      // positions allow: always without the causal mask, and with it when
+      // the queries lie past the keys), and their K rows here repeat row
+      // Nk - 1
+      const bool tail = kt == nkt - 1 && (Nk & 63);
+      const int lim = (int)(Nk - (long long)kt * 64);
+      constexpr int NR = 4 + 2 * HB;  // LDS reads per reduction step
       u32x4 fb[4][2], fa[4][HB];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 5; ++ks) {
+        if (ks < 4) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) fb[ks][qb] = tr_frag_asm_at<S::ROW_BYTES>(soff[qb] + sh, ks * 16 * S::ROW_BYTES);
+          for (int qb = 0; qb < 2; ++qb) fb[ks][qb] = tr_frag_asm_at<S::ROW_BYTES>(soff[qb] + sh, ks * 16 * S::ROW_BYTES);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < HB; ++db) fa[ks][db] = tr_frag_asm_at<T::ROW_BYTES>(koff[db] + sh, ks * 16 * T::ROW_BYTES);
-      lds_wait_frags(fb[0][0], fb[0][1], fb[1][0], fb[1][1]);
-      lds_wait_frags(fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
-      if (kt == nkt - 1 && (Nk & 63)) {
-        // keys past Nk in the last tile: the dK/dV pass does not mask them
-        // (their scores come from zero K rows and are visible wherever the
-        // positions allow: always without the causal mask, and with it when
-        // the queries lie past the keys), and their K rows here repeat row
-        // Nk - 1
-        const int lim = (int)(Nk - (long long)kt * 64);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+          for (int db = 0; db < HB; ++db) fa[ks][db] = tr_frag_asm_at<T::ROW_BYTES>(koff[db] + sh, ks * 16 * T::ROW_BYTES);
+        }
+        const int m = ks - 1;  // step multiplied after this one's reads are issued
+        if (m < 0) continue;
+        // reads complete in issue order: step m has landed once only the
+        // reads of step m + 1 (if issued) are outstanding
+        if constexpr (HB == 2) {
+          if (m < 3) lds_wait_frags_n<NR>(fb[m][0], fb[m][1], fa[m][0], fa[m][1]);
+          else lds_wait_frags_n<0>(fb[m][0], fb[m][1], fa[m][0], fa[m][1]);
+        } else {
+          if (m < 3) lds_wait_frags_n<NR>(fb[m][0], fb[m][1], fa[m][0]);
+          else lds_wait_frags_n<0>(fb[m][0], fb[m][1], fa[m][0]);
+        }
+        if (tail) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-              const int k0 = 16 * ks + 8 * grp + 2 * w;
-              fb[ks][qb][w] &= (k0 < lim ? 0x0000FFFFu : 0u) | (k0 + 1 < lim ? 0xFFFF0000u : 0u);
+              const int k0 = 16 * m + 8 * grp + 2 * w;  // keys k0 (low half), k0 + 1 (high half)
+              fb[m][qb][w] &= (k0 < lim ? 0x0000FFFFu : 0u) | (k0 + 1 < lim ? 0xFFFF0000u : 0u);
             }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if constexpr (HB == 2) {
-          lds_wait_frags2(fa[ks][0], fa[ks][1]);
         }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int db = 0; db < HB; ++db)
-            acc[qb][db] = mfma32x32x16(as_bf16x8(fa[ks][db]), as_bf16x8(fb[ks][qb]), acc[qb][db]);
+            acc[qb][db] = mfma32x32x16(as_bf16x8(fa[m][db]), as_bf16x8(fb[m][qb]), acc[qb][db]);
       }
     }
   }

@@ -287,11 +287,20 @@ __device__ __forceinline__ void lds_wait_frags(u32x4& a, u32x4& b, u32x4& c, u32
 
 // Wait until at most N of this wave's LDS operations are outstanding.  LDS
 // operations complete in issue order, so every read issued before the last N
-// has landed (scalar memory operations only add to the count).
+// has landed (scalar memory operations only add to the count).  The statement
+// is volatile so that it keeps its place after the reads issued before it in
+// the source (the reads are volatile too): moved above some of them, it would
+// count fewer reads in flight and return too early.
 template <int N>
 __device__ __forceinline__ void lds_wait_frags_n(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
   static_assert(N >= 0 && N < 16, "lgkmcnt holds 4 bits");
-  asm("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_frags_n(u32x4& a, u32x4& b, u32x4& c) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt holds 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "i"(N));
 }
 
 // The same for two fragments.  Every operand must be a distinct variable: an
