@@ -913,7 +913,7 @@ def cpu_baseline():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share only: this build runs no collectives, so --gpus must be 1",
+        print("bench.py measures one GPU's share only: the library runs no collectives, so --gpus must be 1",
               file=sys.stderr)
         sys.exit(2)
 
