@@ -55,23 +55,32 @@ def pair_flops_block(Hq, D, N, a, b):
     return 4.0 * Hq * D * pairs
 
 
-KERNEL_SOURCES = {"bwd_dkdv_kernel": "attn_bwd.hip", "bwd_dq_kernel": "attn_bwd.hip", "bwd_dq_ds_kernel": "attn_bwd.hip",
+# (the dK/dV kernel's dense stored-dS instances are compiled from attn_bwd.hip
+# in the unit attn_bwd_ds.hip, with that unit's flags)
+KERNEL_SOURCES = {"bwd_dkdv_kernel": ("attn_bwd.hip", "attn_bwd_ds.hip"), "bwd_dq_kernel": "attn_bwd.hip", "bwd_dq_ds_kernel": "attn_bwd.hip",
                   "bwd_delta_kernel": "attn_bwd.hip", "bwd_dkdv_reduce_kernel": "attn_bwd.hip",
                   "attn_fwd_kernel": "attn_fwd.hip", "attn_fwd_kernel_fp32out": "attn_fwd.hip",
                   "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}
 
 
 def kernel_source_digest(name):
-    """sha256 of the sources a kernel is compiled from (to tell whether
-    committed counter figures still describe it)."""
+    """sha256 of the sources a kernel is compiled from and of that file's
+    own compiler flags (to tell whether committed counter figures still
+    describe it)."""
+    from long_context_attention_fwd_amd.build import PER_FILE
     f = KERNEL_SOURCES.get(name)
     if f is None:
         return None
+    files = f if isinstance(f, tuple) else (f,)
     csrc = os.path.join(ROOT, "long_context_attention_fwd_amd", "csrc")
     h = hashlib.sha256()
-    for fn in (f, "device_common.hpp"):
+    for fn in (*files, "device_common.hpp"):
         with open(os.path.join(csrc, fn), "rb") as fh:
             h.update(fh.read())
+    for fn in files:
+        flags = PER_FILE.get(fn)
+        if flags:
+            h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 

@@ -512,11 +512,27 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
   }
 }
 
+}  // namespace
+
+// The dK/dV kernel has external linkage: its instances that store dS at
+// D = 128 for contiguous tensors are compiled in a unit of their own
+// (attn_bwd_ds.hip, the same source with another instruction-scheduling
+// strategy) and only launched from here.
 template <int D, bool PARTIAL, bool DENSE, bool DS>
 __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
                                                                              float* __restrict__ dv_part) {
   bwd_dkdv_body<D, PARTIAL, DENSE, DS>(a, dk_part, dv_part, wg_number(), gridDim.x, gridDim.y);
 }
+
+#ifdef LCATTN_BWD_DKDV_DS_UNIT
+template __global__ void bwd_dkdv_split_kernel<128, false, true, true>(BwdArgs, float*, float*);
+template __global__ void bwd_dkdv_split_kernel<128, true, true, true>(BwdArgs, float*, float*);
+}  // namespace lcattn
+#else
+extern template __global__ void bwd_dkdv_split_kernel<128, false, true, true>(BwdArgs, float*, float*);
+extern template __global__ void bwd_dkdv_split_kernel<128, true, true, true>(BwdArgs, float*, float*);
+
+namespace {
 
 // Independent block-backward calls in one launch (a ring step's calls that
 // share neither a query chunk nor a key/value chunk): grid z = call * B +
@@ -1433,3 +1449,4 @@ hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta
 }
 
 }  // namespace lcattn
+#endif  // LCATTN_BWD_DKDV_DS_UNIT
