@@ -55,9 +55,11 @@ def pair_flops_block(Hq, D, N, a, b):
     return 4.0 * Hq * D * pairs
 
 
-# (the dK/dV kernel's dense stored-dS instances are compiled from attn_bwd.hip
-# in the unit attn_bwd_ds.hip, with that unit's flags)
-KERNEL_SOURCES = {"bwd_dkdv_kernel": ("attn_bwd.hip", "attn_bwd_ds.hip"), "bwd_dq_kernel": "attn_bwd.hip", "bwd_dq_ds_kernel": "attn_bwd.hip",
+# (the dK/dV kernel's dense D = 128 instances are compiled from attn_bwd.hip
+# in the units attn_bwd_ds.hip and attn_bwd_dkdv_recompute.hip, with their
+# flags)
+KERNEL_SOURCES = {"bwd_dkdv_kernel": ("attn_bwd.hip", "attn_bwd_ds.hip", "attn_bwd_dkdv_recompute.hip"),
+                  "bwd_dq_kernel": "attn_bwd.hip", "bwd_dq_ds_kernel": "attn_bwd.hip",
                   "bwd_delta_kernel": "attn_bwd.hip", "bwd_dkdv_reduce_kernel": "attn_bwd.hip",
                   "attn_fwd_kernel": "attn_fwd.hip", "attn_fwd_kernel_fp32out": "attn_fwd.hip",
                   "transpose_rows_kernel": "relayout.hip", "merge_kernel": "merge.hip"}

@@ -514,23 +514,30 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, float* __restric
 
 }  // namespace
 
-// The dK/dV kernel has external linkage: its instances that store dS at
-// D = 128 for contiguous tensors are compiled in a unit of their own
-// (attn_bwd_ds.hip, the same source with another instruction-scheduling
-// strategy) and only launched from here.
+// The dK/dV kernel has external linkage: its D = 128 instances for
+// contiguous tensors are compiled in units of their own, the same source with
+// another instruction-scheduling strategy (attn_bwd_ds.hip: the instances
+// that store dS; attn_bwd_dkdv_recompute.hip: those of the recomputing path),
+// and only launched from here.
 template <int D, bool PARTIAL, bool DENSE, bool DS>
 __global__ __launch_bounds__(64 * kSplitWaves, 1) void bwd_dkdv_split_kernel(BwdArgs a, float* __restrict__ dk_part,
                                                                              float* __restrict__ dv_part) {
   bwd_dkdv_body<D, PARTIAL, DENSE, DS>(a, dk_part, dv_part, wg_number(), gridDim.x, gridDim.y);
 }
 
-#ifdef LCATTN_BWD_DKDV_DS_UNIT
+#if defined(LCATTN_BWD_DKDV_UNIT) && LCATTN_BWD_DKDV_UNIT == 1
 template __global__ void bwd_dkdv_split_kernel<128, false, true, true>(BwdArgs, float*, float*);
 template __global__ void bwd_dkdv_split_kernel<128, true, true, true>(BwdArgs, float*, float*);
+}  // namespace lcattn
+#elif defined(LCATTN_BWD_DKDV_UNIT) && LCATTN_BWD_DKDV_UNIT == 2
+template __global__ void bwd_dkdv_split_kernel<128, false, true, false>(BwdArgs, float*, float*);
+template __global__ void bwd_dkdv_split_kernel<128, true, true, false>(BwdArgs, float*, float*);
 }  // namespace lcattn
 #else
 extern template __global__ void bwd_dkdv_split_kernel<128, false, true, true>(BwdArgs, float*, float*);
 extern template __global__ void bwd_dkdv_split_kernel<128, true, true, true>(BwdArgs, float*, float*);
+extern template __global__ void bwd_dkdv_split_kernel<128, false, true, false>(BwdArgs, float*, float*);
+extern template __global__ void bwd_dkdv_split_kernel<128, true, true, false>(BwdArgs, float*, float*);
 
 namespace {
 
@@ -1449,4 +1456,4 @@ hipError_t launch_bwd_delta(const uint16_t* o, const uint16_t* d_o, float* delta
 }
 
 }  // namespace lcattn
-#endif  // LCATTN_BWD_DKDV_DS_UNIT
+#endif  // LCATTN_BWD_DKDV_UNIT
